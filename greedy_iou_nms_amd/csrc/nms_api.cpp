@@ -1,0 +1,347 @@
+// Host side of libgreedy_nms: argument checks, workspace carve-up, stage
+// launches on the caller's stream, and the single device-to-host read-back
+// of {error bits, flags, kept count} that ends every call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "../../include/greedy_nms.h"
+#include "nms_internal.h"
+
+namespace gnms {
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool make_layout(int64_t n, Layout *out) {
+    Layout L;
+    L.n = n;
+    L.words = (n + 63) / 64;
+    L.npad = 64 * L.words;
+    // worst-case row stride over both strip widths (a multiple of 16 words)
+    L.mstride = ((L.words + STRIP_SINGLE - 1) / STRIP_SINGLE) * STRIP_SINGLE;
+    const size_t np = (size_t)L.npad;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    L.off_ctrl = take(sizeof(Ctrl));
+    L.off_keys0 = take(np * 4);
+    L.off_keys1 = take(np * 4);
+    L.off_vals0 = take(np * 4);
+    L.off_vals1 = take(np * 4);
+    L.off_order = take(np * 4);
+    L.off_score_order = take(np * 4);
+    L.off_seg = take(np * 4);
+    L.off_inv = take(np * 4);
+    L.off_sb = take(np * 16);
+    L.off_area = take(np * 4);
+    L.off_tile_cend = take((size_t)L.words * 4 + 4);
+    L.off_item_base = take((size_t)L.words * 4 + 4);
+    L.off_kept = take((size_t)L.words * 8 + 8);
+    L.off_mask = take((size_t)n * (size_t)L.mstride * 8);
+    L.total = off;
+    *out = L;
+    return true;
+}
+
+Work carve(void *workspace, const Layout &L) {
+    char *b = static_cast<char *>(workspace);
+    Work w;
+    w.ctrl = reinterpret_cast<Ctrl *>(b + L.off_ctrl);
+    w.keys0 = reinterpret_cast<uint32_t *>(b + L.off_keys0);
+    w.keys1 = reinterpret_cast<uint32_t *>(b + L.off_keys1);
+    w.vals0 = reinterpret_cast<uint32_t *>(b + L.off_vals0);
+    w.vals1 = reinterpret_cast<uint32_t *>(b + L.off_vals1);
+    w.order = reinterpret_cast<int32_t *>(b + L.off_order);
+    w.score_order = reinterpret_cast<int32_t *>(b + L.off_score_order);
+    w.seg = reinterpret_cast<uint32_t *>(b + L.off_seg);
+    w.inv = reinterpret_cast<int32_t *>(b + L.off_inv);
+    w.sb = reinterpret_cast<float4 *>(b + L.off_sb);
+    w.area = reinterpret_cast<float *>(b + L.off_area);
+    w.tile_cend = reinterpret_cast<int32_t *>(b + L.off_tile_cend);
+    w.item_base = reinterpret_cast<int32_t *>(b + L.off_item_base);
+    w.kept = reinterpret_cast<uint64_t *>(b + L.off_kept);
+    w.mask = reinterpret_cast<uint64_t *>(b + L.off_mask);
+    return w;
+}
+
+namespace {
+
+struct Readback {
+    uint32_t error;
+    uint32_t flags;
+    int32_t count;
+    int32_t num_items;
+};
+
+// A small pinned host buffer per thread for the read-back (pageable memory
+// would force a staged copy).  It is never freed: the HIP runtime may already
+// be gone when thread-local destructors run at exit.
+Readback *pinned_readback() {
+    thread_local Readback *buf = nullptr;
+    thread_local bool tried = false;
+    if (!tried) {
+        tried = true;
+        void *p = nullptr;
+        if (hipHostMalloc(&p, sizeof(Readback), hipHostMallocDefault) == hipSuccess)
+            buf = static_cast<Readback *>(p);
+    }
+    return buf;
+}
+
+nms_status check_common(int64_t n, float thresh, const int64_t *offsets, int64_t num_images) {
+    if (n < 0 || std::isnan(thresh)) return NMS_INVALID_ARG;
+    if (offsets == nullptr && num_images > 1) return NMS_INVALID_ARG;
+    if (offsets != nullptr && num_images < 1) return NMS_INVALID_ARG;
+    if (num_images < 0 || num_images > (int64_t)0x7fffffff) return NMS_INVALID_ARG;
+    if (n > NMS_MAX_BOXES) return NMS_TOO_LARGE;
+    return NMS_OK;
+}
+
+Problem make_problem(const float *boxes, const float *scores, int64_t n, float thresh,
+                     const int32_t *class_ids, const int64_t *offsets, int64_t num_images) {
+    Problem P;
+    P.boxes = boxes;
+    P.scores = scores;
+    P.n = (int)n;
+    P.thresh = thresh;
+    P.class_ids = class_ids;
+    P.offsets = offsets;
+    P.num_images = offsets ? (int)num_images : 1;
+    P.grouped = class_ids != nullptr || offsets != nullptr;
+    P.strip = P.grouped ? STRIP_GROUPED : STRIP_SINGLE;
+    return P;
+}
+
+nms_status hip_status(hipError_t e) { return e == hipSuccess ? NMS_OK : NMS_HIP_ERROR; }
+
+// Copies the control block back (the call's only device-to-host transfer)
+// and synchronises the stream.
+nms_status read_back(const Work &w, hipStream_t stream, Readback *out) {
+    Readback *pin = pinned_readback();
+    hipError_t e;
+    if (pin) {
+        e = hipMemcpyAsync(pin, w.ctrl, sizeof(Readback), hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e == hipSuccess) *out = *pin;
+    } else {
+        e = hipMemcpyAsync(out, w.ctrl, sizeof(Readback), hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    }
+    return hip_status(e);
+}
+
+nms_status device_error(uint32_t err) {
+    if (err & ERR_BAD_OFFSETS) return NMS_BAD_OFFSETS;
+    if (err & ERR_NONFINITE) return NMS_NONFINITE_INPUT;
+    return NMS_OK;
+}
+
+struct EventSet {
+    hipEvent_t ev[NMS_NUM_STAGES + 1];
+    bool made = false;
+    bool create() {
+        for (int i = 0; i <= NMS_NUM_STAGES; ++i) {
+            if (hipEventCreate(&ev[i]) != hipSuccess) {
+                for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+                return false;
+            }
+        }
+        made = true;
+        return true;
+    }
+    ~EventSet() {
+        if (made)
+            for (int i = 0; i <= NMS_NUM_STAGES; ++i) (void)hipEventDestroy(ev[i]);
+    }
+};
+
+nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thresh,
+                   const int32_t *class_ids, const int64_t *offsets, int64_t num_images,
+                   int64_t *keep_out, int64_t *num_kept, void *workspace, size_t ws_bytes,
+                   void *stream_ptr, float *stage_ms) {
+    if (num_kept == nullptr) return NMS_INVALID_ARG;
+    *num_kept = 0;
+    if (stage_ms)
+        for (int i = 0; i < NMS_NUM_STAGES; ++i) stage_ms[i] = 0.0f;
+    nms_status st = check_common(n, thresh, offsets, num_images);
+    if (st != NMS_OK) return st;
+    if (n == 0) return NMS_OK;
+    if (!boxes || !scores || !keep_out || !workspace) return NMS_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(boxes) & 15u) != 0 ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return NMS_INVALID_ARG;
+    Layout L;
+    make_layout(n, &L);
+    if (ws_bytes < L.total) return NMS_WORKSPACE_TOO_SMALL;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    const Problem P = make_problem(boxes, scores, n, thresh, class_ids, offsets, num_images);
+    const Work w = carve(workspace, L);
+
+    EventSet events;
+    if (stage_ms && !events.create()) return NMS_HIP_ERROR;
+    auto mark = [&](int i) -> hipError_t {
+        return stage_ms ? hipEventRecord(events.ev[i], stream) : hipSuccess;
+    };
+
+    hipError_t e = mark(0);
+    if (e == hipSuccess) e = launch_sort(P, L, w, stream);
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess) e = launch_gather(P, L, w, stream);
+    if (e == hipSuccess) e = mark(2);
+    if (e == hipSuccess) e = launch_mask(P, L, w, stream);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = launch_sweep(P, L, w, keep_out, stream);
+    if (e == hipSuccess) e = mark(4);
+    if (e == hipSuccess && P.grouped) e = launch_compact(P, L, w, keep_out, stream);
+    if (e == hipSuccess) e = mark(5);
+    if (e != hipSuccess) return NMS_HIP_ERROR;
+
+    Readback rb;
+    st = read_back(w, stream, &rb);
+    if (st != NMS_OK) return st;
+    st = device_error(rb.error);
+    if (st != NMS_OK) return st;
+    if (stage_ms) {
+        for (int i = 0; i < NMS_NUM_STAGES; ++i) {
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, events.ev[i], events.ev[i + 1]) != hipSuccess)
+                return NMS_HIP_ERROR;
+            stage_ms[i] = ms;
+        }
+    }
+    *num_kept = rb.count;
+    return NMS_OK;
+}
+
+}  // namespace
+}  // namespace gnms
+
+using namespace gnms;
+
+extern "C" {
+
+nms_status nms_workspace_size(int64_t n, int64_t num_images, int has_classes, size_t *bytes) {
+    (void)num_images;
+    (void)has_classes;
+    if (bytes == nullptr || n < 0) return NMS_INVALID_ARG;
+    if (n > NMS_MAX_BOXES) return NMS_TOO_LARGE;
+    Layout L;
+    make_layout(n, &L);
+    *bytes = L.total;
+    return NMS_OK;
+}
+
+nms_status nms_f32(const float *boxes, const float *scores, int64_t n, float iou_thresh,
+                   const int32_t *class_ids, const int64_t *batch_offsets, int64_t num_images,
+                   int64_t *keep_out, int64_t *num_kept, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
+                   num_kept, workspace, workspace_bytes, stream, nullptr);
+}
+
+nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
+                            float iou_thresh, const int32_t *class_ids,
+                            const int64_t *batch_offsets, int64_t num_images,
+                            int64_t *keep_out, int64_t *num_kept, void *workspace,
+                            size_t workspace_bytes, void *stream, float *stage_ms) {
+    if (stage_ms == nullptr) return NMS_INVALID_ARG;
+    return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
+                   num_kept, workspace, workspace_bytes, stream, stage_ms);
+}
+
+const char *nms_status_string(nms_status status) {
+    switch (status) {
+        case NMS_OK: return "NMS_OK";
+        case NMS_INVALID_ARG: return "NMS_INVALID_ARG";
+        case NMS_WORKSPACE_TOO_SMALL: return "NMS_WORKSPACE_TOO_SMALL";
+        case NMS_NONFINITE_INPUT: return "NMS_NONFINITE_INPUT";
+        case NMS_BAD_OFFSETS: return "NMS_BAD_OFFSETS";
+        case NMS_TOO_LARGE: return "NMS_TOO_LARGE";
+        case NMS_HIP_ERROR: return "NMS_HIP_ERROR";
+    }
+    return "NMS_UNKNOWN_STATUS";
+}
+
+nms_status nms_debug_order(const float *scores, int64_t n, const int32_t *class_ids,
+                           const int64_t *batch_offsets, int64_t num_images,
+                           int32_t *order_out, int32_t *score_order_out, void *workspace,
+                           size_t workspace_bytes, void *stream_ptr) {
+    nms_status st = check_common(n, 0.5f, batch_offsets, num_images);
+    if (st != NMS_OK) return st;
+    if (n == 0) return NMS_OK;
+    if (!scores || !order_out || !workspace) return NMS_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return NMS_INVALID_ARG;
+    Layout L;
+    make_layout(n, &L);
+    if (workspace_bytes < L.total) return NMS_WORKSPACE_TOO_SMALL;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    const Problem P = make_problem(nullptr, scores, n, 0.5f, class_ids, batch_offsets, num_images);
+    const Work w = carve(workspace, L);
+    hipError_t e = launch_sort(P, L, w, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(order_out, w.order, (size_t)n * 4, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess && score_order_out) {
+        if (P.grouped)
+            e = hipMemcpyAsync(score_order_out, w.score_order, (size_t)n * 4,
+                               hipMemcpyDeviceToDevice, stream);
+        else
+            e = hipMemcpyAsync(score_order_out, w.order, (size_t)n * 4,
+                               hipMemcpyDeviceToDevice, stream);
+    }
+    if (e != hipSuccess) return NMS_HIP_ERROR;
+    Readback rb;
+    st = read_back(w, stream, &rb);
+    if (st != NMS_OK) return st;
+    return device_error(rb.error);
+}
+
+nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
+                          float iou_thresh, const int32_t *class_ids,
+                          const int64_t *batch_offsets, int64_t num_images,
+                          uint64_t *mask_out, int32_t *order_out, void *workspace,
+                          size_t workspace_bytes, void *stream_ptr) {
+    nms_status st = check_common(n, iou_thresh, batch_offsets, num_images);
+    if (st != NMS_OK) return st;
+    if (n == 0) return NMS_OK;
+    if (!boxes || !scores || !mask_out || !workspace) return NMS_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(boxes) & 15u) != 0 ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return NMS_INVALID_ARG;
+    Layout L;
+    make_layout(n, &L);
+    if (workspace_bytes < L.total) return NMS_WORKSPACE_TOO_SMALL;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    const Problem P =
+        make_problem(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images);
+    const Work w = carve(workspace, L);
+    hipError_t e = launch_sort(P, L, w, stream);
+    if (e == hipSuccess) e = launch_gather(P, L, w, stream);
+    if (e == hipSuccess) e = launch_mask(P, L, w, stream);
+    if (e == hipSuccess) e = launch_expand_mask(P, L, w, mask_out, stream);
+    if (e == hipSuccess && order_out)
+        e = hipMemcpyAsync(order_out, w.order, (size_t)n * 4, hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return NMS_HIP_ERROR;
+    Readback rb;
+    st = read_back(w, stream, &rb);
+    if (st != NMS_OK) return st;
+    return device_error(rb.error);
+}
+
+nms_status nms_debug_decide(const float *inter, const float *uni, int64_t count,
+                            float iou_thresh, int all_positive_areas, uint8_t *out,
+                            void *stream_ptr) {
+    if (count < 0 || std::isnan(iou_thresh)) return NMS_INVALID_ARG;
+    if (count == 0) return NMS_OK;
+    if (!inter || !uni || !out) return NMS_INVALID_ARG;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    hipError_t e =
+        launch_decide(inter, uni, count, iou_thresh, all_positive_areas != 0, out, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    return hip_status(e);
+}
+
+}  // extern "C"

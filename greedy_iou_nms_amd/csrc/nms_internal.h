@@ -1,0 +1,107 @@
+// Internal declarations shared by the HIP translation units of libgreedy_nms.
+// Nothing here is part of the public ABI (include/greedy_nms.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gnms {
+
+// Error bits raised on the device (Ctrl::error).
+constexpr uint32_t ERR_NONFINITE = 1u;
+constexpr uint32_t ERR_BAD_OFFSETS = 2u;
+
+// Ctrl::flags bits.
+constexpr uint32_t FLAG_POSITIVE_AREAS = 1u;  // every box has a finite area > 0
+
+// Per-call control block at the start of the workspace.  The sort kernel
+// initialises it; later kernels read plan fields and raise error bits.  The
+// first 16 bytes are copied back to the host at the end of a call.
+struct Ctrl {
+    uint32_t error;
+    uint32_t flags;
+    int32_t count;          // kept boxes
+    int32_t num_items;      // mask work items (row tile x strip)
+    int32_t band_stride;    // mask row stride in 64-bit words
+    int32_t num_segments;   // groups present (1 for a single image)
+    int32_t reserved[10];
+};
+static_assert(sizeof(Ctrl) == 64, "Ctrl layout");
+
+// Column tiles per mask work item ("strip"): 16 for one image, 4 for grouped
+// input whose bands are only a few tiles wide.
+constexpr int STRIP_SINGLE = 16;
+constexpr int STRIP_GROUPED = 4;
+
+constexpr int SORT_THREADS = 1024;
+constexpr int SWEEP_THREADS = 1024;
+constexpr int MASK_THREADS = 256;
+
+// Workspace carve-up, computed on the host from n alone.
+struct Layout {
+    int64_t n = 0;
+    int64_t words = 0;      // W = ceil(n / 64): words per full mask row, row tiles
+    int64_t npad = 0;       // 64 * W
+    int64_t mstride = 0;    // worst-case mask row stride in words
+    size_t off_ctrl = 0, off_keys0 = 0, off_keys1 = 0, off_vals0 = 0, off_vals1 = 0;
+    size_t off_order = 0, off_score_order = 0, off_seg = 0, off_inv = 0;
+    size_t off_sb = 0, off_area = 0, off_tile_cend = 0, off_item_base = 0, off_kept = 0;
+    size_t off_mask = 0, total = 0;
+};
+
+bool make_layout(int64_t n, Layout *out);
+
+// Device pointers into one workspace.
+struct Work {
+    Ctrl *ctrl;
+    uint32_t *keys0, *keys1, *vals0, *vals1;
+    int32_t *order;        // sorted position -> input index (group order)
+    int32_t *score_order;  // score rank -> input index (grouped input only)
+    uint32_t *seg;         // sorted position -> segment id (grouped input only)
+    int32_t *inv;          // input index -> sorted position (grouped input only)
+    float4 *sb;            // sorted boxes, padded to npad
+    float *area;           // sorted areas, padded to npad
+    int32_t *tile_cend;    // per row tile: one past the last column tile of its band
+    int32_t *item_base;    // per row tile: first mask work item; [W] = total
+    uint64_t *kept;        // W words: bit p = sorted position p kept
+    uint64_t *mask;        // suppression bitmask rows
+};
+
+Work carve(void *workspace, const Layout &L);
+
+struct Problem {
+    const float *boxes;
+    const float *scores;
+    int n;
+    float thresh;
+    const int32_t *class_ids;
+    const int64_t *offsets;
+    int num_images;
+    bool grouped;          // class_ids or more than one image
+    int strip;             // STRIP_SINGLE or STRIP_GROUPED
+};
+
+// Stage launchers; all enqueue on `stream` and return the launch status.
+hipError_t launch_sort(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
+hipError_t launch_gather(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
+hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
+hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
+                        hipStream_t stream);
+hipError_t launch_compact(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
+                          hipStream_t stream);
+hipError_t launch_expand_mask(const Problem &P, const Layout &L, const Work &w,
+                              uint64_t *mask_out, hipStream_t stream);
+hipError_t launch_decide(const float *inter, const float *uni, int64_t count, float thresh,
+                         bool positive_areas, uint8_t *out, hipStream_t stream);
+
+// Threshold constants for the mask kernel's division-free test (see mask.hip).
+struct Threshold {
+    float t;
+    double mid;      // t + ulp(t)/2, exact in binary64
+    bool odd;        // t's last significand bit is 1 (ties round away from t)
+    bool exact_ok;   // t is finite and > 0: the division-free test applies
+};
+Threshold make_threshold(float t);
+
+}  // namespace gnms

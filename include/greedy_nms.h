@@ -1,0 +1,187 @@
+/*
+ * greedy_nms.h -- C ABI of the MI355X (gfx950) greedy IoU non-maximum
+ * suppression library (libgreedy_nms.so).
+ *
+ * What the library computes.  Greedy NMS as described on "LeetCUDA 14-nms"
+ * (introduction and "algorithm and data flow"): visit the boxes by score,
+ * highest first, with equal scores in ascending input order (stable sort);
+ * keep a box unless an already-kept box of its group overlaps it with
+ * IoU > iou_thresh (strictly); return the kept boxes as their original input
+ * indices (that page's bug-3 fix), int64, in visiting order.  A group is the
+ * pair (image, class): boxes of different images or classes never suppress
+ * each other (the class check of "YOLOv5 post-processing GPU port",
+ * section 2.2, extended to images).  With several groups the result is one
+ * list over all boxes in global score order, with global indices.
+ *
+ * The IoU is this float32 expression, one IEEE binary32 operation per step,
+ * no fused multiply-add (none of the pages prints its IoU routine; this
+ * expression is the one the library fixes):
+ *     area  = (x2 - x1) * (y2 - y1)
+ *     w     = max(min(x2i, x2j) - max(x1i, x1j), 0)
+ *     h     = max(min(y2i, y2j) - max(y1i, y1j), 0)
+ *     inter = w * h
+ *     union = (area_i + area_j) - inter
+ *     suppress  iff  inter / union > iou_thresh      (correctly rounded)
+ * No clipping or reordering of coordinates is applied.
+ *
+ * Memory.  Every pointer argument named "device" is HIP device memory on the
+ * current device; the caller allocates and owns every buffer (inputs, output,
+ * workspace).  The library allocates nothing, keeps no pointer after a call
+ * returns and holds no device state between calls, so calls on different
+ * streams with distinct workspaces may run concurrently.
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  All work
+ * is enqueued on it; each nms_* compute call returns after one
+ * hipStreamSynchronize, which makes *num_kept (a host pointer) valid.  Inputs
+ * must not change until the call returns.
+ *
+ * Errors.  No exception crosses the ABI.  Every call returns an nms_status;
+ * on any status other than NMS_OK, *num_kept (when given) is 0 and keep_out is
+ * unspecified.  Device-detected errors (non-finite input, bad offsets) arrive
+ * with the same read-back that carries the kept count.
+ */
+#ifndef GREEDY_NMS_H
+#define GREEDY_NMS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nms_status {
+    NMS_OK = 0,
+    /* A null pointer with n > 0, n < 0, iou_thresh NaN, num_images
+     * inconsistent with batch_offsets, or a misaligned boxes pointer. */
+    NMS_INVALID_ARG = 1,
+    /* workspace_bytes is below what nms_workspace_size reports. */
+    NMS_WORKSPACE_TOO_SMALL = 2,
+    /* A NaN score or a non-finite box coordinate (detected on the device). */
+    NMS_NONFINITE_INPUT = 3,
+    /* batch_offsets not non-decreasing from 0 to n (detected on the device). */
+    NMS_BAD_OFFSETS = 4,
+    /* n above NMS_MAX_BOXES. */
+    NMS_TOO_LARGE = 5,
+    /* A HIP runtime call or kernel launch failed. */
+    NMS_HIP_ERROR = 6
+} nms_status;
+
+/* Largest n accepted: one workgroup keeps the removed bitmap (n/8 bytes) in
+ * at most 64 KiB of LDS during the sweep. */
+#define NMS_MAX_BOXES 512000
+
+/* Stages timed by nms_f32_profiled, in launch order. */
+#define NMS_STAGE_SORT 0     /* score keys, stable LSD radix sort, grouping  */
+#define NMS_STAGE_GATHER 1   /* sorted box gather + areas + input checks     */
+#define NMS_STAGE_MASK 2     /* triangle-tiled IoU suppression bitmask       */
+#define NMS_STAGE_SWEEP 3    /* greedy sweep over the mask (+ compaction)    */
+#define NMS_STAGE_COMPACT 4  /* score-order compaction (grouped input only)  */
+#define NMS_NUM_STAGES 5
+
+/*
+ * nms_workspace_size -- device workspace needed by nms_f32 for n boxes.
+ *   n            number of boxes (0 <= n <= NMS_MAX_BOXES)
+ *   num_images   number of images in batch_offsets (0 or 1 when there are
+ *                none); has_classes: nonzero when class_ids will be given.
+ *   *bytes       receives the size; it is a bound computed from n alone
+ *                (dominated by the n * ceil(n/64) * 8-byte suppression
+ *                bitmask), so no device synchronisation is needed.
+ * Returns NMS_OK, NMS_INVALID_ARG (bytes NULL, n < 0) or NMS_TOO_LARGE.
+ */
+nms_status nms_workspace_size(int64_t n, int64_t num_images, int has_classes, size_t *bytes);
+
+/*
+ * nms_f32 -- greedy IoU NMS (see the file comment for the exact result).
+ *   boxes          device, n*4 floats, row k = (x1, y1, x2, y2) of box k;
+ *                  16-byte aligned.
+ *   scores         device, n floats.
+ *   n              number of boxes; n = 0 returns NMS_OK with *num_kept = 0.
+ *   iou_thresh     float32 threshold; any value but NaN (values < 0 remove
+ *                  every later box of a group with a defined IoU).
+ *   class_ids      device, n int32 class ids, or NULL (one class).
+ *   batch_offsets  device, num_images+1 int64 offsets; image m holds boxes
+ *                  [off[m], off[m+1]).  NULL = one image (num_images 0 or 1).
+ *   keep_out       device, capacity n int64: receives the kept input indices
+ *                  in descending score order (ties: ascending index).
+ *   num_kept       host: receives the number of kept boxes.
+ *   workspace      device scratch of at least nms_workspace_size() bytes,
+ *                  256-byte aligned; its contents on entry do not matter.
+ *   stream         hipStream_t or NULL.
+ * Sorting follows "LeetCUDA 14-nms" step 1 (stable, descending); the
+ * bitmask layout follows its Phase 1 (bit k of word w of row i means sorted
+ * box 64w + k; only boxes after row i vote); the sweep follows its Phase 2
+ * (removed bitmap in on-chip memory, kept rows ORed in in score order); the
+ * map-back follows its host section.
+ */
+nms_status nms_f32(const float *boxes, const float *scores, int64_t n, float iou_thresh,
+                   const int32_t *class_ids, const int64_t *batch_offsets, int64_t num_images,
+                   int64_t *keep_out, int64_t *num_kept, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * nms_f32_profiled -- nms_f32 with HIP events recorded on `stream` around
+ * each stage.  stage_ms (host, NMS_NUM_STAGES floats) receives each stage's
+ * elapsed GPU time in milliseconds (0 for a stage that did not run).  The
+ * result is identical to nms_f32's.
+ */
+nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
+                            float iou_thresh, const int32_t *class_ids,
+                            const int64_t *batch_offsets, int64_t num_images,
+                            int64_t *keep_out, int64_t *num_kept, void *workspace,
+                            size_t workspace_bytes, void *stream, float *stage_ms);
+
+/* Human-readable name of a status ("NMS_OK", ...); never NULL. */
+const char *nms_status_string(nms_status status);
+
+/* ---- test-only exports: copy out one stage's intermediate result ---- */
+
+/*
+ * nms_debug_order -- run the sort stage only.
+ *   order_out        device, n int32: input index at each sorted position
+ *                    (grouped input: ascending image, then class, then
+ *                    descending score, then ascending index).
+ *   score_order_out  device, n int32 or NULL: the plain score order
+ *                    (descending score, ascending index).
+ * Other arguments as for nms_f32.
+ */
+nms_status nms_debug_order(const float *scores, int64_t n, const int32_t *class_ids,
+                           const int64_t *batch_offsets, int64_t num_images,
+                           int32_t *order_out, int32_t *score_order_out, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * nms_debug_mask -- run sort, gather and the IoU-mask stage, then expand the
+ * mask into a dense row-major array.
+ *   mask_out   device, n * ceil(n/64) uint64: word c of row p (sorted
+ *              position p) has bit l set iff box q = 64c + l satisfies
+ *              p < q < n, q in p's group and IoU > iou_thresh.  Words the
+ *              kernel never computes (below the diagonal tile, beyond the
+ *              group's last tile) read 0.
+ *   order_out  device, n int32 or NULL: the sorted order the rows refer to.
+ */
+nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
+                          float iou_thresh, const int32_t *class_ids,
+                          const int64_t *batch_offsets, int64_t num_images,
+                          uint64_t *mask_out, int32_t *order_out, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * nms_debug_decide -- the IoU-mask kernel's threshold test alone.
+ *   inter, uni  device, count floats each: an intersection and a union value.
+ *   out         device, count bytes: 1 iff the test "inter / uni > t" holds
+ *               as the mask kernel decides it.
+ *   all_positive_areas  nonzero selects the division-free test the mask
+ *               kernel uses when every box has a finite positive area (it
+ *               presumes 0 <= inter <= union, union > 0); zero selects the
+ *               literal float32 division.
+ */
+nms_status nms_debug_decide(const float *inter, const float *uni, int64_t count,
+                            float iou_thresh, int all_positive_areas, uint8_t *out,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GREEDY_NMS_H */
