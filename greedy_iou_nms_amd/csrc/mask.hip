@@ -97,6 +97,7 @@ struct GatherArgs {
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     const int p = blockIdx.x * 256 + threadIdx.x;
     if (p >= a.npad) return;
+    a.w.rowcnt[p] = 0u;  // the mask kernel counts each row's nonzero words here
     bool finite = true, positive = true;
     if (p < a.n) {
         const int i = a.w.order[p];
@@ -139,6 +140,9 @@ struct MaskPtrs {
     const int32_t *__restrict__ tile_cend;
     const int32_t *__restrict__ item_base;
     uint64_t *__restrict__ mask;
+    uint32_t *__restrict__ rowcnt;
+    uint32_t *__restrict__ lidx;
+    uint64_t *__restrict__ lval;
 };
 
 // v_writelane_b32: lane `lane` of the returned VGPR value becomes `val` (an
@@ -221,11 +225,34 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
         }
     }
     if (lane < rows) {
-        uint64_t *dst = m_.mask + (size_t)(p0 + lane) * (size_t)stride + (size_t)(c0 - s0 * S);
+        const int p = p0 + lane;
+        uint64_t *dst = m_.mask + (size_t)p * (size_t)stride + (size_t)(c0 - s0 * S);
         uint4 *d4 = reinterpret_cast<uint4 *>(dst);
 #pragma unroll
         for (int t = 0; t < S; t += 2)
             d4[t / 2] = make_uint4(out_lo[t], out_hi[t], out_lo[t + 1], out_hi[t + 1]);
+        // Record this strip's nonzero words in the row's list.  Slots are
+        // claimed with an atomic counter, so the list order may differ from
+        // run to run; the sweep only ORs the entries together, which does not
+        // depend on their order.  Entries past the capacity are dropped and
+        // the count (which still grows) tells the sweep to use the dense row.
+        uint32_t nz = 0;
+#pragma unroll
+        for (int t = 0; t < S; ++t) nz += (out_lo[t] | out_hi[t]) != 0u;
+        if (nz) {
+            uint32_t at = atomicAdd(&m_.rowcnt[p], nz);
+#pragma unroll
+            for (int t = 0; t < S; ++t) {
+                if ((out_lo[t] | out_hi[t]) != 0u) {
+                    if (at < (uint32_t)ROW_LIST_CAP) {
+                        m_.lidx[(size_t)p * ROW_LIST_CAP + at] = (uint32_t)(c0 + t);
+                        m_.lval[(size_t)p * ROW_LIST_CAP + at] =
+                            ((uint64_t)out_hi[t] << 32) | out_lo[t];
+                    }
+                    ++at;
+                }
+            }
+        }
     }
 }
 
@@ -234,8 +261,9 @@ __global__ __launch_bounds__(MASK_THREADS) void mask_kernel(
     MaskArgs a, const Ctrl *__restrict__ ctrl, const float4 *__restrict__ sb,
     const float *__restrict__ area, const uint32_t *__restrict__ seg,
     const int32_t *__restrict__ tile_cend, const int32_t *__restrict__ item_base,
-    uint64_t *__restrict__ mask) {
-    const MaskPtrs m_{sb, area, seg, tile_cend, item_base, mask};
+    uint64_t *__restrict__ mask, uint32_t *__restrict__ rowcnt, uint32_t *__restrict__ lidx,
+    uint64_t *__restrict__ lval) {
+    const MaskPtrs m_{sb, area, seg, tile_cend, item_base, mask, rowcnt, lidx, lval};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves_per_block = MASK_THREADS / 64;
     const int num_items = ctrl->num_items;
@@ -341,11 +369,11 @@ hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStre
     if (P.grouped)
         hipLaunchKernelGGL((mask_kernel<STRIP_GROUPED, true>), dim3((unsigned)blocks),
                            dim3(MASK_THREADS), 0, stream, a, w.ctrl, w.sb, w.area, w.seg,
-                           w.tile_cend, w.item_base, w.mask);
+                           w.tile_cend, w.item_base, w.mask, w.rowcnt, w.lidx, w.lval);
     else
         hipLaunchKernelGGL((mask_kernel<STRIP_SINGLE, false>), dim3((unsigned)blocks),
                            dim3(MASK_THREADS), 0, stream, a, w.ctrl, w.sb, w.area, w.seg,
-                           w.tile_cend, w.item_base, w.mask);
+                           w.tile_cend, w.item_base, w.mask, w.rowcnt, w.lidx, w.lval);
     return hipGetLastError();
 }
 

@@ -41,6 +41,9 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_tile_cend = take((size_t)L.words * 4 + 4);
     L.off_item_base = take((size_t)L.words * 4 + 4);
     L.off_kept = take((size_t)L.words * 8 + 8);
+    L.off_rowcnt = take(np * 4);
+    L.off_lidx = take((size_t)n * ROW_LIST_CAP * 4);
+    L.off_lval = take((size_t)n * ROW_LIST_CAP * 8);
     L.off_mask = take((size_t)n * (size_t)L.mstride * 8);
     L.total = off;
     *out = L;
@@ -64,6 +67,9 @@ Work carve(void *workspace, const Layout &L) {
     w.tile_cend = reinterpret_cast<int32_t *>(b + L.off_tile_cend);
     w.item_base = reinterpret_cast<int32_t *>(b + L.off_item_base);
     w.kept = reinterpret_cast<uint64_t *>(b + L.off_kept);
+    w.rowcnt = reinterpret_cast<uint32_t *>(b + L.off_rowcnt);
+    w.lidx = reinterpret_cast<uint32_t *>(b + L.off_lidx);
+    w.lval = reinterpret_cast<uint64_t *>(b + L.off_lval);
     w.mask = reinterpret_cast<uint64_t *>(b + L.off_mask);
     return w;
 }

@@ -35,8 +35,13 @@ constexpr int STRIP_SINGLE = 16;
 constexpr int STRIP_GROUPED = 4;
 
 constexpr int SORT_THREADS = 1024;
-constexpr int SWEEP_THREADS = 1024;
+constexpr int SWEEP_THREADS = 256;
 constexpr int MASK_THREADS = 256;
+
+// Nonzero mask words recorded per row (word index and value) besides the
+// dense row.  A row with more nonzero words than this is flagged by its count
+// exceeding the capacity and the sweep reads its dense row instead.
+constexpr int ROW_LIST_CAP = 16;
 
 // Workspace carve-up, computed on the host from n alone.
 struct Layout {
@@ -47,6 +52,7 @@ struct Layout {
     size_t off_ctrl = 0, off_keys0 = 0, off_keys1 = 0, off_vals0 = 0, off_vals1 = 0;
     size_t off_order = 0, off_score_order = 0, off_seg = 0, off_inv = 0;
     size_t off_sb = 0, off_area = 0, off_tile_cend = 0, off_item_base = 0, off_kept = 0;
+    size_t off_rowcnt = 0, off_lidx = 0, off_lval = 0;
     size_t off_mask = 0, total = 0;
 };
 
@@ -65,6 +71,9 @@ struct Work {
     int32_t *tile_cend;    // per row tile: one past the last column tile of its band
     int32_t *item_base;    // per row tile: first mask work item; [W] = total
     uint64_t *kept;        // W words: bit p = sorted position p kept
+    uint32_t *rowcnt;      // per sorted position: nonzero mask words in its row
+    uint32_t *lidx;        // [n][ROW_LIST_CAP] word index of a nonzero word
+    uint64_t *lval;        // [n][ROW_LIST_CAP] its value
     uint64_t *mask;        // suppression bitmask rows
 };
 

@@ -26,11 +26,22 @@ namespace {
 constexpr int NT = SORT_THREADS;
 constexpr int NWAVES = NT / 64;
 
+// Elements per thread per scatter tile.  Element i of a tile sits at
+// (wave, e, lane) with i = wave * 64 * E + e * 64 + lane, so walking waves,
+// then e, then lanes is walking indices in order, which keeps the pass stable.
+constexpr int E = 8;
+constexpr int TILE = NT * E;
+
 struct SortSmem {
-    uint32_t hist[256];
-    uint32_t base[256];
+    uint32_t hist4[4][256];
+    uint32_t base[256];     // next global position of each digit
+    uint32_t tcnt[256];     // digit counts of the current tile
+    uint32_t tbase[256];    // start of each digit's run inside the staged tile
+    int32_t gsh[256];       // global position minus staged slot, per digit
     uint32_t wcnt[NWAVES][256];
     uint32_t wpre[NWAVES][256];
+    uint32_t stage_k[TILE];  // one tile, reordered by digit, before it is written
+    uint32_t stage_v[TILE];
     uint32_t part[NWAVES];
     uint32_t part2[NWAVES];
     uint32_t rev[NT];
@@ -151,28 +162,50 @@ __device__ uint32_t block_suffix_min_after(uint32_t v, SortSmem &sm) {
     return r;
 }
 
+// Histograms of all four 8-bit digits of ks[0..n) (the digit counts do not
+// depend on the order the keys are in, so one read serves four passes).
+__device__ void digit_histograms(const uint32_t *ks, int n, SortSmem &sm) {
+    const int tid = threadIdx.x;
+    uint32_t *h = &sm.hist4[0][0];
+    for (int j = tid; j < 4 * 256; j += NT) h[j] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+        const uint32_t k = ks[i];
+        atomicAdd(&sm.hist4[0][k & 255u], 1u);
+        atomicAdd(&sm.hist4[1][(k >> 8) & 255u], 1u);
+        atomicAdd(&sm.hist4[2][(k >> 16) & 255u], 1u);
+        atomicAdd(&sm.hist4[3][k >> 24], 1u);
+    }
+    __syncthreads();
+}
+
 // One stable counting pass over the 8-bit digit at `shift`: (ks, vs) ->
-// (kd, vd).  Returns false (and moves nothing) when every key has the same
-// digit.  Buffers are plain pointers: they are written and re-read inside
-// this kernel, so none of them may be treated as read-only.
-__device__ bool radix_pass(const uint32_t *ks, const uint32_t *vs, uint32_t *kd, uint32_t *vd,
-                           int n, int shift, SortSmem &sm) {
+// (kd, vd), using the digit histogram sm.hist4[shift / 8].  Returns false
+// (and moves nothing) when every key has the same digit.
+//
+// Each tile is first ranked (per wave, with 64-lane ballots deciding which
+// lanes share a digit), then reordered by digit in LDS, and only then written
+// out: consecutive threads then write consecutive positions of one digit's
+// run instead of scattering single words across memory, which a single
+// compute unit could only issue one cache line at a time.
+//
+// Buffers are plain pointers: they are written and re-read inside this
+// kernel, so none of them may be treated as read-only.
+__device__ __forceinline__ bool radix_pass(const uint32_t *ks, const uint32_t *vs, uint32_t *kd,
+                                           uint32_t *vd, int n, int shift, SortSmem &sm) {
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    if (tid < 256) sm.hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) atomicAdd(&sm.hist[(ks[i] >> shift) & 255u], 1u);
-    __syncthreads();
+    const uint32_t *hist = sm.hist4[shift >> 3];
     if (wave == 0) {
-        uint32_t h0 = sm.hist[4 * lane], h1 = sm.hist[4 * lane + 1];
-        uint32_t h2 = sm.hist[4 * lane + 2], h3 = sm.hist[4 * lane + 3];
-        uint32_t s = h0 + h1 + h2 + h3;
-        uint32_t ex = wave_incl_sum(s) - s;
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        const uint32_t s = h0 + h1 + h2 + h3;
+        const uint32_t ex = wave_incl_sum(s) - s;
         sm.base[4 * lane] = ex;
         sm.base[4 * lane + 1] = ex + h0;
         sm.base[4 * lane + 2] = ex + h0 + h1;
         sm.base[4 * lane + 3] = ex + h0 + h1 + h2;
         const uint32_t un = (uint32_t)n;
-        uint64_t one = __ballot(h0 == un || h1 == un || h2 == un || h3 == un);
+        const uint64_t one = __ballot(h0 == un || h1 == un || h2 == un || h3 == un);
         if (lane == 0) sm.flag = one ? 1u : 0u;
     }
     __syncthreads();
@@ -180,45 +213,83 @@ __device__ bool radix_pass(const uint32_t *ks, const uint32_t *vs, uint32_t *kd,
         __syncthreads();
         return false;
     }
-    const int tiles = (n + NT - 1) / NT;
-    for (int tile = 0; tile < tiles; ++tile) {
-        const int i = tile * NT + tid;
-        const bool valid = i < n;
-        const uint32_t k = valid ? ks[i] : 0u;
-        const uint32_t v = valid ? vs[i] : 0u;
-        const uint32_t d = (k >> shift) & 255u;
-        // lanes of this wave holding the same digit
-        uint64_t peers = __ballot(valid);
+    for (int t0 = 0; t0 < n; t0 += TILE) {
+        const int wbase = t0 + wave * 64 * E;
+        uint32_t k[E], v[E], rk[E];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const bool bit = (d >> b) & 1u;
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
+        for (int e = 0; e < E; ++e) {
+            const int i = wbase + e * 64 + lane;
+            k[e] = i < n ? ks[i] : 0u;
+            v[e] = i < n ? vs[i] : 0u;
         }
-        const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
         for (int j = lane; j < 256; j += 64) sm.wcnt[wave][j] = 0;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        if (valid && rank == 0) sm.wcnt[wave][d] = (uint32_t)__popcll(peers);
+        // rank of each element among this wave's elements with the same digit
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool valid = wbase + e * 64 + lane < n;
+            const uint32_t d = (k[e] >> shift) & 255u;
+            uint64_t peers = __ballot(valid);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const bool bit = (d >> b) & 1u;
+                const uint64_t m = __ballot(bit);
+                peers &= bit ? m : ~m;
+            }
+            const uint32_t r_in = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(peers >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
+            const uint32_t before = sm.wcnt[wave][d];
+            rk[e] = before + r_in;
+            // the lowest lane of each digit group advances the wave's count;
+            // the read above precedes this write in the wave's LDS order
+            if (valid && r_in == 0) sm.wcnt[wave][d] = before + (uint32_t)__popcll(peers);
+        }
         __syncthreads();
+        // per digit: offsets of the waves inside the tile, and the tile count
         if (tid < 256) {
-            uint32_t run = sm.base[tid];
+            uint32_t run = 0;
 #pragma unroll
             for (int wv = 0; wv < NWAVES; ++wv) {
                 const uint32_t c = sm.wcnt[wv][tid];
                 sm.wpre[wv][tid] = run;
                 run += c;
             }
-            sm.base[tid] = run;
+            sm.tcnt[tid] = run;
         }
         __syncthreads();
-        if (valid) {
-            const uint32_t pos = sm.wpre[wave][d] + rank;
-            kd[pos] = k;
-            vd[pos] = v;
+        // digit runs inside the staged tile
+        if (wave == 0) {
+            const uint32_t h0 = sm.tcnt[4 * lane], h1 = sm.tcnt[4 * lane + 1];
+            const uint32_t h2 = sm.tcnt[4 * lane + 2], h3 = sm.tcnt[4 * lane + 3];
+            const uint32_t s = h0 + h1 + h2 + h3;
+            const uint32_t ex = wave_incl_sum(s) - s;
+            const uint32_t tb[4] = {ex, ex + h0, ex + h0 + h1, ex + h0 + h1 + h2};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sm.tbase[4 * lane + j] = tb[j];
+                sm.gsh[4 * lane + j] = (int32_t)sm.base[4 * lane + j] - (int32_t)tb[j];
+            }
         }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (wbase + e * 64 + lane < n) {
+                const uint32_t d = (k[e] >> shift) & 255u;
+                const uint32_t slot = sm.tbase[d] + sm.wpre[wave][d] + rk[e];
+                sm.stage_k[slot] = k[e];
+                sm.stage_v[slot] = v[e];
+            }
+        }
+        __syncthreads();
+        const int count = n - t0 < TILE ? n - t0 : TILE;
+        for (int s = tid; s < count; s += NT) {
+            const uint32_t key = sm.stage_k[s];
+            const int pos = s + sm.gsh[(key >> shift) & 255u];
+            kd[pos] = key;
+            vd[pos] = sm.stage_v[s];
+        }
+        if (tid < 256) sm.base[tid] += sm.tcnt[tid];
+        __syncthreads();
     }
-    __syncthreads();
     return true;
 }
 
@@ -257,38 +328,31 @@ __global__ __launch_bounds__(NT) void sort_kernel(SortArgs a) {
     }
     __syncthreads();
 
+    // Phase 0 sorts by score.  Grouped input adds phase 1 (class id) and
+    // phase 2 (image), each a stable sort of the previous phase's order, so
+    // the final order is by (image, class, score, index).  One call site for
+    // the pass keeps the kernel small.
     uint32_t *ks = w.keys0, *vs = w.vals0, *kd = w.keys1, *vd = w.vals1;
-    for (int shift = 0; shift < 32; shift += 8) {
-        if (radix_pass(ks, vs, kd, vd, n, shift, sm)) {
-            uint32_t *t0 = ks; ks = kd; kd = t0;
-            uint32_t *t1 = vs; vs = vd; vd = t1;
-        }
-    }
-
-    if (a.grouped) {
-        // the plain score order is kept for the final compaction
-        for (int p = tid; p < n; p += NT) w.score_order[p] = (int32_t)vs[p];
-        if (a.offsets) {
-            for (int m = tid; m <= a.num_images; m += NT) {
-                const int64_t o = a.offsets[m];
-                bool bad = (m == 0 && o != 0) || (m == a.num_images && o != (int64_t)n);
-                if (m > 0 && o < a.offsets[m - 1]) bad = true;
-                if (bad) err |= ERR_BAD_OFFSETS;
+    const int phases = a.grouped ? 3 : 1;
+    for (int phase = 0; phase < phases; ++phase) {
+        if (phase == 1) {
+            // the plain score order is kept for the final compaction
+            for (int p = tid; p < n; p += NT) w.score_order[p] = (int32_t)vs[p];
+            if (a.offsets) {
+                for (int m = tid; m <= a.num_images; m += NT) {
+                    const int64_t o = a.offsets[m];
+                    bool bad = (m == 0 && o != 0) || (m == a.num_images && o != (int64_t)n);
+                    if (m > 0 && o < a.offsets[m - 1]) bad = true;
+                    if (bad) err |= ERR_BAD_OFFSETS;
+                }
             }
+            for (int p = tid; p < n; p += NT) ks[p] = class_key(a.class_ids, vs[p]);
+        } else if (phase == 2) {
+            for (int p = tid; p < n; p += NT)
+                ks[p] = a.offsets ? image_of(a.offsets, a.num_images, vs[p]) : 0u;
         }
-        // stable passes on the class id ...
-        for (int p = tid; p < n; p += NT) ks[p] = class_key(a.class_ids, vs[p]);
         __syncthreads();
-        for (int shift = 0; shift < 32; shift += 8) {
-            if (radix_pass(ks, vs, kd, vd, n, shift, sm)) {
-                uint32_t *t0 = ks; ks = kd; kd = t0;
-                uint32_t *t1 = vs; vs = vd; vd = t1;
-            }
-        }
-        // ... then on the image index
-        for (int p = tid; p < n; p += NT)
-            ks[p] = a.offsets ? image_of(a.offsets, a.num_images, vs[p]) : 0u;
-        __syncthreads();
+        digit_histograms(ks, n, sm);
         for (int shift = 0; shift < 32; shift += 8) {
             if (radix_pass(ks, vs, kd, vd, n, shift, sm)) {
                 uint32_t *t0 = ks; ks = kd; kd = t0;
