@@ -90,14 +90,16 @@ __device__ __forceinline__ bool suppresses(float rx1, float ry1, float rx2, floa
 
 struct GatherArgs {
     const float4 *boxes;
-    int n, npad, grouped;
+    int n, npad, words, grouped;
     Work w;
 };
 
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     const int p = blockIdx.x * 256 + threadIdx.x;
     if (p >= a.npad) return;
-    a.w.rowcnt[p] = 0u;  // the mask kernel counts each row's nonzero words here
+    if (p < a.words) a.w.tcount[p] = 0u;  // the mask kernel counts each tile's nonzero words
+    // near words stay 0 where the tile lies outside the row's band
+    for (int j = 0; j <= NEAR_TILES; ++j) a.w.tnear[(size_t)j * a.npad + p] = 0ull;
     bool finite = true, positive = true;
     if (p < a.n) {
         const int i = a.w.order[p];
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 // ---------------------------------------------------------------- mask
 
 struct MaskArgs {
-    int n, words, mstride;
+    int n, words, mstride, npad;
     float t;
     double mid;
     int odd, exact_ok;
@@ -140,9 +142,10 @@ struct MaskPtrs {
     const int32_t *__restrict__ tile_cend;
     const int32_t *__restrict__ item_base;
     uint64_t *__restrict__ mask;
-    uint32_t *__restrict__ rowcnt;
-    uint32_t *__restrict__ lidx;
-    uint64_t *__restrict__ lval;
+    uint32_t *__restrict__ tcount;
+    uint32_t *__restrict__ tent_wk;
+    uint64_t *__restrict__ tent_val;
+    uint64_t *__restrict__ tnear;
 };
 
 // v_writelane_b32: lane `lane` of the returned VGPR value becomes `val` (an
@@ -151,6 +154,16 @@ struct MaskPtrs {
 __device__ __forceinline__ uint32_t write_lane(uint32_t old, uint32_t val, int lane) {
     asm("v_writelane_b32 %0, %1, m0" : "+v"(old) : "s"(val), "{m0}"(lane));
     return old;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    return v;
 }
 
 // Word mask of valid column boxes in tile c (boxes >= n never vote).
@@ -231,26 +244,41 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
 #pragma unroll
         for (int t = 0; t < S; t += 2)
             d4[t / 2] = make_uint4(out_lo[t], out_hi[t], out_lo[t + 1], out_hi[t + 1]);
-        // Record this strip's nonzero words in the row's list.  Slots are
-        // claimed with an atomic counter, so the list order may differ from
-        // run to run; the sweep only ORs the entries together, which does not
-        // depend on their order.  Entries past the capacity are dropped and
-        // the count (which still grows) tells the sweep to use the dense row.
-        uint32_t nz = 0;
+        // transposed copies of the words for tiles r .. r + NEAR_TILES
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            const int j = t - t_diag;
+            if (j >= 0 && j <= NEAR_TILES && c0 + t < cend)
+                m_.tnear[(size_t)j * a.npad + p] = ((uint64_t)out_hi[t] << 32) | out_lo[t];
+        }
+    }
+    // Record the strip's nonzero words in the row tile's list.  A wave-wide
+    // prefix sum gives each lane its place and one atomic claims the wave's
+    // slots, so the list order may differ from run to run; the sweep only ORs
+    // entries together, which does not depend on their order.  Entries past
+    // the capacity are dropped and the count (which still grows) tells the
+    // sweep to read dense rows instead.
+    uint32_t nz = 0;
+    if (lane < rows) {
 #pragma unroll
         for (int t = 0; t < S; ++t) nz += (out_lo[t] | out_hi[t]) != 0u;
-        if (nz) {
-            uint32_t at = atomicAdd(&m_.rowcnt[p], nz);
+    }
+    const uint32_t incl = wave_incl_sum(nz);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    if (total) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&m_.tcount[r], total);
+        base = __builtin_amdgcn_readlane(base, 0);
+        uint32_t at = base + incl - nz;
 #pragma unroll
-            for (int t = 0; t < S; ++t) {
-                if ((out_lo[t] | out_hi[t]) != 0u) {
-                    if (at < (uint32_t)ROW_LIST_CAP) {
-                        m_.lidx[(size_t)p * ROW_LIST_CAP + at] = (uint32_t)(c0 + t);
-                        m_.lval[(size_t)p * ROW_LIST_CAP + at] =
-                            ((uint64_t)out_hi[t] << 32) | out_lo[t];
-                    }
-                    ++at;
+        for (int t = 0; t < S; ++t) {
+            if ((out_lo[t] | out_hi[t]) != 0u && lane < rows) {
+                if (at < (uint32_t)TILE_LIST_CAP) {
+                    const size_t e = (size_t)r * TILE_LIST_CAP + at;
+                    m_.tent_wk[e] = ((uint32_t)(c0 + t) << 6) | (uint32_t)lane;
+                    m_.tent_val[e] = ((uint64_t)out_hi[t] << 32) | out_lo[t];
                 }
+                ++at;
             }
         }
     }
@@ -261,9 +289,9 @@ __global__ __launch_bounds__(MASK_THREADS) void mask_kernel(
     MaskArgs a, const Ctrl *__restrict__ ctrl, const float4 *__restrict__ sb,
     const float *__restrict__ area, const uint32_t *__restrict__ seg,
     const int32_t *__restrict__ tile_cend, const int32_t *__restrict__ item_base,
-    uint64_t *__restrict__ mask, uint32_t *__restrict__ rowcnt, uint32_t *__restrict__ lidx,
-    uint64_t *__restrict__ lval) {
-    const MaskPtrs m_{sb, area, seg, tile_cend, item_base, mask, rowcnt, lidx, lval};
+    uint64_t *__restrict__ mask, uint32_t *__restrict__ tcount, uint32_t *__restrict__ tent_wk,
+    uint64_t *__restrict__ tent_val, uint64_t *__restrict__ tnear) {
+    const MaskPtrs m_{sb, area, seg, tile_cend, item_base, mask, tcount, tent_wk, tent_val, tnear};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves_per_block = MASK_THREADS / 64;
     const int num_items = ctrl->num_items;
@@ -334,6 +362,7 @@ hipError_t launch_gather(const Problem &P, const Layout &L, const Work &w, hipSt
     a.boxes = reinterpret_cast<const float4 *>(P.boxes);
     a.n = P.n;
     a.npad = (int)L.npad;
+    a.words = (int)L.words;
     a.grouped = P.grouped ? 1 : 0;
     a.w = w;
     const int blocks = (int)((L.npad + 255) / 256);
@@ -345,6 +374,7 @@ hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStre
     const Threshold th = make_threshold(P.thresh);
     MaskArgs a;
     a.n = P.n;
+    a.npad = (int)L.npad;
     a.words = (int)L.words;
     a.mstride = (int)L.mstride;
     a.t = th.t;
@@ -369,11 +399,13 @@ hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStre
     if (P.grouped)
         hipLaunchKernelGGL((mask_kernel<STRIP_GROUPED, true>), dim3((unsigned)blocks),
                            dim3(MASK_THREADS), 0, stream, a, w.ctrl, w.sb, w.area, w.seg,
-                           w.tile_cend, w.item_base, w.mask, w.rowcnt, w.lidx, w.lval);
+                           w.tile_cend, w.item_base, w.mask, w.tcount, w.tent_wk, w.tent_val,
+                           w.tnear);
     else
         hipLaunchKernelGGL((mask_kernel<STRIP_SINGLE, false>), dim3((unsigned)blocks),
                            dim3(MASK_THREADS), 0, stream, a, w.ctrl, w.sb, w.area, w.seg,
-                           w.tile_cend, w.item_base, w.mask, w.rowcnt, w.lidx, w.lval);
+                           w.tile_cend, w.item_base, w.mask, w.tcount, w.tent_wk, w.tent_val,
+                           w.tnear);
     return hipGetLastError();
 }
 

@@ -41,9 +41,10 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_tile_cend = take((size_t)L.words * 4 + 4);
     L.off_item_base = take((size_t)L.words * 4 + 4);
     L.off_kept = take((size_t)L.words * 8 + 8);
-    L.off_rowcnt = take(np * 4);
-    L.off_lidx = take((size_t)n * ROW_LIST_CAP * 4);
-    L.off_lval = take((size_t)n * ROW_LIST_CAP * 8);
+    L.off_tcount = take((size_t)L.words * 4);
+    L.off_tent_wk = take((size_t)L.words * TILE_LIST_CAP * 4);
+    L.off_tent_val = take((size_t)L.words * TILE_LIST_CAP * 8);
+    L.off_tnear = take(np * 8 * (NEAR_TILES + 1));
     L.off_mask = take((size_t)n * (size_t)L.mstride * 8);
     L.total = off;
     *out = L;
@@ -67,9 +68,10 @@ Work carve(void *workspace, const Layout &L) {
     w.tile_cend = reinterpret_cast<int32_t *>(b + L.off_tile_cend);
     w.item_base = reinterpret_cast<int32_t *>(b + L.off_item_base);
     w.kept = reinterpret_cast<uint64_t *>(b + L.off_kept);
-    w.rowcnt = reinterpret_cast<uint32_t *>(b + L.off_rowcnt);
-    w.lidx = reinterpret_cast<uint32_t *>(b + L.off_lidx);
-    w.lval = reinterpret_cast<uint64_t *>(b + L.off_lval);
+    w.tcount = reinterpret_cast<uint32_t *>(b + L.off_tcount);
+    w.tent_wk = reinterpret_cast<uint32_t *>(b + L.off_tent_wk);
+    w.tent_val = reinterpret_cast<uint64_t *>(b + L.off_tent_val);
+    w.tnear = reinterpret_cast<uint64_t *>(b + L.off_tnear);
     w.mask = reinterpret_cast<uint64_t *>(b + L.off_mask);
     return w;
 }
@@ -141,6 +143,7 @@ nms_status read_back(const Work &w, hipStream_t stream, Readback *out) {
 }
 
 nms_status device_error(uint32_t err) {
+    if (err & ERR_INTERNAL) return NMS_HIP_ERROR;
     if (err & ERR_BAD_OFFSETS) return NMS_BAD_OFFSETS;
     if (err & ERR_NONFINITE) return NMS_NONFINITE_INPUT;
     return NMS_OK;

@@ -11,6 +11,7 @@ namespace gnms {
 // Error bits raised on the device (Ctrl::error).
 constexpr uint32_t ERR_NONFINITE = 1u;
 constexpr uint32_t ERR_BAD_OFFSETS = 2u;
+constexpr uint32_t ERR_INTERNAL = 4u;  // a bounded wait inside a kernel gave up
 
 // Ctrl::flags bits.
 constexpr uint32_t FLAG_POSITIVE_AREAS = 1u;  // every box has a finite area > 0
@@ -35,13 +36,20 @@ constexpr int STRIP_SINGLE = 16;
 constexpr int STRIP_GROUPED = 4;
 
 constexpr int SORT_THREADS = 1024;
-constexpr int SWEEP_THREADS = 256;
+constexpr int SWEEP_THREADS = 512;
 constexpr int MASK_THREADS = 256;
 
-// Nonzero mask words recorded per row (word index and value) besides the
-// dense row.  A row with more nonzero words than this is flagged by its count
-// exceeding the capacity and the sweep reads its dense row instead.
-constexpr int ROW_LIST_CAP = 16;
+// Nonzero mask words recorded per row tile (row, word index, value) besides
+// the dense rows.  A tile with more nonzero words than this is flagged by its
+// count exceeding the capacity, and the sweep reads the dense rows of its
+// kept boxes instead.
+constexpr int TILE_LIST_CAP = 2048;
+
+// Words of a row that the sweep's resolver applies itself: the row's own
+// tile (j = 0) and the next NEAR_TILES tiles.  They are copied, transposed,
+// into tnear so that the 64 rows of a tile read word j with one coalesced
+// load.  Words further right are applied by helper waves from the lists.
+constexpr int NEAR_TILES = 4;
 
 // Workspace carve-up, computed on the host from n alone.
 struct Layout {
@@ -52,7 +60,7 @@ struct Layout {
     size_t off_ctrl = 0, off_keys0 = 0, off_keys1 = 0, off_vals0 = 0, off_vals1 = 0;
     size_t off_order = 0, off_score_order = 0, off_seg = 0, off_inv = 0;
     size_t off_sb = 0, off_area = 0, off_tile_cend = 0, off_item_base = 0, off_kept = 0;
-    size_t off_rowcnt = 0, off_lidx = 0, off_lval = 0;
+    size_t off_tcount = 0, off_tent_wk = 0, off_tent_val = 0, off_tnear = 0;
     size_t off_mask = 0, total = 0;
 };
 
@@ -71,9 +79,13 @@ struct Work {
     int32_t *tile_cend;    // per row tile: one past the last column tile of its band
     int32_t *item_base;    // per row tile: first mask work item; [W] = total
     uint64_t *kept;        // W words: bit p = sorted position p kept
-    uint32_t *rowcnt;      // per sorted position: nonzero mask words in its row
-    uint32_t *lidx;        // [n][ROW_LIST_CAP] word index of a nonzero word
-    uint64_t *lval;        // [n][ROW_LIST_CAP] its value
+    uint32_t *tcount;      // per row tile: nonzero mask words in its 64 rows
+    // per row tile r, entries [r * TILE_LIST_CAP, ...): (word << 6 | row in tile)
+    uint32_t *tent_wk;
+    uint64_t *tent_val;    // the word's value
+    // [j][p] for j = 0..NEAR_TILES: row p's mask word for tile (p / 64) + j,
+    // 0 where that tile lies outside the row's band
+    uint64_t *tnear;
     uint64_t *mask;        // suppression bitmask rows
 };
 

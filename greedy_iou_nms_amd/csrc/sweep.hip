@@ -3,24 +3,32 @@
 //
 // Sweep ("LeetCUDA 14-nms", Phase 2).  The removed bitmap (one bit per sorted
 // box, W = ceil(n/64) words) lives in LDS and the boxes are visited in score
-// order, 64 at a time (one row tile, "chunk" c):
-//   * resolve: lane k holds the diagonal word M[64c + k][c]; the chunk is
-//     settled serially in scalar registers.  The lowest not-yet-removed row k
-//     whose diagonal word is nonzero is kept and its word ORed into the
-//     chunk's removed word; rows whose diagonal word is zero cannot remove
-//     anything inside the chunk, so only rows that survive and suppress cost a
-//     step.  Every row still clear at the end is kept.  A row's word only has
-//     bits above the row, so a later step never changes an earlier decision.
-//   * propagate: each kept row ORs its nonzero words for later column tiles
-//     into the bitmap.  The mask kernel lists every row's nonzero words (word
-//     index, value); the sweep walks those lists instead of the dense rows,
-//     which realistic inputs leave almost entirely zero.  A row whose list
-//     overflowed is read densely instead.
-// The page's sweep takes one workgroup barrier per box.  Here one wave does
-// the whole chain with no barrier at all: LDS operations of one wave complete
-// in order, so the ORs of chunk c are visible when chunk c + 1 reads its
-// removed word.  The diagonal words and row lists of chunk c + 1 do not
-// depend on any decision and are loaded while chunk c is resolved.
+// order, 64 at a time (one row tile, "chunk" c).  Settling chunk c needs the
+// removed word c complete, i.e. every kept row before the chunk ORed in.  A
+// row's words for the next few tiles are needed soon; words far to the right
+// of it can be ORed in any time before the sweep gets there.  The workgroup
+// is split accordingly:
+//   * the resolver (wave 0) walks the chunks in order.  Lane k holds the
+//     diagonal word M[64c + k][c]; the chunk is settled serially in scalar
+//     registers: the lowest not-yet-removed row k whose diagonal word is
+//     nonzero is kept and ORs its word in; rows whose diagonal word is zero
+//     remove nothing inside the chunk, so only rows that survive and suppress
+//     cost a step; every row still clear at the end is kept.  It publishes
+//     the kept set and ORs the kept rows' words for the next NEAR tiles into
+//     words c + 1 .. c + NEAR itself.
+//   * appliers (waves 1..7) own every 7th chunk.  Long before the resolver
+//     gets there, an applier loads its chunk's diagonal and near words
+//     (which it stages in LDS for the resolver), the row tile's count of
+//     nonzero words and then the tile's list of them (row, word, value)
+//     written by the mask kernel; when the kept set is published it ORs the
+//     kept rows' words for column tiles c + NEAR + 1 and later into the
+//     bitmap.  A tile whose list overflowed has its kept rows read densely.
+// The resolver waits for chunk c - NEAR - 1 to be applied before it reads
+// word c, so an applier has NEAR chunk settlements of slack.
+// The page's sweep takes one barrier per box; here no barrier is taken: the
+// waves hand chunks over through LDS flags (release/acquire at workgroup
+// scope), and every wait is bounded -- a wait that gives up raises an
+// internal error and all waves leave, so no configuration can hang the GPU.
 // A box is kept iff its removed bit is clear when the sweep reaches it, and
 // later rows never set bits at or below their own position, so the kept set
 // is the complement of the final bitmap.
@@ -44,13 +52,14 @@ struct SweepArgs {
     const uint64_t *mask;
     const int32_t *tile_cend;
     const int32_t *order;
-    const uint32_t *rowcnt;
-    const uint32_t *lidx;
-    const uint64_t *lval;
+    const uint32_t *tcount;
+    const uint32_t *tent_wk;
+    const uint64_t *tent_val;
+    const uint64_t *tnear;
     Ctrl *ctrl;
     uint64_t *kept;
     int64_t *keep_out;
-    int n, words, mstride, strip, grouped;
+    int n, words, npad, mstride, strip, grouped;
 };
 
 __device__ __forceinline__ uint64_t rows_valid(int c, int n) {
@@ -100,138 +109,343 @@ __device__ uint32_t block_excl_sum(uint32_t v, uint32_t *part, uint32_t *part2, 
     return r;
 }
 
-// What the sweep needs of row 64c + lane: its diagonal word and its list.
-struct ChunkRows {
-    uint64_t diag;
-    uint32_t cnt;
-    uint32_t idx[ROW_LIST_CAP];
-    uint64_t val[ROW_LIST_CAP];
+constexpr int APPLIERS = NWAVES - 1;
+// Bounded waits: about a second of polling before a wait gives up.
+constexpr uint32_t SPIN_LIMIT = 1u << 23;
+
+// Entries of a row tile's list held in registers: RMAX rounds of 64.
+constexpr int RMAX = 16;
+
+constexpr int NEAR = NEAR_TILES;
+
+struct SweepSmem {
+    uint64_t near[APPLIERS][2][NEAR + 1][64];  // staged words for tiles c .. c + NEAR
+    uint64_t kept[APPLIERS];          // published kept set of the slot's chunk
+    uint32_t data_ready[APPLIERS][2]; // chunk + 1 once diag/super are staged
+    uint32_t k_ready[APPLIERS];       // chunk + 1 once kept[] is published
+    uint32_t applied[APPLIERS];       // chunk + 1 once its far words are ORed in
+    uint32_t abort;
+    uint32_t part[NWAVES], part2[NWAVES], tot;
 };
 
-// Loads are unconditional (rows past n and chunks past the end re-read the
-// last valid row, and their values are never used) so the loop carries no
-// branch around them and the wait for them can be placed by hand.
-__device__ __forceinline__ void fetch_chunk(const SweepArgs &a, int c, int stride, ChunkRows &r) {
-    const int cc = c < a.words ? c : a.words - 1;
-    int p = 64 * cc + (int)(threadIdx.x & 63);
-    p = p < a.n ? p : a.n - 1;
-    const int col0 = (cc / a.strip) * a.strip;
-    const int tile = p >> 6;  // == cc
-    r.diag = a.mask[(size_t)p * stride + (size_t)(tile - col0)];
-    r.cnt = a.rowcnt[p];
-    const uint4 *ip = reinterpret_cast<const uint4 *>(a.lidx + (size_t)p * ROW_LIST_CAP);
-    const ulonglong2 *vp = reinterpret_cast<const ulonglong2 *>(a.lval + (size_t)p * ROW_LIST_CAP);
-#pragma unroll
-    for (int j = 0; j < ROW_LIST_CAP / 4; ++j) {
-        const uint4 q = ip[j];
-        r.idx[4 * j] = q.x;
-        r.idx[4 * j + 1] = q.y;
-        r.idx[4 * j + 2] = q.z;
-        r.idx[4 * j + 3] = q.w;
+// Hand-over flags.  Everything handed over between waves lives in LDS, and
+// the LDS unit performs one wave's operations in the order they are issued.
+// So a writer that issues its data writes and then the flag write, and a
+// reader that sees the flag and only then issues its data reads, are ordered
+// by the hardware; only the compiler must be kept from moving memory accesses
+// across the flag (the empty asm with a memory clobber).  Workgroup-scope
+// release/acquire would also be correct, but a release waits for every
+// outstanding global load, stalling the prefetch this kernel relies on.
+__device__ __forceinline__ void compiler_barrier() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t flag_load(const uint32_t *p) {
+    const uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    compiler_barrier();
+    return v;
+}
+__device__ __forceinline__ void flag_store(uint32_t *p, uint32_t v) {
+    compiler_barrier();
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Wait until *flag >= target.  Returns false (and raises the abort flag and
+// the internal error bit) if it takes too long or another wave aborted.
+__device__ __forceinline__ bool wait_flag(const uint32_t *flag, uint32_t target, SweepSmem &sm,
+                                          Ctrl *ctrl) {
+    uint32_t spins = 0;
+    while (flag_load(flag) < target) {
+        if (flag_load(&sm.abort)) return false;
+        if (++spins > SPIN_LIMIT) {
+            if ((threadIdx.x & 63) == 0) {
+                flag_store(&sm.abort, 1u);
+                atomicOr(&ctrl->error, ERR_INTERNAL);
+            }
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
     }
-#pragma unroll
-    for (int j = 0; j < ROW_LIST_CAP / 2; ++j) {
-        const ulonglong2 q = vp[j];
-        r.val[2 * j] = q.x;
-        r.val[2 * j + 1] = q.y;
-    }
+    return true;
 }
 
 // s_waitcnt vmcnt(0): every vector memory load issued so far has returned.
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Settle chunk c from `cur` (already loaded) and propagate its kept rows.
-__device__ __forceinline__ void sweep_chunk(const SweepArgs &a, int c, int stride,
-                                            const ChunkRows &cur, uint64_t *removed) {
-    const int lane = threadIdx.x & 63;
-    // keep the compiler from moving this chunk's LDS accesses across the
-    // previous chunk's (the hardware keeps one wave's LDS operations in order)
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    const uint64_t valid = rows_valid(c, a.n);
-    const uint64_t nz = __ballot(cur.diag != 0ull);
-    uint64_t rem = uniform64(removed[c]);
-    uint64_t cand = ~rem & nz & valid;
-    while (cand) {
-        const int k = __builtin_amdgcn_readfirstlane(__builtin_ctzll(cand));
-        rem |= read_lane64(cur.diag, k);
-        const uint64_t above = k == 63 ? 0ull : (~0ull << (k + 1));
-        cand = ~rem & nz & valid & above;
-    }
-    if (lane == 0) removed[c] = rem;
-    const uint64_t kept = ~rem & valid;
-    const bool mine = (kept >> lane) & 1ull;
-    if (mine && cur.cnt <= (uint32_t)ROW_LIST_CAP) {
+// First-level data of a chunk: lane k's words for tiles c .. c + NEAR (rows
+// 64c + k; zeros past n or outside the band) and the tile's list length.
+struct Level1 {
+    uint64_t near[NEAR + 1];
+    uint32_t count;
+};
+
+__device__ __forceinline__ void load_level1(const SweepArgs &a, int c, Level1 &l) {
+    const int p = 64 * c + (int)(threadIdx.x & 63);
 #pragma unroll
-        for (int j = 0; j < ROW_LIST_CAP; ++j) {
-            const uint32_t w = cur.idx[j];
-            if ((uint32_t)j < cur.cnt && w > (uint32_t)c) atomicOr(&removed[w], cur.val[j]);
+    for (int j = 0; j <= NEAR; ++j) l.near[j] = a.tnear[(size_t)j * a.npad + p];
+    l.count = a.tcount[c];
+}
+
+// The tile's list entries, round i holding entry 64 i + lane.
+struct Entries {
+    uint32_t wk[RMAX];
+    uint64_t val[RMAX];
+};
+
+__device__ __forceinline__ int rounds_of(uint32_t count) {
+    const uint32_t held = count < (uint32_t)TILE_LIST_CAP ? count : (uint32_t)TILE_LIST_CAP;
+    return (int)((held + 63u) / 64u);
+}
+
+__device__ __forceinline__ void load_entries(const SweepArgs &a, int c, int rounds, Entries &e) {
+    const size_t base = (size_t)c * TILE_LIST_CAP + (threadIdx.x & 63);
+#pragma unroll
+    for (int i = 0; i < RMAX; ++i) {
+        if (i < rounds) {
+            e.wk[i] = a.tent_wk[base + 64 * i];
+            e.val[i] = a.tent_val[base + 64 * i];
         }
     }
-    // Rows with more nonzero words than their list holds: read the dense
-    // rows, four rows and two 64-word blocks per row per round, so that eight
-    // loads are in flight at once.
-    uint64_t over = __ballot(mine && cur.cnt > (uint32_t)ROW_LIST_CAP);
-    if (over) {
-        const int cend = a.tile_cend[c];
-        const int col0 = (c / a.strip) * a.strip;
-        while (over) {
-            int kr[4];
+}
+
+__device__ __forceinline__ void apply_entry(uint32_t wk, uint64_t val, bool live, uint64_t kept,
+                                            int c, uint64_t *removed) {
+    const uint32_t k = wk & 63u, w = wk >> 6;
+    if (live && ((kept >> k) & 1ull) && w > (uint32_t)(c + NEAR)) atomicOr(&removed[w], val);
+}
+
+// Apply rounds I, I+1, ... < rounds of the register-held entries.  Nested
+// uniform branches (rather than a loop) keep every register index constant
+// and skip the rounds that do not exist.
+template <int I>
+__device__ __forceinline__ void apply_rounds(const Entries &e, int rounds, uint32_t count,
+                                             uint64_t kept, int c, uint64_t *removed) {
+    if constexpr (I < RMAX) {
+        if (I < rounds) {
+            const uint32_t lane = threadIdx.x & 63;
+            apply_entry(e.wk[I], e.val[I], 64u * I + lane < count, kept, c, removed);
+            apply_rounds<I + 1>(e, rounds, count, kept, c, removed);
+        }
+    }
+}
+
+// OR of a 64-bit value over the lanes of the wave (DPP prefix over rows of
+// 16 lanes, then row broadcasts; lane 63 ends up holding the whole wave).
+__device__ __forceinline__ uint32_t wave_or32(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
+    const uint32_t lo = wave_or32((uint32_t)v);
+    const uint32_t hi = wave_or32((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// What the resolver reads from LDS for one chunk: the two hand-over flags,
+// the staged words and the chunk's removed word, issued as one batch.
+struct ResolverBatch {
+    uint32_t f_data, f_app;
+    uint64_t nw[NEAR + 1];
+    uint64_t rem;
+};
+
+__device__ __forceinline__ void resolver_slots(int c, int &slot, int &par, uint32_t &app_slot,
+                                               uint32_t &app_need) {
+    slot = c % APPLIERS;
+    par = (c / APPLIERS) & 1;
+    const int lag = c - NEAR - 1;  // the chunk whose far words must be in
+    app_slot = (uint32_t)((lag + 2 * APPLIERS) % APPLIERS);
+    app_need = lag >= 0 ? (uint32_t)lag + 1u : 0u;
+}
+
+// The LDS performs the reads in order, so data read after a flag that is
+// already set is the data that flag announces.
+__device__ __forceinline__ void resolver_read(int c, const uint64_t *removed, SweepSmem &sm,
+                                              ResolverBatch &b) {
+    const int lane = threadIdx.x & 63;
+    int slot, par;
+    uint32_t app_slot, app_need;
+    resolver_slots(c, slot, par, app_slot, app_need);
+    b.f_data = flag_load(&sm.data_ready[slot][par]);
+    b.f_app = flag_load(&sm.applied[app_slot]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                kr[q] = over ? __builtin_amdgcn_readfirstlane(__builtin_ctzll(over)) : -1;
-                over &= over - 1ull;
+    for (int j = 0; j <= NEAR; ++j) b.nw[j] = sm.near[slot][par][j][lane];
+    b.rem = removed[c];
+    compiler_barrier();
+}
+
+// Resolver: settle the chunks in order.  The reads for chunk c + 1 are issued
+// before chunk c is settled; the kept rows' words for tile c + 1 reach chunk
+// c + 1 through a register (a wave-wide OR), the words for tiles c + 2 ..
+// c + NEAR through LDS atomics, which the hardware orders before the later
+// reads of those words.
+__device__ void resolve_chunks(const SweepArgs &a, uint64_t *removed, SweepSmem &sm) {
+    const int lane = threadIdx.x & 63;
+    const int W = a.words;
+    ResolverBatch cur, nxt;
+    resolver_read(0, removed, sm, cur);
+    uint64_t carry = 0ull;  // kept rows of chunk c - 1, words for tile c
+    for (int c = 0; c < W; ++c) {
+        int slot, par;
+        uint32_t app_slot, app_need;
+        resolver_slots(c, slot, par, app_slot, app_need);
+        if (cur.f_data < (uint32_t)c + 1u || cur.f_app < app_need) {
+            if (!wait_flag(&sm.data_ready[slot][par], (uint32_t)c + 1u, sm, a.ctrl)) return;
+            if (!wait_flag(&sm.applied[app_slot], app_need, sm, a.ctrl)) return;
+            resolver_read(c, removed, sm, cur);
+        }
+        if (c + 1 < W) resolver_read(c + 1, removed, sm, nxt);
+        const uint64_t d = cur.nw[0];
+        const uint64_t valid = rows_valid(c, a.n);
+        const uint64_t nz = __ballot(d != 0ull);
+        uint64_t rem = uniform64(cur.rem) | carry;
+        uint64_t cand = ~rem & nz & valid;
+        while (cand) {
+            const int k = __builtin_amdgcn_readfirstlane(__builtin_ctzll(cand));
+            rem |= read_lane64(d, k);
+            const uint64_t above = k == 63 ? 0ull : (~0ull << (k + 1));
+            cand = ~rem & nz & valid & above;
+        }
+        const uint64_t kept = ~rem & valid;
+        const bool mine = (kept >> lane) & 1ull;
+        // Most kept rows have no word near them, and lanes that OR into the
+        // same LDS word serialise, so only nonzero words are sent.
+        carry = __ballot(mine && cur.nw[1] != 0ull) ? wave_or64(mine ? cur.nw[1] : 0ull) : 0ull;
+        if (mine) {
+            // removed has NEAR spare words past the end for the last chunks
+#pragma unroll
+            for (int j = 2; j <= NEAR; ++j)
+                if (cur.nw[j] != 0ull) atomicOr(&removed[c + j], cur.nw[j]);
+        }
+        if (lane == 0) {
+            removed[c] = rem;
+            sm.kept[slot] = kept;
+            flag_store(&sm.k_ready[slot], (uint32_t)c + 1u);
+        }
+        cur = nxt;
+    }
+}
+
+// Kept rows of an overflowed tile: OR their dense words for tiles
+// c + NEAR + 1 .. cend - 1, four rows and two 64-word blocks per row per round.
+__device__ void apply_dense(const SweepArgs &a, int c, int stride, uint64_t kept,
+                            uint64_t *removed) {
+    const int lane = threadIdx.x & 63;
+    const int cend = a.tile_cend[c];
+    const int col0 = (c / a.strip) * a.strip;
+    uint64_t rows = kept;
+    while (rows) {
+        int kr[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            kr[t] = rows ? __builtin_amdgcn_readfirstlane(__builtin_ctzll(rows)) : -1;
+            rows &= rows - 1ull;
+        }
+        for (int w0 = c + NEAR + 1; w0 < cend; w0 += 128) {
+            uint64_t v[4][2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int w = w0 + 64 * j + lane;
+                    v[t][j] = (kr[t] >= 0 && w < cend)
+                                  ? a.mask[(size_t)(64 * c + kr[t]) * stride + (size_t)(w - col0)]
+                                  : 0ull;
+                }
             }
-            for (int w0 = c + 1; w0 < cend; w0 += 128) {
-                uint64_t v[4][2];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+            for (int t = 0; t < 4; ++t) {
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int w = w0 + 64 * j + lane;
-                        v[q][j] = (kr[q] >= 0 && w < cend)
-                                      ? a.mask[(size_t)(64 * c + kr[q]) * stride + (size_t)(w - col0)]
-                                      : 0ull;
-                    }
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        if (v[q][j]) atomicOr(&removed[w0 + 64 * j + lane], v[q][j]);
-                }
+                for (int j = 0; j < 2; ++j)
+                    if (v[t][j]) atomicOr(&removed[w0 + 64 * j + lane], v[t][j]);
             }
         }
     }
 }
 
+// Applier q (1..APPLIERS): chunks q-1, q-1+APPLIERS, ...  Loads run two
+// levels ahead: while chunk c is waiting for its kept set, the first level
+// (diagonal words, list length) of chunk c + 2A and the entries of chunk
+// c + A are in flight (A = APPLIERS).
+__device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, SweepSmem &sm,
+                             int q) {
+    const int lane = threadIdx.x & 63;
+    const int W = a.words;
+    const int slot = q - 1;
+    const int A = APPLIERS;
+    int c = q - 1;
+    if (c >= W) return;
+    Level1 l1;
+    Entries e;
+    // prologue: chunk c staged, its entries and chunk c + A's first level issued
+    load_level1(a, c, l1);
+    wait_loads();
+#pragma unroll
+    for (int j = 0; j <= NEAR; ++j) sm.near[slot][0][j][lane] = l1.near[j];
+    if (lane == 0) flag_store(&sm.data_ready[slot][0], (uint32_t)c + 1u);
+    uint32_t count = __builtin_amdgcn_readfirstlane(l1.count);
+    load_entries(a, c, rounds_of(count), e);
+    if (c + A < W) load_level1(a, c + A, l1);
+    for (; c < W; c += A) {
+        wait_loads();
+        uint32_t count_next = 0;
+        if (c + A < W) {
+            const int par = ((c + A) / A) & 1;
+#pragma unroll
+            for (int j = 0; j <= NEAR; ++j) sm.near[slot][par][j][lane] = l1.near[j];
+            if (lane == 0) flag_store(&sm.data_ready[slot][par], (uint32_t)(c + A) + 1u);
+            count_next = __builtin_amdgcn_readfirstlane(l1.count);
+            if (c + 2 * A < W) load_level1(a, c + 2 * A, l1);
+        }
+        if (!wait_flag(&sm.k_ready[slot], (uint32_t)c + 1u, sm, a.ctrl)) return;
+        const uint64_t kept = uniform64(sm.kept[slot]);
+        if (kept) {
+            if (count > (uint32_t)TILE_LIST_CAP) {
+                apply_dense(a, c, stride, kept, removed);
+            } else {
+                const int rounds = rounds_of(count);
+                apply_rounds<0>(e, rounds, count, kept, c, removed);
+                // rounds beyond the registers: load and apply them now
+                const size_t base = (size_t)c * TILE_LIST_CAP + lane;
+                for (int i = RMAX; i < rounds; ++i) {
+                    const uint32_t wk = a.tent_wk[base + 64 * i];
+                    const uint64_t val = a.tent_val[base + 64 * i];
+                    apply_entry(wk, val, (uint32_t)(64 * i + lane) < count, kept, c, removed);
+                }
+            }
+        }
+        if (lane == 0) flag_store(&sm.applied[slot], (uint32_t)c + 1u);
+        if (c + A < W) load_entries(a, c + A, rounds_of(count_next), e);
+        count = count_next;
+    }
+}
+
 __global__ __launch_bounds__(NT) void sweep_kernel(SweepArgs a) {
     extern __shared__ uint64_t removed[];
-    __shared__ uint32_t part[NWAVES], part2[NWAVES], tot;
+    __shared__ SweepSmem sm;
     const int tid = threadIdx.x;
+    const int wave = tid >> 6;
     const int W = a.words, n = a.n;
     const int stride = a.grouped ? a.ctrl->band_stride : a.mstride;
 
-    for (int w = tid; w < W; w += NT) removed[w] = 0ull;
+    for (int w = tid; w < W + NEAR_TILES; w += NT) removed[w] = 0ull;
+    if (tid < APPLIERS) {
+        sm.data_ready[tid][0] = 0u;
+        sm.data_ready[tid][1] = 0u;
+        sm.k_ready[tid] = 0u;
+        sm.applied[tid] = 0u;
+    }
+    if (tid == 0) sm.abort = 0u;
     __syncthreads();
 
-    if ((tid >> 6) == 0) {
-        // two register sets, alternating, so the prefetch needs no copies
-        // Each step first waits for the rows loaded in the previous step,
-        // then issues the loads for the next chunk, then settles this one:
-        // the loads of chunk c + 1 fly while chunk c is being resolved.
-        ChunkRows ra, rb;
-        fetch_chunk(a, 0, stride, ra);
-        for (int c = 0; c < W; c += 2) {
-            wait_loads();
-            fetch_chunk(a, c + 1, stride, rb);
-            sweep_chunk(a, c, stride, ra, removed);
-            if (c + 1 >= W) break;
-            wait_loads();
-            fetch_chunk(a, c + 2, stride, ra);
-            sweep_chunk(a, c + 1, stride, rb, removed);
-        }
-    }
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    if (wv == 0) resolve_chunks(a, removed, sm);
+    else apply_chunks(a, stride, removed, sm, wv);
     __syncthreads();
+    if (sm.abort) return;
 
     // kept bitmap = complement of removed, limited to existing boxes
     for (int w = tid; w < W; w += NT) a.kept[w] = ~removed[w] & rows_valid(w, n);
@@ -244,7 +458,7 @@ __global__ __launch_bounds__(NT) void sweep_kernel(SweepArgs a) {
     uint32_t cnt = 0;
     for (int w = lo; w < hi; ++w) cnt += (uint32_t)__popcll(~removed[w] & rows_valid(w, n));
     uint32_t total = 0;
-    uint32_t pos = block_excl_sum(cnt, part, part2, &tot, &total);
+    uint32_t pos = block_excl_sum(cnt, sm.part, sm.part2, &sm.tot, &total);
     for (int w = lo; w < hi; ++w) {
         uint64_t bits = ~removed[w] & rows_valid(w, n);
         while (bits) {
@@ -311,18 +525,20 @@ hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_
     a.mask = w.mask;
     a.tile_cend = w.tile_cend;
     a.order = w.order;
-    a.rowcnt = w.rowcnt;
-    a.lidx = w.lidx;
-    a.lval = w.lval;
+    a.tcount = w.tcount;
+    a.tent_wk = w.tent_wk;
+    a.tent_val = w.tent_val;
+    a.tnear = w.tnear;
     a.ctrl = w.ctrl;
     a.kept = w.kept;
     a.keep_out = keep_out;
     a.n = P.n;
     a.words = (int)L.words;
+    a.npad = (int)L.npad;
     a.mstride = (int)L.mstride;
     a.strip = P.strip;
     a.grouped = P.grouped ? 1 : 0;
-    const size_t lds = (size_t)L.words * sizeof(uint64_t);
+    const size_t lds = (size_t)(L.words + NEAR_TILES) * sizeof(uint64_t);
     hipLaunchKernelGGL(sweep_kernel, dim3(1), dim3(NT), lds, stream, a);
     return hipGetLastError();
 }
