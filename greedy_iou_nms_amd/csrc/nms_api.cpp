@@ -20,6 +20,7 @@ bool make_layout(int64_t n, Layout *out) {
     L.npad = 64 * L.words;
     // worst-case row stride over both strip widths (a multiple of 16 words)
     L.mstride = ((L.words + STRIP_SINGLE - 1) / STRIP_SINGLE) * STRIP_SINGLE;
+    L.tiles = (L.npad + RADIX_TILE - 1) / RADIX_TILE;
     const size_t np = (size_t)L.npad;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -45,6 +46,10 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_tent_wk = take((size_t)L.words * TILE_LIST_CAP * 4);
     L.off_tent_val = take((size_t)L.words * TILE_LIST_CAP * 8);
     L.off_tnear = take(np * 8 * (NEAR_TILES + 1));
+    L.off_hist_tile = take((size_t)L.tiles * 4 * 256 * 4);
+    L.off_lb_status = take((size_t)4 * L.tiles * 256 * 4);
+    L.off_tickets = take(4 * 4);
+    L.off_err_tile = take((size_t)L.tiles * 4);
     L.off_mask = take((size_t)n * (size_t)L.mstride * 8);
     L.total = off;
     *out = L;
@@ -72,6 +77,10 @@ Work carve(void *workspace, const Layout &L) {
     w.tent_wk = reinterpret_cast<uint32_t *>(b + L.off_tent_wk);
     w.tent_val = reinterpret_cast<uint64_t *>(b + L.off_tent_val);
     w.tnear = reinterpret_cast<uint64_t *>(b + L.off_tnear);
+    w.hist_tile = reinterpret_cast<uint32_t *>(b + L.off_hist_tile);
+    w.lb_status = reinterpret_cast<uint32_t *>(b + L.off_lb_status);
+    w.tickets = reinterpret_cast<uint32_t *>(b + L.off_tickets);
+    w.err_tile = reinterpret_cast<uint32_t *>(b + L.off_err_tile);
     w.mask = reinterpret_cast<uint64_t *>(b + L.off_mask);
     return w;
 }
@@ -197,9 +206,10 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     };
 
     hipError_t e = mark(0);
-    if (e == hipSuccess) e = launch_sort(P, L, w, stream);
+    if (e == hipSuccess) e = P.grouped ? launch_sort(P, L, w, stream)
+                                       : launch_radix_sort(P, L, w, stream);
     if (e == hipSuccess) e = mark(1);
-    if (e == hipSuccess) e = launch_gather(P, L, w, stream);
+    if (e == hipSuccess && P.grouped) e = launch_gather(P, L, w, stream);
     if (e == hipSuccess) e = mark(2);
     if (e == hipSuccess) e = launch_mask(P, L, w, stream);
     if (e == hipSuccess) e = mark(3);
@@ -290,7 +300,7 @@ nms_status nms_debug_order(const float *scores, int64_t n, const int32_t *class_
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     const Problem P = make_problem(nullptr, scores, n, 0.5f, class_ids, batch_offsets, num_images);
     const Work w = carve(workspace, L);
-    hipError_t e = launch_sort(P, L, w, stream);
+    hipError_t e = P.grouped ? launch_sort(P, L, w, stream) : launch_radix_sort(P, L, w, stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(order_out, w.order, (size_t)n * 4, hipMemcpyDeviceToDevice, stream);
     if (e == hipSuccess && score_order_out) {
@@ -327,8 +337,8 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
     const Problem P =
         make_problem(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images);
     const Work w = carve(workspace, L);
-    hipError_t e = launch_sort(P, L, w, stream);
-    if (e == hipSuccess) e = launch_gather(P, L, w, stream);
+    hipError_t e = P.grouped ? launch_sort(P, L, w, stream) : launch_radix_sort(P, L, w, stream);
+    if (e == hipSuccess && P.grouped) e = launch_gather(P, L, w, stream);
     if (e == hipSuccess) e = launch_mask(P, L, w, stream);
     if (e == hipSuccess) e = launch_expand_mask(P, L, w, mask_out, stream);
     if (e == hipSuccess && order_out)

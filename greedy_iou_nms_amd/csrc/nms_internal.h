@@ -36,6 +36,12 @@ constexpr int STRIP_SINGLE = 16;
 constexpr int STRIP_GROUPED = 4;
 
 constexpr int SORT_THREADS = 1024;
+
+// Multi-workgroup radix sort (one image): a workgroup of RADIX_THREADS ranks
+// one tile of RADIX_TILE keys per pass.
+constexpr int RADIX_THREADS = 256;
+constexpr int RADIX_E = 16;
+constexpr int RADIX_TILE = RADIX_THREADS * RADIX_E;
 constexpr int SWEEP_THREADS = 512;
 constexpr int MASK_THREADS = 256;
 
@@ -57,10 +63,12 @@ struct Layout {
     int64_t words = 0;      // W = ceil(n / 64): words per full mask row, row tiles
     int64_t npad = 0;       // 64 * W
     int64_t mstride = 0;    // worst-case mask row stride in words
+    int64_t tiles = 0;      // radix-sort tiles, ceil(npad / RADIX_TILE)
     size_t off_ctrl = 0, off_keys0 = 0, off_keys1 = 0, off_vals0 = 0, off_vals1 = 0;
     size_t off_order = 0, off_score_order = 0, off_seg = 0, off_inv = 0;
     size_t off_sb = 0, off_area = 0, off_tile_cend = 0, off_item_base = 0, off_kept = 0;
     size_t off_tcount = 0, off_tent_wk = 0, off_tent_val = 0, off_tnear = 0;
+    size_t off_hist_tile = 0, off_lb_status = 0, off_tickets = 0, off_err_tile = 0;
     size_t off_mask = 0, total = 0;
 };
 
@@ -87,6 +95,13 @@ struct Work {
     // 0 where that tile lies outside the row's band
     uint64_t *tnear;
     uint64_t *mask;        // suppression bitmask rows
+    // radix sort, one image: per-tile 4-digit histograms [tile][4][256],
+    // look-back status words [pass][tile][256], one ticket per pass, and
+    // per-tile error bits from key generation
+    uint32_t *hist_tile;
+    uint32_t *lb_status;
+    uint32_t *tickets;
+    uint32_t *err_tile;
 };
 
 Work carve(void *workspace, const Layout &L);
@@ -104,6 +119,10 @@ struct Problem {
 };
 
 // Stage launchers; all enqueue on `stream` and return the launch status.
+// One image: launch_radix_sort sorts and also gathers the sorted boxes (no
+// separate gather launch).  Grouped input: launch_sort, then launch_gather.
+hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
+                             hipStream_t stream);
 hipError_t launch_sort(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
 hipError_t launch_gather(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
 hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
