@@ -80,7 +80,13 @@ __device__ __forceinline__ bool suppresses(float rx1, float ry1, float rx2, floa
     const float xx2 = min2(rx2, cx2, ninf);
     const float yy2 = min2(ry2, cy2, ninf);
     const float w = max2(xx2 - xx1, 0.0f, pinf);
-    const float h = max2(yy2 - yy1, 0.0f, pinf);
+    // The division-free tests (positive areas, t > 0) need only one clamp:
+    // with w >= 0 and h unclamped, boxes that do not overlap give w * h <= 0
+    // (a zero or negative product, never above m * union > 0), so the
+    // decision is the same as with max(h, 0); boxes that overlap give the
+    // very product of the definition.  The literal test keeps both clamps.
+    const float dh = yy2 - yy1;
+    const float h = MODE == MODE_LITERAL ? max2(dh, 0.0f, pinf) : dh;
     const float inter = w * h;
     const float uni = (ra + ca) - inter;
     return exceeds<MODE>(inter, uni, t, mid);

@@ -6,7 +6,7 @@
 #include <cmath>
 #include <cstring>
 
-#include "../../include/greedy_nms.h"
+#include "greedy_nms.h"
 #include "nms_internal.h"
 
 namespace gnms {

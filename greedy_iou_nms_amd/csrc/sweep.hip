@@ -117,15 +117,25 @@ constexpr uint32_t SPIN_LIMIT = 1u << 23;
 constexpr int RMAX = 16;
 
 constexpr int NEAR = NEAR_TILES;
+static_assert(NEAR >= 2, "the resolver carries the words for the next two tiles in registers");
+
+// Appliers have slack; their polling shares the LDS with the resolver.
+constexpr int APPLIER_SLEEP = 1;
 
 struct SweepSmem {
     uint64_t near[APPLIERS][2][NEAR + 1][64];  // staged words for tiles c .. c + NEAR
-    uint64_t kept[APPLIERS];          // published kept set of the slot's chunk
+    // per staged chunk: rows whose diagonal word is nonzero, rows with a
+    // nonzero word for one of the next NEAR tiles
+    uint64_t summ[APPLIERS][2][2];
     uint32_t data_ready[APPLIERS][2]; // chunk + 1 once diag/super are staged
-    uint32_t k_ready[APPLIERS];       // chunk + 1 once kept[] is published
+    uint32_t k_ready[APPLIERS];       // chunk + 1 once removed[chunk] is final
     uint32_t applied[APPLIERS];       // chunk + 1 once its far words are ORed in
     uint32_t abort;
     uint32_t part[NWAVES], part2[NWAVES], tot;
+    // where the resolver's lanes other than lane 0 direct their publishing
+    // writes (every lane stores, so the store needs no branch)
+    uint64_t sink_rem[64];
+    uint32_t sink_flag[64];
 };
 
 // Hand-over flags.  Everything handed over between waves lives in LDS, and
@@ -150,6 +160,7 @@ __device__ __forceinline__ void flag_store(uint32_t *p, uint32_t v) {
 
 // Wait until *flag >= target.  Returns false (and raises the abort flag and
 // the internal error bit) if it takes too long or another wave aborted.
+template <int SLEEP = 1>
 __device__ __forceinline__ bool wait_flag(const uint32_t *flag, uint32_t target, SweepSmem &sm,
                                           Ctrl *ctrl) {
     uint32_t spins = 0;
@@ -162,7 +173,7 @@ __device__ __forceinline__ bool wait_flag(const uint32_t *flag, uint32_t target,
             }
             return false;
         }
-        __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_s_sleep(SLEEP);
     }
     return true;
 }
@@ -182,6 +193,25 @@ __device__ __forceinline__ void load_level1(const SweepArgs &a, int c, Level1 &l
 #pragma unroll
     for (int j = 0; j <= NEAR; ++j) l.near[j] = a.tnear[(size_t)j * a.npad + p];
     l.count = a.tcount[c];
+}
+
+// Stage chunk c's near words and their summary masks for the resolver, then
+// announce them.
+__device__ __forceinline__ void stage_level1(const Level1 &l, int c, int slot, int par,
+                                             SweepSmem &sm) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j <= NEAR; ++j) sm.near[slot][par][j][lane] = l.near[j];
+    uint64_t ahead = 0ull;
+#pragma unroll
+    for (int j = 1; j <= NEAR; ++j) ahead |= l.near[j];
+    const uint64_t nz0 = __ballot(l.near[0] != 0ull);
+    const uint64_t nzn = __ballot(ahead != 0ull);
+    if (lane == 0) {
+        sm.summ[slot][par][0] = nz0;
+        sm.summ[slot][par][1] = nzn;
+        flag_store(&sm.data_ready[slot][par], (uint32_t)c + 1u);
+    }
 }
 
 // The tile's list entries, round i holding entry 64 i + lane.
@@ -244,88 +274,153 @@ __device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// What the resolver reads from LDS for one chunk: the two hand-over flags,
-// the staged words and the chunk's removed word, issued as one batch.
+// What the resolver reads from LDS for one chunk, issued as one batch: the
+// two hand-over flags, the chunk's summary masks and removed word (the same
+// for every lane) and lane k's staged words for row 64c + k.
 struct ResolverBatch {
     uint32_t f_data, f_app;
+    uint64_t nz0, nzn, rem;
     uint64_t nw[NEAR + 1];
-    uint64_t rem;
 };
 
-__device__ __forceinline__ void resolver_slots(int c, int &slot, int &par, uint32_t &app_slot,
-                                               uint32_t &app_need) {
-    slot = c % APPLIERS;
-    par = (c / APPLIERS) & 1;
-    const int lag = c - NEAR - 1;  // the chunk whose far words must be in
-    app_slot = (uint32_t)((lag + 2 * APPLIERS) % APPLIERS);
-    app_need = lag >= 0 ? (uint32_t)lag + 1u : 0u;
-}
+// Where chunk c's data sits: slot c mod A, parity (c / A) mod 2, and the
+// slot of chunk c - NEAR - 1, whose far words must be in before word c is
+// read.  Stepped from chunk to chunk instead of divided out.
+struct ResolverPos {
+    int slot, par, app_slot;
+    __device__ __forceinline__ void init(int c) {
+        slot = c % APPLIERS;
+        par = (c / APPLIERS) & 1;
+        app_slot = ((c - NEAR - 1) % APPLIERS + APPLIERS) % APPLIERS;
+    }
+    __device__ __forceinline__ void next() {
+        if (++slot == APPLIERS) {
+            slot = 0;
+            par ^= 1;
+        }
+        if (++app_slot == APPLIERS) app_slot = 0;
+    }
+};
 
 // The LDS performs the reads in order, so data read after a flag that is
 // already set is the data that flag announces.
-__device__ __forceinline__ void resolver_read(int c, const uint64_t *removed, SweepSmem &sm,
-                                              ResolverBatch &b) {
+__device__ __forceinline__ void resolver_read(int c, const ResolverPos &q, const uint64_t *removed,
+                                              SweepSmem &sm, ResolverBatch &b) {
     const int lane = threadIdx.x & 63;
-    int slot, par;
-    uint32_t app_slot, app_need;
-    resolver_slots(c, slot, par, app_slot, app_need);
-    b.f_data = flag_load(&sm.data_ready[slot][par]);
-    b.f_app = flag_load(&sm.applied[app_slot]);
-#pragma unroll
-    for (int j = 0; j <= NEAR; ++j) b.nw[j] = sm.near[slot][par][j][lane];
+    b.f_data = flag_load(&sm.data_ready[q.slot][q.par]);
+    b.f_app = flag_load(&sm.applied[q.app_slot]);
+    b.nz0 = sm.summ[q.slot][q.par][0];
+    b.nzn = sm.summ[q.slot][q.par][1];
     b.rem = removed[c];
+#pragma unroll
+    for (int j = 0; j <= NEAR; ++j) b.nw[j] = sm.near[q.slot][q.par][j][lane];
     compiler_barrier();
 }
 
-// Resolver: settle the chunks in order.  The reads for chunk c + 1 are issued
-// before chunk c is settled; the kept rows' words for tile c + 1 reach chunk
-// c + 1 through a register (a wave-wide OR), the words for tiles c + 2 ..
-// c + NEAR through LDS atomics, which the hardware orders before the later
-// reads of those words.
-__device__ void resolve_chunks(const SweepArgs &a, uint64_t *removed, SweepSmem &sm) {
+// s_waitcnt lgkmcnt(0): every LDS access issued so far has completed.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// Resolver state carried from chunk to chunk in scalar registers.
+struct ResolverState {
+    ResolverPos at;      // chunk c
+    ResolverPos ahead;   // chunk c + 2, whose batch is read while c is settled
+    uint64_t carry1;     // kept rows' words for tile c (chunks c - 1 and c - 2)
+    uint64_t carry2;     // kept rows' words for tile c + 1 (chunk c - 1)
+};
+
+// Settle chunk c from its batch cur, after issuing the reads of chunk c + 2
+// into ahead.  Returns false if a wait gave up.
+//
+// Word c + 2 is read before chunk c is settled.  That is safe because chunk
+// c's and chunk c + 1's words for it travel in registers (carry2, then
+// carry1), the words of chunks c - 1 and c - 2 for it were ORed into LDS
+// (atomics) before this read is issued, and the far words of chunks up to
+// c + 2 - NEAR - 1 are in once the applied flag read with it says so.  Reading
+// two chunks ahead keeps LDS latency, and this chunk's own LDS writes, off
+// the path from one chunk to the next.
+__device__ __forceinline__ bool resolve_one(const SweepArgs &a, uint64_t *removed, SweepSmem &sm,
+                                            int c, ResolverState &st, ResolverBatch &cur,
+                                            ResolverBatch &ahead) {
     const int lane = threadIdx.x & 63;
-    const int W = a.words;
-    ResolverBatch cur, nxt;
-    resolver_read(0, removed, sm, cur);
-    uint64_t carry = 0ull;  // kept rows of chunk c - 1, words for tile c
-    for (int c = 0; c < W; ++c) {
-        int slot, par;
-        uint32_t app_slot, app_need;
-        resolver_slots(c, slot, par, app_slot, app_need);
-        if (cur.f_data < (uint32_t)c + 1u || cur.f_app < app_need) {
-            if (!wait_flag(&sm.data_ready[slot][par], (uint32_t)c + 1u, sm, a.ctrl)) return;
-            if (!wait_flag(&sm.applied[app_slot], app_need, sm, a.ctrl)) return;
-            resolver_read(c, removed, sm, cur);
-        }
-        if (c + 1 < W) resolver_read(c + 1, removed, sm, nxt);
+    constexpr int LAG = NEAR + 1;
+    const uint32_t app_need = c >= LAG ? (uint32_t)(c - LAG) + 1u : 0u;
+    if (cur.f_data < (uint32_t)c + 1u || cur.f_app < app_need) {
+        if (!wait_flag(&sm.data_ready[st.at.slot][st.at.par], (uint32_t)c + 1u, sm, a.ctrl))
+            return false;
+        if (!wait_flag(&sm.applied[st.at.app_slot], app_need, sm, a.ctrl)) return false;
+        resolver_read(c, st.at, removed, sm, cur);
+        wait_lds();
+    }
+    // Issued for every chunk, also past the last one (removed[] has NEAR >= 2
+    // spare words and the staging slots are a ring), so that the number of
+    // LDS accesses in flight is the same on every path through the loop and
+    // the compiler's waits for a batch do not wait for later accesses.
+    st.ahead.next();
+    resolver_read(c + 2, st.ahead, removed, sm, ahead);
+    const int slot = st.at.slot;
+    st.at.next();
+
+    const uint64_t valid = rows_valid(c, a.n);
+    uint64_t rem = uniform64(cur.rem) | st.carry1;
+    uint64_t cand = ~rem & uniform64(cur.nz0) & valid;
+    if (cand) {
         const uint64_t d = cur.nw[0];
-        const uint64_t valid = rows_valid(c, a.n);
-        const uint64_t nz = __ballot(d != 0ull);
-        uint64_t rem = uniform64(cur.rem) | carry;
-        uint64_t cand = ~rem & nz & valid;
-        while (cand) {
-            const int k = __builtin_amdgcn_readfirstlane(__builtin_ctzll(cand));
+        const uint64_t nz = cand;
+        do {
+            const int k = __builtin_ctzll(cand);
             rem |= read_lane64(d, k);
             const uint64_t above = k == 63 ? 0ull : (~0ull << (k + 1));
-            cand = ~rem & nz & valid & above;
-        }
-        const uint64_t kept = ~rem & valid;
+            cand = ~rem & nz & above;
+        } while (cand);
+    }
+    const uint64_t kept = ~rem & valid;
+    uint64_t c1 = st.carry2, c2 = 0ull;
+    if (kept & uniform64(cur.nzn)) {
         const bool mine = (kept >> lane) & 1ull;
-        // Most kept rows have no word near them, and lanes that OR into the
-        // same LDS word serialise, so only nonzero words are sent.
-        carry = __ballot(mine && cur.nw[1] != 0ull) ? wave_or64(mine ? cur.nw[1] : 0ull) : 0ull;
+        // wave-wide ORs only where some kept row has a nonzero word
+        if (__ballot(mine && cur.nw[1] != 0ull)) c1 |= wave_or64(mine ? cur.nw[1] : 0ull);
+        if (__ballot(mine && cur.nw[2] != 0ull)) c2 = wave_or64(mine ? cur.nw[2] : 0ull);
         if (mine) {
             // removed has NEAR spare words past the end for the last chunks
 #pragma unroll
-            for (int j = 2; j <= NEAR; ++j)
+            for (int j = 3; j <= NEAR; ++j)
                 if (cur.nw[j] != 0ull) atomicOr(&removed[c + j], cur.nw[j]);
         }
-        if (lane == 0) {
-            removed[c] = rem;
-            sm.kept[slot] = kept;
-            flag_store(&sm.k_ready[slot], (uint32_t)c + 1u);
-        }
-        cur = nxt;
+    }
+    st.carry1 = c1;
+    st.carry2 = c2;
+    // lane 0 publishes; the other lanes store to their own sink words
+    uint64_t *rem_at = lane == 0 ? &removed[c] : &sm.sink_rem[lane];
+    uint32_t *flag_at = lane == 0 ? &sm.k_ready[slot] : &sm.sink_flag[lane];
+    *rem_at = rem;
+    flag_store(flag_at, (uint32_t)c + 1u);
+    return true;
+}
+
+// Resolver: settle the chunks in order.  A chunk in which no surviving row
+// has a nonzero diagonal word, and no kept row a nonzero word for the next
+// NEAR tiles (most chunks, when overlaps are sparse), costs only its summary
+// masks and removed word.  Otherwise the kept rows' words for tiles c + 1 and
+// c + 2 are ORed across the wave into registers, those for tiles c + 3 ..
+// c + NEAR into LDS with atomics.
+__device__ void resolve_chunks(const SweepArgs &a, uint64_t *removed, SweepSmem &sm) {
+    const int W = a.words;
+    ResolverState st;
+    st.at.init(0);
+    st.ahead.init(1);  // advanced to chunk 2 before its first read
+    st.carry1 = 0ull;
+    st.carry2 = 0ull;
+    ResolverBatch b0, b1, b2;
+    resolver_read(0, st.at, removed, sm, b0);
+    resolver_read(1, st.ahead, removed, sm, b1);
+    // Every path into the loop arrives with these batches in registers, so
+    // the reads in flight inside the loop are only those issued there.
+    wait_lds();
+    // three chunks per trip, so the three batches trade roles without copies
+    for (int c = 0; c < W; c += 3) {
+        if (!resolve_one(a, removed, sm, c, st, b0, b2)) return;
+        if (c + 1 < W && !resolve_one(a, removed, sm, c + 1, st, b1, b0)) return;
+        if (c + 2 < W && !resolve_one(a, removed, sm, c + 2, st, b2, b1)) return;
     }
 }
 
@@ -383,9 +478,7 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
     // prologue: chunk c staged, its entries and chunk c + A's first level issued
     load_level1(a, c, l1);
     wait_loads();
-#pragma unroll
-    for (int j = 0; j <= NEAR; ++j) sm.near[slot][0][j][lane] = l1.near[j];
-    if (lane == 0) flag_store(&sm.data_ready[slot][0], (uint32_t)c + 1u);
+    stage_level1(l1, c, slot, 0, sm);
     uint32_t count = __builtin_amdgcn_readfirstlane(l1.count);
     load_entries(a, c, rounds_of(count), e);
     if (c + A < W) load_level1(a, c + A, l1);
@@ -393,15 +486,13 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
         wait_loads();
         uint32_t count_next = 0;
         if (c + A < W) {
-            const int par = ((c + A) / A) & 1;
-#pragma unroll
-            for (int j = 0; j <= NEAR; ++j) sm.near[slot][par][j][lane] = l1.near[j];
-            if (lane == 0) flag_store(&sm.data_ready[slot][par], (uint32_t)(c + A) + 1u);
+            stage_level1(l1, c + A, slot, ((c + A) / A) & 1, sm);
             count_next = __builtin_amdgcn_readfirstlane(l1.count);
             if (c + 2 * A < W) load_level1(a, c + 2 * A, l1);
         }
-        if (!wait_flag(&sm.k_ready[slot], (uint32_t)c + 1u, sm, a.ctrl)) return;
-        const uint64_t kept = uniform64(sm.kept[slot]);
+        if (!wait_flag<APPLIER_SLEEP>(&sm.k_ready[slot], (uint32_t)c + 1u, sm, a.ctrl)) return;
+        // the resolver wrote the chunk's final removed word before the flag
+        const uint64_t kept = ~uniform64(removed[c]) & rows_valid(c, a.n);
         if (kept) {
             if (count > (uint32_t)TILE_LIST_CAP) {
                 apply_dense(a, c, stride, kept, removed);
