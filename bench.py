@@ -12,6 +12,9 @@ device memory.  Prints one JSON line:
   n8192        the same measurement on the N = 8192 clustered workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --copy-calibration BYTES
+         (device-to-device copies of a known size, run under rocprofv3 --pmc
+          to scale the FETCH_SIZE / WRITE_SIZE counters to bytes)
 """
 import argparse
 import json
@@ -67,6 +70,66 @@ def _measure(w, steps, warmup):
     return elapsed, stage_ms, last, deterministic
 
 
+# Counter-derived HBM traffic of the mask kernel, recorded in a profile
+# summary together with a hash of the kernel's sources; reported only while
+# the sources are unchanged.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_mask_kernel_n65536_large_mixed.md")
+MASK_SOURCES = [os.path.join(ROOT, "greedy_iou_nms_amd", "csrc", f)
+                for f in ("mask.hip", "nms_internal.h")]
+
+
+def mask_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in MASK_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _traffic():
+    """(bytes per launch, detail) from the recorded counters, or (None, reason)."""
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None, "no counter record"
+    rec = None
+    with open(TRAFFIC_RECORD) as fh:
+        for line in fh:
+            if line.startswith("traffic-record: "):
+                rec = json.loads(line[len("traffic-record: "):])
+    if rec is None:
+        return None, "no counter record"
+    if rec.get("source_sha256") != mask_source_sha256():
+        return None, "mask kernel changed since the counters were taken"
+    detail = {k: rec[k] for k in ("fetch_bytes", "write_bytes", "fetch_scale", "write_scale",
+                                  "record") if k in rec}
+    return rec["fetch_bytes"] + rec["write_bytes"], detail
+
+
+def _mask_algorithmic_bytes(w):
+    """Bytes the mask kernel must move for one single-image call: every word
+    of the row band it writes, the sorted boxes and areas it reads once."""
+    n = w.n
+    words = (n + 63) // 64
+    strip = 16
+    total = 0
+    for r in range(words):
+        rows = min(64, n - 64 * r)
+        total += rows * (words - (r // strip) * strip) * 8
+    return total + 20 * n
+
+
+def _copy_calibration(nbytes, launches=5):
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": launches}), flush=True)
+
+
 def _pairs(w):
     import numpy as np
     if w.batch_offsets is None and w.class_ids is None:
@@ -85,11 +148,16 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--main-only", action="store_true",
                     help="time only the N=65536 workload (for profiler runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run device copies of BYTES bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs on a single MI355X "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        _copy_calibration(args.copy_calibration)
+        return
 
     import workloads
 
@@ -99,6 +167,9 @@ def main():
     pairs = _pairs(w)
     mask_ms = stage_ms["mask"]
     achieved = OPS_PER_PAIR * pairs / (mask_ms * 1e-3) / 1e12
+
+    traffic, traffic_detail = _traffic()
+    alg_bytes = _mask_algorithmic_bytes(w)
 
     w2 = None if args.main_only else workloads.config(2, seed=0)
     if w2 is not None:
@@ -133,7 +204,9 @@ def main():
             "peak": VALU_PEAK_TOPS,
             "unit": "TFLOP/s",
             "frac": achieved / VALU_PEAK_TOPS,
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_detail": traffic_detail,
+            "algorithmic_bytes": alg_bytes,
             "ops_per_pair": OPS_PER_PAIR,
             "pairs_per_launch": pairs,
             "launch_ms": mask_ms,

@@ -1,0 +1,48 @@
+"""Host-side pieces of bench.py: algorithmic bytes and the counter record."""
+import json
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads  # noqa: E402
+
+
+def test_mask_bytes_small_case_by_hand():
+    # 130 boxes: 3 row tiles, all in strip 0, so every row writes 3 words
+    w = workloads.random_small(0, 130)
+    assert bench._mask_algorithmic_bytes(w) == 130 * 3 * 8 + 20 * 130
+
+
+def test_mask_bytes_strip_offsets():
+    # 64 * 20 boxes: row tiles 0..15 start at column 0 (20 words), row tiles
+    # 16..19 at column 16 (4 words)
+    w = workloads.random_small(0, 64 * 20)
+    assert bench._mask_algorithmic_bytes(w) == 64 * (16 * 20 + 4 * 4) * 8 + 20 * 64 * 20
+
+
+def test_traffic_record_matches_current_sources():
+    # the committed record must belong to the committed mask kernel
+    traffic, detail = bench._traffic()
+    assert traffic is not None, detail
+    assert traffic == detail["fetch_bytes"] + detail["write_bytes"]
+
+
+def test_traffic_is_null_when_sources_change(tmp_path, monkeypatch):
+    rec = {"source_sha256": "0" * 64, "fetch_bytes": 1, "write_bytes": 2}
+    p = tmp_path / "rec.md"
+    p.write_text("x\ntraffic-record: " + json.dumps(rec) + "\n")
+    monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(p))
+    traffic, why = bench._traffic()
+    assert traffic is None and "changed" in why
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "single MI355X" in r.stderr
