@@ -73,9 +73,9 @@ def _measure(w, steps, warmup):
 # Counter-derived HBM traffic of the mask kernel, recorded in a profile
 # summary together with a hash of the kernel's sources; reported only while
 # the sources are unchanged.
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_mask_kernel_n65536_large_mixed.md")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_mask_sweep_kernel_n65536_large_mixed.md")
 MASK_SOURCES = [os.path.join(ROOT, "greedy_iou_nms_amd", "csrc", f)
-                for f in ("mask.hip", "nms_internal.h")]
+                for f in ("mask_core.h", "sweep.hip", "nms_internal.h")]
 
 
 def mask_source_sha256():

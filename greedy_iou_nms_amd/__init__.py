@@ -57,7 +57,7 @@ def _load():
     common = [c_vp, c_vp, c_i64, c_f, c_vp, c_vp, c_i64, c_vp, p_i64, c_vp, c_sz, c_vp]
     lib.nms_f32.argtypes = common
     lib.nms_f32.restype = ctypes.c_int
-    lib.nms_f32_profiled.argtypes = common + [ctypes.POINTER(ctypes.c_float)]
+    lib.nms_f32_profiled.argtypes = common + [ctypes.POINTER(ctypes.c_float), ctypes.c_int]
     lib.nms_f32_profiled.restype = ctypes.c_int
     lib.nms_status_string.argtypes = [ctypes.c_int]
     lib.nms_status_string.restype = ctypes.c_char_p
@@ -150,7 +150,11 @@ def _check_inputs(boxes, scores, class_ids, batch_offsets):
     return boxes, scores, class_ids, batch_offsets, num_images
 
 
-def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, profiled):
+PROFILE_NO_FUSION = 1  # nms_f32_profiled flag: mask and sweep as separate launches
+
+
+def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, profiled,
+         fuse=True):
     boxes, scores, class_ids, batch_offsets, num_images = _check_inputs(
         boxes, scores, class_ids, batch_offsets)
     device = boxes.device
@@ -169,7 +173,7 @@ def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out,
         stage = None
         if profiled:
             stage = (ctypes.c_float * len(STAGES))()
-            _check(_lib.nms_f32_profiled(*args, stage))
+            _check(_lib.nms_f32_profiled(*args, stage, 0 if fuse else PROFILE_NO_FUSION))
         else:
             _check(_lib.nms_f32(*args))
     keep = out[:count.value]
@@ -189,10 +193,13 @@ def nms(boxes: torch.Tensor, scores: torch.Tensor, iou_threshold: float,
 
 
 def nms_profiled(boxes, scores, iou_threshold, class_ids=None, batch_offsets=None,
-                 workspace=None, out=None) -> Tuple[torch.Tensor, Dict[str, float]]:
+                 workspace=None, out=None, fuse=True) -> Tuple[torch.Tensor, Dict[str, float]]:
     """``nms`` plus per-stage GPU times in milliseconds (HIP events on the
-    launch stream)."""
-    return _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, True)
+    launch stream).  ``fuse=False`` runs the mask and the sweep as separate
+    launches even where ``nms`` fuses them, so the mask kernel is timed
+    alone."""
+    return _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, True,
+                fuse)
 
 
 def debug_order(scores: torch.Tensor, class_ids=None, batch_offsets=None):

@@ -1,0 +1,286 @@
+// The per-item IoU mask computation, shared by the standalone mask kernel
+// (mask.hip, which also describes the bitmask layout, the mapping to
+// gfx950 and the division-free threshold test) and the fused mask + sweep
+// kernel (sweep.hip).
+#pragma once
+
+#include <cmath>
+
+#include "nms_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace gnms {
+namespace maskcore {
+
+enum TestMode { MODE_EVEN = 0, MODE_ODD = 1, MODE_LITERAL = 2 };
+
+template <int MODE>
+__device__ __forceinline__ bool exceeds(float inter, float uni, float t, double mid) {
+    if (MODE == MODE_LITERAL) {
+        const float iou = inter / uni;
+        return iou > t;
+    } else {
+        const double lhs = (double)inter;
+        const double rhs = mid * (double)uni;
+        return MODE == MODE_ODD ? lhs >= rhs : lhs > rhs;
+    }
+}
+
+// max and min of finite floats as v_med3_f32 against +-infinity: med3(a, b,
+// +inf) = max(a, b) and med3(a, b, -inf) = min(a, b) for non-NaN a, b.  The
+// infinities arrive as kernel arguments, so the compiler cannot fold the
+// median back into fmaxf/fminf, which in the IEEE mode kernels run in must
+// first quiet possible signalling NaNs (an extra instruction per operand and
+// use).  Coordinates are checked finite before a result is accepted, and the
+// sign of a zero (the only thing these forms might treat differently) never
+// changes a decision.
+__device__ __forceinline__ float max2(float a, float b, float pinf) {
+    return __builtin_amdgcn_fmed3f(a, b, pinf);
+}
+__device__ __forceinline__ float min2(float a, float b, float ninf) {
+    return __builtin_amdgcn_fmed3f(a, b, ninf);
+}
+
+template <int MODE>
+__device__ __forceinline__ bool suppresses(float rx1, float ry1, float rx2, float ry2, float ra,
+                                           float cx1, float cy1, float cx2, float cy2, float ca,
+                                           float t, double mid, float pinf, float ninf) {
+    const float xx1 = max2(rx1, cx1, pinf);
+    const float yy1 = max2(ry1, cy1, pinf);
+    const float xx2 = min2(rx2, cx2, ninf);
+    const float yy2 = min2(ry2, cy2, ninf);
+    const float w = max2(xx2 - xx1, 0.0f, pinf);
+    // The division-free tests (positive areas, t > 0) need only one clamp:
+    // with w >= 0 and h unclamped, boxes that do not overlap give w * h <= 0
+    // (a zero or negative product, never above m * union > 0), so the
+    // decision is the same as with max(h, 0); boxes that overlap give the
+    // very product of the definition.  The literal test keeps both clamps.
+    const float dh = yy2 - yy1;
+    const float h = MODE == MODE_LITERAL ? max2(dh, 0.0f, pinf) : dh;
+    const float inter = w * h;
+    const float uni = (ra + ca) - inter;
+    return exceeds<MODE>(inter, uni, t, mid);
+}
+
+struct MaskArgs {
+    int n, words, mstride, npad;
+    float t;
+    double mid;
+    int odd, exact_ok;
+    float pinf, ninf;  // +inf and -inf, see max2/min2
+};
+
+// Read-only inputs and the output of the mask kernel.  They are separate
+// __restrict__ kernel parameters so the compiler can prove the uniform row
+// loads never alias the mask stores and serve them from the scalar cache.
+// Stores for data another workgroup reads while this kernel runs: device
+// scope (coherent across the XCDs' L2 caches) when COHERENT.
+template <bool COHERENT>
+__device__ __forceinline__ void put64(uint64_t *p, uint64_t v) {
+    if (COHERENT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+template <bool COHERENT>
+__device__ __forceinline__ void put32(uint32_t *p, uint32_t v) {
+    if (COHERENT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+struct MaskPtrs {
+    const float4 *__restrict__ sb;
+    const float *__restrict__ area;
+    const uint32_t *__restrict__ seg;
+    const int32_t *__restrict__ tile_cend;
+    const int32_t *__restrict__ item_base;
+    uint64_t *__restrict__ mask;
+    uint32_t *__restrict__ tcount;
+    uint32_t *__restrict__ tent_wk;
+    uint64_t *__restrict__ tent_val;
+    uint64_t *__restrict__ tnear;
+};
+
+// v_writelane_b32: lane `lane` of the returned VGPR value becomes `val` (an
+// SGPR); every other lane keeps `old`.  Used to park row k's mask word in
+// lane k without touching the execution mask.
+__device__ __forceinline__ uint32_t write_lane(uint32_t old, uint32_t val, int lane) {
+    asm("v_writelane_b32 %0, %1, m0" : "+v"(old) : "s"(val), "{m0}"(lane));
+    return old;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// Word mask of valid column boxes in tile c (boxes >= n never vote).
+__device__ __forceinline__ uint64_t column_valid(int c, int n) {
+    const int rem = n - 64 * c;
+    return rem >= 64 ? ~0ull : ((1ull << rem) - 1ull);
+}
+
+// One work item.  COHERENT (the fused mask + sweep kernel): the near words
+// and list entries, which the sweep reads while other items are still
+// running, are written with device-scope stores, and once they have all
+// completed the item adds 64 to done[r] (one per lane), the count of
+// finished items of its row tile times 64.  Plain stores may sit in the L2 of this XCD, which the sweep's
+// XCD does not see.
+template <int S, bool GROUPED, int MODE, bool COHERENT>
+__device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_, int item,
+                                          int stride, uint32_t *done) {
+    const int lane = threadIdx.x & 63;
+    // row tile of this item: the largest r with item_base[r] <= item
+    int lo = 0, hi = a.words - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (m_.item_base[mid] <= item) lo = mid;
+        else hi = mid - 1;
+    }
+    const int r = lo;
+    const int s0 = r / S;
+    const int c0 = (s0 + (item - m_.item_base[r])) * S;
+    const int cend = m_.tile_cend[r];
+    const int p0 = 64 * r;
+    const int rows = a.n - p0 < 64 ? a.n - p0 : 64;
+    const int t_diag = r - c0;  // the diagonal tile's slot, if it lies in this strip
+
+    // Column boxes of the strip, one per lane and tile.  Tiles outside
+    // [r, cend) are evaluated on real boxes and masked out (tmask = 0), which
+    // costs less than branching around them.
+    float cx1[S], cy1[S], cx2[S], cy2[S], ca[S];
+    uint32_t cg[S];
+    uint64_t tmask[S];
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+        const int c = c0 + t;
+        const bool active = c >= r && c < cend;
+        const int q = active ? 64 * c + lane : lane;
+        const float4 b = m_.sb[q];
+        cx1[t] = b.x;
+        cy1[t] = b.y;
+        cx2[t] = b.z;
+        cy2[t] = b.w;
+        ca[t] = m_.area[q];
+        if (GROUPED) cg[t] = m_.seg[q];
+        tmask[t] = active ? column_valid(c, a.n) : 0ull;
+    }
+    uint32_t out_lo[S], out_hi[S];
+#pragma unroll
+    for (int t = 0; t < S; ++t) out_lo[t] = out_hi[t] = 0u;
+
+    for (int k = 0; k < rows; ++k) {
+        const int p = p0 + k;
+        const float4 rb = m_.sb[p];
+        const float rx1 = rb.x;
+        const float ry1 = rb.y;
+        const float rx2 = rb.z;
+        const float ry2 = rb.w;
+        const float ra = m_.area[p];
+        const uint32_t rg = GROUPED ? m_.seg[p] : 0u;
+        // in the diagonal tile only boxes after row k vote
+        const uint64_t dmask = k == 63 ? 0ull : (~0ull << (k + 1));
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            bool pred = suppresses<MODE>(rx1, ry1, rx2, ry2, ra, cx1[t], cy1[t], cx2[t], cy2[t],
+                                         ca[t], a.t, a.mid, a.pinf, a.ninf);
+            if (GROUPED) pred = pred && (cg[t] == rg);
+            uint64_t m = __ballot(pred) & tmask[t];
+            m &= (t == t_diag) ? dmask : ~0ull;
+            out_lo[t] = write_lane(out_lo[t], (uint32_t)m, k);
+            out_hi[t] = write_lane(out_hi[t], (uint32_t)(m >> 32), k);
+        }
+    }
+    if (lane < rows) {
+        const int p = p0 + lane;
+        uint64_t *dst = m_.mask + (size_t)p * (size_t)stride + (size_t)(c0 - s0 * S);
+        uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+        for (int t = 0; t < S; t += 2)
+            d4[t / 2] = make_uint4(out_lo[t], out_hi[t], out_lo[t + 1], out_hi[t + 1]);
+        // transposed copies of the words for tiles r .. r + NEAR_TILES
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            const int j = t - t_diag;
+            if (j >= 0 && j <= NEAR_TILES && c0 + t < cend)
+                put64<COHERENT>(&m_.tnear[(size_t)j * a.npad + p],
+                                ((uint64_t)out_hi[t] << 32) | out_lo[t]);
+        }
+    }
+    // Record the strip's nonzero words in the row tile's list.  A wave-wide
+    // prefix sum gives each lane its place and one atomic claims the wave's
+    // slots, so the list order may differ from run to run; the sweep only ORs
+    // entries together, which does not depend on their order.  Entries past
+    // the capacity are dropped and the count (which still grows) tells the
+    // sweep to read dense rows instead.
+    uint32_t nz = 0;
+    if (lane < rows) {
+#pragma unroll
+        for (int t = 0; t < S; ++t) nz += (out_lo[t] | out_hi[t]) != 0u;
+    }
+    const uint32_t incl = wave_incl_sum(nz);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    if (total) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&m_.tcount[r], total);
+        base = __builtin_amdgcn_readlane(base, 0);
+        uint32_t at = base + incl - nz;
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            if ((out_lo[t] | out_hi[t]) != 0u && lane < rows) {
+                if (at < (uint32_t)TILE_LIST_CAP) {
+                    const size_t e = (size_t)r * TILE_LIST_CAP + at;
+                    put32<COHERENT>(&m_.tent_wk[e], ((uint32_t)(c0 + t) << 6) | (uint32_t)lane);
+                    put64<COHERENT>(&m_.tent_val[e], ((uint64_t)out_hi[t] << 32) | out_lo[t]);
+                }
+                ++at;
+            }
+        }
+    }
+    if (COHERENT) {
+        // The data the sweep reads was written with device-scope stores,
+        // which write through this XCD's L2; once they are acknowledged
+        // (s_waitcnt vmcnt(0) also counts stores) they are visible to
+        // device-scope loads on every XCD, so a reader that sees the count
+        // sees the data.  No L2 write-back (a release fence) is needed: that
+        // is for plain stores, and the sweep reads none of those.
+        // Every lane adds 1 (an item counts 64): a lane-0-only branch here
+        // would put a lane-divergent region at the end of the caller's loop.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        asm volatile("" ::: "memory");
+        __hip_atomic_fetch_add(&done[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// The work items of one launch, handed out to waves in item order (row tile
+// by row tile): wave slot `first` of `slots` takes items first, first +
+// slots, ...
+template <int S, bool GROUPED, bool COHERENT>
+__device__ __forceinline__ void mask_items(const MaskArgs &a, const MaskPtrs &m_,
+                                           const Ctrl *__restrict__ ctrl, int first, int slots,
+                                           uint32_t *done) {
+    const int num_items = ctrl->num_items;
+    const bool fast = (ctrl->flags & FLAG_POSITIVE_AREAS) && a.exact_ok;
+    const int stride = GROUPED ? ctrl->band_stride : a.mstride;
+    for (int item = first; item < num_items; item += slots) {
+        if (fast) {
+            if (a.odd) mask_item<S, GROUPED, MODE_ODD, COHERENT>(a, m_, item, stride, done);
+            else mask_item<S, GROUPED, MODE_EVEN, COHERENT>(a, m_, item, stride, done);
+        } else {
+            mask_item<S, GROUPED, MODE_LITERAL, COHERENT>(a, m_, item, stride, done);
+        }
+    }
+}
+
+// Kernel arguments of the mask stage, filled on the host.
+MaskArgs make_mask_args(const Problem &P, const Layout &L);
+// Upper bound on the work items of a launch (every row tile covers all
+// strips to the end).
+int64_t mask_items_upper_bound(const Problem &P, const Layout &L);
+
+}  // namespace maskcore
+}  // namespace gnms

@@ -50,6 +50,7 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_lb_status = take((size_t)4 * L.tiles * 256 * 4);
     L.off_tickets = take(4 * 4);
     L.off_err_tile = take((size_t)L.tiles * 4);
+    L.off_done = take((size_t)L.words * 4);
     L.off_mask = take((size_t)n * (size_t)L.mstride * 8);
     L.total = off;
     *out = L;
@@ -82,6 +83,7 @@ Work carve(void *workspace, const Layout &L) {
     w.tickets = reinterpret_cast<uint32_t *>(b + L.off_tickets);
     w.err_tile = reinterpret_cast<uint32_t *>(b + L.off_err_tile);
     w.mask = reinterpret_cast<uint64_t *>(b + L.off_mask);
+    w.done = reinterpret_cast<uint32_t *>(b + L.off_done);
     return w;
 }
 
@@ -180,7 +182,7 @@ struct EventSet {
 nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thresh,
                    const int32_t *class_ids, const int64_t *offsets, int64_t num_images,
                    int64_t *keep_out, int64_t *num_kept, void *workspace, size_t ws_bytes,
-                   void *stream_ptr, float *stage_ms) {
+                   void *stream_ptr, float *stage_ms, bool allow_fusion) {
     if (num_kept == nullptr) return NMS_INVALID_ARG;
     *num_kept = 0;
     if (stage_ms)
@@ -211,7 +213,13 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess && P.grouped) e = launch_gather(P, L, w, stream);
     if (e == hipSuccess) e = mark(2);
-    if (e == hipSuccess) e = launch_mask(P, L, w, stream);
+    // One image of moderate size: the sweep runs inside the mask launch.  The
+    // plain sweep launch still follows; it does nothing when the fused sweep
+    // finished.
+    const bool fused = allow_fusion && !P.grouped && L.words >= FUSE_MIN_WORDS &&
+                       L.words <= FUSE_MAX_WORDS;
+    if (e == hipSuccess)
+        e = fused ? launch_mask_sweep(P, L, w, keep_out, stream) : launch_mask(P, L, w, stream);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = launch_sweep(P, L, w, keep_out, stream);
     if (e == hipSuccess) e = mark(4);
@@ -259,17 +267,19 @@ nms_status nms_f32(const float *boxes, const float *scores, int64_t n, float iou
                    int64_t *keep_out, int64_t *num_kept, void *workspace,
                    size_t workspace_bytes, void *stream) {
     return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
-                   num_kept, workspace, workspace_bytes, stream, nullptr);
+                   num_kept, workspace, workspace_bytes, stream, nullptr, true);
 }
 
 nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
                             float iou_thresh, const int32_t *class_ids,
                             const int64_t *batch_offsets, int64_t num_images,
                             int64_t *keep_out, int64_t *num_kept, void *workspace,
-                            size_t workspace_bytes, void *stream, float *stage_ms) {
-    if (stage_ms == nullptr) return NMS_INVALID_ARG;
+                            size_t workspace_bytes, void *stream, float *stage_ms,
+                            int flags) {
+    if (stage_ms == nullptr || (flags & ~NMS_PROFILE_NO_FUSION) != 0) return NMS_INVALID_ARG;
     return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
-                   num_kept, workspace, workspace_bytes, stream, stage_ms);
+                   num_kept, workspace, workspace_bytes, stream, stage_ms,
+                   (flags & NMS_PROFILE_NO_FUSION) == 0);
 }
 
 const char *nms_status_string(nms_status status) {

@@ -26,7 +26,8 @@ struct Ctrl {
     int32_t num_items;      // mask work items (row tile x strip)
     int32_t band_stride;    // mask row stride in 64-bit words
     int32_t num_segments;   // groups present (1 for a single image)
-    int32_t reserved[10];
+    uint32_t fused_done;    // 1 once the fused mask + sweep kernel finished the sweep
+    int32_t reserved[9];
 };
 static_assert(sizeof(Ctrl) == 64, "Ctrl layout");
 
@@ -57,6 +58,14 @@ constexpr int TILE_LIST_CAP = 2048;
 // load.  Words further right are applied by helper waves from the lists.
 constexpr int NEAR_TILES = 4;
 
+// One image with FUSE_MIN_WORDS .. FUSE_MAX_WORDS row tiles runs the mask
+// and the sweep in one launch (the sweep's workgroup overlaps the mask's).
+// Below the minimum the mask's items all finish at about the same time and
+// there is nothing to overlap; above the maximum the sweep's LDS (removed
+// bitmap) would no longer fit beside two mask workgroups per CU.
+constexpr int FUSE_MIN_WORDS = 512;
+constexpr int FUSE_MAX_WORDS = 4096;
+
 // Workspace carve-up, computed on the host from n alone.
 struct Layout {
     int64_t n = 0;
@@ -69,6 +78,7 @@ struct Layout {
     size_t off_sb = 0, off_area = 0, off_tile_cend = 0, off_item_base = 0, off_kept = 0;
     size_t off_tcount = 0, off_tent_wk = 0, off_tent_val = 0, off_tnear = 0;
     size_t off_hist_tile = 0, off_lb_status = 0, off_tickets = 0, off_err_tile = 0;
+    size_t off_done = 0;
     size_t off_mask = 0, total = 0;
 };
 
@@ -102,6 +112,8 @@ struct Work {
     uint32_t *lb_status;
     uint32_t *tickets;
     uint32_t *err_tile;
+    // fused mask + sweep: per row tile, mask work items finished
+    uint32_t *done;
 };
 
 Work carve(void *workspace, const Layout &L);
@@ -128,6 +140,15 @@ hipError_t launch_gather(const Problem &P, const Layout &L, const Work &w, hipSt
 hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
 hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
                         hipStream_t stream);
+// One image with FUSE_MIN_WORDS <= L.words <= FUSE_MAX_WORDS: mask and
+// sweep in one launch.
+// launch_sweep must still follow; it returns at once when the fused sweep
+// finished and otherwise (a tile's list overflowed) runs the sweep.
+hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
+                             hipStream_t stream);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
 hipError_t launch_compact(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
                           hipStream_t stream);
 hipError_t launch_expand_mask(const Problem &P, const Layout &L, const Work &w,

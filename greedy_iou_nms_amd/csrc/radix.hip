@@ -135,6 +135,7 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
         c->num_items = item_base_full(a.words, a.words, a.strip);
         c->band_stride = a.mstride;
         c->num_segments = 1;
+        c->fused_done = 0u;
     }
     // Per-call initialisation, spread over the whole grid: the plan of the
     // mask kernel (every row tile covers all column tiles), the padding rows
@@ -146,6 +147,7 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
         if (r < a.words) {
             w.tile_cend[r] = a.words;
             w.tcount[r] = 0u;
+            w.done[r] = 0u;
         }
     }
     for (int p = gid; p < a.npad; p += gsz) {

@@ -437,6 +437,7 @@ __global__ __launch_bounds__(NT) void sort_kernel(SortArgs a) {
         c->num_items = (int32_t)total_items;
         c->band_stride = (int32_t)(band * (uint32_t)S);
         c->num_segments = (int32_t)num_segments;
+        c->fused_done = 0u;
     }
 }
 

@@ -40,6 +40,7 @@
 // compaction kernel walks the plain score order and looks each box's sorted
 // position up through the inverse permutation, so the output is one list in
 // global score order.
+#include "mask_core.h"
 #include "nms_internal.h"
 
 namespace gnms {
@@ -59,8 +60,19 @@ struct SweepArgs {
     Ctrl *ctrl;
     uint64_t *kept;
     int64_t *keep_out;
+    // fused with the mask: per row tile, mask work items finished
+    const uint32_t *done;
     int n, words, npad, mstride, strip, grouped;
+    int strip_groups;  // ceil(W / strip): mask work items of row tile 0
 };
+
+// Reads of data the mask stage writes.  In the fused kernel the mask is still
+// running on other XCDs, so they are device-scope (coherent) loads.
+template <bool FUSED, typename T>
+__device__ __forceinline__ T get(const T *p) {
+    if (FUSED) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return *p;
+}
 
 __device__ __forceinline__ uint64_t rows_valid(int c, int n) {
     const int rem = n - 64 * c;
@@ -131,6 +143,7 @@ struct SweepSmem {
     uint32_t k_ready[APPLIERS];       // chunk + 1 once removed[chunk] is final
     uint32_t applied[APPLIERS];       // chunk + 1 once its far words are ORed in
     uint32_t abort;
+    uint32_t done_upto;  // fused kernel: row tiles below this are known finished
     uint32_t part[NWAVES], part2[NWAVES], tot;
     // where the resolver's lanes other than lane 0 direct their publishing
     // writes (every lane stores, so the store needs no branch)
@@ -158,23 +171,79 @@ __device__ __forceinline__ void flag_store(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Wait until *flag >= target.  Returns false (and raises the abort flag and
-// the internal error bit) if it takes too long or another wave aborted.
-template <int SLEEP = 1>
+// sm.abort values.  ABORT_ERROR: a wait gave up (internal error raised).
+// ABORT_BAIL: the fused sweep stops without a result (a tile's list
+// overflowed, or the mask took too long) and the plain sweep kernel that
+// follows it does the work.
+constexpr uint32_t ABORT_ERROR = 1u;
+constexpr uint32_t ABORT_BAIL = 2u;
+
+// Give up: the fused sweep bails out quietly, the plain sweep reports an
+// internal error.
+template <bool FUSED>
+__device__ __forceinline__ void give_up(SweepSmem &sm, Ctrl *ctrl) {
+    if ((threadIdx.x & 63) == 0) {
+        flag_store(&sm.abort, FUSED ? ABORT_BAIL : ABORT_ERROR);
+        if (!FUSED) atomicOr(&ctrl->error, ERR_INTERNAL);
+    }
+}
+
+// Wait until *flag >= target.  Returns false if it takes too long (and gives
+// up) or another wave gave up.
+template <bool FUSED, int SLEEP = 1>
 __device__ __forceinline__ bool wait_flag(const uint32_t *flag, uint32_t target, SweepSmem &sm,
                                           Ctrl *ctrl) {
     uint32_t spins = 0;
     while (flag_load(flag) < target) {
         if (flag_load(&sm.abort)) return false;
         if (++spins > SPIN_LIMIT) {
-            if ((threadIdx.x & 63) == 0) {
-                flag_store(&sm.abort, 1u);
-                atomicOr(&ctrl->error, ERR_INTERNAL);
-            }
+            give_up<FUSED>(sm, ctrl);
             return false;
         }
         __builtin_amdgcn_s_sleep(SLEEP);
     }
+    return true;
+}
+
+// Fused kernel: wait until every mask work item of row tile c has finished
+// (each adds 64 to done[c] after its stores have completed).  Row tiles
+// finish roughly in order, so the waves share a frontier in LDS (every tile
+// below sm.done_upto has finished); a wave that must look reads the counts
+// of the 64 tiles from the frontier on, one per lane, and moves the frontier
+// past those that finished in a row.  Data a wave reads after learning of a
+// finished tile from the frontier is visible to it as well: the mask's
+// stores were visible device-wide before its count was raised.
+__device__ __forceinline__ bool wait_tile_done(const SweepArgs &a, int c, SweepSmem &sm) {
+    const int lane = threadIdx.x & 63;
+    uint32_t spins = 0;
+    for (;;) {
+        const uint32_t base = flag_load(&sm.done_upto);
+        if ((uint32_t)c < base) break;
+        const int t = (int)base + lane;
+        bool fin = false;
+        if (t < a.words) {
+            const uint32_t items = 64u * (uint32_t)(a.strip_groups - t / a.strip);
+            fin = __hip_atomic_load(&a.done[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                  items;
+        }
+        const uint64_t m = __ballot(fin);
+        const uint32_t run = m == ~0ull ? 64u : (uint32_t)__builtin_ctzll(~m);
+        if (run) {
+            // every lane stores the same maximum: no lane-divergent region
+            // inside a loop whose exit the wave takes together
+            __hip_atomic_fetch_max(&sm.done_upto, base + run, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            if ((uint32_t)c < base + run) break;
+            continue;
+        }
+        if (flag_load(&sm.abort)) return false;
+        if (++spins > SPIN_LIMIT) {
+            give_up<true>(sm, a.ctrl);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    compiler_barrier();
     return true;
 }
 
@@ -188,11 +257,15 @@ struct Level1 {
     uint32_t count;
 };
 
-__device__ __forceinline__ void load_level1(const SweepArgs &a, int c, Level1 &l) {
+// Returns false if the fused sweep gave up while waiting for the mask.
+template <bool FUSED>
+__device__ __forceinline__ bool load_level1(const SweepArgs &a, int c, Level1 &l, SweepSmem &sm) {
+    if (FUSED && !wait_tile_done(a, c, sm)) return false;
     const int p = 64 * c + (int)(threadIdx.x & 63);
 #pragma unroll
-    for (int j = 0; j <= NEAR; ++j) l.near[j] = a.tnear[(size_t)j * a.npad + p];
-    l.count = a.tcount[c];
+    for (int j = 0; j <= NEAR; ++j) l.near[j] = get<FUSED>(&a.tnear[(size_t)j * a.npad + p]);
+    l.count = get<FUSED>(&a.tcount[c]);
+    return true;
 }
 
 // Stage chunk c's near words and their summary masks for the resolver, then
@@ -225,13 +298,14 @@ __device__ __forceinline__ int rounds_of(uint32_t count) {
     return (int)((held + 63u) / 64u);
 }
 
+template <bool FUSED>
 __device__ __forceinline__ void load_entries(const SweepArgs &a, int c, int rounds, Entries &e) {
     const size_t base = (size_t)c * TILE_LIST_CAP + (threadIdx.x & 63);
 #pragma unroll
     for (int i = 0; i < RMAX; ++i) {
         if (i < rounds) {
-            e.wk[i] = a.tent_wk[base + 64 * i];
-            e.val[i] = a.tent_val[base + 64 * i];
+            e.wk[i] = get<FUSED>(&a.tent_wk[base + 64 * i]);
+            e.val[i] = get<FUSED>(&a.tent_val[base + 64 * i]);
         }
     }
 }
@@ -326,6 +400,7 @@ struct ResolverState {
     ResolverPos ahead;   // chunk c + 2, whose batch is read while c is settled
     uint64_t carry1;     // kept rows' words for tile c (chunks c - 1 and c - 2)
     uint64_t carry2;     // kept rows' words for tile c + 1 (chunk c - 1)
+    bool stale_next;     // chunk c + 1's batch must be read again (see resolve_one)
 };
 
 // Settle chunk c from its batch cur, after issuing the reads of chunk c + 2
@@ -335,22 +410,32 @@ struct ResolverState {
 // c's and chunk c + 1's words for it travel in registers (carry2, then
 // carry1), the words of chunks c - 1 and c - 2 for it were ORed into LDS
 // (atomics) before this read is issued, and the far words of chunks up to
-// c + 2 - NEAR - 1 are in once the applied flag read with it says so.  Reading
-// two chunks ahead keeps LDS latency, and this chunk's own LDS writes, off
-// the path from one chunk to the next.
+// c + 2 - NEAR - 1 are in once the applied flag read with it says so and no
+// earlier batch had to wait (a batch read before such a wait is read again).
+// Reading two chunks ahead keeps LDS latency, and this chunk's own LDS
+// writes, off the path from one chunk to the next.
+template <bool FUSED>
 __device__ __forceinline__ bool resolve_one(const SweepArgs &a, uint64_t *removed, SweepSmem &sm,
                                             int c, ResolverState &st, ResolverBatch &cur,
                                             ResolverBatch &ahead) {
     const int lane = threadIdx.x & 63;
     constexpr int LAG = NEAR + 1;
     const uint32_t app_need = c >= LAG ? (uint32_t)(c - LAG) + 1u : 0u;
-    if (cur.f_data < (uint32_t)c + 1u || cur.f_app < app_need) {
-        if (!wait_flag(&sm.data_ready[st.at.slot][st.at.par], (uint32_t)c + 1u, sm, a.ctrl))
+    // A batch is complete only if every chunk up to c - NEAR - 1 had been
+    // applied when it was read; its own flag covers the last of them, and
+    // the earlier ones were covered by the earlier batches' flags.  When a
+    // flag was not yet set, the waits below happen after chunk c + 1's
+    // batch was read, so that batch may miss far words of chunk c - NEAR - 1
+    // and is read again at the next chunk.
+    const bool late = cur.f_data < (uint32_t)c + 1u || cur.f_app < app_need;
+    if (late || st.stale_next) {
+        if (!wait_flag<FUSED>(&sm.data_ready[st.at.slot][st.at.par], (uint32_t)c + 1u, sm, a.ctrl))
             return false;
-        if (!wait_flag(&sm.applied[st.at.app_slot], app_need, sm, a.ctrl)) return false;
+        if (!wait_flag<FUSED>(&sm.applied[st.at.app_slot], app_need, sm, a.ctrl)) return false;
         resolver_read(c, st.at, removed, sm, cur);
         wait_lds();
     }
+    st.stale_next = late;
     // Issued for every chunk, also past the last one (removed[] has NEAR >= 2
     // spare words and the staging slots are a ring), so that the number of
     // LDS accesses in flight is the same on every path through the loop and
@@ -403,6 +488,7 @@ __device__ __forceinline__ bool resolve_one(const SweepArgs &a, uint64_t *remove
 // masks and removed word.  Otherwise the kept rows' words for tiles c + 1 and
 // c + 2 are ORed across the wave into registers, those for tiles c + 3 ..
 // c + NEAR into LDS with atomics.
+template <bool FUSED>
 __device__ void resolve_chunks(const SweepArgs &a, uint64_t *removed, SweepSmem &sm) {
     const int W = a.words;
     ResolverState st;
@@ -410,6 +496,7 @@ __device__ void resolve_chunks(const SweepArgs &a, uint64_t *removed, SweepSmem 
     st.ahead.init(1);  // advanced to chunk 2 before its first read
     st.carry1 = 0ull;
     st.carry2 = 0ull;
+    st.stale_next = false;
     ResolverBatch b0, b1, b2;
     resolver_read(0, st.at, removed, sm, b0);
     resolver_read(1, st.ahead, removed, sm, b1);
@@ -418,9 +505,9 @@ __device__ void resolve_chunks(const SweepArgs &a, uint64_t *removed, SweepSmem 
     wait_lds();
     // three chunks per trip, so the three batches trade roles without copies
     for (int c = 0; c < W; c += 3) {
-        if (!resolve_one(a, removed, sm, c, st, b0, b2)) return;
-        if (c + 1 < W && !resolve_one(a, removed, sm, c + 1, st, b1, b0)) return;
-        if (c + 2 < W && !resolve_one(a, removed, sm, c + 2, st, b2, b1)) return;
+        if (!resolve_one<FUSED>(a, removed, sm, c, st, b0, b2)) return;
+        if (c + 1 < W && !resolve_one<FUSED>(a, removed, sm, c + 1, st, b1, b0)) return;
+        if (c + 2 < W && !resolve_one<FUSED>(a, removed, sm, c + 2, st, b2, b1)) return;
     }
 }
 
@@ -465,6 +552,7 @@ __device__ void apply_dense(const SweepArgs &a, int c, int stride, uint64_t kept
 // levels ahead: while chunk c is waiting for its kept set, the first level
 // (diagonal words, list length) of chunk c + 2A and the entries of chunk
 // c + A are in flight (A = APPLIERS).
+template <bool FUSED>
 __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, SweepSmem &sm,
                              int q) {
     const int lane = threadIdx.x & 63;
@@ -476,25 +564,32 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
     Level1 l1;
     Entries e;
     // prologue: chunk c staged, its entries and chunk c + A's first level issued
-    load_level1(a, c, l1);
+    if (!load_level1<FUSED>(a, c, l1, sm)) return;
     wait_loads();
     stage_level1(l1, c, slot, 0, sm);
     uint32_t count = __builtin_amdgcn_readfirstlane(l1.count);
-    load_entries(a, c, rounds_of(count), e);
-    if (c + A < W) load_level1(a, c + A, l1);
+    load_entries<FUSED>(a, c, rounds_of(count), e);
+    if (c + A < W && !load_level1<FUSED>(a, c + A, l1, sm)) return;
     for (; c < W; c += A) {
         wait_loads();
         uint32_t count_next = 0;
         if (c + A < W) {
             stage_level1(l1, c + A, slot, ((c + A) / A) & 1, sm);
             count_next = __builtin_amdgcn_readfirstlane(l1.count);
-            if (c + 2 * A < W) load_level1(a, c + 2 * A, l1);
+            if (c + 2 * A < W && !load_level1<FUSED>(a, c + 2 * A, l1, sm)) return;
         }
-        if (!wait_flag<APPLIER_SLEEP>(&sm.k_ready[slot], (uint32_t)c + 1u, sm, a.ctrl)) return;
+        if (!wait_flag<FUSED, APPLIER_SLEEP>(&sm.k_ready[slot], (uint32_t)c + 1u, sm, a.ctrl))
+            return;
         // the resolver wrote the chunk's final removed word before the flag
         const uint64_t kept = ~uniform64(removed[c]) & rows_valid(c, a.n);
         if (kept) {
             if (count > (uint32_t)TILE_LIST_CAP) {
+                // dense rows are plain stores of the mask stage, not visible
+                // to the fused sweep: leave the work to the plain sweep
+                if (FUSED) {
+                    give_up<true>(sm, a.ctrl);
+                    return;
+                }
                 apply_dense(a, c, stride, kept, removed);
             } else {
                 const int rounds = rounds_of(count);
@@ -502,21 +597,22 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
                 // rounds beyond the registers: load and apply them now
                 const size_t base = (size_t)c * TILE_LIST_CAP + lane;
                 for (int i = RMAX; i < rounds; ++i) {
-                    const uint32_t wk = a.tent_wk[base + 64 * i];
-                    const uint64_t val = a.tent_val[base + 64 * i];
+                    const uint32_t wk = get<FUSED>(&a.tent_wk[base + 64 * i]);
+                    const uint64_t val = get<FUSED>(&a.tent_val[base + 64 * i]);
                     apply_entry(wk, val, (uint32_t)(64 * i + lane) < count, kept, c, removed);
                 }
             }
         }
         if (lane == 0) flag_store(&sm.applied[slot], (uint32_t)c + 1u);
-        if (c + A < W) load_entries(a, c + A, rounds_of(count_next), e);
+        if (c + A < W) load_entries<FUSED>(a, c + A, rounds_of(count_next), e);
         count = count_next;
     }
 }
 
-__global__ __launch_bounds__(NT) void sweep_kernel(SweepArgs a) {
-    extern __shared__ uint64_t removed[];
-    __shared__ SweepSmem sm;
+// The whole sweep in one workgroup: LDS set-up, the resolver and applier
+// waves, then the kept bitmap and (one image) the compaction.
+template <bool FUSED>
+__device__ __forceinline__ void sweep_body(const SweepArgs &a, uint64_t *removed, SweepSmem &sm) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int W = a.words, n = a.n;
@@ -529,12 +625,15 @@ __global__ __launch_bounds__(NT) void sweep_kernel(SweepArgs a) {
         sm.k_ready[tid] = 0u;
         sm.applied[tid] = 0u;
     }
-    if (tid == 0) sm.abort = 0u;
+    if (tid == 0) {
+        sm.abort = 0u;
+        sm.done_upto = 0u;
+    }
     __syncthreads();
 
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    if (wv == 0) resolve_chunks(a, removed, sm);
-    else apply_chunks(a, stride, removed, sm, wv);
+    if (wv == 0) resolve_chunks<FUSED>(a, removed, sm);
+    else apply_chunks<FUSED>(a, stride, removed, sm, wv);
     __syncthreads();
     if (sm.abort) return;
 
@@ -558,7 +657,45 @@ __global__ __launch_bounds__(NT) void sweep_kernel(SweepArgs a) {
             a.keep_out[pos++] = (int64_t)a.order[64 * w + k];
         }
     }
-    if (tid == 0) a.ctrl->count = (int32_t)total;
+    if (tid == 0) {
+        a.ctrl->count = (int32_t)total;
+        if (FUSED) a.ctrl->fused_done = 1u;
+    }
+}
+
+__global__ __launch_bounds__(NT) void sweep_kernel(SweepArgs a) {
+    extern __shared__ uint64_t removed[];
+    __shared__ SweepSmem sm;
+    // the fused mask + sweep kernel already produced the result
+    if (a.ctrl->fused_done) return;
+    sweep_body<false>(a, removed, sm);
+}
+
+// Mask and sweep in one launch (one image).  Workgroup 0 runs the sweep; the
+// waves of the other workgroups take the mask work items in turn (wave slot
+// s: items s, s + slots, ...).  The launch is no larger than what the GPU
+// holds at once, so items start in order, row tile by row tile, and the
+// sweep follows the finished row tiles while later ones are still being
+// computed.  No mask wave ever waits for the sweep, so every item completes
+// whatever the order in which workgroups are scheduled.
+__global__ __launch_bounds__(NT) void mask_sweep_kernel(
+    maskcore::MaskArgs ma, const Ctrl *ctrl, const float4 *__restrict__ sb,
+    const float *__restrict__ area, const int32_t *__restrict__ tile_cend,
+    const int32_t *__restrict__ item_base, uint64_t *__restrict__ mask,
+    uint32_t *__restrict__ tcount, uint32_t *__restrict__ tent_wk,
+    uint64_t *__restrict__ tent_val, uint64_t *__restrict__ tnear, uint32_t *__restrict__ done,
+    SweepArgs sa) {
+    extern __shared__ uint64_t removed[];
+    __shared__ SweepSmem sm;
+    if (blockIdx.x == 0) {
+        sweep_body<true>(sa, removed, sm);
+        return;
+    }
+    const maskcore::MaskPtrs m_{sb,     area,   nullptr, tile_cend, item_base,
+                                mask,   tcount, tent_wk, tent_val,  tnear};
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    maskcore::mask_items<STRIP_SINGLE, false, true>(ma, m_, ctrl, (blockIdx.x - 1) * NWAVES + wave,
+                                                    (gridDim.x - 1) * NWAVES, done);
 }
 
 struct CompactArgs {
@@ -608,10 +745,7 @@ __global__ void expand_kernel(const uint64_t *mask, const int32_t *tile_cend, co
     out[idx] = v;
 }
 
-}  // namespace
-
-hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
-                        hipStream_t stream) {
+SweepArgs make_sweep_args(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out) {
     SweepArgs a;
     a.mask = w.mask;
     a.tile_cend = w.tile_cend;
@@ -629,8 +763,59 @@ hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_
     a.mstride = (int)L.mstride;
     a.strip = P.strip;
     a.grouped = P.grouped ? 1 : 0;
+    a.done = w.done;
+    a.strip_groups = (int)((L.words + P.strip - 1) / P.strip);
+    return a;
+}
+
+}  // namespace
+
+hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
+                        hipStream_t stream) {
+    const SweepArgs a = make_sweep_args(P, L, w, keep_out);
     const size_t lds = (size_t)(L.words + NEAR_TILES) * sizeof(uint64_t);
     hipLaunchKernelGGL(sweep_kernel, dim3(1), dim3(NT), lds, stream, a);
+    return hipGetLastError();
+}
+
+// Workgroups of the fused kernel resident per CU, for the largest removed
+// bitmap the fused kernel takes (asked once per device: the query costs more
+// than a launch).  Two at most: the kernel's registers allow no more.
+int fused_blocks_per_cu(size_t lds) {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        const size_t worst = (size_t)(FUSE_MAX_WORDS + NEAR_TILES) * sizeof(uint64_t);
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mask_sweep_kernel, NT, worst) !=
+                hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        cached[dev] = per_cu;
+    }
+    (void)lds;
+    return cached[dev];
+}
+
+hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
+                             hipStream_t stream) {
+    if (P.grouped || L.words < FUSE_MIN_WORDS || L.words > FUSE_MAX_WORDS)
+        return hipErrorInvalidValue;
+    const SweepArgs sa = make_sweep_args(P, L, w, keep_out);
+    const maskcore::MaskArgs ma = maskcore::make_mask_args(P, L);
+    const int64_t items_ub = maskcore::mask_items_upper_bound(P, L);
+    // no more workgroups than the GPU holds at once (the sweep's included),
+    // so that no item waits for a workgroup to start
+    const size_t lds = (size_t)(L.words + NEAR_TILES) * sizeof(uint64_t);
+    const int per_cu = fused_blocks_per_cu(lds);
+    int64_t blocks = (items_ub + NWAVES - 1) / NWAVES;
+    const int64_t cap = (int64_t)device_cu_count() * per_cu - 1;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(mask_sweep_kernel, dim3((unsigned)(blocks + 1)), dim3(NT), lds, stream, ma,
+                       w.ctrl, w.sb, w.area, w.tile_cend, w.item_base, w.mask, w.tcount,
+                       w.tent_wk, w.tent_val, w.tnear, w.done, sa);
     return hipGetLastError();
 }
 

@@ -74,8 +74,13 @@ typedef enum nms_status {
 /* Stages timed by nms_f32_profiled, in launch order. */
 #define NMS_STAGE_SORT 0     /* score keys, stable LSD radix sort, grouping  */
 #define NMS_STAGE_GATHER 1   /* sorted box gather + areas + input checks     */
-#define NMS_STAGE_MASK 2     /* triangle-tiled IoU suppression bitmask       */
-#define NMS_STAGE_SWEEP 3    /* greedy sweep over the mask (+ compaction)    */
+#define NMS_STAGE_MASK 2     /* triangle-tiled IoU suppression bitmask; one  */
+                             /* image of 32705 to 262144 boxes: mask and     */
+                             /* sweep in one launch (sweep overlaps mask)    */
+#define NMS_STAGE_SWEEP 3    /* greedy sweep over the mask (+ compaction);   */
+                             /* after the fused launch, only its completion  */
+                             /* check (or the sweep, if a tile's list of     */
+                             /* nonzero words overflowed)                    */
 #define NMS_STAGE_COMPACT 4  /* score-order compaction (grouped input only)  */
 #define NMS_NUM_STAGES 5
 
@@ -119,17 +124,23 @@ nms_status nms_f32(const float *boxes, const float *scores, int64_t n, float iou
                    int64_t *keep_out, int64_t *num_kept, void *workspace,
                    size_t workspace_bytes, void *stream);
 
+/* nms_f32_profiled flags. */
+#define NMS_PROFILE_NO_FUSION 1  /* run the mask and the sweep as separate */
+                                 /* launches (to time the mask kernel alone) */
+
 /*
  * nms_f32_profiled -- nms_f32 with HIP events recorded on `stream` around
  * each stage.  stage_ms (host, NMS_NUM_STAGES floats) receives each stage's
- * elapsed GPU time in milliseconds (0 for a stage that did not run).  The
- * result is identical to nms_f32's.
+ * elapsed GPU time in milliseconds (0 for a stage that did not run).  flags:
+ * 0 or NMS_PROFILE_NO_FUSION (other bits: NMS_INVALID_ARG).  The result is
+ * identical to nms_f32's either way.
  */
 nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
                             float iou_thresh, const int32_t *class_ids,
                             const int64_t *batch_offsets, int64_t num_images,
                             int64_t *keep_out, int64_t *num_kept, void *workspace,
-                            size_t workspace_bytes, void *stream, float *stage_ms);
+                            size_t workspace_bytes, void *stream, float *stage_ms,
+                            int flags);
 
 /* Human-readable name of a status ("NMS_OK", ...); never NULL. */
 const char *nms_status_string(nms_status status);
