@@ -175,6 +175,12 @@ MaskArgs make_mask_args(const Problem &P, const Layout &L) {
     a.exact_ok = th.exact_ok ? 1 : 0;
     a.pinf = INFINITY;
     a.ninf = -INFINITY;
+    // enough work items to give every CU 16 waves, splitting pairs into up
+    // to 4 groups of rows when there are too few
+    const int64_t pairs = mask_items_upper_bound(P, L);
+    const int64_t want = (int64_t)device_cu_count() * 16;
+    a.qshift = 0;
+    while (a.qshift < 2 && (pairs << a.qshift) < want) ++a.qshift;
     return a;
 }
 
@@ -193,7 +199,7 @@ int64_t mask_items_upper_bound(const Problem &P, const Layout &L) {
 
 hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStream_t stream) {
     const maskcore::MaskArgs a = maskcore::make_mask_args(P, L);
-    const int64_t items_ub = maskcore::mask_items_upper_bound(P, L);
+    const int64_t items_ub = maskcore::mask_items_upper_bound(P, L) << a.qshift;
     const int waves_per_block = MASK_THREADS / 64;
     int64_t blocks = (items_ub + waves_per_block - 1) / waves_per_block;
     const int64_t cap = (int64_t)device_cu_count() * 8;

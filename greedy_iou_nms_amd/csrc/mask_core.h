@@ -69,6 +69,10 @@ struct MaskArgs {
     double mid;
     int odd, exact_ok;
     float pinf, ninf;  // +inf and -inf, see max2/min2
+    // Each (row tile, strip) pair is split into 1 << qshift work items of
+    // 64 >> qshift rows: with few row tiles, whole pairs would leave most of
+    // the GPU idle while one wave works through 64 rows.
+    int qshift;
 };
 
 // Read-only inputs and the output of the mask kernel.  They are separate
@@ -134,19 +138,25 @@ template <int S, bool GROUPED, int MODE, bool COHERENT>
 __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_, int item,
                                           int stride, uint32_t *done) {
     const int lane = threadIdx.x & 63;
-    // row tile of this item: the largest r with item_base[r] <= item
+    // the item's rows within its (row tile, strip) pair
+    const int pair = item >> a.qshift;
+    const int k_lo = (item & ((1 << a.qshift) - 1)) * (64 >> a.qshift);
+    // row tile of this pair: the largest r with item_base[r] <= pair
     int lo = 0, hi = a.words - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (m_.item_base[mid] <= item) lo = mid;
+        if (m_.item_base[mid] <= pair) lo = mid;
         else hi = mid - 1;
     }
     const int r = lo;
     const int s0 = r / S;
-    const int c0 = (s0 + (item - m_.item_base[r])) * S;
+    const int c0 = (s0 + (pair - m_.item_base[r])) * S;
     const int cend = m_.tile_cend[r];
     const int p0 = 64 * r;
-    const int rows = a.n - p0 < 64 ? a.n - p0 : 64;
+    const int tile_rows = a.n - p0 < 64 ? a.n - p0 : 64;
+    const int k_hi = k_lo + (64 >> a.qshift) < tile_rows ? k_lo + (64 >> a.qshift) : tile_rows;
+    // lanes k_lo .. k_hi - 1 end up holding the words of rows k_lo .. k_hi - 1
+    const bool mine = lane >= k_lo && lane < k_hi;
     const int t_diag = r - c0;  // the diagonal tile's slot, if it lies in this strip
 
     // Column boxes of the strip, one per lane and tile.  Tiles outside
@@ -173,7 +183,7 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
 #pragma unroll
     for (int t = 0; t < S; ++t) out_lo[t] = out_hi[t] = 0u;
 
-    for (int k = 0; k < rows; ++k) {
+    for (int k = k_lo; k < k_hi; ++k) {
         const int p = p0 + k;
         const float4 rb = m_.sb[p];
         const float rx1 = rb.x;
@@ -195,7 +205,7 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
             out_hi[t] = write_lane(out_hi[t], (uint32_t)(m >> 32), k);
         }
     }
-    if (lane < rows) {
+    if (mine) {
         const int p = p0 + lane;
         uint64_t *dst = m_.mask + (size_t)p * (size_t)stride + (size_t)(c0 - s0 * S);
         uint4 *d4 = reinterpret_cast<uint4 *>(dst);
@@ -218,7 +228,7 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
     // the capacity are dropped and the count (which still grows) tells the
     // sweep to read dense rows instead.
     uint32_t nz = 0;
-    if (lane < rows) {
+    if (mine) {
 #pragma unroll
         for (int t = 0; t < S; ++t) nz += (out_lo[t] | out_hi[t]) != 0u;
     }
@@ -231,7 +241,7 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
         uint32_t at = base + incl - nz;
 #pragma unroll
         for (int t = 0; t < S; ++t) {
-            if ((out_lo[t] | out_hi[t]) != 0u && lane < rows) {
+            if ((out_lo[t] | out_hi[t]) != 0u && mine) {
                 if (at < (uint32_t)TILE_LIST_CAP) {
                     const size_t e = (size_t)r * TILE_LIST_CAP + at;
                     put32<COHERENT>(&m_.tent_wk[e], ((uint32_t)(c0 + t) << 6) | (uint32_t)lane);
@@ -263,7 +273,7 @@ template <int S, bool GROUPED, bool COHERENT>
 __device__ __forceinline__ void mask_items(const MaskArgs &a, const MaskPtrs &m_,
                                            const Ctrl *__restrict__ ctrl, int first, int slots,
                                            uint32_t *done) {
-    const int num_items = ctrl->num_items;
+    const int num_items = ctrl->num_items << a.qshift;
     const bool fast = (ctrl->flags & FLAG_POSITIVE_AREAS) && a.exact_ok;
     const int stride = GROUPED ? ctrl->band_stride : a.mstride;
     for (int item = first; item < num_items; item += slots) {

@@ -803,7 +803,8 @@ hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, i
     if (P.grouped || L.words < FUSE_MIN_WORDS || L.words > FUSE_MAX_WORDS)
         return hipErrorInvalidValue;
     const SweepArgs sa = make_sweep_args(P, L, w, keep_out);
-    const maskcore::MaskArgs ma = maskcore::make_mask_args(P, L);
+    maskcore::MaskArgs ma = maskcore::make_mask_args(P, L);
+    ma.qshift = 0;  // whole pairs: the finished counts assume one item per pair
     const int64_t items_ub = maskcore::mask_items_upper_bound(P, L);
     // no more workgroups than the GPU holds at once (the sweep's included),
     // so that no item waits for a workgroup to start
