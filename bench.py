@@ -1,15 +1,22 @@
 """Benchmark: greedy IoU NMS on one MI355X.
 
-One step = one full NMS call (sort, gather, IoU mask, sweep, compaction and
-the kept-count read-back) over the N = 65536 single-image workload (half
-uniform boxes, half clustered; threshold 0.5), inputs already resident in
-device memory.  Prints one JSON line:
+One step = one full NMS call (sort, IoU mask, sweep, compaction and the
+kept-count read-back) over the N = 65536 single-image workload (half uniform
+boxes, half clustered; threshold 0.5), inputs already resident in device
+memory.  Prints one JSON line:
 
-  value        boxes/s over the timed steps (whole job, one GPU)
-  roofline     the IoU-mask kernel against the chip's fp32 VALU issue rate,
-               timed with HIP events on the launch stream
-  cpu_baseline the CPU oracle on the same workload, on this host
-  n8192        the same measurement on the N = 8192 clustered workload
+  value          boxes/s over the timed steps (whole job, one GPU)
+  roofline       the dominant kernel of the timed steps (at this size the
+                 fused IoU-mask launch, whose sweep workgroup runs beside the
+                 mask) against the chip's fp32 VALU issue rate, timed with HIP
+                 events on the launch stream
+  mask_kernel_alone, sweep_alone
+                 the mask and the sweep as separate launches (a few extra
+                 steps), so each is measured on its own line
+  e2e_roofline   max(VALU time of all pairs, HBM time of the algorithmic
+                 bytes) over the measured median call time
+  cpu_baseline   the CPU oracle on the same workload, on this host
+  n8192          the same measurement on the N = 8192 clustered workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-calibration BYTES
@@ -34,7 +41,10 @@ VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
 
 
-def _measure(w, steps, warmup):
+def _measure(w, steps, warmup, fuse=True):
+    """Time `steps` calls after `warmup` untimed ones.  Every call ends with
+    the library's read-back of the kept count (a stream synchronisation), so
+    the host clock around a call is its end-to-end time."""
     import numpy as np
     import torch
 
@@ -47,32 +57,42 @@ def _measure(w, steps, warmup):
     offs = None if w.batch_offsets is None else torch.from_numpy(w.batch_offsets).to(dev)
     ws = g.Workspace(dev)
     out = torch.empty(w.n, dtype=torch.int64, device=dev)
+
+    def call():
+        return g.nms_profiled(boxes, scores, w.iou_threshold, cls, offs, workspace=ws, out=out,
+                              fuse=fuse)
+
     first = None
     for _ in range(warmup):
-        keep, _ = g.nms_profiled(boxes, scores, w.iou_threshold, cls, offs, workspace=ws, out=out)
+        keep, _ = call()
         if first is None:
             first = keep.cpu().numpy().copy()
     torch.cuda.synchronize()
     stage_sum = {s: 0.0 for s in g.STAGES}
-    deterministic = True
+    call_ms = []
     t0 = time.perf_counter()
     for _ in range(steps):
-        keep, st = g.nms_profiled(boxes, scores, w.iou_threshold, cls, offs, workspace=ws,
-                                  out=out)
+        t1 = time.perf_counter()
+        keep, st = call()
+        call_ms.append(1000.0 * (time.perf_counter() - t1))
         for k, v in st.items():
             stage_sum[k] += v
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     last = keep.cpu().numpy().copy()
-    if first is not None and not np.array_equal(first, last):
-        deterministic = False
-    stage_ms = {k: v / steps for k, v in stage_sum.items()}
-    return elapsed, stage_ms, last, deterministic
+    deterministic = first is None or bool(np.array_equal(first, last))
+    return {
+        "elapsed": elapsed,
+        "stage_ms": {k: v / steps for k, v in stage_sum.items()},
+        "call_ms": {"median": float(np.median(call_ms)), "min": float(np.min(call_ms))},
+        "keep": last,
+        "deterministic": deterministic,
+    }
 
 
-# Counter-derived HBM traffic of the mask kernel, recorded in a profile
-# summary together with a hash of the kernel's sources; reported only while
-# the sources are unchanged.
+# Counter-derived HBM traffic of the dominant kernel (the fused mask + sweep
+# launch), recorded in a profile summary together with a hash of the
+# kernel's sources; reported only while the sources are unchanged.
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_mask_sweep_kernel_n65536_large_mixed.md")
 MASK_SOURCES = [os.path.join(ROOT, "greedy_iou_nms_amd", "csrc", f)
                 for f in ("mask_core.h", "sweep.hip", "nms_internal.h")]
@@ -100,8 +120,8 @@ def _traffic():
         return None, "no counter record"
     if rec.get("source_sha256") != mask_source_sha256():
         return None, "mask kernel changed since the counters were taken"
-    detail = {k: rec[k] for k in ("fetch_bytes", "write_bytes", "fetch_scale", "write_scale",
-                                  "record") if k in rec}
+    detail = {k: rec[k] for k in ("kernel", "fetch_bytes", "write_bytes", "fetch_scale",
+                                  "write_scale", "record") if k in rec}
     return rec["fetch_bytes"] + rec["write_bytes"], detail
 
 
@@ -116,6 +136,21 @@ def _mask_algorithmic_bytes(w):
         rows = min(64, n - 64 * r)
         total += rows * (words - (r // strip) * strip) * 8
     return total + 20 * n
+
+
+def _sweep_dense_bytes(w, keep):
+    """Bytes a dense-row sweep reads: the 64 diagonal words of every row tile
+    and, for every kept box at sorted position p, its words right of its own
+    tile (W - p // 64 - 1 of them).  This sweep reads sparse lists instead,
+    so this is the dense equivalent the rate is quoted against."""
+    import numpy as np
+    n = w.n
+    words = (n + 63) // 64
+    order = np.lexsort((np.arange(n), -w.scores.astype(np.float64)))
+    pos = np.empty(n, np.int64)
+    pos[order] = np.arange(n)
+    kept_pos = pos[np.asarray(keep, np.int64)]
+    return int(8 * n + 8 * np.sum(words - kept_pos // 64 - 1))
 
 
 def _copy_calibration(nbytes, launches=5):
@@ -140,6 +175,33 @@ def _pairs(w):
     return int(np.sum(counts * (counts - 1) // 2))
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _workload_line(w, r):
+    """Per-workload figures shared by the main line and the n8192 object."""
+    pairs = _pairs(w)
+    ms = r["call_ms"]["median"]
+    return {
+        "workload": w.name,
+        "boxes_per_s": w.n / (ms * 1e-3),
+        "pairwise_iou_per_s": pairs / (ms * 1e-3),
+        "pairwise_iou_per_s_mask_stage": pairs / (r["stage_ms"]["mask"] * 1e-3),
+        "ms_per_call": r["call_ms"],
+        "stage_ms": r["stage_ms"],
+        "kept": int(r["keep"].size),
+        "deterministic": r["deterministic"],
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,7 +209,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--main-only", action="store_true",
-                    help="time only the N=65536 workload (for profiler runs)")
+                    help="time only the N=65536 workload as the library runs it (for profiler runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run device copies of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -162,20 +224,13 @@ def main():
     import workloads
 
     w = workloads.config(5, seed=0)
-    elapsed, stage_ms, keep, det = _measure(w, args.steps, args.warmup)
-    ms_per_step = 1000.0 * elapsed / args.steps
+    r = _measure(w, args.steps, args.warmup)
+    ms_per_step = 1000.0 * r["elapsed"] / args.steps
     pairs = _pairs(w)
-    mask_ms = stage_ms["mask"]
-    achieved = OPS_PER_PAIR * pairs / (mask_ms * 1e-3) / 1e12
-
+    launch_ms = r["stage_ms"]["mask"]
+    achieved = OPS_PER_PAIR * pairs / (launch_ms * 1e-3) / 1e12
     traffic, traffic_detail = _traffic()
     alg_bytes = _mask_algorithmic_bytes(w)
-
-    w2 = None if args.main_only else workloads.config(2, seed=0)
-    if w2 is not None:
-        el2, st2, keep2, det2 = _measure(w2, args.steps, args.warmup)
-        ms2 = 1000.0 * el2 / args.steps
-        pairs2 = _pairs(w2)
 
     line = {
         "metric": "NMS boxes/s and pairwise IoU/s at N=8192 and N=65536 (1 MI355X); % of roofline",
@@ -192,39 +247,57 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "n": w.n, "iou_threshold": w.iou_threshold,
                    "seed": 0, "input_sha256": w.sha256()[:16]},
-        "pairwise_iou_per_s": pairs / (ms_per_step * 1e-3),
-        "pairwise_iou_per_s_mask_stage": pairs / (mask_ms * 1e-3),
-        "stage_ms": stage_ms,
-        "kept": int(keep.size),
-        "deterministic": det,
-        "roofline": {
-            "kernel": "mask_kernel (IoU suppression bitmask)",
-            "bound": "alu",
-            "achieved": achieved,
-            "peak": VALU_PEAK_TOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved / VALU_PEAK_TOPS,
-            "traffic": traffic,
-            "traffic_detail": traffic_detail,
-            "algorithmic_bytes": alg_bytes,
-            "ops_per_pair": OPS_PER_PAIR,
-            "pairs_per_launch": pairs,
-            "launch_ms": mask_ms,
-            "frac_of_fp32_vector_157tf": achieved / 157.3,
-            "mask_bytes_written_gbs": (pairs / 8.0) / (mask_ms * 1e-3) / 1e9,
-        },
     }
-    if w2 is not None:
-        line["n8192"] = {
-            "workload": w2.name,
-            "boxes_per_s": w2.n / (ms2 * 1e-3),
-            "pairwise_iou_per_s": pairs2 / (ms2 * 1e-3),
-            "pairwise_iou_per_s_mask_stage": pairs2 / (st2["mask"] * 1e-3),
-            "ms_per_step": ms2,
-            "stage_ms": st2,
-            "kept": int(keep2.size),
-            "deterministic": det2,
+    line.update({k: v for k, v in _workload_line(w, r).items() if k != "workload"})
+    line["roofline"] = {
+        "kernel": "mask_sweep_kernel (IoU suppression bitmask; the sweep's workgroup runs "
+                  "beside it)",
+        "bound": "alu",
+        "achieved": achieved,
+        "peak": VALU_PEAK_TOPS,
+        "unit": "TFLOP/s",
+        "frac": achieved / VALU_PEAK_TOPS,
+        "traffic": traffic,
+        "traffic_detail": traffic_detail,
+        "algorithmic_bytes": alg_bytes,
+        "ops_per_pair": OPS_PER_PAIR,
+        "pairs_per_launch": pairs,
+        "launch_ms": launch_ms,
+        "frac_of_fp32_vector_157tf": achieved / 157.3,
+        "mask_bytes_written_gbs": alg_bytes / (launch_ms * 1e-3) / 1e9,
+    }
+
+    if not args.main_only:
+        # the mask and the sweep as separate launches, each on its own line
+        sep_steps = max(1, min(args.steps, 20))
+        s = _measure(w, sep_steps, min(args.warmup, 3), fuse=False)
+        m_ms = s["stage_ms"]["mask"]
+        m_ach = OPS_PER_PAIR * pairs / (m_ms * 1e-3) / 1e12
+        line["mask_kernel_alone"] = {
+            "kernel": "mask_kernel (separate launch)", "launch_ms": m_ms, "achieved": m_ach,
+            "peak": VALU_PEAK_TOPS, "unit": "TFLOP/s", "frac": m_ach / VALU_PEAK_TOPS,
+            "steps": sep_steps,
         }
+        sw_ms = s["stage_ms"]["sweep"]
+        dense = _sweep_dense_bytes(w, s["keep"])
+        line["sweep_alone"] = {
+            "kernel": "sweep_kernel (separate launch, one workgroup)", "ms": sw_ms,
+            "dense_equivalent_bytes": dense, "dense_equivalent_gbs": dense / (sw_ms * 1e-3) / 1e9,
+            "us_per_row_tile": 1000.0 * sw_ms / ((w.n + 63) // 64), "steps": sep_steps,
+        }
+        valu_ms = 1000.0 * OPS_PER_PAIR * pairs / (VALU_PEAK_TOPS * 1e12)
+        hbm_ms = 1000.0 * alg_bytes / (HBM_PEAK_GBS * 1e9)
+        roof_ms = max(valu_ms, hbm_ms)
+        line["e2e_roofline"] = {
+            "roofline_ms": roof_ms, "valu_ms": valu_ms, "hbm_ms": hbm_ms,
+            "measured_ms": r["call_ms"]["median"],
+            "ratio": roof_ms / r["call_ms"]["median"],
+        }
+
+        w2 = workloads.config(2, seed=0)
+        r2 = _measure(w2, args.steps, args.warmup)
+        line["n8192"] = _workload_line(w2, r2)
+
     if not args.no_cpu:
         import numpy as np
 
@@ -234,10 +307,11 @@ def main():
         cpu_s = time.perf_counter() - t0
         line["cpu_baseline"] = {
             "value": w.n / cpu_s, "unit": "boxes/s", "cores": 1, "kind": "oracle",
-            "sample": "the full %s workload, one single-threaded run (%.1f s); host has %d "
-                      "usable cores" % (w.name, cpu_s, len(os.sched_getaffinity(0))),
+            "sample": "the full %s workload, one single-threaded run (%.1f s) on %s; host has %d "
+                      "usable cores" % (w.name, cpu_s, _cpu_model(),
+                                        len(os.sched_getaffinity(0))),
         }
-        line["parity_vs_oracle"] = bool(np.array_equal(keep, want))
+        line["parity_vs_oracle"] = bool(np.array_equal(r["keep"], want))
     print(json.dumps(line), flush=True)
 
 

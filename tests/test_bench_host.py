@@ -46,3 +46,13 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "single MI355X" in r.stderr
+
+
+def test_sweep_dense_bytes_by_hand():
+    import numpy as np
+    # 130 boxes (3 row tiles); scores descending in index, so sorted position
+    # = index; kept boxes at positions 0, 64 and 129
+    scores = np.linspace(1.0, 0.5, 130).astype(np.float32)
+    w = workloads.Workload("t", np.zeros((130, 4), np.float32), scores, 0.5)
+    got = bench._sweep_dense_bytes(w, [0, 64, 129])
+    assert got == 8 * 130 + 8 * ((3 - 0 - 1) + (3 - 1 - 1) + (3 - 2 - 1))
