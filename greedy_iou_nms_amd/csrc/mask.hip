@@ -1,5 +1,4 @@
-// Stages (a, gather) and (b): sorted box gather, then the triangle-tiled IoU
-// suppression bitmask.
+// Stage (b): the triangle-tiled IoU suppression bitmask.
 //
 // Bitmask layout ("LeetCUDA 14-nms", Phase 1, with 64-bit words): row p of
 // the mask belongs to sorted box p; bit l of its word for column tile c is 1
@@ -44,42 +43,6 @@ namespace gnms {
 namespace {
 
 using namespace maskcore;
-
-// ---------------------------------------------------------------- gather
-
-struct GatherArgs {
-    const float4 *boxes;
-    int n, npad, words, grouped;
-    Work w;
-};
-
-__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
-    const int p = blockIdx.x * 256 + threadIdx.x;
-    if (p >= a.npad) return;
-    if (p < a.words) a.w.tcount[p] = 0u;  // the mask kernel counts each tile's nonzero words
-    // near words stay 0 where the tile lies outside the row's band
-    for (int j = 0; j <= NEAR_TILES; ++j) a.w.tnear[(size_t)j * a.npad + p] = 0ull;
-    bool finite = true, positive = true;
-    if (p < a.n) {
-        const int i = a.w.order[p];
-        const float4 b = a.boxes[i];
-        finite = isfinite(b.x) && isfinite(b.y) && isfinite(b.z) && isfinite(b.w);
-        const float ar = (b.z - b.x) * (b.w - b.y);
-        positive = ar > 0.0f && ar < INFINITY;
-        a.w.sb[p] = b;
-        a.w.area[p] = ar;
-        if (a.grouped) a.w.inv[i] = p;
-    } else {
-        a.w.sb[p] = make_float4(0.f, 0.f, 0.f, 0.f);
-        a.w.area[p] = 0.0f;
-    }
-    const uint64_t bad_f = __ballot(!finite);
-    const uint64_t bad_a = __ballot(!positive);
-    if ((threadIdx.x & 63) == 0) {
-        if (bad_f) atomicOr(&a.w.ctrl->error, ERR_NONFINITE);
-        if (bad_a) atomicAnd(&a.w.ctrl->flags, ~FLAG_POSITIVE_AREAS);
-    }
-}
 
 // ---------------------------------------------------------------- mask
 
@@ -147,22 +110,9 @@ Threshold make_threshold(float t) {
     return th;
 }
 
-hipError_t launch_gather(const Problem &P, const Layout &L, const Work &w, hipStream_t stream) {
-    GatherArgs a;
-    a.boxes = reinterpret_cast<const float4 *>(P.boxes);
-    a.n = P.n;
-    a.npad = (int)L.npad;
-    a.words = (int)L.words;
-    a.grouped = P.grouped ? 1 : 0;
-    a.w = w;
-    const int blocks = (int)((L.npad + 255) / 256);
-    hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(256), 0, stream, a);
-    return hipGetLastError();
-}
-
 namespace maskcore {
 
-MaskArgs make_mask_args(const Problem &P, const Layout &L) {
+MaskArgs make_mask_args(const Problem &P, const Layout &L, int64_t slots) {
     const Threshold th = make_threshold(P.thresh);
     MaskArgs a;
     a.n = P.n;
@@ -175,12 +125,13 @@ MaskArgs make_mask_args(const Problem &P, const Layout &L) {
     a.exact_ok = th.exact_ok ? 1 : 0;
     a.pinf = INFINITY;
     a.ninf = -INFINITY;
-    // enough work items to give every CU 16 waves, splitting pairs into up
-    // to 4 groups of rows when there are too few
+    // Too few pairs to give every slot one: split them into up to 4 groups
+    // of rows.  Grouped input has short bands, and the bound here counts
+    // full rows, so its pairs are always split.
     const int64_t pairs = mask_items_upper_bound(P, L);
-    const int64_t want = (int64_t)device_cu_count() * 16;
     a.qshift = 0;
-    while (a.qshift < 2 && (pairs << a.qshift) < want) ++a.qshift;
+    while (a.qshift < 2 && (pairs << a.qshift) < slots) ++a.qshift;
+    if (P.grouped) a.qshift = 2;
     return a;
 }
 
@@ -198,9 +149,11 @@ int64_t mask_items_upper_bound(const Problem &P, const Layout &L) {
 }  // namespace maskcore
 
 hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStream_t stream) {
-    const maskcore::MaskArgs a = maskcore::make_mask_args(P, L);
-    const int64_t items_ub = maskcore::mask_items_upper_bound(P, L) << a.qshift;
     const int waves_per_block = MASK_THREADS / 64;
+    // resident waves: 4 per SIMD at the kernel's register count
+    const int64_t slots = (int64_t)device_cu_count() * 16;
+    const maskcore::MaskArgs a = maskcore::make_mask_args(P, L, slots);
+    const int64_t items_ub = maskcore::mask_items_upper_bound(P, L) << a.qshift;
     int64_t blocks = (items_ub + waves_per_block - 1) / waves_per_block;
     const int64_t cap = (int64_t)device_cu_count() * 8;
     if (blocks > cap) blocks = cap;

@@ -138,9 +138,10 @@ template <int S, bool GROUPED, int MODE, bool COHERENT>
 __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_, int item,
                                           int stride, uint32_t *done) {
     const int lane = threadIdx.x & 63;
-    // the item's rows within its (row tile, strip) pair
+    // the item's pair and rows within it
+    const int rpi = 64 >> a.qshift;
     const int pair = item >> a.qshift;
-    const int k_lo = (item & ((1 << a.qshift) - 1)) * (64 >> a.qshift);
+    const int k_lo = (item & ((1 << a.qshift) - 1)) * rpi;
     // row tile of this pair: the largest r with item_base[r] <= pair
     int lo = 0, hi = a.words - 1;
     while (lo < hi) {
@@ -154,7 +155,7 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
     const int cend = m_.tile_cend[r];
     const int p0 = 64 * r;
     const int tile_rows = a.n - p0 < 64 ? a.n - p0 : 64;
-    const int k_hi = k_lo + (64 >> a.qshift) < tile_rows ? k_lo + (64 >> a.qshift) : tile_rows;
+    const int k_hi = k_lo + rpi < tile_rows ? k_lo + rpi : tile_rows;
     // lanes k_lo .. k_hi - 1 end up holding the words of rows k_lo .. k_hi - 1
     const bool mine = lane >= k_lo && lane < k_hi;
     const int t_diag = r - c0;  // the diagonal tile's slot, if it lies in this strip
@@ -258,8 +259,9 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
         // device-scope loads on every XCD, so a reader that sees the count
         // sees the data.  No L2 write-back (a release fence) is needed: that
         // is for plain stores, and the sweep reads none of those.
-        // Every lane adds 1 (an item counts 64): a lane-0-only branch here
-        // would put a lane-divergent region at the end of the caller's loop.
+        // Every lane adds 1, so a finished pair counts 64 << qshift: a
+        // lane-0-only branch here would put a lane-divergent region at the
+        // end of the caller's loop.
         __builtin_amdgcn_s_waitcnt(0x0F70);
         asm volatile("" ::: "memory");
         __hip_atomic_fetch_add(&done[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -286,8 +288,9 @@ __device__ __forceinline__ void mask_items(const MaskArgs &a, const MaskPtrs &m_
     }
 }
 
-// Kernel arguments of the mask stage, filled on the host.
-MaskArgs make_mask_args(const Problem &P, const Layout &L);
+// Kernel arguments of the mask stage, filled on the host; `slots` is the
+// number of waves that take work items at once.
+MaskArgs make_mask_args(const Problem &P, const Layout &L, int64_t slots);
 // Upper bound on the work items of a launch (every row tile covers all
 // strips to the end).
 int64_t mask_items_upper_bound(const Problem &P, const Layout &L);

@@ -46,11 +46,17 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_tent_wk = take((size_t)L.words * TILE_LIST_CAP * 4);
     L.off_tent_val = take((size_t)L.words * TILE_LIST_CAP * 8);
     L.off_tnear = take(np * 8 * (NEAR_TILES + 1));
-    L.off_hist_tile = take((size_t)L.tiles * 4 * 256 * 4);
-    L.off_lb_status = take((size_t)4 * L.tiles * 256 * 4);
-    L.off_tickets = take(4 * 4);
+    L.off_hist_tile = take((size_t)L.tiles * RADIX_PASSES * 256 * 4);
+    L.off_lb_status = take((size_t)RADIX_PASSES * L.tiles * 256 * 4);
+    L.off_tickets = take(RADIX_PASSES * 4);
     L.off_err_tile = take((size_t)L.tiles * 4);
+    L.off_gcls = take(np * 4);
+    L.off_gimg = take(np * 4);
+    L.off_pass_plan = take(RADIX_PASSES * sizeof(RadixPassPlan));
+    L.off_gbase = take((size_t)RADIX_PASSES * 256 * 4);
     L.off_done = take((size_t)L.words * 4);
+    L.off_seg_start = take(np * 4 + 4);
+    L.off_block_cnt = take(((size_t)n / COMPACT_CHUNK + 1) * 4);
     L.off_mask = take((size_t)n * (size_t)L.mstride * 8);
     L.total = off;
     *out = L;
@@ -84,6 +90,12 @@ Work carve(void *workspace, const Layout &L) {
     w.err_tile = reinterpret_cast<uint32_t *>(b + L.off_err_tile);
     w.mask = reinterpret_cast<uint64_t *>(b + L.off_mask);
     w.done = reinterpret_cast<uint32_t *>(b + L.off_done);
+    w.seg_start = reinterpret_cast<int32_t *>(b + L.off_seg_start);
+    w.block_cnt = reinterpret_cast<uint32_t *>(b + L.off_block_cnt);
+    w.gcls = reinterpret_cast<uint32_t *>(b + L.off_gcls);
+    w.gimg = reinterpret_cast<uint32_t *>(b + L.off_gimg);
+    w.pass_plan = reinterpret_cast<RadixPassPlan *>(b + L.off_pass_plan);
+    w.gbase = reinterpret_cast<uint32_t *>(b + L.off_gbase);
     return w;
 }
 
@@ -208,10 +220,8 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     };
 
     hipError_t e = mark(0);
-    if (e == hipSuccess) e = P.grouped ? launch_sort(P, L, w, stream)
-                                       : launch_radix_sort(P, L, w, stream);
+    if (e == hipSuccess) e = launch_radix_sort(P, L, w, stream);
     if (e == hipSuccess) e = mark(1);
-    if (e == hipSuccess && P.grouped) e = launch_gather(P, L, w, stream);
     if (e == hipSuccess) e = mark(2);
     // One image of moderate size: the sweep runs inside the mask launch.  The
     // plain sweep launch still follows; it does nothing when the fused sweep
@@ -221,6 +231,7 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     if (e == hipSuccess)
         e = fused ? launch_mask_sweep(P, L, w, keep_out, stream) : launch_mask(P, L, w, stream);
     if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess && P.grouped) e = launch_group_sweep(P, L, w, stream);
     if (e == hipSuccess) e = launch_sweep(P, L, w, keep_out, stream);
     if (e == hipSuccess) e = mark(4);
     if (e == hipSuccess && P.grouped) e = launch_compact(P, L, w, keep_out, stream);
@@ -310,7 +321,7 @@ nms_status nms_debug_order(const float *scores, int64_t n, const int32_t *class_
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     const Problem P = make_problem(nullptr, scores, n, 0.5f, class_ids, batch_offsets, num_images);
     const Work w = carve(workspace, L);
-    hipError_t e = P.grouped ? launch_sort(P, L, w, stream) : launch_radix_sort(P, L, w, stream);
+    hipError_t e = launch_radix_sort(P, L, w, stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(order_out, w.order, (size_t)n * 4, hipMemcpyDeviceToDevice, stream);
     if (e == hipSuccess && score_order_out) {
@@ -347,8 +358,7 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
     const Problem P =
         make_problem(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images);
     const Work w = carve(workspace, L);
-    hipError_t e = P.grouped ? launch_sort(P, L, w, stream) : launch_radix_sort(P, L, w, stream);
-    if (e == hipSuccess && P.grouped) e = launch_gather(P, L, w, stream);
+    hipError_t e = launch_radix_sort(P, L, w, stream);
     if (e == hipSuccess) e = launch_mask(P, L, w, stream);
     if (e == hipSuccess) e = launch_expand_mask(P, L, w, mask_out, stream);
     if (e == hipSuccess && order_out)

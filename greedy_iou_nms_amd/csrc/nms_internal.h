@@ -26,7 +26,9 @@ struct Ctrl {
     int32_t num_items;      // mask work items (row tile x strip)
     int32_t band_stride;    // mask row stride in 64-bit words
     int32_t num_segments;   // groups present (1 for a single image)
-    uint32_t fused_done;    // 1 once the fused mask + sweep kernel finished the sweep
+    // 1 once a sweep that may give up (the fused single-image sweep, the
+    // parallel grouped sweep) finished; the plain sweep kernel then returns
+    uint32_t sweep_done;
     int32_t reserved[9];
 };
 static_assert(sizeof(Ctrl) == 64, "Ctrl layout");
@@ -36,14 +38,28 @@ static_assert(sizeof(Ctrl) == 64, "Ctrl layout");
 constexpr int STRIP_SINGLE = 16;
 constexpr int STRIP_GROUPED = 4;
 
-constexpr int SORT_THREADS = 1024;
-
 // Multi-workgroup radix sort (one image): a workgroup of RADIX_THREADS ranks
 // one tile of RADIX_TILE keys per pass.
 constexpr int RADIX_THREADS = 256;
 constexpr int RADIX_E = 16;
 constexpr int RADIX_TILE = RADIX_THREADS * RADIX_E;
+// 8-bit digit passes: 4 on the score key, then (grouped input) 4 on the
+// class key and 4 on the image.
+constexpr int RADIX_PASSES = 12;
+
+// Per radix pass, decided on the device from the digit counts.
+struct RadixPassPlan {
+    uint32_t skip;        // every key has the same digit: the pass moves nothing
+    uint32_t src;         // which of the two key/value buffers the pass reads
+    uint32_t last;        // the last pass that runs: writes the sorted arrays
+    uint32_t last_score;  // the last score pass that runs: writes the score order
+};
 constexpr int SWEEP_THREADS = 512;
+// Grouped compaction: score ranks per workgroup.
+constexpr int COMPACT_CHUNK = 2048;
+// Grouped sweep: one wave per segment keeps the removed words of the next
+// GROUP_SWEEP_WIN row tiles; wider bands fall back to the plain sweep.
+constexpr int GROUP_SWEEP_WIN = 256;
 constexpr int MASK_THREADS = 256;
 
 // Nonzero mask words recorded per row tile (row, word index, value) besides
@@ -78,7 +94,8 @@ struct Layout {
     size_t off_sb = 0, off_area = 0, off_tile_cend = 0, off_item_base = 0, off_kept = 0;
     size_t off_tcount = 0, off_tent_wk = 0, off_tent_val = 0, off_tnear = 0;
     size_t off_hist_tile = 0, off_lb_status = 0, off_tickets = 0, off_err_tile = 0;
-    size_t off_done = 0;
+    size_t off_gcls = 0, off_gimg = 0, off_pass_plan = 0, off_gbase = 0;
+    size_t off_done = 0, off_seg_start = 0, off_block_cnt = 0;
     size_t off_mask = 0, total = 0;
 };
 
@@ -105,15 +122,24 @@ struct Work {
     // 0 where that tile lies outside the row's band
     uint64_t *tnear;
     uint64_t *mask;        // suppression bitmask rows
-    // radix sort, one image: per-tile 4-digit histograms [tile][4][256],
-    // look-back status words [pass][tile][256], one ticket per pass, and
-    // per-tile error bits from key generation
+    // radix sort: per-tile digit histograms [tile][RADIX_PASSES][256],
+    // look-back status words [pass][tile][256], one ticket per pass, per-tile
+    // error bits from key generation, the grouped keys of every input box
+    // (class key, image), and per pass its plan and digit starts [pass][256]
     uint32_t *hist_tile;
     uint32_t *lb_status;
     uint32_t *tickets;
     uint32_t *err_tile;
+    uint32_t *gcls;
+    uint32_t *gimg;
+    RadixPassPlan *pass_plan;
+    uint32_t *gbase;
     // fused mask + sweep: per row tile, mask work items finished
     uint32_t *done;
+    // grouped: first sorted position of every segment, then n
+    int32_t *seg_start;
+    // grouped compaction: kept boxes per block of COMPACT_CHUNK score ranks
+    uint32_t *block_cnt;
 };
 
 Work carve(void *workspace, const Layout &L);
@@ -131,12 +157,10 @@ struct Problem {
 };
 
 // Stage launchers; all enqueue on `stream` and return the launch status.
-// One image: launch_radix_sort sorts and also gathers the sorted boxes (no
-// separate gather launch).  Grouped input: launch_sort, then launch_gather.
+// launch_radix_sort sorts, gathers the sorted boxes and (grouped input)
+// plans the segments and the mask work.
 hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
                              hipStream_t stream);
-hipError_t launch_sort(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
-hipError_t launch_gather(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
 hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
 hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
                         hipStream_t stream);
@@ -151,6 +175,10 @@ hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, i
 int device_cu_count();
 hipError_t launch_compact(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
                           hipStream_t stream);
+// Grouped input: sweep every segment with its own wave.  launch_sweep must
+// still follow; it returns at once unless a band is wider than the window.
+hipError_t launch_group_sweep(const Problem &P, const Layout &L, const Work &w,
+                              hipStream_t stream);
 hipError_t launch_expand_mask(const Problem &P, const Layout &L, const Work &w,
                               uint64_t *mask_out, hipStream_t stream);
 hipError_t launch_decide(const float *inter, const float *uni, int64_t count, float thresh,

@@ -1,33 +1,46 @@
-// Stage (a) for one image: stable LSD radix sort over all compute units,
-// fused with the sorted box gather.
+// Stage (a): stable LSD radix sort over all compute units, fused with the
+// sorted box gather, and (grouped input) the segment plan of the mask.
 //
 // Greedy NMS visits boxes by score, highest first, with equal scores in input
 // order ("LeetCUDA 14-nms", algorithm and data flow, step 1: a stable sort).
 // Each score maps to a 32-bit key whose ascending order is descending score
-// (-0.0 folded onto +0.0 so the two tie); four stable passes over 8-bit digits
-// starting from input order leave equal keys in ascending index order, so the
-// index never takes part in a pass.
+// (-0.0 folded onto +0.0 so the two tie); stable passes over 8-bit digits
+// starting from input order leave equal keys in ascending index order, so
+// the index never takes part in a pass.  Grouped input (class ids and/or
+// several images) continues with stable passes on the class key and then on
+// the image, which makes every (image, class) group contiguous, in score
+// order inside; the order after the score passes is kept as the plain score
+// order for the final compaction.
 //
-//   radix_keys_kernel   one workgroup per tile of 4096 boxes: keys, each
-//                       tile's histogram of all four digits (digit counts do
-//                       not depend on the order, so one read serves all
-//                       passes), and the per-call initialisation of the
-//                       plan, the control block and the sweep's side arrays.
-//   radix_pass_kernel   one workgroup per tile, four launches.  A tile is
-//                       ranked (64-lane ballots tell which lanes share a
+//   radix_keys_kernel   one workgroup per tile of 4096 boxes: the keys (score;
+//                       grouped: class key and image of every box), each
+//                       tile's histograms of every digit (digit counts do not
+//                       depend on the order, so one read serves all passes),
+//                       the input checks and the per-call initialisation.
+//   radix_plan_kernel   one workgroup: per pass the global digit counts, their
+//                       prefix (where each digit's run starts), whether the
+//                       pass can be skipped (every key has the same digit),
+//                       which buffer it reads, and which pass is the last.
+//   radix_pass_kernel   one workgroup per tile, one launch per pass.  A tile
+//                       is ranked (64-lane ballots tell which lanes share a
 //                       digit; walking waves, then elements, then lanes walks
 //                       indices in order, which keeps the pass stable), its
 //                       per-digit offset among earlier tiles comes from a
 //                       decoupled look-back over the tiles' published counts,
 //                       and the tile is reordered by digit in LDS so that the
 //                       writes are coalesced runs.  The last pass writes the
-//                       sorted order and the sorted boxes and areas directly.
+//                       sorted order, the sorted boxes and areas and (grouped)
+//                       the inverse permutation.
+//   group_plan_kernel   grouped input, one workgroup: segment of every sorted
+//                       position, the band of column tiles of every row tile
+//                       and the mask work items.
 //
 // The look-back waits only on tiles that took their ticket earlier, which are
 // already running, and every wait is bounded: a wait that gives up raises an
 // internal error instead of hanging.
 #include <cmath>
 
+#include "greedy_nms.h"
 #include "nms_internal.h"
 
 #pragma clang fp contract(off)
@@ -66,9 +79,26 @@ __device__ __forceinline__ uint32_t score_key(float s) {
     return ~asc;
 }
 
+// signed class id -> unsigned key with the same order
+__device__ __forceinline__ uint32_t class_key(int32_t c) { return (uint32_t)c ^ 0x80000000u; }
+
+// Image of input box i: the largest m < num_images with off[m] <= i.
+__device__ __forceinline__ uint32_t image_of(const int64_t *off, int num_images, int64_t i) {
+    int lo = 0, hi = num_images - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= i) lo = mid;
+        else hi = mid - 1;
+    }
+    return (uint32_t)lo;
+}
+
 struct KeysArgs {
     const float *scores;
-    int n, npad, words, strip, mstride, tiles;
+    const int32_t *class_ids;  // grouped input only (may be null)
+    const int64_t *offsets;    // grouped input only (may be null)
+    int num_images;
+    int n, npad, words, strip, mstride, tiles, grouped;
     Work w;
 };
 
@@ -83,71 +113,100 @@ __device__ __forceinline__ int32_t item_base_full(int r, int W, int S) {
 // Lanes add into HIST_COPIES interleaved copies of the histograms: keys of
 // real scores share their top digits (the float exponent), and atomics of
 // many lanes on one LDS word serialise.
-constexpr int HIST_COPIES = 8;
+constexpr int HIST_COPIES = 4;
 
 __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
-    __shared__ uint32_t hcopy[HIST_COPIES][4][256];
+    __shared__ uint32_t hcopy[HIST_COPIES][RADIX_PASSES][256];
     __shared__ uint32_t err_sh;
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int tile = blockIdx.x;
     const Work &w = a.w;
-    for (int j = tid; j < HIST_COPIES * 4 * 256; j += NT) (&hcopy[0][0][0])[j] = 0u;
+    const int digits = a.grouped ? RADIX_PASSES : 4;
+    for (int j = tid; j < HIST_COPIES * RADIX_PASSES * 256; j += NT) (&hcopy[0][0][0])[j] = 0u;
     if (tid == 0) err_sh = 0u;
     __syncthreads();
     uint32_t (*hist)[256] = hcopy[lane % HIST_COPIES];
     uint32_t err = 0;
     const int base = tile * TILE + wave * 64 * E + lane;
+    float s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = base + e * 64;
+        s[e] = i < a.n ? a.scores[i] : 0.0f;
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int i = base + e * 64;
         if (i < a.n) {
-            const float s = a.scores[i];
-            if (s != s) err |= ERR_NONFINITE;
-            const uint32_t k = score_key(s);
+            if (s[e] != s[e]) err |= ERR_NONFINITE;
+            const uint32_t k = score_key(s[e]);
             w.keys0[i] = k;
             w.vals0[i] = (uint32_t)i;
             atomicAdd(&hist[0][k & 255u], 1u);
             atomicAdd(&hist[1][(k >> 8) & 255u], 1u);
             atomicAdd(&hist[2][(k >> 16) & 255u], 1u);
             atomicAdd(&hist[3][k >> 24], 1u);
+            if (a.grouped) {
+                // the plain score order, should every score pass be skipped
+                w.score_order[i] = i;
+                const uint32_t c = a.class_ids ? class_key(a.class_ids[i]) : 0u;
+                const uint32_t m = a.offsets ? image_of(a.offsets, a.num_images, i) : 0u;
+                w.gcls[i] = c;
+                w.gimg[i] = m;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    atomicAdd(&hist[4 + d][(c >> (8 * d)) & 255u], 1u);
+                    atomicAdd(&hist[8 + d][(m >> (8 * d)) & 255u], 1u);
+                }
+            }
+        }
+    }
+    const int gid = tile * NT + tid, gsz = a.tiles * NT;
+    // batch offsets must rise from 0 to n
+    if (a.grouped && a.offsets) {
+        for (int m = gid; m <= a.num_images; m += gsz) {
+            const int64_t o = a.offsets[m];
+            bool bad = (m == 0 && o != 0) || (m == a.num_images && o != (int64_t)a.n);
+            if (m > 0 && o < a.offsets[m - 1]) bad = true;
+            if (bad) err |= ERR_BAD_OFFSETS;
         }
     }
     if (err) atomicOr(&err_sh, err);
     __syncthreads();
-    for (int j = tid; j < 4 * 256; j += NT) {
+    for (int j = tid; j < digits * 256; j += NT) {
         uint32_t sum = 0;
 #pragma unroll
         for (int q = 0; q < HIST_COPIES; ++q) sum += (&hcopy[q][0][0])[j];
-        w.hist_tile[(size_t)tile * 1024 + j] = sum;
+        w.hist_tile[(size_t)tile * RADIX_PASSES * 256 + j] = sum;
     }
-    // the four passes' look-back words of this tile start empty
-    for (int j = tid; j < 4 * 256; j += NT) {
+    // every pass's look-back words of this tile start empty
+    for (int j = tid; j < digits * 256; j += NT) {
         const int pass = j >> 8, d = j & 255;
         w.lb_status[((size_t)pass * a.tiles + tile) * 256 + d] = 0u;
     }
     if (tid == 0) w.err_tile[tile] = err_sh;
     if (tile == 0 && tid == 0) {
-        for (int p = 0; p < 4; ++p) w.tickets[p] = 0u;
+        for (int p = 0; p < RADIX_PASSES; ++p) w.tickets[p] = 0u;
         Ctrl *c = w.ctrl;
         c->error = 0u;
         c->flags = FLAG_POSITIVE_AREAS;
         c->count = 0;
-        c->num_items = item_base_full(a.words, a.words, a.strip);
+        c->num_items = a.grouped ? 0 : item_base_full(a.words, a.words, a.strip);
         c->band_stride = a.mstride;
         c->num_segments = 1;
-        c->fused_done = 0u;
+        c->sweep_done = 0u;
     }
-    // Per-call initialisation, spread over the whole grid: the plan of the
-    // mask kernel (every row tile covers all column tiles), the padding rows
-    // of the sorted arrays, and the sweep's side arrays that the mask kernel
-    // only partly writes.
-    const int gid = tile * NT + tid, gsz = a.tiles * NT;
+    // Per-call initialisation, spread over the whole grid: the side arrays
+    // the mask kernel only partly writes, the padding rows of the sorted
+    // arrays, and (one image) the plan of the mask kernel (every row tile
+    // covers all column tiles).
     for (int r = gid; r <= a.words; r += gsz) {
-        w.item_base[r] = item_base_full(r, a.words, a.strip);
+        if (!a.grouped) w.item_base[r] = item_base_full(r, a.words, a.strip);
         if (r < a.words) {
-            w.tile_cend[r] = a.words;
+            if (!a.grouped) w.tile_cend[r] = a.words;
             w.tcount[r] = 0u;
             w.done[r] = 0u;
+            if (a.grouped) w.kept[r] = 0ull;  // the grouped sweep ORs segments in
         }
     }
     for (int p = gid; p < a.npad; p += gsz) {
@@ -157,34 +216,12 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
             w.order[p] = 0;
             w.sb[p] = make_float4(0.f, 0.f, 0.f, 0.f);
             w.area[p] = 0.0f;
+            if (a.grouped) w.seg[p] = 0xFFFFFFFFu;
         }
     }
 }
 
-struct PassArgs {
-    const uint32_t *src_k, *src_v;
-    uint32_t *dst_k, *dst_v;
-    const float4 *boxes;  // last pass only: gather the sorted boxes (may be null)
-    int n, tiles, pass;
-    Work w;
-};
-
-struct PassSmem {
-    uint32_t gbase[256];   // global start of each digit
-    uint32_t tcnt[256];    // digit counts of this tile
-    uint32_t tbase[256];   // start of each digit's run inside the staged tile
-    int32_t gsh[256];      // global position minus staged slot, per digit
-    uint32_t wcnt[NWAVES][256];
-    uint32_t wpre[NWAVES][256];
-    uint32_t stage_k[TILE];
-    uint32_t stage_v[TILE];
-    uint32_t part[NWAVES];
-    uint32_t tile;
-    uint32_t err;
-    uint32_t bad_area;
-};
-
-// Exclusive scan of v[0..256) into out[] by the first wave (4 per lane).
+// Exclusive scan of v[0..256) into out[] by one wave (4 per lane).
 __device__ __forceinline__ void scan256(const uint32_t *v, uint32_t *out) {
     const int lane = lane_id();
     const uint32_t h0 = v[4 * lane], h1 = v[4 * lane + 1], h2 = v[4 * lane + 2],
@@ -197,12 +234,108 @@ __device__ __forceinline__ void scan256(const uint32_t *v, uint32_t *out) {
     out[4 * lane + 3] = ex + h0 + h1 + h2;
 }
 
-template <bool LAST>
+struct PlanArgs {
+    int n, tiles, passes;
+    Work w;
+};
+
+// One workgroup: for each pass the global start of each digit's run, and
+// whether the pass moves anything.  A pass whose digit is the same for every
+// key is skipped; the buffer a pass reads is the one the last moving pass
+// before it wrote.  If no pass moves, the last pass still runs (as a copy)
+// to write the sorted order and boxes.
+__global__ __launch_bounds__(NT) void radix_plan_kernel(PlanArgs a) {
+    __shared__ uint32_t tot[256];
+    __shared__ uint32_t skip[RADIX_PASSES];
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const Work &w = a.w;
+    for (int pass = 0; pass < a.passes; ++pass) {
+        uint32_t t = 0;
+        for (int tl = 0; tl < a.tiles; ++tl)
+            t += w.hist_tile[((size_t)tl * RADIX_PASSES + pass) * 256 + tid];
+        tot[tid] = t;
+        __syncthreads();
+        if (wave == 0) {
+            scan256(tot, &w.gbase[pass * 256]);
+            const uint32_t un = (uint32_t)a.n;
+            const bool one = tot[4 * lane] == un || tot[4 * lane + 1] == un ||
+                             tot[4 * lane + 2] == un || tot[4 * lane + 3] == un;
+            const uint64_t any = __ballot(one);
+            if (lane == 0) skip[pass] = any ? 1u : 0u;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        int last = -1, last_score = -1;
+        for (int p = 0; p < a.passes; ++p)
+            if (!skip[p]) {
+                last = p;
+                if (p < 4) last_score = p;
+            }
+        if (last < 0) {
+            last = a.passes - 1;
+            skip[last] = 0u;
+        }
+        uint32_t moved = 0;
+        for (int p = 0; p < a.passes; ++p) {
+            RadixPassPlan pl;
+            pl.skip = skip[p];
+            pl.src = moved & 1u;
+            pl.last = p == last ? 1u : 0u;
+            pl.last_score = p == last_score ? 1u : 0u;
+            w.pass_plan[p] = pl;
+            if (!skip[p]) ++moved;
+        }
+    }
+}
+
+struct PassArgs {
+    const float4 *boxes;  // the sorted-box gather of the last pass (may be null)
+    int n, tiles, pass, grouped;
+    // Grouped input runs a plan kernel first (12 passes, most of which skip).
+    // One image runs its four passes unconditionally, each summing the
+    // tiles' histograms itself, which saves the plan's launch.
+    int planned;
+    Work w;
+};
+
+struct PassSmem {
+    uint32_t gbase[256];   // global start of each digit
+    uint32_t tcnt[256];    // digit counts of this tile
+    uint32_t tbase[256];   // start of each digit's run inside the staged tile
+    int32_t gsh[256];      // global position minus staged slot, per digit
+    uint32_t wcnt[NWAVES][256];
+    uint32_t wpre[NWAVES][256];
+    uint32_t stage_k[TILE];
+    uint32_t stage_v[TILE];
+    uint32_t tile;
+    uint32_t err;
+    uint32_t bad_area;
+};
+
+// Passes 0-3 sort on the score key (read from the key buffer), 4-7 on the
+// class key, 8-11 on the image; the last two read the key of each element's
+// input index, so only the values move.
 __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
     __shared__ PassSmem sm;
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const int shift = 8 * a.pass;
     const Work &w = a.w;
+    RadixPassPlan pl;
+    if (a.planned) {
+        pl = w.pass_plan[a.pass];
+        if (pl.skip) return;
+    } else {
+        pl.skip = 0u;
+        pl.src = (uint32_t)(a.pass & 1);
+        pl.last = a.pass == 3 ? 1u : 0u;
+        pl.last_score = 0u;
+    }
+    const int shift = 8 * (a.pass & 3);
+    const int kind = a.pass >> 2;  // 0 score, 1 class, 2 image
+    const uint32_t *src_k = pl.src ? w.keys1 : w.keys0;
+    const uint32_t *src_v = pl.src ? w.vals1 : w.vals0;
+    uint32_t *dst_k = pl.src ? w.keys0 : w.keys1;
+    uint32_t *dst_v = pl.src ? w.vals0 : w.vals1;
     if (tid == 0) {
         // tiles are numbered in the order their workgroups start, so a tile
         // only ever waits on tiles that are already running
@@ -210,19 +343,20 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
         sm.err = 0u;
         sm.bad_area = 0u;
     }
-    __syncthreads();
-    const int tile = (int)sm.tile;
-    if (a.pass == 0 && tid == 0 && w.err_tile[tile]) atomicOr(&w.ctrl->error, w.err_tile[tile]);
-
-    // global start of each digit: all tiles' counts of this pass's digit
-    {
+    if (a.planned) {
+        sm.gbase[tid] = w.gbase[a.pass * 256 + tid];
+    } else {
+        // global start of each digit: all tiles' counts of this pass's digit
         uint32_t tot = 0;
         for (int t = 0; t < a.tiles; ++t)
-            tot += w.hist_tile[(size_t)t * 1024 + a.pass * 256 + tid];
+            tot += w.hist_tile[((size_t)t * RADIX_PASSES + a.pass) * 256 + tid];
         sm.tcnt[tid] = tot;  // scratch until the scan below
+        __syncthreads();
+        if (wave == 0) scan256(sm.tcnt, sm.gbase);
     }
     __syncthreads();
-    if (wave == 0) scan256(sm.tcnt, sm.gbase);
+    const int tile = (int)sm.tile;
+    if (tid == 0 && pl.last && w.err_tile[tile]) atomicOr(&w.ctrl->error, w.err_tile[tile]);
 
     // load and rank the tile
     const int wbase = tile * TILE + wave * 64 * E;
@@ -230,8 +364,16 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int i = wbase + e * 64 + lane;
-        k[e] = i < a.n ? a.src_k[i] : 0u;
-        v[e] = i < a.n ? a.src_v[i] : 0u;
+        v[e] = i < a.n ? src_v[i] : 0u;
+        k[e] = kind == 0 && i < a.n ? src_k[i] : 0u;
+    }
+    if (kind != 0) {
+        const uint32_t *gk = kind == 1 ? w.gcls : w.gimg;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = wbase + e * 64 + lane;
+            k[e] = i < a.n ? gk[v[e]] : 0u;
+        }
     }
     for (int j = lane; j < 256; j += 64) sm.wcnt[wave][j] = 0u;
 #pragma unroll
@@ -335,23 +477,25 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
         const uint32_t key = sm.stage_k[s];
         const int pos = s + sm.gsh[(key >> shift) & 255u];
         const uint32_t val = sm.stage_v[s];
-        if (!LAST) {
-            a.dst_k[pos] = key;
-            a.dst_v[pos] = val;
-        } else {
-            // the sorted order, and (when boxes are given: the sort-only test
-            // export passes none) the sorted boxes with their areas
-            w.order[pos] = (int32_t)val;
-            if (a.boxes == nullptr) continue;
-            const float4 b = a.boxes[val];
-            finite = finite && isfinite(b.x) && isfinite(b.y) && isfinite(b.z) && isfinite(b.w);
-            const float ar = (b.z - b.x) * (b.w - b.y);
-            positive = positive && ar > 0.0f && ar < INFINITY;
-            w.sb[pos] = b;
-            w.area[pos] = ar;
+        if (a.grouped && pl.last_score) w.score_order[pos] = (int32_t)val;
+        if (!pl.last) {
+            if (kind == 0) dst_k[pos] = key;
+            dst_v[pos] = val;
+            continue;
         }
+        // the sorted order, and (when boxes are given: the sort-only test
+        // export passes none) the sorted boxes with their areas
+        w.order[pos] = (int32_t)val;
+        if (a.grouped) w.inv[val] = pos;
+        if (a.boxes == nullptr) continue;
+        const float4 b = a.boxes[val];
+        finite = finite && isfinite(b.x) && isfinite(b.y) && isfinite(b.z) && isfinite(b.w);
+        const float ar = (b.z - b.x) * (b.w - b.y);
+        positive = positive && ar > 0.0f && ar < INFINITY;
+        w.sb[pos] = b;
+        w.area[pos] = ar;
     }
-    if (LAST) {
+    if (pl.last) {
         if (!finite) atomicOr(&sm.err, ERR_NONFINITE);
         if (!positive) atomicOr(&sm.bad_area, 1u);
     }
@@ -362,6 +506,138 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- grouped plan
+
+constexpr int GP_THREADS = 1024;
+constexpr int GP_WAVES = GP_THREADS / 64;
+
+struct GroupPlanArgs {
+    int n, words, npad, strip;
+    Work w;
+};
+
+struct GroupPlanSmem {
+    uint64_t start[(NMS_MAX_BOXES + 63) / 64];  // bit p: a segment starts at sorted position p
+    uint32_t part[GP_WAVES], part2[GP_WAVES], total;
+};
+
+// Exclusive workgroup-wide prefix sum; *total receives the sum.
+__device__ uint32_t gp_excl_sum(uint32_t v, GroupPlanSmem &sm, uint32_t *total) {
+    const int lane = lane_id(), wave = wave_id();
+    const uint32_t incl = wave_incl_sum(v);
+    if (lane == 63) sm.part[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t s = lane < GP_WAVES ? sm.part[lane] : 0u;
+        const uint32_t si = wave_incl_sum(s);
+        if (lane < GP_WAVES) sm.part2[lane] = si - s;
+        if (lane == GP_WAVES - 1) sm.total = si;
+    }
+    __syncthreads();
+    const uint32_t r = sm.part2[wave] + incl - v;
+    *total = sm.total;
+    __syncthreads();
+    return r;
+}
+
+// Sorted position of the last row of the segment holding sorted position p:
+// one before the next segment start after p (n - 1 if there is none).
+__device__ __forceinline__ int segment_end(const GroupPlanSmem &sm, int p, int n) {
+    const int nw = (n + 63) / 64;
+    int wi = p >> 6;
+    uint64_t bits = (p & 63) == 63 ? 0ull : (sm.start[wi] & (~0ull << ((p & 63) + 1)));
+    while (bits == 0ull) {
+        if (++wi >= nw) return n - 1;
+        bits = sm.start[wi];
+    }
+    return 64 * wi + __builtin_ctzll(bits) - 1;
+}
+
+// Grouped input after the sort: segment ids, the band of every row tile (its
+// columns run through the tile holding the end of the segment that holds
+// the tile's last row), the work items of the mask kernel and the mask row
+// stride.
+__global__ __launch_bounds__(GP_THREADS) void group_plan_kernel(GroupPlanArgs a) {
+    __shared__ GroupPlanSmem sm;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const Work &w = a.w;
+    const int n = a.n, W = a.words, S = a.strip;
+    const int nw = (n + 63) / 64;
+    // segment starts, one 64-bit word per wave and step
+    for (int wi = wave; wi < nw; wi += GP_WAVES) {
+        const int p = 64 * wi + lane;
+        bool st = false;
+        if (p < n) {
+            if (p == 0) {
+                st = true;
+            } else {
+                const uint32_t i = (uint32_t)w.order[p], j = (uint32_t)w.order[p - 1];
+                st = w.gimg[i] != w.gimg[j] || w.gcls[i] != w.gcls[j];
+            }
+        }
+        const uint64_t m = __ballot(st);
+        if (lane == 0) sm.start[wi] = m;
+    }
+    __syncthreads();
+    // segment id of every position: starts up to and including it, minus one
+    const int chunk = (nw + GP_THREADS - 1) / GP_THREADS;
+    const int lo = tid * chunk < nw ? tid * chunk : nw;
+    const int hi = lo + chunk < nw ? lo + chunk : nw;
+    uint32_t cnt = 0;
+    for (int wi = lo; wi < hi; ++wi) cnt += (uint32_t)__popcll(sm.start[wi]);
+    uint32_t segments = 0;
+    uint32_t before = gp_excl_sum(cnt, sm, &segments);
+    for (int wi = lo; wi < hi; ++wi) {
+        const uint64_t bits = sm.start[wi];
+        for (int k = 0; k < 64; ++k) {
+            const int p = 64 * wi + k;
+            if (p >= n) break;
+            if ((bits >> k) & 1ull) w.seg_start[before++] = p;
+            w.seg[p] = before - 1u;
+        }
+    }
+    // band of every row tile and its work items
+    const int tchunk = (W + GP_THREADS - 1) / GP_THREADS;
+    const int rlo = tid * tchunk < W ? tid * tchunk : W;
+    const int rhi = rlo + tchunk < W ? rlo + tchunk : W;
+    uint32_t items = 0, widest = 0;
+    int seg_end = -1;  // end of the segment found last (tiles come in order)
+    for (int r = rlo; r < rhi; ++r) {
+        const int last = 64 * r + 63 < n - 1 ? 64 * r + 63 : n - 1;
+        if (last > seg_end) seg_end = segment_end(sm, last, n);
+        const int cend = (seg_end >> 6) + 1;
+        w.tile_cend[r] = cend;
+        const uint32_t it = (uint32_t)((cend + S - 1) / S - r / S);
+        items += it;
+        widest = it > widest ? it : widest;
+    }
+    uint32_t total_items = 0;
+    uint32_t base = gp_excl_sum(items, sm, &total_items);
+    for (int r = rlo; r < rhi; ++r) {
+        w.item_base[r] = (int32_t)base;
+        base += (uint32_t)((w.tile_cend[r] + S - 1) / S - r / S);
+    }
+    // the widest band sets the row stride of the mask
+    uint32_t wmax = widest;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_xor(wmax, o, 64);
+        wmax = wmax > u ? wmax : u;
+    }
+    if (lane == 0) sm.part[wave] = wmax;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t band = 0;
+        for (int i = 0; i < GP_WAVES; ++i) band = sm.part[i] > band ? sm.part[i] : band;
+        w.item_base[W] = (int32_t)total_items;
+        Ctrl *c = w.ctrl;
+        c->num_items = (int32_t)total_items;
+        c->band_stride = (int32_t)(band * (uint32_t)S);
+        c->num_segments = (int32_t)segments;
+        w.seg_start[segments] = n;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
@@ -369,32 +645,49 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
     const int tiles = (int)L.tiles;
     KeysArgs ka;
     ka.scores = P.scores;
+    ka.class_ids = P.class_ids;
+    ka.offsets = P.offsets;
+    ka.num_images = P.num_images;
     ka.n = P.n;
     ka.npad = (int)L.npad;
     ka.words = (int)L.words;
     ka.strip = P.strip;
     ka.mstride = (int)L.mstride;
     ka.tiles = tiles;
+    ka.grouped = P.grouped ? 1 : 0;
     ka.w = w;
     hipLaunchKernelGGL(radix_keys_kernel, dim3(tiles), dim3(NT), 0, stream, ka);
     hipError_t e = hipGetLastError();
-    uint32_t *bk[2] = {w.keys0, w.keys1};
-    uint32_t *bv[2] = {w.vals0, w.vals1};
-    for (int pass = 0; pass < 4 && e == hipSuccess; ++pass) {
+    const int passes = P.grouped ? RADIX_PASSES : 4;
+    if (e == hipSuccess && P.grouped) {
+        PlanArgs pa;
+        pa.n = P.n;
+        pa.tiles = tiles;
+        pa.passes = passes;
+        pa.w = w;
+        hipLaunchKernelGGL(radix_plan_kernel, dim3(1), dim3(NT), 0, stream, pa);
+        e = hipGetLastError();
+    }
+    for (int pass = 0; pass < passes && e == hipSuccess; ++pass) {
         PassArgs pa;
-        pa.src_k = bk[pass & 1];
-        pa.src_v = bv[pass & 1];
-        pa.dst_k = bk[(pass + 1) & 1];
-        pa.dst_v = bv[(pass + 1) & 1];
         pa.boxes = reinterpret_cast<const float4 *>(P.boxes);
         pa.n = P.n;
         pa.tiles = tiles;
         pa.pass = pass;
+        pa.grouped = P.grouped ? 1 : 0;
+        pa.planned = P.grouped ? 1 : 0;
         pa.w = w;
-        if (pass < 3)
-            hipLaunchKernelGGL(radix_pass_kernel<false>, dim3(tiles), dim3(NT), 0, stream, pa);
-        else
-            hipLaunchKernelGGL(radix_pass_kernel<true>, dim3(tiles), dim3(NT), 0, stream, pa);
+        hipLaunchKernelGGL(radix_pass_kernel, dim3(tiles), dim3(NT), 0, stream, pa);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess && P.grouped) {
+        GroupPlanArgs ga;
+        ga.n = P.n;
+        ga.words = (int)L.words;
+        ga.npad = (int)L.npad;
+        ga.strip = P.strip;
+        ga.w = w;
+        hipLaunchKernelGGL(group_plan_kernel, dim3(1), dim3(GP_THREADS), 0, stream, ga);
         e = hipGetLastError();
     }
     return e;

@@ -63,7 +63,8 @@ struct SweepArgs {
     // fused with the mask: per row tile, mask work items finished
     const uint32_t *done;
     int n, words, npad, mstride, strip, grouped;
-    int strip_groups;  // ceil(W / strip): mask work items of row tile 0
+    int strip_groups;  // ceil(W / strip): mask work pairs of row tile 0
+    int done_shift;    // fused: a finished pair adds 64 << done_shift to done[]
 };
 
 // Reads of data the mask stage writes.  In the fused kernel the mask is still
@@ -222,7 +223,7 @@ __device__ __forceinline__ bool wait_tile_done(const SweepArgs &a, int c, SweepS
         const int t = (int)base + lane;
         bool fin = false;
         if (t < a.words) {
-            const uint32_t items = 64u * (uint32_t)(a.strip_groups - t / a.strip);
+            const uint32_t items = (64u << a.done_shift) * (uint32_t)(a.strip_groups - t / a.strip);
             fin = __hip_atomic_load(&a.done[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
                   items;
         }
@@ -659,16 +660,85 @@ __device__ __forceinline__ void sweep_body(const SweepArgs &a, uint64_t *removed
     }
     if (tid == 0) {
         a.ctrl->count = (int32_t)total;
-        if (FUSED) a.ctrl->fused_done = 1u;
+        if (FUSED) a.ctrl->sweep_done = 1u;
     }
 }
 
 __global__ __launch_bounds__(NT) void sweep_kernel(SweepArgs a) {
     extern __shared__ uint64_t removed[];
     __shared__ SweepSmem sm;
-    // the fused mask + sweep kernel already produced the result
-    if (a.ctrl->fused_done) return;
+    // the fused mask + sweep kernel, or the grouped sweep (which runs
+    // whenever every band fits its window), already produced the result
+    if (a.ctrl->sweep_done) return;
+    if (a.grouped && a.ctrl->band_stride <= GROUP_SWEEP_WIN) return;
     sweep_body<false>(a, removed, sm);
+}
+
+// ---------------------------------------------------------------- grouped sweep
+
+constexpr int GS_THREADS = 256;
+constexpr int GS_WAVES = GS_THREADS / 64;
+
+struct GroupSweepArgs {
+    const uint64_t *mask;
+    const int32_t *seg_start;
+    const Ctrl *ctrl;
+    uint64_t *kept;
+    int n, strip;
+};
+
+// Grouped input: boxes of different (image, class) groups never suppress
+// each other -- their bits in each other's words are zero -- so every group
+// (segment of sorted positions) can be swept on its own.  One wave per
+// segment walks the segment's row tiles in order: the diagonal words settle
+// the segment's rows of the tile as in the plain resolver, then the kept
+// rows' words for the later tiles of the segment are ORed across the wave
+// into a ring of removed words kept in LDS, one slot per row tile ahead.
+// Segments sharing a row tile OR their kept rows into its kept word.
+__global__ __launch_bounds__(GS_THREADS) void group_sweep_kernel(GroupSweepArgs a) {
+    __shared__ uint64_t ring[GS_WAVES][GROUP_SWEEP_WIN];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int stride = a.ctrl->band_stride;
+    if (stride > GROUP_SWEEP_WIN) return;  // the plain sweep does the work
+    const int nseg = a.ctrl->num_segments;
+    const int S = a.strip;
+    uint64_t *rw = ring[wave];
+    for (int j = lane; j < GROUP_SWEEP_WIN; j += 64) rw[j] = 0ull;
+    for (int g = blockIdx.x * GS_WAVES + wave; g < nseg; g += gridDim.x * GS_WAVES) {
+        const int s0 = a.seg_start[g], s1 = a.seg_start[g + 1];
+        const int t0 = s0 >> 6, tl = (s1 - 1) >> 6;
+        for (int t = t0; t <= tl; ++t) {
+            const int p = 64 * t + lane;
+            const bool in_seg = p >= s0 && p < s1;
+            // word c of row p sits at row[c]: rows hold their band only, and
+            // the band of any row of the segment reaches the segment's end
+            const uint64_t *row = a.mask + (size_t)p * stride - (t / S) * S;
+            const uint64_t d = in_seg ? row[t] : 0ull;
+            uint64_t rem = uniform64(rw[t % GROUP_SWEEP_WIN]);
+            const uint64_t valid = __ballot(in_seg);
+            uint64_t cand = ~rem & __ballot(d != 0ull) & valid;
+            const uint64_t nz = cand;
+            while (cand) {
+                const int kk = __builtin_ctzll(cand);
+                rem |= read_lane64(d, kk);
+                const uint64_t above = kk == 63 ? 0ull : (~0ull << (kk + 1));
+                cand = ~rem & nz & above;
+            }
+            const uint64_t kept = ~rem & valid;
+            const bool mine = (kept >> lane) & 1ull;
+            for (int u = t + 1; u <= tl; ++u) {
+                const uint64_t wu = mine ? row[u] : 0ull;
+                if (__ballot(wu != 0ull)) {
+                    const uint64_t o = wave_or64(wu);
+                    if (lane == 0) rw[u % GROUP_SWEEP_WIN] |= o;
+                }
+            }
+            if (lane == 0) {
+                rw[t % GROUP_SWEEP_WIN] = 0ull;  // free for row tile t + GROUP_SWEEP_WIN
+                if (kept) atomicOr(&a.kept[t], kept);
+            }
+        }
+    }
 }
 
 // Mask and sweep in one launch (one image).  Workgroup 0 runs the sweep; the
@@ -698,35 +768,91 @@ __global__ __launch_bounds__(NT) void mask_sweep_kernel(
                                                     (gridDim.x - 1) * NWAVES, done);
 }
 
+// ---------------------------------------------------------------- compaction
+
 struct CompactArgs {
     const int32_t *score_order;
     const int32_t *inv;
     const uint64_t *kept;
+    uint32_t *block_cnt;
     Ctrl *ctrl;
     int64_t *keep_out;
-    int n;
+    int n, blocks;
 };
 
-__global__ __launch_bounds__(NT) void compact_kernel(CompactArgs a) {
-    __shared__ uint32_t part[NWAVES], part2[NWAVES], tot;
+constexpr int CT = 256;  // compaction threads per workgroup
+constexpr int CT_ROWS = COMPACT_CHUNK / CT;
+
+// Score rank r's input index and whether it was kept (its sorted position's
+// bit in the kept bitmap).
+__device__ __forceinline__ bool rank_kept(const CompactArgs &a, int r, int32_t &i) {
+    i = a.score_order[r];
+    const int p = a.inv[i];
+    return (a.kept[p >> 6] >> (p & 63)) & 1ull;
+}
+
+// Grouped input, pass 1: kept boxes per block of COMPACT_CHUNK score ranks.
+__global__ __launch_bounds__(CT) void compact_count_kernel(CompactArgs a) {
+    __shared__ uint32_t part[CT / 64];
     const int tid = threadIdx.x;
-    const int n = a.n;
-    const int chunk = (n + NT - 1) / NT;
-    const int lo = tid * chunk < n ? tid * chunk : n;
-    const int hi = lo + chunk < n ? lo + chunk : n;
+    const int base = blockIdx.x * COMPACT_CHUNK;
     uint32_t cnt = 0;
-    for (int r = lo; r < hi; ++r) {
-        const int p = a.inv[a.score_order[r]];
-        cnt += (uint32_t)((a.kept[p >> 6] >> (p & 63)) & 1ull);
+#pragma unroll
+    for (int j = 0; j < CT_ROWS; ++j) {
+        const int r = base + j * CT + tid;
+        int32_t i;
+        if (r < a.n && rank_kept(a, r, i)) ++cnt;
     }
-    uint32_t total = 0;
-    uint32_t pos = block_excl_sum(cnt, part, part2, &tot, &total);
-    for (int r = lo; r < hi; ++r) {
-        const int i = a.score_order[r];
-        const int p = a.inv[i];
-        if ((a.kept[p >> 6] >> (p & 63)) & 1ull) a.keep_out[pos++] = (int64_t)i;
+    cnt = wave_incl_sum(cnt);
+    if ((tid & 63) == 63) part[tid >> 6] = cnt;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t t = 0;
+        for (int q = 0; q < CT / 64; ++q) t += part[q];
+        a.block_cnt[blockIdx.x] = t;
     }
-    if (tid == 0) a.ctrl->count = (int32_t)total;
+}
+
+// Grouped input, pass 2: each block writes its kept input indices in score
+// order, after the kept boxes of all earlier blocks; the last block stores
+// the count.
+__global__ __launch_bounds__(CT) void compact_write_kernel(CompactArgs a) {
+    __shared__ uint32_t part[CT / 64];
+    __shared__ uint32_t base_sh;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t before = 0;
+    for (int b = tid; b < (int)blockIdx.x; b += CT) before += a.block_cnt[b];
+    before = wave_incl_sum(before);
+    if (lane == 63) part[wave] = before;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t t = 0;
+        for (int q = 0; q < CT / 64; ++q) t += part[q];
+        base_sh = t;
+    }
+    __syncthreads();
+    uint32_t pos = base_sh;
+    const int base = blockIdx.x * COMPACT_CHUNK;
+    for (int j = 0; j < CT_ROWS; ++j) {
+        const int r = base + j * CT + tid;
+        int32_t i = 0;
+        const bool k = r < a.n && rank_kept(a, r, i);
+        // ranks of this row in thread order: wave counts, then lanes
+        const uint64_t m = __ballot(k);
+        __syncthreads();
+        if (lane == 0) part[wave] = (uint32_t)__popcll(m);
+        __syncthreads();
+        uint32_t off = 0, row_total = 0;
+        for (int q = 0; q < CT / 64; ++q) {
+            if (q < wave) off += part[q];
+            row_total += part[q];
+        }
+        const uint32_t in_wave =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (k) a.keep_out[pos + off + in_wave] = (int64_t)i;
+        pos += row_total;
+    }
+    if (blockIdx.x == (unsigned)(a.blocks - 1) && tid == 0) a.ctrl->count = (int32_t)pos;
 }
 
 // Dense copy of the mask for tests: out[p][c] for all c < W.
@@ -765,6 +891,7 @@ SweepArgs make_sweep_args(const Problem &P, const Layout &L, const Work &w, int6
     a.grouped = P.grouped ? 1 : 0;
     a.done = w.done;
     a.strip_groups = (int)((L.words + P.strip - 1) / P.strip);
+    a.done_shift = 0;
     return a;
 }
 
@@ -803,20 +930,22 @@ hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, i
     if (P.grouped || L.words < FUSE_MIN_WORDS || L.words > FUSE_MAX_WORDS)
         return hipErrorInvalidValue;
     const SweepArgs sa = make_sweep_args(P, L, w, keep_out);
-    maskcore::MaskArgs ma = maskcore::make_mask_args(P, L);
-    ma.qshift = 0;  // whole pairs: the finished counts assume one item per pair
-    const int64_t items_ub = maskcore::mask_items_upper_bound(P, L);
     // no more workgroups than the GPU holds at once (the sweep's included),
     // so that no item waits for a workgroup to start
     const size_t lds = (size_t)(L.words + NEAR_TILES) * sizeof(uint64_t);
     const int per_cu = fused_blocks_per_cu(lds);
-    int64_t blocks = (items_ub + NWAVES - 1) / NWAVES;
     const int64_t cap = (int64_t)device_cu_count() * per_cu - 1;
+    const maskcore::MaskArgs ma = maskcore::make_mask_args(P, L, (cap > 1 ? cap : 1) * NWAVES);
+    const int64_t pairs = maskcore::mask_items_upper_bound(P, L);
+    const int64_t items = pairs << ma.qshift;
+    int64_t blocks = (items + NWAVES - 1) / NWAVES;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
+    SweepArgs sa2 = sa;
+    sa2.done_shift = ma.qshift;  // a finished pair counts 64 << qshift
     hipLaunchKernelGGL(mask_sweep_kernel, dim3((unsigned)(blocks + 1)), dim3(NT), lds, stream, ma,
                        w.ctrl, w.sb, w.area, w.tile_cend, w.item_base, w.mask, w.tcount,
-                       w.tent_wk, w.tent_val, w.tnear, w.done, sa);
+                       w.tent_wk, w.tent_val, w.tnear, w.done, sa2);
     return hipGetLastError();
 }
 
@@ -827,10 +956,33 @@ hipError_t launch_compact(const Problem &P, const Layout &L, const Work &w, int6
     a.score_order = w.score_order;
     a.inv = w.inv;
     a.kept = w.kept;
+    a.block_cnt = w.block_cnt;
     a.ctrl = w.ctrl;
     a.keep_out = keep_out;
     a.n = P.n;
-    hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(NT), 0, stream, a);
+    a.blocks = (P.n + COMPACT_CHUNK - 1) / COMPACT_CHUNK;
+    hipLaunchKernelGGL(compact_count_kernel, dim3(a.blocks), dim3(CT), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(compact_write_kernel, dim3(a.blocks), dim3(CT), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_group_sweep(const Problem &P, const Layout &L, const Work &w,
+                              hipStream_t stream) {
+    GroupSweepArgs a;
+    a.mask = w.mask;
+    a.seg_start = w.seg_start;
+    a.ctrl = w.ctrl;
+    a.kept = w.kept;
+    a.n = P.n;
+    a.strip = P.strip;
+    // one wave per segment, segments are at most n
+    int64_t blocks = (P.n + GS_WAVES - 1) / GS_WAVES;
+    const int64_t cap = (int64_t)device_cu_count() * 4;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(group_sweep_kernel, dim3((unsigned)blocks), dim3(GS_THREADS), 0, stream, a);
     return hipGetLastError();
 }
 
