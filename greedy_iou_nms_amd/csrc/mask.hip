@@ -154,9 +154,10 @@ hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStre
     const int64_t slots = (int64_t)device_cu_count() * 16;
     const maskcore::MaskArgs a = maskcore::make_mask_args(P, L, slots);
     const int64_t items_ub = maskcore::mask_items_upper_bound(P, L) << a.qshift;
+    // one work item per wave: the GPU starts workgroups as earlier ones
+    // leave, which evens out waves that progress at different rates
     int64_t blocks = (items_ub + waves_per_block - 1) / waves_per_block;
-    const int64_t cap = (int64_t)device_cu_count() * 8;
-    if (blocks > cap) blocks = cap;
+    if (blocks > MAX_GRID_THREADS / MASK_THREADS) blocks = MAX_GRID_THREADS / MASK_THREADS;
     if (blocks < 1) blocks = 1;
     if (P.grouped)
         hipLaunchKernelGGL((mask_kernel<STRIP_GROUPED, true>), dim3((unsigned)blocks),

@@ -270,7 +270,8 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
 
 // The work items of one launch, handed out to waves in item order (row tile
 // by row tile): wave slot `first` of `slots` takes items first, first +
-// slots, ...
+// slots, ... (launches give every wave at most one item unless the item
+// count exceeds what a grid can hold)
 template <int S, bool GROUPED, bool COHERENT>
 __device__ __forceinline__ void mask_items(const MaskArgs &a, const MaskPtrs &m_,
                                            const Ctrl *__restrict__ ctrl, int first, int slots,

@@ -56,6 +56,7 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_gbase = take((size_t)RADIX_PASSES * 256 * 4);
     L.off_done = take((size_t)L.words * 4);
     L.off_seg_start = take(np * 4 + 4);
+    L.off_start_bits = take((size_t)L.words * 8);
     L.off_block_cnt = take(((size_t)n / COMPACT_CHUNK + 1) * 4);
     L.off_mask = take((size_t)n * (size_t)L.mstride * 8);
     L.total = off;
@@ -91,6 +92,7 @@ Work carve(void *workspace, const Layout &L) {
     w.mask = reinterpret_cast<uint64_t *>(b + L.off_mask);
     w.done = reinterpret_cast<uint32_t *>(b + L.off_done);
     w.seg_start = reinterpret_cast<int32_t *>(b + L.off_seg_start);
+    w.start_bits = reinterpret_cast<uint64_t *>(b + L.off_start_bits);
     w.block_cnt = reinterpret_cast<uint32_t *>(b + L.off_block_cnt);
     w.gcls = reinterpret_cast<uint32_t *>(b + L.off_gcls);
     w.gimg = reinterpret_cast<uint32_t *>(b + L.off_gimg);

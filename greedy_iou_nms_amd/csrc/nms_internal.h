@@ -73,6 +73,8 @@ constexpr int TILE_LIST_CAP = 2048;
 // into tnear so that the 64 rows of a tile read word j with one coalesced
 // load.  Words further right are applied by helper waves from the lists.
 constexpr int NEAR_TILES = 4;
+// Largest grid (in threads) a launch uses; kernels loop over what lies past it.
+constexpr int64_t MAX_GRID_THREADS = (int64_t)1 << 31;
 
 // One image with FUSE_MIN_WORDS .. FUSE_MAX_WORDS row tiles runs the mask
 // and the sweep in one launch (the sweep's workgroup overlaps the mask's).
@@ -95,7 +97,7 @@ struct Layout {
     size_t off_tcount = 0, off_tent_wk = 0, off_tent_val = 0, off_tnear = 0;
     size_t off_hist_tile = 0, off_lb_status = 0, off_tickets = 0, off_err_tile = 0;
     size_t off_gcls = 0, off_gimg = 0, off_pass_plan = 0, off_gbase = 0;
-    size_t off_done = 0, off_seg_start = 0, off_block_cnt = 0;
+    size_t off_done = 0, off_seg_start = 0, off_start_bits = 0, off_block_cnt = 0;
     size_t off_mask = 0, total = 0;
 };
 
@@ -136,8 +138,10 @@ struct Work {
     uint32_t *gbase;
     // fused mask + sweep: per row tile, mask work items finished
     uint32_t *done;
-    // grouped: first sorted position of every segment, then n
+    // grouped: first sorted position of every segment, then n; bit p of
+    // start_bits: a segment starts at sorted position p
     int32_t *seg_start;
+    uint64_t *start_bits;
     // grouped compaction: kept boxes per block of COMPACT_CHUNK score ranks
     uint32_t *block_cnt;
 };

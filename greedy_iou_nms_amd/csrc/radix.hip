@@ -31,6 +31,8 @@
 //                       writes are coalesced runs.  The last pass writes the
 //                       sorted order, the sorted boxes and areas and (grouped)
 //                       the inverse permutation.
+//   group_starts_kernel grouped input, all compute units: a bitmap of the
+//                       sorted positions where a new (image, class) group starts.
 //   group_plan_kernel   grouped input, one workgroup: segment of every sorted
 //                       position, the band of column tiles of every row tile
 //                       and the mask work items.
@@ -239,32 +241,44 @@ struct PlanArgs {
     Work w;
 };
 
+constexpr int PLAN_THREADS = 1024;
+
 // One workgroup: for each pass the global start of each digit's run, and
 // whether the pass moves anything.  A pass whose digit is the same for every
 // key is skipped; the buffer a pass reads is the one the last moving pass
 // before it wrote.  If no pass moves, the last pass still runs (as a copy)
 // to write the sorted order and boxes.
-__global__ __launch_bounds__(NT) void radix_plan_kernel(PlanArgs a) {
-    __shared__ uint32_t tot[256];
+__global__ __launch_bounds__(PLAN_THREADS) void radix_plan_kernel(PlanArgs a) {
+    __shared__ uint32_t tot[RADIX_PASSES][256];
     __shared__ uint32_t skip[RADIX_PASSES];
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const Work &w = a.w;
-    for (int pass = 0; pass < a.passes; ++pass) {
+    // digit totals over all tiles, (pass, digit) pairs spread over the
+    // threads, the tiles' counts loaded several at a time
+    for (int j = tid; j < a.passes * 256; j += PLAN_THREADS) {
         uint32_t t = 0;
-        for (int tl = 0; tl < a.tiles; ++tl)
-            t += w.hist_tile[((size_t)tl * RADIX_PASSES + pass) * 256 + tid];
-        tot[tid] = t;
-        __syncthreads();
-        if (wave == 0) {
-            scan256(tot, &w.gbase[pass * 256]);
-            const uint32_t un = (uint32_t)a.n;
-            const bool one = tot[4 * lane] == un || tot[4 * lane + 1] == un ||
-                             tot[4 * lane + 2] == un || tot[4 * lane + 3] == un;
-            const uint64_t any = __ballot(one);
-            if (lane == 0) skip[pass] = any ? 1u : 0u;
+        int tl = 0;
+        for (; tl + 4 <= a.tiles; tl += 4) {
+            const uint32_t c0 = w.hist_tile[(size_t)(tl + 0) * RADIX_PASSES * 256 + j];
+            const uint32_t c1 = w.hist_tile[(size_t)(tl + 1) * RADIX_PASSES * 256 + j];
+            const uint32_t c2 = w.hist_tile[(size_t)(tl + 2) * RADIX_PASSES * 256 + j];
+            const uint32_t c3 = w.hist_tile[(size_t)(tl + 3) * RADIX_PASSES * 256 + j];
+            t += (c0 + c1) + (c2 + c3);
         }
-        __syncthreads();
+        for (; tl < a.tiles; ++tl) t += w.hist_tile[(size_t)tl * RADIX_PASSES * 256 + j];
+        tot[j >> 8][j & 255] = t;
     }
+    __syncthreads();
+    // one wave per pass: the digit starts and whether every key shares a digit
+    for (int pass = wave; pass < a.passes; pass += PLAN_THREADS / 64) {
+        scan256(tot[pass], &w.gbase[pass * 256]);
+        const uint32_t un = (uint32_t)a.n;
+        const bool one = tot[pass][4 * lane] == un || tot[pass][4 * lane + 1] == un ||
+                         tot[pass][4 * lane + 2] == un || tot[pass][4 * lane + 3] == un;
+        const uint64_t any = __ballot(one);
+        if (lane == 0) skip[pass] = any ? 1u : 0u;
+    }
+    __syncthreads();
     if (tid == 0) {
         int last = -1, last_score = -1;
         for (int p = 0; p < a.passes; ++p)
@@ -516,8 +530,27 @@ struct GroupPlanArgs {
     Work w;
 };
 
+// Grouped input after the sort, on all compute units: bit p of start_bits
+// says a segment (a new (image, class) group) starts at sorted position p.
+__global__ __launch_bounds__(256) void group_starts_kernel(GroupPlanArgs a) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    const Work &w = a.w;
+    bool st = false;
+    if (p < a.n) {
+        if (p == 0) {
+            st = true;
+        } else {
+            const uint32_t i = (uint32_t)w.order[p], j = (uint32_t)w.order[p - 1];
+            st = w.gimg[i] != w.gimg[j] || w.gcls[i] != w.gcls[j];
+        }
+    }
+    const uint64_t m = __ballot(st);
+    if ((threadIdx.x & 63) == 0 && p < a.n) w.start_bits[p >> 6] = m;
+}
+
 struct GroupPlanSmem {
     uint64_t start[(NMS_MAX_BOXES + 63) / 64];  // bit p: a segment starts at sorted position p
+    uint32_t wpre[(NMS_MAX_BOXES + 63) / 64];   // segment starts in the words before
     uint32_t part[GP_WAVES], part2[GP_WAVES], total;
 };
 
@@ -563,21 +596,8 @@ __global__ __launch_bounds__(GP_THREADS) void group_plan_kernel(GroupPlanArgs a)
     const Work &w = a.w;
     const int n = a.n, W = a.words, S = a.strip;
     const int nw = (n + 63) / 64;
-    // segment starts, one 64-bit word per wave and step
-    for (int wi = wave; wi < nw; wi += GP_WAVES) {
-        const int p = 64 * wi + lane;
-        bool st = false;
-        if (p < n) {
-            if (p == 0) {
-                st = true;
-            } else {
-                const uint32_t i = (uint32_t)w.order[p], j = (uint32_t)w.order[p - 1];
-                st = w.gimg[i] != w.gimg[j] || w.gcls[i] != w.gcls[j];
-            }
-        }
-        const uint64_t m = __ballot(st);
-        if (lane == 0) sm.start[wi] = m;
-    }
+    // the segment starts, from group_starts_kernel
+    for (int wi = tid; wi < nw; wi += GP_THREADS) sm.start[wi] = w.start_bits[wi];
     __syncthreads();
     // segment id of every position: starts up to and including it, minus one
     const int chunk = (nw + GP_THREADS - 1) / GP_THREADS;
@@ -588,13 +608,16 @@ __global__ __launch_bounds__(GP_THREADS) void group_plan_kernel(GroupPlanArgs a)
     uint32_t segments = 0;
     uint32_t before = gp_excl_sum(cnt, sm, &segments);
     for (int wi = lo; wi < hi; ++wi) {
-        const uint64_t bits = sm.start[wi];
-        for (int k = 0; k < 64; ++k) {
-            const int p = 64 * wi + k;
-            if (p >= n) break;
-            if ((bits >> k) & 1ull) w.seg_start[before++] = p;
-            w.seg[p] = before - 1u;
-        }
+        sm.wpre[wi] = before;
+        before += (uint32_t)__popcll(sm.start[wi]);
+    }
+    __syncthreads();
+    for (int p = tid; p < n; p += GP_THREADS) {
+        const uint64_t bits = sm.start[p >> 6];
+        const int k = p & 63;
+        const uint32_t s = sm.wpre[p >> 6] + (uint32_t)__popcll(bits & (~0ull >> (63 - k))) - 1u;
+        w.seg[p] = s;
+        if ((bits >> k) & 1ull) w.seg_start[s] = p;
     }
     // band of every row tile and its work items
     const int tchunk = (W + GP_THREADS - 1) / GP_THREADS;
@@ -665,7 +688,7 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
         pa.tiles = tiles;
         pa.passes = passes;
         pa.w = w;
-        hipLaunchKernelGGL(radix_plan_kernel, dim3(1), dim3(NT), 0, stream, pa);
+        hipLaunchKernelGGL(radix_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, pa);
         e = hipGetLastError();
     }
     for (int pass = 0; pass < passes && e == hipSuccess; ++pass) {
@@ -687,8 +710,13 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
         ga.npad = (int)L.npad;
         ga.strip = P.strip;
         ga.w = w;
-        hipLaunchKernelGGL(group_plan_kernel, dim3(1), dim3(GP_THREADS), 0, stream, ga);
+        hipLaunchKernelGGL(group_starts_kernel, dim3((unsigned)((P.n + 255) / 256)), dim3(256), 0,
+                           stream, ga);
         e = hipGetLastError();
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(group_plan_kernel, dim3(1), dim3(GP_THREADS), 0, stream, ga);
+            e = hipGetLastError();
+        }
     }
     return e;
 }

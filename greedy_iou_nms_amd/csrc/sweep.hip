@@ -741,12 +741,14 @@ __global__ __launch_bounds__(GS_THREADS) void group_sweep_kernel(GroupSweepArgs 
     }
 }
 
-// Mask and sweep in one launch (one image).  Workgroup 0 runs the sweep; the
-// waves of the other workgroups take the mask work items in turn (wave slot
-// s: items s, s + slots, ...).  The launch is no larger than what the GPU
-// holds at once, so items start in order, row tile by row tile, and the
-// sweep follows the finished row tiles while later ones are still being
-// computed.  No mask wave ever waits for the sweep, so every item completes
+// Mask and sweep in one launch (one image).  Workgroup 0 runs the sweep;
+// every wave of the other workgroups computes one mask work item.  The GPU
+// starts workgroups in order as earlier ones leave, so items start row tile
+// by row tile, and a wave that finishes early is replaced by the next
+// workgroup rather than idling at the end, as a fixed share of items per
+// wave would: waves of one compute unit do not progress at the same rate.
+// The sweep follows the finished row tiles while later ones are still being
+// computed.  No mask wave ever waits for anything, so every item completes
 // whatever the order in which workgroups are scheduled.
 __global__ __launch_bounds__(NT) void mask_sweep_kernel(
     maskcore::MaskArgs ma, const Ctrl *ctrl, const float4 *__restrict__ sb,
@@ -930,8 +932,8 @@ hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, i
     if (P.grouped || L.words < FUSE_MIN_WORDS || L.words > FUSE_MAX_WORDS)
         return hipErrorInvalidValue;
     const SweepArgs sa = make_sweep_args(P, L, w, keep_out);
-    // no more workgroups than the GPU holds at once (the sweep's included),
-    // so that no item waits for a workgroup to start
+    // one work item per mask wave; the number of resident waves only sets
+    // how finely the pairs are split
     const size_t lds = (size_t)(L.words + NEAR_TILES) * sizeof(uint64_t);
     const int per_cu = fused_blocks_per_cu(lds);
     const int64_t cap = (int64_t)device_cu_count() * per_cu - 1;
@@ -939,7 +941,8 @@ hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, i
     const int64_t pairs = maskcore::mask_items_upper_bound(P, L);
     const int64_t items = pairs << ma.qshift;
     int64_t blocks = (items + NWAVES - 1) / NWAVES;
-    if (blocks > cap) blocks = cap;
+    // (the grid's thread count must fit in 32 bits; waves loop past that)
+    if (blocks > MAX_GRID_THREADS / NT) blocks = MAX_GRID_THREADS / NT;
     if (blocks < 1) blocks = 1;
     SweepArgs sa2 = sa;
     sa2.done_shift = ma.qshift;  // a finished pair counts 64 << qshift
