@@ -21,16 +21,19 @@
 // matrix-core (MFMA) use: nothing here is a dense contraction.
 //
 // Threshold test.  The mask must agree bit for bit with the float32
-// expression "inter / union > t".  When every box has a finite area > 0
-// (checked by the gather kernel), 0 <= inter <= union and union > 0, and
+// expression "inter / union > t".  When every box is ordered (x1 < x2, y1 <
+// y2) with a finite area > 0 (checked by the last sort pass, which gathers
+// the boxes), 0 <= inter <= union and union > 0, and
 // the test is exactly equivalent to comparing inter against m * union in
 // binary64, where m = t + ulp(t)/2 is the rounding boundary above t: the
 // product of a 25-bit m and a 24-bit union is exact in binary64, and the
 // float32 quotient exceeds t iff the real quotient reaches m (ties at m round
 // up when t's last significand bit is odd, to t when it is even).  That costs
 // two conversions, one multiply and one compare instead of a correctly
-// rounded division.  Otherwise (degenerate or inverted boxes, t <= 0) the
-// kernel performs the literal float32 division.
+// rounded division; the intersection then takes 4 clamps, 2 subtractions
+// and a multiply (see suppresses()), 13 vector instructions per 64 pairs in
+// all.  Otherwise (degenerate or inverted boxes, t <= 0) the kernel performs
+// the literal float32 division.
 #include <cmath>
 #include <cstring>
 

@@ -46,19 +46,31 @@ template <int MODE>
 __device__ __forceinline__ bool suppresses(float rx1, float ry1, float rx2, float ry2, float ra,
                                            float cx1, float cy1, float cx2, float cy2, float ca,
                                            float t, double mid, float pinf, float ninf) {
-    const float xx1 = max2(rx1, cx1, pinf);
-    const float yy1 = max2(ry1, cy1, pinf);
-    const float xx2 = min2(rx2, cx2, ninf);
-    const float yy2 = min2(ry2, cy2, ninf);
-    const float w = max2(xx2 - xx1, 0.0f, pinf);
-    // The division-free tests (positive areas, t > 0) need only one clamp:
-    // with w >= 0 and h unclamped, boxes that do not overlap give w * h <= 0
-    // (a zero or negative product, never above m * union > 0), so the
-    // decision is the same as with max(h, 0); boxes that overlap give the
-    // very product of the definition.  The literal test keeps both clamps.
-    const float dh = yy2 - yy1;
-    const float h = MODE == MODE_LITERAL ? max2(dh, 0.0f, pinf) : dh;
-    const float inter = w * h;
+    if (MODE == MODE_LITERAL) {
+        const float xx1 = max2(rx1, cx1, pinf);
+        const float yy1 = max2(ry1, cy1, pinf);
+        const float xx2 = min2(rx2, cx2, ninf);
+        const float yy2 = min2(ry2, cy2, ninf);
+        const float w = max2(xx2 - xx1, 0.0f, pinf);
+        const float h = max2(yy2 - yy1, 0.0f, pinf);
+        const float inter = w * h;
+        const float uni = (ra + ca) - inter;
+        return exceeds<MODE>(inter, uni, t, mid);
+    }
+    // The division-free modes run only on ordered boxes (x1 < x2, y1 < y2).
+    // Then each column coordinate is clamped into the row box's extent,
+    // med3(c, r1, r2) = min(max(c, r1), r2), and the clamped pair is ordered,
+    // so w and h come out >= 0 with no clamp of their own.  Where the boxes
+    // overlap in x, the clamped coordinates are max(rx1, cx1) and min(rx2,
+    // cx2) themselves (cx1 <= rx2 and cx2 >= rx1 there), so w is the
+    // definition's width bit for bit; where they do not, both clamp to the
+    // same end of the row box and w = 0, as max(0, xx2 - xx1) gives.  The same
+    // holds for h, so the intersection is the definition's in every case.
+    const float xx1 = __builtin_amdgcn_fmed3f(cx1, rx1, rx2);
+    const float xx2 = __builtin_amdgcn_fmed3f(cx2, rx1, rx2);
+    const float yy1 = __builtin_amdgcn_fmed3f(cy1, ry1, ry2);
+    const float yy2 = __builtin_amdgcn_fmed3f(cy2, ry1, ry2);
+    const float inter = (xx2 - xx1) * (yy2 - yy1);
     const float uni = (ra + ca) - inter;
     return exceeds<MODE>(inter, uni, t, mid);
 }
@@ -277,7 +289,7 @@ __device__ __forceinline__ void mask_items(const MaskArgs &a, const MaskPtrs &m_
                                            const Ctrl *__restrict__ ctrl, int first, int slots,
                                            uint32_t *done) {
     const int num_items = ctrl->num_items << a.qshift;
-    const bool fast = (ctrl->flags & FLAG_POSITIVE_AREAS) && a.exact_ok;
+    const bool fast = (ctrl->flags & FLAG_ORDERED_BOXES) && a.exact_ok;
     const int stride = GROUPED ? ctrl->band_stride : a.mstride;
     for (int item = first; item < num_items; item += slots) {
         if (fast) {

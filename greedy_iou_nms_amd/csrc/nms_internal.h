@@ -14,7 +14,8 @@ constexpr uint32_t ERR_BAD_OFFSETS = 2u;
 constexpr uint32_t ERR_INTERNAL = 4u;  // a bounded wait inside a kernel gave up
 
 // Ctrl::flags bits.
-constexpr uint32_t FLAG_POSITIVE_AREAS = 1u;  // every box has a finite area > 0
+// every box has x1 < x2, y1 < y2 and a finite area > 0
+constexpr uint32_t FLAG_ORDERED_BOXES = 1u;
 
 // Per-call control block at the start of the workspace.  The sort kernel
 // initialises it; later kernels read plan fields and raise error bits.  The

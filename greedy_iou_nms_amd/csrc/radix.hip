@@ -191,7 +191,7 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
         for (int p = 0; p < RADIX_PASSES; ++p) w.tickets[p] = 0u;
         Ctrl *c = w.ctrl;
         c->error = 0u;
-        c->flags = FLAG_POSITIVE_AREAS;
+        c->flags = FLAG_ORDERED_BOXES;
         c->count = 0;
         c->num_items = a.grouped ? 0 : item_base_full(a.words, a.words, a.strip);
         c->band_stride = a.mstride;
@@ -324,7 +324,7 @@ struct PassSmem {
     uint32_t stage_v[TILE];
     uint32_t tile;
     uint32_t err;
-    uint32_t bad_area;
+    uint32_t unordered;
 };
 
 // Passes 0-3 sort on the score key (read from the key buffer), 4-7 on the
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
         // only ever waits on tiles that are already running
         sm.tile = atomicAdd(&w.tickets[a.pass], 1u);
         sm.err = 0u;
-        sm.bad_area = 0u;
+        sm.unordered = 0u;
     }
     if (a.planned) {
         sm.gbase[tid] = w.gbase[a.pass * 256 + tid];
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
     }
     __syncthreads();
     const int count = a.n - tile * TILE < TILE ? a.n - tile * TILE : TILE;
-    bool finite = true, positive = true;
+    bool finite = true, ordered = true;
     for (int s = tid; s < count; s += NT) {
         const uint32_t key = sm.stage_k[s];
         const int pos = s + sm.gsh[(key >> shift) & 255u];
@@ -505,18 +505,18 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
         const float4 b = a.boxes[val];
         finite = finite && isfinite(b.x) && isfinite(b.y) && isfinite(b.z) && isfinite(b.w);
         const float ar = (b.z - b.x) * (b.w - b.y);
-        positive = positive && ar > 0.0f && ar < INFINITY;
+        ordered = ordered && b.x < b.z && b.y < b.w && ar > 0.0f && ar < INFINITY;
         w.sb[pos] = b;
         w.area[pos] = ar;
     }
     if (pl.last) {
         if (!finite) atomicOr(&sm.err, ERR_NONFINITE);
-        if (!positive) atomicOr(&sm.bad_area, 1u);
+        if (!ordered) atomicOr(&sm.unordered, 1u);
     }
     __syncthreads();
     if (tid == 0) {
         if (sm.err) atomicOr(&w.ctrl->error, sm.err);
-        if (sm.bad_area) atomicAnd(&w.ctrl->flags, ~FLAG_POSITIVE_AREAS);
+        if (sm.unordered) atomicAnd(&w.ctrl->flags, ~FLAG_ORDERED_BOXES);
     }
 }
 

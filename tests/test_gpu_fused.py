@@ -46,6 +46,21 @@ def test_fused_ragged_sizes(n):
     np.testing.assert_array_equal(sep, want)
 
 
+def test_fused_size_with_inverted_boxes():
+    # a few boxes with x2 < x1 and y2 < y1 (positive area) send the whole
+    # call to the literal division test, at a size the fused launch takes
+    n = 40000 + 37
+    w = workloads.random_small(n, n, canvas=60.0 + n / 8.0)
+    b = w.boxes.copy()
+    b[::997] = b[::997][:, [2, 3, 0, 1]]
+    w.boxes = b
+    note("fused inverted n=%d" % n)
+    fused, sep, _, _, _ = _both(w)
+    want = oracle.c_nms(w.boxes, w.scores, w.iou_threshold)
+    np.testing.assert_array_equal(fused, want)
+    np.testing.assert_array_equal(sep, want)
+
+
 def test_fused_gives_up_on_list_overflow():
     # copies of one box: every row of a tile suppresses all later boxes,
     # 64 rows x hundreds of nonzero words is more than a tile's list holds,

@@ -106,6 +106,16 @@ def test_degenerate_boxes_take_the_division_path():
     _check(w)
 
 
+def test_boxes_inverted_in_both_axes_take_the_division_path():
+    # x2 < x1 and y2 < y1 give (x2 - x1) * (y2 - y1) > 0, a positive area,
+    # but the division-free test clamps coordinates into an ordered extent
+    w = workloads.random_small(6, 500, canvas=80.0, score_levels=4)
+    b = w.boxes.copy()
+    b[::5] = b[::5][:, [2, 3, 0, 1]]
+    w.boxes = b
+    _check(w)
+
+
 def test_equal_scores_everywhere_keep_input_order():
     n = 2000
     rng = np.random.default_rng(9)
