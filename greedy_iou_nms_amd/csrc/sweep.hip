@@ -23,6 +23,11 @@
 //     written by the mask kernel; when the kept set is published it ORs the
 //     kept rows' words for column tiles c + NEAR + 1 and later into the
 //     bitmap.  A tile whose list overflowed has its kept rows read densely.
+//     For one image the applier also writes the chunk's kept boxes to the
+//     output: the resolver hands over, with the kept set, the number of
+//     boxes kept before the chunk, and each kept lane stores order[64c +
+//     lane] at that offset plus its rank in the chunk.  The output is thus
+//     complete when the last chunk is applied.
 // The resolver waits for chunk c - NEAR - 1 to be applied before it reads
 // word c, so an applier has NEAR chunk settlements of slack.
 // The page's sweep takes one barrier per box; here no barrier is taken: the
@@ -34,12 +39,12 @@
 // is the complement of the final bitmap.
 //
 // Compaction (the page's host-side map-back, bug 3, done on the device).  For
-// one image the sorted order is the score order: kept bits are counted per
-// word, prefix-summed across the workgroup and written as int64 input
-// indices order[p].  For grouped input the kept bits are in group order; the
-// compaction kernel walks the plain score order and looks each box's sorted
-// position up through the inverse permutation, so the output is one list in
-// global score order.
+// one image the sorted order is the score order and the appliers write the
+// kept boxes' input indices order[p] as int64 while the sweep runs (above).
+// For grouped input the kept bits are in group order; the compaction kernel
+// walks the plain score order and looks each box's sorted position up
+// through the inverse permutation, so the output is one list in global score
+// order.
 #include "mask_core.h"
 #include "nms_internal.h"
 
@@ -102,27 +107,10 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
     return v;
 }
 
-// exclusive block prefix sum; *total receives the block sum
-__device__ uint32_t block_excl_sum(uint32_t v, uint32_t *part, uint32_t *part2, uint32_t *tot,
-                                   uint32_t *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t incl = wave_incl_sum(v);
-    if (lane == 63) part[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-        const uint32_t s = lane < NWAVES ? part[lane] : 0u;
-        const uint32_t si = wave_incl_sum(s);
-        if (lane < NWAVES) part2[lane] = si - s;
-        if (lane == NWAVES - 1) *tot = si;
-    }
-    __syncthreads();
-    const uint32_t r = part2[wave] + incl - v;
-    *total = *tot;
-    __syncthreads();
-    return r;
-}
-
 constexpr int APPLIERS = NWAVES - 1;
+constexpr int KOFF_RING = 8;
+static_assert(KOFF_RING >= NEAR_TILES + 2 && (KOFF_RING & (KOFF_RING - 1)) == 0,
+              "the offset ring must outlast the resolver's lead over the appliers");
 // Bounded waits: about a second of polling before a wait gives up.
 constexpr uint32_t SPIN_LIMIT = 1u << 23;
 
@@ -143,13 +131,18 @@ struct SweepSmem {
     uint32_t data_ready[APPLIERS][2]; // chunk + 1 once diag/super are staged
     uint32_t k_ready[APPLIERS];       // chunk + 1 once removed[chunk] is final
     uint32_t applied[APPLIERS];       // chunk + 1 once its far words are ORed in
+    // boxes kept before chunk c, at k_off[c % KOFF_RING] (one image): when the
+    // resolver publishes chunk c, every chunk up to c - NEAR - 1 has been
+    // applied, so the ring slot's previous chunk has been read
+    uint32_t k_off[KOFF_RING];
+    uint32_t kept_total;
     uint32_t abort;
     uint32_t done_upto;  // fused kernel: row tiles below this are known finished
-    uint32_t part[NWAVES], part2[NWAVES], tot;
     // where the resolver's lanes other than lane 0 direct their publishing
     // writes (every lane stores, so the store needs no branch)
     uint64_t sink_rem[64];
     uint32_t sink_flag[64];
+    uint32_t sink_off[64];
 };
 
 // Hand-over flags.  Everything handed over between waves lives in LDS, and
@@ -292,6 +285,7 @@ __device__ __forceinline__ void stage_level1(const Level1 &l, int c, int slot, i
 struct Entries {
     uint32_t wk[RMAX];
     uint64_t val[RMAX];
+    int32_t ord;  // order[64c + lane]: input index of the lane's box
 };
 
 __device__ __forceinline__ int rounds_of(uint32_t count) {
@@ -302,6 +296,8 @@ __device__ __forceinline__ int rounds_of(uint32_t count) {
 template <bool FUSED>
 __device__ __forceinline__ void load_entries(const SweepArgs &a, int c, int rounds, Entries &e) {
     const size_t base = (size_t)c * TILE_LIST_CAP + (threadIdx.x & 63);
+    // written by the sort, before this launch: a plain load
+    e.ord = a.order[64 * c + (threadIdx.x & 63)];
 #pragma unroll
     for (int i = 0; i < RMAX; ++i) {
         if (i < rounds) {
@@ -402,6 +398,7 @@ struct ResolverState {
     uint64_t carry1;     // kept rows' words for tile c (chunks c - 1 and c - 2)
     uint64_t carry2;     // kept rows' words for tile c + 1 (chunk c - 1)
     bool stale_next;     // chunk c + 1's batch must be read again (see resolve_one)
+    uint32_t total;      // boxes kept before chunk c
 };
 
 // Settle chunk c from its batch cur, after issuing the reads of chunk c + 2
@@ -477,9 +474,12 @@ __device__ __forceinline__ bool resolve_one(const SweepArgs &a, uint64_t *remove
     st.carry2 = c2;
     // lane 0 publishes; the other lanes store to their own sink words
     uint64_t *rem_at = lane == 0 ? &removed[c] : &sm.sink_rem[lane];
+    uint32_t *off_at = lane == 0 ? &sm.k_off[c & (KOFF_RING - 1)] : &sm.sink_off[lane];
     uint32_t *flag_at = lane == 0 ? &sm.k_ready[slot] : &sm.sink_flag[lane];
     *rem_at = rem;
+    *off_at = st.total;
     flag_store(flag_at, (uint32_t)c + 1u);
+    st.total += (uint32_t)__popcll(kept);
     return true;
 }
 
@@ -498,6 +498,7 @@ __device__ void resolve_chunks(const SweepArgs &a, uint64_t *removed, SweepSmem 
     st.carry1 = 0ull;
     st.carry2 = 0ull;
     st.stale_next = false;
+    st.total = 0u;
     ResolverBatch b0, b1, b2;
     resolver_read(0, st.at, removed, sm, b0);
     resolver_read(1, st.ahead, removed, sm, b1);
@@ -510,6 +511,7 @@ __device__ void resolve_chunks(const SweepArgs &a, uint64_t *removed, SweepSmem 
         if (c + 1 < W && !resolve_one<FUSED>(a, removed, sm, c + 1, st, b1, b0)) return;
         if (c + 2 < W && !resolve_one<FUSED>(a, removed, sm, c + 2, st, b2, b1)) return;
     }
+    sm.kept_total = st.total;  // every lane stores the same value
 }
 
 // Kept rows of an overflowed tile: OR their dense words for tiles
@@ -581,8 +583,14 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
         }
         if (!wait_flag<FUSED, APPLIER_SLEEP>(&sm.k_ready[slot], (uint32_t)c + 1u, sm, a.ctrl))
             return;
-        // the resolver wrote the chunk's final removed word before the flag
+        // the resolver wrote the chunk's final removed word and the count
+        // of boxes kept before it ahead of the flag
         const uint64_t kept = ~uniform64(removed[c]) & rows_valid(c, a.n);
+        if (!a.grouped && ((kept >> lane) & 1ull)) {
+            const uint64_t below = (1ull << lane) - 1ull;
+            const uint32_t at = sm.k_off[c & (KOFF_RING - 1)] + (uint32_t)__popcll(kept & below);
+            a.keep_out[at] = (int64_t)e.ord;
+        }
         if (kept) {
             if (count > (uint32_t)TILE_LIST_CAP) {
                 // dense rows are plain stores of the mask stage, not visible
@@ -641,25 +649,9 @@ __device__ __forceinline__ void sweep_body(const SweepArgs &a, uint64_t *removed
     // kept bitmap = complement of removed, limited to existing boxes
     for (int w = tid; w < W; w += NT) a.kept[w] = ~removed[w] & rows_valid(w, n);
     if (a.grouped) return;
-
-    // one image: compact in sorted (= score) order, mapping back through order[]
-    const int chunk = (W + NT - 1) / NT;
-    const int lo = tid * chunk < W ? tid * chunk : W;
-    const int hi = lo + chunk < W ? lo + chunk : W;
-    uint32_t cnt = 0;
-    for (int w = lo; w < hi; ++w) cnt += (uint32_t)__popcll(~removed[w] & rows_valid(w, n));
-    uint32_t total = 0;
-    uint32_t pos = block_excl_sum(cnt, sm.part, sm.part2, &sm.tot, &total);
-    for (int w = lo; w < hi; ++w) {
-        uint64_t bits = ~removed[w] & rows_valid(w, n);
-        while (bits) {
-            const int k = __builtin_ctzll(bits);
-            bits &= bits - 1ull;
-            a.keep_out[pos++] = (int64_t)a.order[64 * w + k];
-        }
-    }
+    // one image: the appliers have written the output
     if (tid == 0) {
-        a.ctrl->count = (int32_t)total;
+        a.ctrl->count = (int32_t)sm.kept_total;
         if (FUSED) a.ctrl->sweep_done = 1u;
     }
 }
