@@ -117,14 +117,16 @@ __device__ __forceinline__ int32_t item_base_full(int r, int W, int S) {
 // many lanes on one LDS word serialise.
 constexpr int HIST_COPIES = 4;
 
+// One image needs the score digits only (a third of the LDS to clear).
+template <bool GROUPED>
 __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
-    __shared__ uint32_t hcopy[HIST_COPIES][RADIX_PASSES][256];
+    constexpr int DIGITS = GROUPED ? RADIX_PASSES : 4;
+    __shared__ uint32_t hcopy[HIST_COPIES][DIGITS][256];
     __shared__ uint32_t err_sh;
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int tile = blockIdx.x;
     const Work &w = a.w;
-    const int digits = a.grouped ? RADIX_PASSES : 4;
-    for (int j = tid; j < HIST_COPIES * RADIX_PASSES * 256; j += NT) (&hcopy[0][0][0])[j] = 0u;
+    for (int j = tid; j < HIST_COPIES * DIGITS * 256; j += NT) (&hcopy[0][0][0])[j] = 0u;
     if (tid == 0) err_sh = 0u;
     __syncthreads();
     uint32_t (*hist)[256] = hcopy[lane % HIST_COPIES];
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
             atomicAdd(&hist[1][(k >> 8) & 255u], 1u);
             atomicAdd(&hist[2][(k >> 16) & 255u], 1u);
             atomicAdd(&hist[3][k >> 24], 1u);
-            if (a.grouped) {
+            if constexpr (GROUPED) {
                 // the plain score order, should every score pass be skipped
                 w.score_order[i] = i;
                 const uint32_t c = a.class_ids ? class_key(a.class_ids[i]) : 0u;
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
     }
     const int gid = tile * NT + tid, gsz = a.tiles * NT;
     // batch offsets must rise from 0 to n
-    if (a.grouped && a.offsets) {
+    if (GROUPED && a.offsets) {
         for (int m = gid; m <= a.num_images; m += gsz) {
             const int64_t o = a.offsets[m];
             bool bad = (m == 0 && o != 0) || (m == a.num_images && o != (int64_t)a.n);
@@ -175,14 +177,14 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
     }
     if (err) atomicOr(&err_sh, err);
     __syncthreads();
-    for (int j = tid; j < digits * 256; j += NT) {
+    for (int j = tid; j < DIGITS * 256; j += NT) {
         uint32_t sum = 0;
 #pragma unroll
         for (int q = 0; q < HIST_COPIES; ++q) sum += (&hcopy[q][0][0])[j];
         w.hist_tile[(size_t)tile * RADIX_PASSES * 256 + j] = sum;
     }
     // every pass's look-back words of this tile start empty
-    for (int j = tid; j < digits * 256; j += NT) {
+    for (int j = tid; j < DIGITS * 256; j += NT) {
         const int pass = j >> 8, d = j & 255;
         w.lb_status[((size_t)pass * a.tiles + tile) * 256 + d] = 0u;
     }
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
         c->error = 0u;
         c->flags = FLAG_ORDERED_BOXES;
         c->count = 0;
-        c->num_items = a.grouped ? 0 : item_base_full(a.words, a.words, a.strip);
+        c->num_items = GROUPED ? 0 : item_base_full(a.words, a.words, a.strip);
         c->band_stride = a.mstride;
         c->num_segments = 1;
         c->sweep_done = 0u;
@@ -203,12 +205,12 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
     // arrays, and (one image) the plan of the mask kernel (every row tile
     // covers all column tiles).
     for (int r = gid; r <= a.words; r += gsz) {
-        if (!a.grouped) w.item_base[r] = item_base_full(r, a.words, a.strip);
+        if (!GROUPED) w.item_base[r] = item_base_full(r, a.words, a.strip);
         if (r < a.words) {
-            if (!a.grouped) w.tile_cend[r] = a.words;
+            if (!GROUPED) w.tile_cend[r] = a.words;
             w.tcount[r] = 0u;
             w.done[r] = 0u;
-            if (a.grouped) w.kept[r] = 0ull;  // the grouped sweep ORs segments in
+            if (GROUPED) w.kept[r] = 0ull;  // the grouped sweep ORs segments in
         }
     }
     for (int p = gid; p < a.npad; p += gsz) {
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
             w.order[p] = 0;
             w.sb[p] = make_float4(0.f, 0.f, 0.f, 0.f);
             w.area[p] = 0.0f;
-            if (a.grouped) w.seg[p] = 0xFFFFFFFFu;
+            if (GROUPED) w.seg[p] = 0xFFFFFFFFu;
         }
     }
 }
@@ -360,10 +362,19 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
     if (a.planned) {
         sm.gbase[tid] = w.gbase[a.pass * 256 + tid];
     } else {
-        // global start of each digit: all tiles' counts of this pass's digit
+        // global start of each digit: all tiles' counts of this pass's digit,
+        // eight tiles' loads in flight at a time
+        const uint32_t *h = w.hist_tile + (size_t)a.pass * 256 + tid;
+        constexpr size_t TS = (size_t)RADIX_PASSES * 256;  // one tile's counts
         uint32_t tot = 0;
-        for (int t = 0; t < a.tiles; ++t)
-            tot += w.hist_tile[((size_t)t * RADIX_PASSES + a.pass) * 256 + tid];
+        int t = 0;
+        for (; t + 8 <= a.tiles; t += 8) {
+            uint32_t c[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = h[(size_t)(t + j) * TS];
+            tot += ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
+        }
+        for (; t < a.tiles; ++t) tot += h[(size_t)t * TS];
         sm.tcnt[tid] = tot;  // scratch until the scan below
         __syncthreads();
         if (wave == 0) scan256(sm.tcnt, sm.gbase);
@@ -487,27 +498,54 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
     __syncthreads();
     const int count = a.n - tile * TILE < TILE ? a.n - tile * TILE : TILE;
     bool finite = true, ordered = true;
-    for (int s = tid; s < count; s += NT) {
-        const uint32_t key = sm.stage_k[s];
-        const int pos = s + sm.gsh[(key >> shift) & 255u];
-        const uint32_t val = sm.stage_v[s];
-        if (a.grouped && pl.last_score) w.score_order[pos] = (int32_t)val;
-        if (!pl.last) {
+    if (!pl.last) {
+        for (int s = tid; s < count; s += NT) {
+            const uint32_t key = sm.stage_k[s];
+            const int pos = s + sm.gsh[(key >> shift) & 255u];
+            const uint32_t val = sm.stage_v[s];
+            if (a.grouped && pl.last_score) w.score_order[pos] = (int32_t)val;
             if (kind == 0) dst_k[pos] = key;
             dst_v[pos] = val;
-            continue;
         }
-        // the sorted order, and (when boxes are given: the sort-only test
-        // export passes none) the sorted boxes with their areas
-        w.order[pos] = (int32_t)val;
-        if (a.grouped) w.inv[val] = pos;
-        if (a.boxes == nullptr) continue;
-        const float4 b = a.boxes[val];
-        finite = finite && isfinite(b.x) && isfinite(b.y) && isfinite(b.z) && isfinite(b.w);
-        const float ar = (b.z - b.x) * (b.w - b.y);
-        ordered = ordered && b.x < b.z && b.y < b.w && ar > 0.0f && ar < INFINITY;
-        w.sb[pos] = b;
-        w.area[pos] = ar;
+    } else {
+        // The sorted order, and (when boxes are given: the sort-only test
+        // export passes none) the sorted boxes with their areas.  The box
+        // loads of GB elements are issued before any of their stores, which
+        // the compiler may not move across one another.
+        constexpr int GB = 8;
+        for (int s0 = tid; s0 < count; s0 += NT * GB) {
+            int pos[GB];
+            uint32_t val[GB];
+            float4 b[GB];
+#pragma unroll
+            for (int j = 0; j < GB; ++j) {
+                const int s = s0 + j * NT;
+                pos[j] = -1;
+                val[j] = 0u;
+                if (s < count) {
+                    const uint32_t key = sm.stage_k[s];
+                    pos[j] = s + sm.gsh[(key >> shift) & 255u];
+                    val[j] = sm.stage_v[s];
+                }
+                b[j] = a.boxes != nullptr && pos[j] >= 0 ? a.boxes[val[j]]
+                                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int j = 0; j < GB; ++j) {
+                if (pos[j] < 0) continue;
+                if (a.grouped && pl.last_score) w.score_order[pos[j]] = (int32_t)val[j];
+                w.order[pos[j]] = (int32_t)val[j];
+                if (a.grouped) w.inv[val[j]] = pos[j];
+                if (a.boxes == nullptr) continue;
+                const float4 bj = b[j];
+                finite = finite && isfinite(bj.x) && isfinite(bj.y) && isfinite(bj.z) &&
+                         isfinite(bj.w);
+                const float ar = (bj.z - bj.x) * (bj.w - bj.y);
+                ordered = ordered && bj.x < bj.z && bj.y < bj.w && ar > 0.0f && ar < INFINITY;
+                w.sb[pos[j]] = bj;
+                w.area[pos[j]] = ar;
+            }
+        }
     }
     if (pl.last) {
         if (!finite) atomicOr(&sm.err, ERR_NONFINITE);
@@ -679,7 +717,10 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
     ka.tiles = tiles;
     ka.grouped = P.grouped ? 1 : 0;
     ka.w = w;
-    hipLaunchKernelGGL(radix_keys_kernel, dim3(tiles), dim3(NT), 0, stream, ka);
+    if (P.grouped)
+        hipLaunchKernelGGL(radix_keys_kernel<true>, dim3(tiles), dim3(NT), 0, stream, ka);
+    else
+        hipLaunchKernelGGL(radix_keys_kernel<false>, dim3(tiles), dim3(NT), 0, stream, ka);
     hipError_t e = hipGetLastError();
     const int passes = P.grouped ? RADIX_PASSES : 4;
     if (e == hipSuccess && P.grouped) {
