@@ -50,7 +50,8 @@ using namespace maskcore;
 // ---------------------------------------------------------------- mask
 
 template <int S, bool GROUPED>
-__global__ __launch_bounds__(MASK_THREADS) void mask_kernel(
+// (4 waves per SIMD: at most 128 registers)
+__global__ __launch_bounds__(MASK_THREADS, 4) void mask_kernel(
     MaskArgs a, const Ctrl *__restrict__ ctrl, const float4 *__restrict__ sb,
     const float *__restrict__ area, const uint32_t *__restrict__ seg,
     const int32_t *__restrict__ tile_cend, const int32_t *__restrict__ item_base,

@@ -742,7 +742,8 @@ __global__ __launch_bounds__(GS_THREADS) void group_sweep_kernel(GroupSweepArgs 
 // The sweep follows the finished row tiles while later ones are still being
 // computed.  No mask wave ever waits for anything, so every item completes
 // whatever the order in which workgroups are scheduled.
-__global__ __launch_bounds__(NT) void mask_sweep_kernel(
+// (two workgroups per compute unit, 4 waves per SIMD: at most 128 registers)
+__global__ __launch_bounds__(NT, 4) void mask_sweep_kernel(
     maskcore::MaskArgs ma, const Ctrl *ctrl, const float4 *__restrict__ sb,
     const float *__restrict__ area, const int32_t *__restrict__ tile_cend,
     const int32_t *__restrict__ item_base, uint64_t *__restrict__ mask,
