@@ -44,6 +44,8 @@ constexpr int STRIP_GROUPED = 4;
 constexpr int RADIX_THREADS = 256;
 constexpr int RADIX_E = 16;
 constexpr int RADIX_TILE = RADIX_THREADS * RADIX_E;
+// One image of at most this many boxes is sorted by one workgroup.
+constexpr int SMALL_SORT_MAX = 8192;
 // 8-bit digit passes: 4 on the score key, then (grouped input) 4 on the
 // class key and 4 on the image.
 constexpr int RADIX_PASSES = 12;

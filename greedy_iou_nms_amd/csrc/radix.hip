@@ -12,6 +12,8 @@
 // order inside; the order after the score passes is kept as the plain score
 // order for the final compaction.
 //
+//   small_sort_kernel   one image of at most 8192 boxes: everything below in
+//                       one workgroup, the keys kept in LDS between passes.
 //   radix_keys_kernel   one workgroup per tile of 4096 boxes: the keys (score;
 //                       grouped: class key and image of every box), each
 //                       tile's histograms of every digit (digit counts do not
@@ -112,6 +114,34 @@ __device__ __forceinline__ int32_t item_base_full(int r, int W, int S) {
     return (int32_t)(S * (g * G - g * (g - 1) / 2) + u * (G - g));
 }
 
+// Per-call initialisation, spread over the threads gid = 0 .. gsz - 1: the
+// side arrays the mask kernel only partly writes, the padding rows of the
+// sorted arrays, and (one image) the plan of the mask kernel (every row tile
+// covers all column tiles).
+template <bool GROUPED>
+__device__ __forceinline__ void per_call_init(const KeysArgs &a, int gid, int gsz) {
+    const Work &w = a.w;
+    for (int r = gid; r <= a.words; r += gsz) {
+        if (!GROUPED) w.item_base[r] = item_base_full(r, a.words, a.strip);
+        if (r < a.words) {
+            if (!GROUPED) w.tile_cend[r] = a.words;
+            w.tcount[r] = 0u;
+            w.done[r] = 0u;
+            if (GROUPED) w.kept[r] = 0ull;  // the grouped sweep ORs segments in
+        }
+    }
+    for (int p = gid; p < a.npad; p += gsz) {
+#pragma unroll
+        for (int j = 0; j <= NEAR_TILES; ++j) w.tnear[(size_t)j * a.npad + p] = 0ull;
+        if (p >= a.n) {
+            w.order[p] = 0;
+            w.sb[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+            w.area[p] = 0.0f;
+            if (GROUPED) w.seg[p] = 0xFFFFFFFFu;
+        }
+    }
+}
+
 // Lanes add into HIST_COPIES interleaved copies of the histograms: keys of
 // real scores share their top digits (the float exponent), and atomics of
 // many lanes on one LDS word serialise.
@@ -200,29 +230,7 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
         c->num_segments = 1;
         c->sweep_done = 0u;
     }
-    // Per-call initialisation, spread over the whole grid: the side arrays
-    // the mask kernel only partly writes, the padding rows of the sorted
-    // arrays, and (one image) the plan of the mask kernel (every row tile
-    // covers all column tiles).
-    for (int r = gid; r <= a.words; r += gsz) {
-        if (!GROUPED) w.item_base[r] = item_base_full(r, a.words, a.strip);
-        if (r < a.words) {
-            if (!GROUPED) w.tile_cend[r] = a.words;
-            w.tcount[r] = 0u;
-            w.done[r] = 0u;
-            if (GROUPED) w.kept[r] = 0ull;  // the grouped sweep ORs segments in
-        }
-    }
-    for (int p = gid; p < a.npad; p += gsz) {
-#pragma unroll
-        for (int j = 0; j <= NEAR_TILES; ++j) w.tnear[(size_t)j * a.npad + p] = 0ull;
-        if (p >= a.n) {
-            w.order[p] = 0;
-            w.sb[p] = make_float4(0.f, 0.f, 0.f, 0.f);
-            w.area[p] = 0.0f;
-            if (GROUPED) w.seg[p] = 0xFFFFFFFFu;
-        }
-    }
+    per_call_init<GROUPED>(a, gid, gsz);
 }
 
 // Exclusive scan of v[0..256) into out[] by one wave (4 per lane).
@@ -236,6 +244,144 @@ __device__ __forceinline__ void scan256(const uint32_t *v, uint32_t *out) {
     out[4 * lane + 1] = ex + h0;
     out[4 * lane + 2] = ex + h0 + h1;
     out[4 * lane + 3] = ex + h0 + h1 + h2;
+}
+
+// ---------------------------------------------------------------- small sort
+
+// One image of at most SMALL_SORT_MAX boxes: keys, the four score passes,
+// the sorted-box gather and the per-call initialisation in one workgroup,
+// with the keys held in LDS between passes.  This replaces five launches
+// (and their look-back round trips) with one.  The passes rank exactly as
+// radix_pass_kernel does (waves, then elements, then lanes walk the
+// positions in order), so the order is the same stable one.
+constexpr int SMALL_THREADS = 1024;
+constexpr int SMALL_WAVES = SMALL_THREADS / 64;
+constexpr int SMALL_E = SMALL_SORT_MAX / SMALL_THREADS;
+static_assert(SMALL_E * SMALL_THREADS == SMALL_SORT_MAX, "small sort tiling");
+
+struct SmallSortSmem {
+    uint32_t wcnt[SMALL_WAVES][256];  // per wave: digit counts, then their prefix
+    uint32_t tot[256];
+    uint32_t tbase[256];
+    uint32_t key[SMALL_SORT_MAX];
+    uint32_t val[SMALL_SORT_MAX];
+    uint32_t err;
+    uint32_t unordered;
+};
+
+__global__ __launch_bounds__(SMALL_THREADS) void small_sort_kernel(KeysArgs a,
+                                                                   const float4 *boxes) {
+    __shared__ SmallSortSmem sm;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const Work &w = a.w;
+    if (tid == 0) {
+        sm.err = 0u;
+        sm.unordered = 0u;
+    }
+    const int base = wave * 64 * SMALL_E + lane;  // position of element 0 of this lane
+    uint32_t k[SMALL_E], v[SMALL_E], rk[SMALL_E];
+    uint32_t err = 0;
+#pragma unroll
+    for (int e = 0; e < SMALL_E; ++e) {
+        const int i = base + e * 64;
+        const float sc = i < a.n ? a.scores[i] : 0.0f;
+        if (sc != sc) err |= ERR_NONFINITE;
+        k[e] = score_key(sc);
+        v[e] = (uint32_t)i;
+    }
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 8 * pass;
+        for (int j = lane; j < 256; j += 64) sm.wcnt[wave][j] = 0u;
+#pragma unroll
+        for (int e = 0; e < SMALL_E; ++e) {
+            const bool valid = base + e * 64 < a.n;
+            const uint32_t d = (k[e] >> shift) & 255u;
+            uint64_t peers = __ballot(valid);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const bool bit = (d >> b) & 1u;
+                const uint64_t m = __ballot(bit);
+                peers &= bit ? m : ~m;
+            }
+            const uint32_t r_in = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(peers >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
+            const uint32_t before = sm.wcnt[wave][d];
+            rk[e] = before + r_in;
+            // the lowest lane of each digit group advances the wave's count;
+            // the read above precedes this write in the wave's LDS order
+            if (valid && r_in == 0) sm.wcnt[wave][d] = before + (uint32_t)__popcll(peers);
+        }
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t run = 0;
+#pragma unroll
+            for (int wv = 0; wv < SMALL_WAVES; ++wv) {
+                const uint32_t c = sm.wcnt[wv][tid];
+                sm.wcnt[wv][tid] = run;
+                run += c;
+            }
+            sm.tot[tid] = run;
+        }
+        __syncthreads();
+        if (wave == 0) scan256(sm.tot, sm.tbase);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < SMALL_E; ++e) {
+            if (base + e * 64 < a.n) {
+                const uint32_t d = (k[e] >> shift) & 255u;
+                const uint32_t slot = sm.tbase[d] + sm.wcnt[wave][d] + rk[e];
+                sm.key[slot] = k[e];
+                sm.val[slot] = v[e];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < SMALL_E; ++e) {
+            const int j = base + e * 64;
+            if (j < a.n) {
+                k[e] = sm.key[j];
+                v[e] = sm.val[j];
+            }
+        }
+        __syncthreads();
+    }
+    // sorted position base + 64 e holds input index v[e]: the order and
+    // (when boxes are given: the sort-only test export passes none) the
+    // sorted boxes and their areas, all box loads issued before any store
+    float4 b[SMALL_E];
+#pragma unroll
+    for (int e = 0; e < SMALL_E; ++e)
+        b[e] = boxes != nullptr && base + e * 64 < a.n ? boxes[v[e]]
+                                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    bool finite = true, ordered = true;
+#pragma unroll
+    for (int e = 0; e < SMALL_E; ++e) {
+        const int j = base + e * 64;
+        if (j >= a.n) continue;
+        w.order[j] = (int32_t)v[e];
+        if (boxes == nullptr) continue;
+        const float4 bj = b[e];
+        finite = finite && isfinite(bj.x) && isfinite(bj.y) && isfinite(bj.z) && isfinite(bj.w);
+        const float ar = (bj.z - bj.x) * (bj.w - bj.y);
+        ordered = ordered && bj.x < bj.z && bj.y < bj.w && ar > 0.0f && ar < INFINITY;
+        w.sb[j] = bj;
+        w.area[j] = ar;
+    }
+    if (!finite) err |= ERR_NONFINITE;
+    if (err) atomicOr(&sm.err, err);
+    if (!ordered) atomicOr(&sm.unordered, 1u);
+    per_call_init<false>(a, tid, SMALL_THREADS);
+    __syncthreads();
+    if (tid == 0) {
+        Ctrl *c = w.ctrl;
+        c->error = sm.err;
+        c->flags = sm.unordered ? 0u : FLAG_ORDERED_BOXES;
+        c->count = 0;
+        c->num_items = item_base_full(a.words, a.words, a.strip);
+        c->band_stride = a.mstride;
+        c->num_segments = 1;
+        c->sweep_done = 0u;
+    }
 }
 
 struct PlanArgs {
@@ -717,6 +863,11 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
     ka.tiles = tiles;
     ka.grouped = P.grouped ? 1 : 0;
     ka.w = w;
+    if (!P.grouped && P.n <= SMALL_SORT_MAX) {
+        hipLaunchKernelGGL(small_sort_kernel, dim3(1), dim3(SMALL_THREADS), 0, stream, ka,
+                           reinterpret_cast<const float4 *>(P.boxes));
+        return hipGetLastError();
+    }
     if (P.grouped)
         hipLaunchKernelGGL(radix_keys_kernel<true>, dim3(tiles), dim3(NT), 0, stream, ka);
     else

@@ -106,6 +106,14 @@ def test_degenerate_boxes_take_the_division_path():
     _check(w)
 
 
+@pytest.mark.parametrize("n", [8192, 8193])
+def test_sort_boundary_sizes_with_ties(n):
+    # the largest one-workgroup sort and the smallest multi-workgroup one,
+    # with few score levels so that the stable order decides
+    w = workloads.random_small(800 + n, n, canvas=4.0 * np.sqrt(n) + 30, score_levels=8)
+    _check(w)
+
+
 def test_boxes_inverted_in_both_axes_take_the_division_path():
     # x2 < x1 and y2 < y1 give (x2 - x1) * (y2 - y1) > 0, a positive area,
     # but the division-free test clamps coordinates into an ordered extent

@@ -20,7 +20,8 @@ def _g():
 
 # ---------------------------------------------------------------- sort
 
-@pytest.mark.parametrize("n", [1, 2, 100, 1024, 1025, 5000, 65536])
+# 8192 is the largest one-workgroup sort, 8193 the smallest multi-workgroup one
+@pytest.mark.parametrize("n", [1, 2, 100, 1024, 1025, 5000, 8191, 8192, 8193, 65536])
 def test_sort_order_is_stable_descending(n):
     dev = device()
     rng = np.random.default_rng(n)
