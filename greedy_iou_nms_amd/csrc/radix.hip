@@ -254,10 +254,11 @@ __device__ __forceinline__ void scan256(const uint32_t *v, uint32_t *out) {
 // (and their look-back round trips) with one.  The passes rank exactly as
 // radix_pass_kernel does (waves, then elements, then lanes walk the
 // positions in order), so the order is the same stable one.
+// SE elements per thread: the smallest power of two with 1024 SE >= n, so
+// that small inputs do not rank empty slots.
 constexpr int SMALL_THREADS = 1024;
 constexpr int SMALL_WAVES = SMALL_THREADS / 64;
-constexpr int SMALL_E = SMALL_SORT_MAX / SMALL_THREADS;
-static_assert(SMALL_E * SMALL_THREADS == SMALL_SORT_MAX, "small sort tiling");
+static_assert(SMALL_SORT_MAX == 8 * SMALL_THREADS, "small sort tiling");
 
 struct SmallSortSmem {
     uint32_t wcnt[SMALL_WAVES][256];  // per wave: digit counts, then their prefix
@@ -269,6 +270,7 @@ struct SmallSortSmem {
     uint32_t unordered;
 };
 
+template <int SE>
 __global__ __launch_bounds__(SMALL_THREADS) void small_sort_kernel(KeysArgs a,
                                                                    const float4 *boxes) {
     __shared__ SmallSortSmem sm;
@@ -278,11 +280,11 @@ __global__ __launch_bounds__(SMALL_THREADS) void small_sort_kernel(KeysArgs a,
         sm.err = 0u;
         sm.unordered = 0u;
     }
-    const int base = wave * 64 * SMALL_E + lane;  // position of element 0 of this lane
-    uint32_t k[SMALL_E], v[SMALL_E], rk[SMALL_E];
+    const int base = wave * 64 * SE + lane;  // position of element 0 of this lane
+    uint32_t k[SE], v[SE], rk[SE];
     uint32_t err = 0;
 #pragma unroll
-    for (int e = 0; e < SMALL_E; ++e) {
+    for (int e = 0; e < SE; ++e) {
         const int i = base + e * 64;
         const float sc = i < a.n ? a.scores[i] : 0.0f;
         if (sc != sc) err |= ERR_NONFINITE;
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(SMALL_THREADS) void small_sort_kernel(KeysArgs a,
         const int shift = 8 * pass;
         for (int j = lane; j < 256; j += 64) sm.wcnt[wave][j] = 0u;
 #pragma unroll
-        for (int e = 0; e < SMALL_E; ++e) {
+        for (int e = 0; e < SE; ++e) {
             const bool valid = base + e * 64 < a.n;
             const uint32_t d = (k[e] >> shift) & 255u;
             uint64_t peers = __ballot(valid);
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(SMALL_THREADS) void small_sort_kernel(KeysArgs a,
         if (wave == 0) scan256(sm.tot, sm.tbase);
         __syncthreads();
 #pragma unroll
-        for (int e = 0; e < SMALL_E; ++e) {
+        for (int e = 0; e < SE; ++e) {
             if (base + e * 64 < a.n) {
                 const uint32_t d = (k[e] >> shift) & 255u;
                 const uint32_t slot = sm.tbase[d] + sm.wcnt[wave][d] + rk[e];
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(SMALL_THREADS) void small_sort_kernel(KeysArgs a,
         }
         __syncthreads();
 #pragma unroll
-        for (int e = 0; e < SMALL_E; ++e) {
+        for (int e = 0; e < SE; ++e) {
             const int j = base + e * 64;
             if (j < a.n) {
                 k[e] = sm.key[j];
@@ -348,14 +350,14 @@ __global__ __launch_bounds__(SMALL_THREADS) void small_sort_kernel(KeysArgs a,
     // sorted position base + 64 e holds input index v[e]: the order and
     // (when boxes are given: the sort-only test export passes none) the
     // sorted boxes and their areas, all box loads issued before any store
-    float4 b[SMALL_E];
+    float4 b[SE];
 #pragma unroll
-    for (int e = 0; e < SMALL_E; ++e)
+    for (int e = 0; e < SE; ++e)
         b[e] = boxes != nullptr && base + e * 64 < a.n ? boxes[v[e]]
                                                        : make_float4(0.f, 0.f, 0.f, 0.f);
     bool finite = true, ordered = true;
 #pragma unroll
-    for (int e = 0; e < SMALL_E; ++e) {
+    for (int e = 0; e < SE; ++e) {
         const int j = base + e * 64;
         if (j >= a.n) continue;
         w.order[j] = (int32_t)v[e];
@@ -864,8 +866,16 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
     ka.grouped = P.grouped ? 1 : 0;
     ka.w = w;
     if (!P.grouped && P.n <= SMALL_SORT_MAX) {
-        hipLaunchKernelGGL(small_sort_kernel, dim3(1), dim3(SMALL_THREADS), 0, stream, ka,
-                           reinterpret_cast<const float4 *>(P.boxes));
+        const float4 *bx = reinterpret_cast<const float4 *>(P.boxes);
+        const dim3 g(1), b(SMALL_THREADS);
+        if (P.n <= SMALL_THREADS)
+            hipLaunchKernelGGL(small_sort_kernel<1>, g, b, 0, stream, ka, bx);
+        else if (P.n <= 2 * SMALL_THREADS)
+            hipLaunchKernelGGL(small_sort_kernel<2>, g, b, 0, stream, ka, bx);
+        else if (P.n <= 4 * SMALL_THREADS)
+            hipLaunchKernelGGL(small_sort_kernel<4>, g, b, 0, stream, ka, bx);
+        else
+            hipLaunchKernelGGL(small_sort_kernel<8>, g, b, 0, stream, ka, bx);
         return hipGetLastError();
     }
     if (P.grouped)

@@ -20,8 +20,10 @@ def _g():
 
 # ---------------------------------------------------------------- sort
 
-# 8192 is the largest one-workgroup sort, 8193 the smallest multi-workgroup one
-@pytest.mark.parametrize("n", [1, 2, 100, 1024, 1025, 5000, 8191, 8192, 8193, 65536])
+# one-workgroup sort up to 8192 (1, 2, 4 or 8 keys per thread), multi-workgroup
+# from 8193
+@pytest.mark.parametrize("n", [1, 2, 100, 1024, 1025, 2048, 2049, 4096, 4097, 8191, 8192, 8193,
+                               65536])
 def test_sort_order_is_stable_descending(n):
     dev = device()
     rng = np.random.default_rng(n)
