@@ -173,3 +173,106 @@ void oracle_pair_iou(const float *boxes, const int64_t *a, const int64_t *b, int
         iou_out[k] = box_iou(bi, box_area(bi), bj, box_area(bj));
     }
 }
+
+/*
+ * oracle_matrix_nms: Matrix NMS with the Gaussian decay, by definition
+ * ("Fastest Matrix NMS in the West (Part 2)", "What do we need to compute?"
+ * and optimisation 4).
+ *
+ *   1. Validate: finite coordinates, no NaN score, x1 <= x2 and y1 <= y2 for
+ *      every box (so an IoU is 0..1 or 0/0), sigma finite and > 0, the
+ *      threshold not NaN.
+ *   2. Stable descending score sort, as for greedy NMS (the page's extension
+ *      sorts with stable=true).
+ *   3. O[p][q] for sorted positions p < q: the float32 IoU expression above of
+ *      father p and child q; 0/0 (two empty boxes) counts as overlap 0.
+ *   4. omax[q] = the largest O[p][q] over the fathers p < q (0 for q = 0).
+ *   5. Box q is dropped iff its score is below the threshold or some father p
+ *      gives a candidate decayed score below it:
+ *          x    = ((double)omax[p]^2 - (double)O[p][q]^2) / sigma
+ *          cand = exp(x) * (double)score
+ *          cand < (double)score_thresh
+ *      (the page: s'_j = s_j min_i d_ij with d_ij = exp((O_max,i^2 -
+ *      O_ij^2)/sigma), and "s'_j < t iff some s_j d_ij < t" for non-negative
+ *      scores; for a box with no fathers, or any box whose score is below t,
+ *      the decay of the first box -- which never exceeds 1 -- makes the score
+ *      alone decide).  The decay is evaluated in binary64, after the float32
+ *      IoUs.
+ *   6. The kept boxes as original input indices, in sorted order.
+ *
+ * borderline_out (may be NULL): boxes decided by a candidate within a
+ * relative 1e-9 of the threshold, where two exp() implementations could
+ * disagree.  Status values as oracle_nms, plus 5 = a box with x1 > x2 or
+ * y1 > y2.
+ */
+#define ORACLE_BAD_BOXES 5
+
+static float overlap_or_zero(const float *bi, float ai, const float *bj, float aj) {
+    float o = box_iou(bi, ai, bj, aj);
+    return o == o ? o : 0.0f;
+}
+
+int oracle_matrix_nms(const float *boxes, const float *scores, int64_t n, float score_thresh,
+                      double sigma, int64_t *keep_out, int64_t *num_kept,
+                      int64_t *borderline_out) {
+    if (num_kept == NULL || n < 0 || isnan(score_thresh) || !isfinite(sigma) || !(sigma > 0.0))
+        return ORACLE_INVALID_ARG;
+    if (n > 0 && (boxes == NULL || scores == NULL || keep_out == NULL)) return ORACLE_INVALID_ARG;
+    *num_kept = 0;
+    if (borderline_out) *borderline_out = 0;
+    for (int64_t k = 0; k < n; ++k) {
+        if (isnan(scores[k])) return ORACLE_NONFINITE;
+        for (int c = 0; c < 4; ++c)
+            if (!isfinite(boxes[4 * k + c])) return ORACLE_NONFINITE;
+    }
+    for (int64_t k = 0; k < n; ++k)
+        if (boxes[4 * k] > boxes[4 * k + 2] || boxes[4 * k + 1] > boxes[4 * k + 3])
+            return ORACLE_BAD_BOXES;
+    if (n == 0) return ORACLE_OK;
+
+    int64_t *order = (int64_t *)malloc((size_t)n * sizeof(int64_t));
+    int64_t *tmp = (int64_t *)malloc((size_t)n * sizeof(int64_t));
+    float *area = (float *)malloc((size_t)n * sizeof(float));
+    float *omax = (float *)calloc((size_t)n, sizeof(float));
+    if (!order || !tmp || !area || !omax) {
+        free(order); free(tmp); free(area); free(omax);
+        return ORACLE_INVALID_ARG;
+    }
+    for (int64_t k = 0; k < n; ++k) {
+        order[k] = k;
+        area[k] = box_area(boxes + 4 * k);
+    }
+    stable_sort_desc(order, tmp, n, scores);
+
+    for (int64_t q = 1; q < n; ++q) {
+        const int64_t j = order[q];
+        float m = 0.0f;
+        for (int64_t p = 0; p < q; ++p) {
+            const int64_t i = order[p];
+            float o = overlap_or_zero(boxes + 4 * i, area[i], boxes + 4 * j, area[j]);
+            if (o > m) m = o;
+        }
+        omax[q] = m;
+    }
+
+    const double t = (double)score_thresh;
+    int64_t kept = 0, borderline = 0;
+    for (int64_t q = 0; q < n; ++q) {
+        const int64_t j = order[q];
+        const double s = (double)scores[j];
+        int drop = s < t;
+        for (int64_t p = 0; p < q && !drop; ++p) {
+            const int64_t i = order[p];
+            float o = overlap_or_zero(boxes + 4 * i, area[i], boxes + 4 * j, area[j]);
+            double x = ((double)omax[p] * (double)omax[p] - (double)o * (double)o) / sigma;
+            double cand = exp(x) * s;
+            if (fabs(cand - t) <= 1e-9 * fabs(t)) ++borderline;
+            if (cand < t) drop = 1;
+        }
+        if (!drop) keep_out[kept++] = j;
+    }
+    *num_kept = kept;
+    if (borderline_out) *borderline_out = borderline;
+    free(order); free(tmp); free(area); free(omax);
+    return ORACLE_OK;
+}

@@ -38,7 +38,8 @@ _SRC = os.path.join(_HERE, "nms_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 # The oracle's own status numbering (nms_oracle.c).
-ORACLE_STATUS = {0: "OK", 1: "INVALID_ARG", 3: "NONFINITE_INPUT", 4: "BAD_OFFSETS"}
+ORACLE_STATUS = {0: "OK", 1: "INVALID_ARG", 3: "NONFINITE_INPUT", 4: "BAD_OFFSETS",
+                 5: "BAD_BOXES"}
 
 C_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-mfpmath=sse",
            "-msse2", "-fPIC", "-shared"]
@@ -75,6 +76,11 @@ def _load(path: str = _LIB):
         f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+        m = lib.oracle_matrix_nms
+        m.restype = ctypes.c_int
+        m.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                      ctypes.c_double, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+                      ctypes.POINTER(ctypes.c_int64)]
         g = lib.oracle_pair_iou
         g.restype = None
         g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -106,6 +112,28 @@ def c_nms(boxes, scores, iou_threshold, class_ids=None, batch_offsets=None,
     st = lib.oracle_nms(_ptr(boxes), _ptr(scores), n, ctypes.c_float(iou_threshold),
                         _ptr(cls), _ptr(offs), num_images, _ptr(keep), ctypes.byref(cnt),
                         ctypes.byref(border))
+    if st != 0:
+        raise OracleError(ORACLE_STATUS.get(st, "UNKNOWN_%d" % st))
+    out = keep[:cnt.value].copy()
+    return (out, border.value) if return_borderline else out
+
+
+def c_matrix_nms(boxes, scores, score_threshold, sigma=0.5, lib_path: str = _LIB,
+                 return_borderline: bool = False):
+    """Matrix NMS (Gaussian decay) through the C oracle: kept int64 input
+    indices in descending score order (and, when asked, the number of boxes
+    decided within a relative 1e-9 of the threshold)."""
+    boxes = np.ascontiguousarray(boxes, dtype=np.float32).reshape(-1, 4)
+    scores = np.ascontiguousarray(scores, dtype=np.float32).reshape(-1)
+    n = boxes.shape[0]
+    if scores.shape[0] != n:
+        raise OracleError("INVALID_ARG")
+    keep = np.zeros(max(n, 1), dtype=np.int64)
+    cnt = ctypes.c_int64(-1)
+    border = ctypes.c_int64(0)
+    st = _load(lib_path).oracle_matrix_nms(_ptr(boxes), _ptr(scores), n,
+                                           ctypes.c_float(score_threshold), float(sigma),
+                                           _ptr(keep), ctypes.byref(cnt), ctypes.byref(border))
     if st != 0:
         raise OracleError(ORACLE_STATUS.get(st, "UNKNOWN_%d" % st))
     out = keep[:cnt.value].copy()
@@ -323,3 +351,43 @@ def mask_rows(boxes, iou_threshold, order, group=None):
             bits[p + 1:n] = hit
         out[p] = np.packbits(bits, bitorder="little").view("<u8")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Matrix NMS, the page's naive formulation
+# ---------------------------------------------------------------------------
+
+def np_matrix_nms(boxes, scores, score_threshold, sigma=0.5):
+    """Matrix NMS with the Gaussian decay, following the naive steps listed on
+    "Fastest Matrix NMS in the West (Part 2)" ("What do we need to compute?"):
+    build the triangular IoU matrix (father p < child q, zero elsewhere),
+    reduce it to the per-box maximum overlap with its own fathers, broadcast,
+    build the whole decay matrix exp((omax_p^2 - O_pq^2) / sigma), reduce it
+    to one decay per box (minimum over every p), multiply the scores and keep
+    those >= the threshold.  float32 IoUs (0/0 counted as 0), binary64 decay.
+    For non-negative scores this equals the C oracle's per-pair test; it is an
+    independent second implementation for small inputs."""
+    boxes = np.asarray(boxes, dtype=np.float32).reshape(-1, 4)
+    scores = np.asarray(scores, dtype=np.float32).reshape(-1)
+    n = boxes.shape[0]
+    if scores.shape[0] != n or np.isnan(np.float32(score_threshold)) or not sigma > 0:
+        raise OracleError("INVALID_ARG")
+    if np.any(np.isnan(scores)) or not np.all(np.isfinite(boxes)):
+        raise OracleError("NONFINITE_INPUT")
+    if np.any(boxes[:, 0] > boxes[:, 2]) or np.any(boxes[:, 1] > boxes[:, 3]):
+        raise OracleError("BAD_BOXES")
+    if n == 0:
+        return np.zeros(0, dtype=np.int64)
+    order = stable_order(scores)
+    sb = boxes[order]
+    s = scores[order].astype(np.float64)
+    area = areas_f32(sb)
+    O = np.zeros((n, n), dtype=np.float32)
+    for p in range(n - 1):
+        o = iou_row_f32(sb[p], area[p], sb[p + 1:], area[p + 1:])
+        O[p, p + 1:] = np.where(np.isnan(o), np.float32(0.0), o)
+    omax = O.max(axis=0).astype(np.float64)
+    Od = O.astype(np.float64)
+    decay = np.exp((omax[:, None] * omax[:, None] - Od * Od) / float(sigma))
+    s_new = s * decay.min(axis=0)
+    return order[s_new >= float(np.float32(score_threshold))]
