@@ -19,15 +19,18 @@ import torch
 __all__ = [
     "NMSError", "STAGES", "nms", "nms_profiled", "workspace_size", "Workspace",
     "debug_order", "debug_mask", "debug_decide", "library_path",
+    "MATRIX_STAGES", "matrix_nms", "matrix_nms_profiled", "matrix_workspace_size",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgreedy_nms.so")
 
 STAGES = ("sort", "gather", "mask", "sweep", "compact")
+MATRIX_STAGES = ("sort", "overlap_max", "decay")
 _STATUS = {
     0: "NMS_OK", 1: "NMS_INVALID_ARG", 2: "NMS_WORKSPACE_TOO_SMALL",
     3: "NMS_NONFINITE_INPUT", 4: "NMS_BAD_OFFSETS", 5: "NMS_TOO_LARGE", 6: "NMS_HIP_ERROR",
+    7: "NMS_BAD_BOXES",
 }
 
 
@@ -68,6 +71,13 @@ def _load():
     lib.nms_debug_mask.restype = ctypes.c_int
     lib.nms_debug_decide.argtypes = [c_vp, c_vp, c_i64, c_f, ctypes.c_int, c_vp, c_vp]
     lib.nms_debug_decide.restype = ctypes.c_int
+    lib.nms_matrix_workspace_size.argtypes = [c_i64, ctypes.POINTER(c_sz)]
+    lib.nms_matrix_workspace_size.restype = ctypes.c_int
+    matrix = [c_vp, c_vp, c_i64, c_f, ctypes.c_double, c_vp, p_i64, c_vp, c_sz, c_vp]
+    lib.nms_matrix_f32.argtypes = matrix
+    lib.nms_matrix_f32.restype = ctypes.c_int
+    lib.nms_matrix_f32_profiled.argtypes = matrix + [ctypes.POINTER(ctypes.c_float)]
+    lib.nms_matrix_f32_profiled.restype = ctypes.c_int
     return lib
 
 
@@ -259,3 +269,51 @@ def debug_decide(inter: torch.Tensor, uni: torch.Tensor, iou_threshold: float,
                                      int(bool(positive_areas)), _ptr(out),
                                      ctypes.c_void_p(stream)))
     return out
+
+
+# ---------------------------------------------------------------- Matrix NMS
+
+def matrix_workspace_size(n: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.nms_matrix_workspace_size(int(n), ctypes.byref(out)))
+    return int(out.value)
+
+
+def _run_matrix(boxes, scores, score_threshold, sigma, workspace, out, profiled):
+    boxes, scores, _, _, _ = _check_inputs(boxes, scores, None, None)
+    device = boxes.device
+    n = boxes.shape[0]
+    with torch.cuda.device(device):
+        stream = torch.cuda.current_stream(device).cuda_stream
+        nbytes = matrix_workspace_size(n)
+        ws = workspace if workspace is not None else _default_workspace(device, stream)
+        buf = ws.get(nbytes, device)
+        if out is None or out.numel() < max(n, 1) or out.device != device:
+            out = torch.empty(max(n, 1), dtype=torch.int64, device=device)
+        count = ctypes.c_int64(0)
+        args = [_ptr(boxes), _ptr(scores), n, ctypes.c_float(float(score_threshold)),
+                ctypes.c_double(float(sigma)), _ptr(out), ctypes.byref(count), _ptr(buf),
+                buf.numel(), ctypes.c_void_p(stream)]
+        stage = None
+        if profiled:
+            stage = (ctypes.c_float * len(MATRIX_STAGES))()
+            _check(_lib.nms_matrix_f32_profiled(*args, stage))
+        else:
+            _check(_lib.nms_matrix_f32(*args))
+    keep = out[:count.value]
+    if profiled:
+        return keep, {name: float(stage[i]) for i, name in enumerate(MATRIX_STAGES)}
+    return keep
+
+
+def matrix_nms(boxes: torch.Tensor, scores: torch.Tensor, score_threshold: float,
+               sigma: float = 0.5, workspace: Optional[Workspace] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Matrix NMS with the Gaussian decay (see include/greedy_nms.h): the kept
+    input indices (int64, on the boxes' device) in descending score order."""
+    return _run_matrix(boxes, scores, score_threshold, sigma, workspace, out, False)
+
+
+def matrix_nms_profiled(boxes, scores, score_threshold, sigma=0.5, workspace=None, out=None):
+    """``matrix_nms`` plus per-stage GPU times in milliseconds."""
+    return _run_matrix(boxes, scores, score_threshold, sigma, workspace, out, True)

@@ -58,6 +58,11 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_seg_start = take(np * 4 + 4);
     L.off_start_bits = take((size_t)L.words * 8);
     L.off_block_cnt = take(((size_t)n / COMPACT_CHUNK + 1) * 4);
+    L.off_momax = take(np * 4);
+    L.off_mscore = take(np * 4);
+    L.off_mlo = take(np * 8);
+    L.off_mhi = take(np * 8);
+    L.off_mdrop = take((size_t)L.words * 8 + 8);
     L.off_mask = take((size_t)n * (size_t)L.mstride * 8);
     L.total = off;
     *out = L;
@@ -98,6 +103,11 @@ Work carve(void *workspace, const Layout &L) {
     w.gimg = reinterpret_cast<uint32_t *>(b + L.off_gimg);
     w.pass_plan = reinterpret_cast<RadixPassPlan *>(b + L.off_pass_plan);
     w.gbase = reinterpret_cast<uint32_t *>(b + L.off_gbase);
+    w.momax = reinterpret_cast<uint32_t *>(b + L.off_momax);
+    w.mscore = reinterpret_cast<float *>(b + L.off_mscore);
+    w.mlo = reinterpret_cast<double *>(b + L.off_mlo);
+    w.mhi = reinterpret_cast<double *>(b + L.off_mhi);
+    w.mdrop = reinterpret_cast<uint64_t *>(b + L.off_mdrop);
     return w;
 }
 
@@ -169,6 +179,7 @@ nms_status read_back(const Work &w, hipStream_t stream, Readback *out) {
 
 nms_status device_error(uint32_t err) {
     if (err & ERR_INTERNAL) return NMS_HIP_ERROR;
+    if (err & ERR_BAD_BOXES) return NMS_BAD_BOXES;
     if (err & ERR_BAD_OFFSETS) return NMS_BAD_OFFSETS;
     if (err & ERR_NONFINITE) return NMS_NONFINITE_INPUT;
     return NMS_OK;
@@ -257,6 +268,64 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     return NMS_OK;
 }
 
+// Matrix NMS: the same sort, then prep, overlap maximum, decay test, kept
+// bitmap and the score-order compaction.  Stage times (when asked): sort,
+// overlap maximum, decay test + compaction.
+nms_status run_matrix(const float *boxes, const float *scores, int64_t n, float score_thresh,
+                      double sigma, int64_t *keep_out, int64_t *num_kept, void *workspace,
+                      size_t ws_bytes, void *stream_ptr, float *stage_ms) {
+    if (num_kept == nullptr) return NMS_INVALID_ARG;
+    *num_kept = 0;
+    if (stage_ms)
+        for (int i = 0; i < NMS_MATRIX_NUM_STAGES; ++i) stage_ms[i] = 0.0f;
+    if (n < 0 || std::isnan(score_thresh) || !std::isfinite(sigma) || !(sigma > 0.0))
+        return NMS_INVALID_ARG;
+    if (n > NMS_MAX_BOXES) return NMS_TOO_LARGE;
+    if (n == 0) return NMS_OK;
+    if (!boxes || !scores || !keep_out || !workspace) return NMS_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(boxes) & 15u) != 0 ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return NMS_INVALID_ARG;
+    Layout L;
+    make_layout(n, &L);
+    if (ws_bytes < L.off_mask) return NMS_WORKSPACE_TOO_SMALL;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    const Problem P = make_problem(boxes, scores, n, score_thresh, nullptr, nullptr, 0);
+    const Work w = carve(workspace, L);
+
+    EventSet events;
+    if (stage_ms && !events.create()) return NMS_HIP_ERROR;
+    auto mark = [&](int i) -> hipError_t {
+        return stage_ms ? hipEventRecord(events.ev[i], stream) : hipSuccess;
+    };
+    hipError_t e = mark(0);
+    if (e == hipSuccess) e = launch_radix_sort(P, L, w, stream);
+    if (e == hipSuccess) e = launch_matrix_prep(P, L, w, sigma, stream);
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess) e = launch_matrix_overlap_max(P, L, w, stream);
+    if (e == hipSuccess) e = mark(2);
+    if (e == hipSuccess) e = launch_matrix_decay(P, L, w, sigma, stream);
+    if (e == hipSuccess) e = launch_compact(P, L, w, keep_out, stream);
+    if (e == hipSuccess) e = mark(3);
+    if (e != hipSuccess) return NMS_HIP_ERROR;
+
+    Readback rb;
+    nms_status st = read_back(w, stream, &rb);
+    if (st != NMS_OK) return st;
+    st = device_error(rb.error);
+    if (st != NMS_OK) return st;
+    if (stage_ms) {
+        for (int i = 0; i < NMS_MATRIX_NUM_STAGES; ++i) {
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, events.ev[i], events.ev[i + 1]) != hipSuccess)
+                return NMS_HIP_ERROR;
+            stage_ms[i] = ms;
+        }
+    }
+    *num_kept = rb.count;
+    return NMS_OK;
+}
+
 }  // namespace
 }  // namespace gnms
 
@@ -295,6 +364,31 @@ nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
                    (flags & NMS_PROFILE_NO_FUSION) == 0);
 }
 
+nms_status nms_matrix_workspace_size(int64_t n, size_t *bytes) {
+    if (bytes == nullptr || n < 0) return NMS_INVALID_ARG;
+    if (n > NMS_MAX_BOXES) return NMS_TOO_LARGE;
+    Layout L;
+    make_layout(n, &L);
+    *bytes = L.off_mask;
+    return NMS_OK;
+}
+
+nms_status nms_matrix_f32(const float *boxes, const float *scores, int64_t n, float score_thresh,
+                          double sigma, int64_t *keep_out, int64_t *num_kept, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    return run_matrix(boxes, scores, n, score_thresh, sigma, keep_out, num_kept, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+nms_status nms_matrix_f32_profiled(const float *boxes, const float *scores, int64_t n,
+                                   float score_thresh, double sigma, int64_t *keep_out,
+                                   int64_t *num_kept, void *workspace, size_t workspace_bytes,
+                                   void *stream, float *stage_ms) {
+    if (stage_ms == nullptr) return NMS_INVALID_ARG;
+    return run_matrix(boxes, scores, n, score_thresh, sigma, keep_out, num_kept, workspace,
+                      workspace_bytes, stream, stage_ms);
+}
+
 const char *nms_status_string(nms_status status) {
     switch (status) {
         case NMS_OK: return "NMS_OK";
@@ -304,6 +398,7 @@ const char *nms_status_string(nms_status status) {
         case NMS_BAD_OFFSETS: return "NMS_BAD_OFFSETS";
         case NMS_TOO_LARGE: return "NMS_TOO_LARGE";
         case NMS_HIP_ERROR: return "NMS_HIP_ERROR";
+        case NMS_BAD_BOXES: return "NMS_BAD_BOXES";
     }
     return "NMS_UNKNOWN_STATUS";
 }

@@ -12,6 +12,7 @@ namespace gnms {
 constexpr uint32_t ERR_NONFINITE = 1u;
 constexpr uint32_t ERR_BAD_OFFSETS = 2u;
 constexpr uint32_t ERR_INTERNAL = 4u;  // a bounded wait inside a kernel gave up
+constexpr uint32_t ERR_BAD_BOXES = 8u;  // Matrix NMS: a box with x1 > x2 or y1 > y2
 
 // Ctrl::flags bits.
 // every box has x1 < x2, y1 < y2 and a finite area > 0
@@ -101,6 +102,8 @@ struct Layout {
     size_t off_hist_tile = 0, off_lb_status = 0, off_tickets = 0, off_err_tile = 0;
     size_t off_gcls = 0, off_gimg = 0, off_pass_plan = 0, off_gbase = 0;
     size_t off_done = 0, off_seg_start = 0, off_start_bits = 0, off_block_cnt = 0;
+    size_t off_momax = 0, off_mscore = 0, off_mlo = 0, off_mhi = 0, off_mdrop = 0;
+    // the suppression bitmask comes last: Matrix NMS uses everything before it
     size_t off_mask = 0, total = 0;
 };
 
@@ -147,6 +150,13 @@ struct Work {
     uint64_t *start_bits;
     // grouped compaction: kept boxes per block of COMPACT_CHUNK score ranks
     uint32_t *block_cnt;
+    // Matrix NMS, per sorted position: the largest overlap with a father
+    // (float bits), the score, the bounds of the decay test's fast path; and
+    // per row tile the drop bits
+    uint32_t *momax;
+    float *mscore;
+    double *mlo, *mhi;
+    uint64_t *mdrop;
 };
 
 Work carve(void *workspace, const Layout &L);
@@ -168,6 +178,15 @@ struct Problem {
 // plans the segments and the mask work.
 hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
                              hipStream_t stream);
+// Matrix NMS after the sort (matrix.hip): scores, bounds and checks; the
+// largest overlap of every box with its fathers; the decay test; the kept
+// bitmap (then launch_compact writes the output).
+hipError_t launch_matrix_prep(const Problem &P, const Layout &L, const Work &w, double sigma,
+                              hipStream_t stream);
+hipError_t launch_matrix_overlap_max(const Problem &P, const Layout &L, const Work &w,
+                                     hipStream_t stream);
+hipError_t launch_matrix_decay(const Problem &P, const Layout &L, const Work &w, double sigma,
+                               hipStream_t stream);
 hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
 hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
                         hipStream_t stream);

@@ -64,7 +64,9 @@ typedef enum nms_status {
     /* n above NMS_MAX_BOXES. */
     NMS_TOO_LARGE = 5,
     /* A HIP runtime call or kernel launch failed. */
-    NMS_HIP_ERROR = 6
+    NMS_HIP_ERROR = 6,
+    /* Matrix NMS: a box with x1 > x2 or y1 > y2 (detected on the device). */
+    NMS_BAD_BOXES = 7
 } nms_status;
 
 /* Largest n accepted: one workgroup keeps the removed bitmap (n/8 bytes) in
@@ -190,6 +192,60 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
 nms_status nms_debug_decide(const float *inter, const float *uni, int64_t count,
                             float iou_thresh, int all_positive_areas, uint8_t *out,
                             void *stream);
+
+/* ------------------------------------------------------------------------
+ * Matrix NMS (Gaussian decay), "Fastest Matrix NMS in the West (Part 2)":
+ * "What do we need to compute?" and optimisation 4.
+ *
+ * With the boxes in descending score order (stable, as for nms_f32), the
+ * overlap of a father p (earlier) and a child q (later) is the float32 IoU
+ * expression above (0/0, two empty boxes, counted as 0); omax[q] is the
+ * largest overlap of q with any of its fathers (0 for the first box).  Box q
+ * is dropped iff its score is below score_thresh, or some father p gives
+ *     exp((omax[p]^2 - O[p][q]^2) / sigma) * score_q  <  score_thresh
+ * evaluated in binary64 from the float32 overlaps (the page's
+ * s'_j = s_j min_i d_ij < t, with d_ij = exp((O_max,i^2 - O_ij^2) / sigma);
+ * the page hard-codes sigma = 0.5).  Every other box is kept; the result is
+ * the kept input indices, int64, in descending score order.  Boxes must have
+ * x1 <= x2 and y1 <= y2.
+ * ------------------------------------------------------------------------ */
+
+/* Stages timed by nms_matrix_f32_profiled. */
+#define NMS_MATRIX_STAGE_SORT 0     /* stable sort, gather, scores and checks */
+#define NMS_MATRIX_STAGE_OVERLAP 1  /* largest overlap of each box with a father */
+#define NMS_MATRIX_STAGE_DECAY 2    /* decay test, kept bitmap, compaction */
+#define NMS_MATRIX_NUM_STAGES 3
+
+/*
+ * nms_matrix_workspace_size -- device workspace needed by nms_matrix_f32 for
+ * n boxes (linear in n: no pairwise matrix is stored).  Returns NMS_OK,
+ * NMS_INVALID_ARG (bytes NULL, n < 0) or NMS_TOO_LARGE.
+ */
+nms_status nms_matrix_workspace_size(int64_t n, size_t *bytes);
+
+/*
+ * nms_matrix_f32 -- Matrix NMS as described above.
+ *   boxes, scores, n, keep_out, num_kept, workspace, stream  as for nms_f32
+ *                  (workspace of at least nms_matrix_workspace_size() bytes).
+ *   score_thresh   float32 threshold t on the decayed score; any value but
+ *                  NaN.
+ *   sigma          Gaussian decay width; finite and > 0 (0.5 on the page).
+ * Returns NMS_OK, NMS_INVALID_ARG, NMS_WORKSPACE_TOO_SMALL, NMS_TOO_LARGE,
+ * NMS_NONFINITE_INPUT, NMS_BAD_BOXES or NMS_HIP_ERROR.
+ */
+nms_status nms_matrix_f32(const float *boxes, const float *scores, int64_t n, float score_thresh,
+                          double sigma, int64_t *keep_out, int64_t *num_kept, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * nms_matrix_f32_profiled -- nms_matrix_f32 with HIP events on the launch
+ * stream around each stage; stage_ms (host, NMS_MATRIX_NUM_STAGES floats)
+ * receives the stage times in milliseconds.
+ */
+nms_status nms_matrix_f32_profiled(const float *boxes, const float *scores, int64_t n,
+                                   float score_thresh, double sigma, int64_t *keep_out,
+                                   int64_t *num_kept, void *workspace, size_t workspace_bytes,
+                                   void *stream, float *stage_ms);
 
 #ifdef __cplusplus
 }

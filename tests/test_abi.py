@@ -36,7 +36,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for want in ("nms_f32", "nms_workspace_size", "nms_status_string", "nms_f32_profiled",
-                 "nms_debug_order", "nms_debug_mask", "nms_debug_decide"):
+                 "nms_debug_order", "nms_debug_mask", "nms_debug_decide",
+                 "nms_matrix_workspace_size", "nms_matrix_f32", "nms_matrix_f32_profiled"):
         assert want in names
 
 
@@ -48,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 STATUS = {0: "NMS_OK", 1: "NMS_INVALID_ARG", 2: "NMS_WORKSPACE_TOO_SMALL",
           3: "NMS_NONFINITE_INPUT", 4: "NMS_BAD_OFFSETS", 5: "NMS_TOO_LARGE",
-          6: "NMS_HIP_ERROR"}
+          6: "NMS_HIP_ERROR", 7: "NMS_BAD_BOXES"}
 
 
 def test_status_strings():
@@ -73,8 +74,9 @@ def test_workspace_size_bound():
         assert st == 0
         words = (n + 63) // 64
         mask = n * (((words + 15) // 16) * 16) * 8
-        # dense mask + O(n) scratch (sort buffers, sorted boxes, row lists)
-        assert mask <= b <= mask + 512 * n + 128 * 1024
+        # dense mask + O(n) scratch (sort buffers, sorted boxes, row lists,
+        # the per-box arrays of Matrix NMS)
+        assert mask <= b <= mask + 576 * n + 128 * 1024
         assert b >= prev
         prev = b
     st, b = _ws(lib, 65536)
@@ -115,3 +117,57 @@ def test_host_argument_checks():
     assert _call(lib, 512001)[0] == "NMS_TOO_LARGE"
     # a failing call reports zero kept boxes
     assert _call(lib, 5, ws_bytes=100)[1] == 0
+
+
+# ---------------------------------------------------------------- Matrix NMS
+
+def _mlib():
+    lib = _lib()
+    c_i64, c_f, c_vp, c_sz = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    lib.nms_matrix_workspace_size.argtypes = [c_i64, ctypes.POINTER(c_sz)]
+    lib.nms_matrix_workspace_size.restype = ctypes.c_int
+    lib.nms_matrix_f32.argtypes = [c_vp, c_vp, c_i64, c_f, ctypes.c_double, c_vp,
+                                   ctypes.POINTER(ctypes.c_int64), c_vp, c_sz, c_vp]
+    lib.nms_matrix_f32.restype = ctypes.c_int
+    return lib
+
+
+def _mws(lib, n):
+    out = ctypes.c_size_t(0)
+    st = lib.nms_matrix_workspace_size(n, ctypes.byref(out))
+    return st, out.value
+
+
+def test_matrix_workspace_is_linear_and_below_greedy():
+    lib = _mlib()
+    for n in (1, 1000, 65536, 512000):
+        st, b = _mws(lib, n)
+        assert st == 0 and b < _ws(lib, n)[1]
+        # no pairwise matrix: a few hundred bytes per box at most
+        assert b <= 576 * n + (1 << 20)
+    assert _mws(lib, 512001)[0] == 5
+    assert lib.nms_matrix_workspace_size(5, None) == 1
+
+
+def _mcall(lib, n, boxes=FAKE, scores=FAKE, t=0.1, sigma=0.5, keep=FAKE, count=True, ws=FAKE,
+           ws_bytes=1 << 40):
+    c = ctypes.c_int64(-1)
+    st = lib.nms_matrix_f32(boxes, scores, n, t, sigma, keep, ctypes.byref(c) if count else None,
+                            ws, ws_bytes, None)
+    return STATUS[st], c.value
+
+
+def test_matrix_host_argument_checks():
+    lib = _mlib()
+    assert _mcall(lib, 0) == ("NMS_OK", 0)
+    assert _mcall(lib, -1)[0] == "NMS_INVALID_ARG"
+    assert _mcall(lib, 5, t=float("nan"))[0] == "NMS_INVALID_ARG"
+    for bad_sigma in (0.0, -1.0, float("nan"), float("inf")):
+        assert _mcall(lib, 5, sigma=bad_sigma)[0] == "NMS_INVALID_ARG"
+    assert _mcall(lib, 5, boxes=None)[0] == "NMS_INVALID_ARG"
+    assert _mcall(lib, 5, keep=None)[0] == "NMS_INVALID_ARG"
+    assert _mcall(lib, 5, count=False)[0] == "NMS_INVALID_ARG"
+    assert _mcall(lib, 5, boxes=FAKE + 4)[0] == "NMS_INVALID_ARG"
+    assert _mcall(lib, 5, ws=FAKE + 64)[0] == "NMS_INVALID_ARG"
+    assert _mcall(lib, 5, ws_bytes=100) == ("NMS_WORKSPACE_TOO_SMALL", 0)
+    assert _mcall(lib, 512001)[0] == "NMS_TOO_LARGE"
