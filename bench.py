@@ -17,6 +17,11 @@ memory.  Prints one JSON line:
                  bytes) over the measured median call time
   cpu_baseline   the CPU oracle on the same workload, on this host
   n8192          the same measurement on the N = 8192 clustered workload
+  matrix_nms     Matrix NMS (Gaussian decay, score threshold 0.1, sigma 0.5)
+                 on the boxes and scores of both workloads: call time, stage
+                 times, pair evaluations per second of its two pairwise
+                 kernels and their fraction of the VALU issue peak; parity
+                 with the CPU oracle at N = 8192
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-calibration BYTES
@@ -39,6 +44,9 @@ OPS_PER_PAIR = 13
 # non-packed fp32 VALU issue peak: 256 CUs x 64 lanes x 2.4 GHz, 1 op per lane
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
+# column tiles per mask work item for one image: a row's words are written
+# from the start of the strip holding its own tile
+MASK_STRIP = 8
 
 
 def _measure(w, steps, warmup, fuse=True):
@@ -130,7 +138,7 @@ def _mask_algorithmic_bytes(w):
     of the row band it writes, the sorted boxes and areas it reads once."""
     n = w.n
     words = (n + 63) // 64
-    strip = 16
+    strip = MASK_STRIP
     total = 0
     for r in range(words):
         rows = min(64, n - 64 * r)
@@ -184,6 +192,54 @@ def _cpu_model():
     except OSError:
         pass
     return "unknown"
+
+
+# Vector instructions per (father, child) pair in the two pairwise Matrix NMS
+# kernels, counted in their gfx950 code: the float32 IoU (4 clamps, 2 sub,
+# mul, add, sub and a 10-instruction correctly rounded division) plus the
+# running maximum (overlap) or the binary64 conversion, FMA and two bound
+# compares (decay, fast path).
+MATRIX_OVERLAP_INSTR = 21
+MATRIX_DECAY_INSTR = 24
+MATRIX_T, MATRIX_SIGMA = 0.1, 0.5
+
+
+def _measure_matrix(w, steps, warmup):
+    import numpy as np
+    import torch
+
+    import greedy_iou_nms_amd as g
+
+    dev = torch.device("cuda:0")
+    boxes = torch.from_numpy(w.boxes).to(dev)
+    scores = torch.from_numpy(w.scores).to(dev)
+    ws = g.Workspace(dev)
+    out = torch.empty(w.n, dtype=torch.int64, device=dev)
+    for _ in range(warmup):
+        g.matrix_nms(boxes, scores, MATRIX_T, MATRIX_SIGMA, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    call_ms, stages = [], []
+    for _ in range(steps):
+        t1 = time.perf_counter()
+        keep = g.matrix_nms(boxes, scores, MATRIX_T, MATRIX_SIGMA, workspace=ws, out=out)
+        call_ms.append(1000.0 * (time.perf_counter() - t1))
+    for _ in range(max(3, steps // 2)):
+        _, st = g.matrix_nms_profiled(boxes, scores, MATRIX_T, MATRIX_SIGMA, workspace=ws,
+                                      out=out)
+        stages.append(st)
+    keep = keep.cpu().numpy().copy()
+    pairs = w.n * (w.n - 1) // 2
+    med = float(np.median(call_ms))
+    st = {k: float(np.median([x[k] for x in stages])) for k in stages[0]}
+    res = {"workload": w.name, "n": w.n, "score_threshold": MATRIX_T, "sigma": MATRIX_SIGMA,
+           "ms_per_call": {"median": med, "min": float(np.min(call_ms))},
+           "boxes_per_s": w.n / (med * 1e-3), "stage_ms": st, "kept": int(keep.size)}
+    for name, key, instr in (("overlap_max", "overlap_max", MATRIX_OVERLAP_INSTR),
+                             ("decay", "decay", MATRIX_DECAY_INSTR)):
+        rate = pairs / (st[key] * 1e-3)
+        res[name + "_pairs_per_s"] = rate
+        res[name + "_valu_frac"] = instr * rate / (VALU_PEAK_TOPS * 1e12)
+    return res, keep
 
 
 def _workload_line(w, r):
@@ -297,6 +353,17 @@ def main():
         w2 = workloads.config(2, seed=0)
         r2 = _measure(w2, args.steps, args.warmup)
         line["n8192"] = _workload_line(w2, r2)
+
+        msteps = max(3, min(args.steps, 20))
+        m2, k2 = _measure_matrix(w2, msteps, min(args.warmup, 3))
+        m5, _ = _measure_matrix(w, msteps, min(args.warmup, 3))
+        line["matrix_nms"] = {"n8192": m2, "n65536": m5}
+        if not args.no_cpu:
+            import numpy as np
+
+            import oracle
+            line["matrix_nms"]["n8192"]["parity_vs_oracle"] = bool(np.array_equal(
+                k2, oracle.c_matrix_nms(w2.boxes, w2.scores, MATRIX_T, MATRIX_SIGMA)))
 
     if not args.no_cpu:
         import numpy as np

@@ -42,6 +42,17 @@ __device__ __forceinline__ float min2(float a, float b, float ninf) {
     return __builtin_amdgcn_fmed3f(a, b, ninf);
 }
 
+// Intersection area of ordered boxes (x1 < x2, y1 < y2), as described in
+// suppresses() below: the column box clamped into the row box's extent.
+__device__ __forceinline__ float intersection(float rx1, float ry1, float rx2, float ry2,
+                                              float cx1, float cy1, float cx2, float cy2) {
+    const float xx1 = __builtin_amdgcn_fmed3f(cx1, rx1, rx2);
+    const float xx2 = __builtin_amdgcn_fmed3f(cx2, rx1, rx2);
+    const float yy1 = __builtin_amdgcn_fmed3f(cy1, ry1, ry2);
+    const float yy2 = __builtin_amdgcn_fmed3f(cy2, ry1, ry2);
+    return (xx2 - xx1) * (yy2 - yy1);
+}
+
 template <int MODE>
 __device__ __forceinline__ bool suppresses(float rx1, float ry1, float rx2, float ry2, float ra,
                                            float cx1, float cy1, float cx2, float cy2, float ca,
@@ -66,11 +77,7 @@ __device__ __forceinline__ bool suppresses(float rx1, float ry1, float rx2, floa
     // definition's width bit for bit; where they do not, both clamp to the
     // same end of the row box and w = 0, as max(0, xx2 - xx1) gives.  The same
     // holds for h, so the intersection is the definition's in every case.
-    const float xx1 = __builtin_amdgcn_fmed3f(cx1, rx1, rx2);
-    const float xx2 = __builtin_amdgcn_fmed3f(cx2, rx1, rx2);
-    const float yy1 = __builtin_amdgcn_fmed3f(cy1, ry1, ry2);
-    const float yy2 = __builtin_amdgcn_fmed3f(cy2, ry1, ry2);
-    const float inter = (xx2 - xx1) * (yy2 - yy1);
+    const float inter = intersection(rx1, ry1, rx2, ry2, cx1, cy1, cx2, cy2);
     const float uni = (ra + ca) - inter;
     return exceeds<MODE>(inter, uni, t, mid);
 }
@@ -173,8 +180,10 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
     const int t_diag = r - c0;  // the diagonal tile's slot, if it lies in this strip
 
     // Column boxes of the strip, one per lane and tile.  Tiles outside
-    // [r, cend) are evaluated on real boxes and masked out (tmask = 0), which
-    // costs less than branching around them.
+    // [r, cend) are evaluated and masked out (tmask = 0), which costs less
+    // than branching around them; their boxes are replaced by an empty box
+    // at 0, whose intersection with anything is exactly 0 (like the padding
+    // boxes past n), so they never look like an overlap.
     float cx1[S], cy1[S], cx2[S], cy2[S], ca[S];
     uint32_t cg[S];
     uint64_t tmask[S];
@@ -183,7 +192,7 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
         const int c = c0 + t;
         const bool active = c >= r && c < cend;
         const int q = active ? 64 * c + lane : lane;
-        const float4 b = m_.sb[q];
+        const float4 b = active ? m_.sb[q] : make_float4(0.f, 0.f, 0.f, 0.f);
         cx1[t] = b.x;
         cy1[t] = b.y;
         cx2[t] = b.z;
@@ -207,15 +216,51 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
         const uint32_t rg = GROUPED ? m_.seg[p] : 0u;
         // in the diagonal tile only boxes after row k vote
         const uint64_t dmask = k == 63 ? 0ull : (~0ull << (k + 1));
+        if (MODE == MODE_LITERAL) {
 #pragma unroll
-        for (int t = 0; t < S; ++t) {
-            bool pred = suppresses<MODE>(rx1, ry1, rx2, ry2, ra, cx1[t], cy1[t], cx2[t], cy2[t],
-                                         ca[t], a.t, a.mid, a.pinf, a.ninf);
-            if (GROUPED) pred = pred && (cg[t] == rg);
-            uint64_t m = __ballot(pred) & tmask[t];
-            m &= (t == t_diag) ? dmask : ~0ull;
-            out_lo[t] = write_lane(out_lo[t], (uint32_t)m, k);
-            out_hi[t] = write_lane(out_hi[t], (uint32_t)(m >> 32), k);
+            for (int t = 0; t < S; ++t) {
+                const uint64_t live = tmask[t] & ((t == t_diag) ? dmask : ~0ull);
+                bool pred = suppresses<MODE>(rx1, ry1, rx2, ry2, ra, cx1[t], cy1[t], cx2[t],
+                                             cy2[t], ca[t], a.t, a.mid, a.pinf, a.ninf);
+                if (GROUPED) pred = pred && (cg[t] == rg);
+                const uint64_t m = __ballot(pred) & live;
+                out_lo[t] = write_lane(out_lo[t], (uint32_t)m, k);
+                out_hi[t] = write_lane(out_hi[t], (uint32_t)(m >> 32), k);
+            }
+        } else {
+            // With t > 0 a pair without overlap (intersection exactly 0)
+            // never suppresses, and most pairs do not overlap.  The
+            // intersections of TG tiles are computed first; only when one of
+            // them is nonzero in some lane (their bit patterns ORed: all are
+            // non-negative) do that group's unions and threshold tests run.
+            // Words that stay 0 need no write (they start at 0).
+            constexpr int TG = 4;
+#pragma unroll
+            for (int t0 = 0; t0 < S; t0 += TG) {
+                float inter[TG];
+                uint32_t any = 0u;
+#pragma unroll
+                for (int j = 0; j < TG; ++j) {
+                    const int t = t0 + j;
+                    inter[j] = intersection(rx1, ry1, rx2, ry2, cx1[t], cy1[t], cx2[t], cy2[t]);
+                    any |= __float_as_uint(inter[j]);
+                }
+                if (__ballot(any != 0u) == 0ull) continue;
+#pragma unroll
+                for (int j = 0; j < TG; ++j) {
+                    const int t = t0 + j;
+                    const uint64_t live = tmask[t] & ((t == t_diag) ? dmask : ~0ull);
+                    const uint64_t touch = __ballot(inter[j] > 0.0f) & live;
+                    if (touch) {
+                        const float uni = (ra + ca[t]) - inter[j];
+                        bool pred = exceeds<MODE>(inter[j], uni, a.t, a.mid);
+                        if (GROUPED) pred = pred && (cg[t] == rg);
+                        const uint64_t m = __ballot(pred) & touch;
+                        out_lo[t] = write_lane(out_lo[t], (uint32_t)m, k);
+                        out_hi[t] = write_lane(out_hi[t], (uint32_t)(m >> 32), k);
+                    }
+                }
+            }
         }
     }
     if (mine) {

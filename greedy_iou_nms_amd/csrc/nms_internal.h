@@ -37,7 +37,7 @@ static_assert(sizeof(Ctrl) == 64, "Ctrl layout");
 
 // Column tiles per mask work item ("strip"): 16 for one image, 4 for grouped
 // input whose bands are only a few tiles wide.
-constexpr int STRIP_SINGLE = 16;
+constexpr int STRIP_SINGLE = 8;
 constexpr int STRIP_GROUPED = 4;
 
 // Multi-workgroup radix sort (one image): a workgroup of RADIX_THREADS ranks

@@ -19,10 +19,12 @@ def test_mask_bytes_small_case_by_hand():
 
 
 def test_mask_bytes_strip_offsets():
-    # 64 * 20 boxes: row tiles 0..15 start at column 0 (20 words), row tiles
-    # 16..19 at column 16 (4 words)
+    # 64 * 20 boxes, strips of 8 column tiles: row tiles 0..7 start at column
+    # 0 (20 words), 8..15 at column 8 (12 words), 16..19 at column 16 (4 words)
+    assert bench.MASK_STRIP == 8
     w = workloads.random_small(0, 64 * 20)
-    assert bench._mask_algorithmic_bytes(w) == 64 * (16 * 20 + 4 * 4) * 8 + 20 * 64 * 20
+    assert bench._mask_algorithmic_bytes(w) == (64 * (8 * 20 + 8 * 12 + 4 * 4) * 8
+                                                + 20 * 64 * 20)
 
 
 def test_traffic_record_is_read_when_sources_match():
