@@ -24,6 +24,8 @@ memory.  Prints one JSON line:
                  with the CPU oracle at N = 8192
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --valu-rates
+         (cycles per wave64 instruction of the VALU classes the kernels use)
        python bench.py --copy-calibration BYTES
          (device-to-device copies of a known size, run under rocprofv3 --pmc
           to scale the FETCH_SIZE / WRITE_SIZE counters to bytes)
@@ -41,8 +43,12 @@ if ROOT not in sys.path:
 # fp32 ops per box pair counted as the algorithmic work of the IoU test:
 # 4 max/min, 2 sub, 2 clamps, 1 mul, 1 add, 1 sub, 1 div, 1 compare
 OPS_PER_PAIR = 13
-# non-packed fp32 VALU issue peak: 256 CUs x 64 lanes x 2.4 GHz, 1 op per lane
-VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+# fp32 vector peak counted in operations (an FMA counts as one): the published
+# 157.3 TFLOP/s is 256 CUs x 4 SIMDs x 32 lanes x 2 (FMA) x 2.4 GHz, so plain
+# fp32 add / sub / mul issue at 256 x 4 x 32 x 2.4 GHz = 78.6 T ops/s (one
+# wave64 instruction per 2 cycles per SIMD; `bench.py --valu-rates` measures
+# it, and the 4-cycle classes: min/max/med3, conversions, fp64, lane writes)
+VALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
 # column tiles per mask work item for one image: a row's words are written
 # from the start of the strip holding its own tile
@@ -194,13 +200,12 @@ def _cpu_model():
     return "unknown"
 
 
-# Vector instructions per (father, child) pair in the two pairwise Matrix NMS
-# kernels, counted in their gfx950 code: the float32 IoU (4 clamps, 2 sub,
-# mul, add, sub and a 10-instruction correctly rounded division) plus the
-# running maximum (overlap) or the binary64 conversion, FMA and two bound
-# compares (decay, fast path).
-MATRIX_OVERLAP_INSTR = 21
-MATRIX_DECAY_INSTR = 24
+# Algorithmic fp32 ops per (father, child) pair of the two pairwise Matrix
+# NMS kernels: the IoU (4 max/min, 2 sub, 2 clamps, mul, add, sub, div) and
+# the running maximum (overlap), or the IoU, its square, the difference with
+# the father's maximum, the scaling by sigma and the compare (decay).
+MATRIX_OVERLAP_INSTR = 13
+MATRIX_DECAY_INSTR = 16
 MATRIX_T, MATRIX_SIGMA = 0.1, 0.5
 
 
@@ -268,7 +273,13 @@ def main():
                     help="time only the N=65536 workload as the library runs it (for profiler runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run device copies of BYTES bytes (counter calibration)")
+    ap.add_argument("--valu-rates", action="store_true",
+                    help="only run the VALU issue-rate probe built next to the library")
     args = ap.parse_args()
+    if args.valu_rates:
+        import subprocess
+        probe = os.path.join(ROOT, "greedy_iou_nms_amd", "valu_rate_probe")
+        sys.exit(subprocess.run([probe]).returncode)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs on a single MI355X "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)

@@ -18,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libgreedy_nms.so")
+# instruction issue-rate probe for the roofline figures (bench.py --valu-rates)
+PROBE = os.path.join(HERE, "valu_rate_probe")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -45,6 +47,11 @@ def build(verbose: bool = False, extra=()) -> str:
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
                                             stderr=subprocess.STDOUT)))
     failed = []
+    probe_cmd = [HIPCC, "--offload-arch=" + ARCH, "-O2", "-Wno-unused-result",
+                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                 os.path.join(CSRC, "valu_rate_probe.hip"), "-o", PROBE + ".tmp"]
+    procs.append(("valu_rate_probe.hip", subprocess.Popen(probe_cmd, stdout=subprocess.PIPE,
+                                                          stderr=subprocess.STDOUT)))
     for src, p in procs:
         out, _ = p.communicate()
         # the host pass does not know the packed-fp32 feature flag; that
@@ -63,6 +70,7 @@ def build(verbose: bool = False, extra=()) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 
