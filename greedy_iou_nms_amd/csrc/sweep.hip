@@ -123,26 +123,33 @@ static_assert(NEAR >= 2, "the resolver carries the words for the next two tiles 
 // Appliers have slack; their polling shares the LDS with the resolver.
 constexpr int APPLIER_SLEEP = 1;
 
+// Chunk c's staged data sits in ring slot c mod RING.  An applier stages
+// chunk x after it has seen its previous chunk, x - A, settled, which came
+// after the resolver settled x - 2A (A = APPLIERS); the slot's previous
+// chunk, x - RING, is settled and read for the last time by then.
+constexpr int RING = 16;
+static_assert(RING >= 2 * APPLIERS && (RING & (RING - 1)) == 0,
+              "the staging ring must outlast an applier's lead over the resolver");
+
+struct StageSlot {
+    uint64_t near[NEAR + 1][64];  // lane k: row 64c + k's words for tiles c .. c + NEAR
+    // rows whose diagonal word is nonzero, rows with a nonzero word for one
+    // of the next NEAR tiles
+    uint64_t nz0, nzn;
+    uint32_t ready;    // chunk + 1 once the words above are staged
+    uint32_t applied;  // chunk + 1 once the chunk's far words are ORed in
+};
+
 struct SweepSmem {
-    uint64_t near[APPLIERS][2][NEAR + 1][64];  // staged words for tiles c .. c + NEAR
-    // per staged chunk: rows whose diagonal word is nonzero, rows with a
-    // nonzero word for one of the next NEAR tiles
-    uint64_t summ[APPLIERS][2][2];
-    uint32_t data_ready[APPLIERS][2]; // chunk + 1 once diag/super are staged
-    uint32_t k_ready[APPLIERS];       // chunk + 1 once removed[chunk] is final
-    uint32_t applied[APPLIERS];       // chunk + 1 once its far words are ORed in
+    StageSlot stage[RING];
     // boxes kept before chunk c, at k_off[c % KOFF_RING] (one image): when the
     // resolver publishes chunk c, every chunk up to c - NEAR - 1 has been
     // applied, so the ring slot's previous chunk has been read
     uint32_t k_off[KOFF_RING];
+    uint32_t resolved;   // chunks settled: removed[c] is final below this
     uint32_t kept_total;
     uint32_t abort;
     uint32_t done_upto;  // fused kernel: row tiles below this are known finished
-    // where the resolver's lanes other than lane 0 direct their publishing
-    // writes (every lane stores, so the store needs no branch)
-    uint64_t sink_rem[64];
-    uint32_t sink_flag[64];
-    uint32_t sink_off[64];
 };
 
 // Hand-over flags.  Everything handed over between waves lives in LDS, and
@@ -264,20 +271,20 @@ __device__ __forceinline__ bool load_level1(const SweepArgs &a, int c, Level1 &l
 
 // Stage chunk c's near words and their summary masks for the resolver, then
 // announce them.
-__device__ __forceinline__ void stage_level1(const Level1 &l, int c, int slot, int par,
-                                             SweepSmem &sm) {
+__device__ __forceinline__ void stage_level1(const Level1 &l, int c, SweepSmem &sm) {
     const int lane = threadIdx.x & 63;
+    StageSlot &s = sm.stage[c & (RING - 1)];
 #pragma unroll
-    for (int j = 0; j <= NEAR; ++j) sm.near[slot][par][j][lane] = l.near[j];
+    for (int j = 0; j <= NEAR; ++j) s.near[j][lane] = l.near[j];
     uint64_t ahead = 0ull;
 #pragma unroll
     for (int j = 1; j <= NEAR; ++j) ahead |= l.near[j];
     const uint64_t nz0 = __ballot(l.near[0] != 0ull);
     const uint64_t nzn = __ballot(ahead != 0ull);
     if (lane == 0) {
-        sm.summ[slot][par][0] = nz0;
-        sm.summ[slot][par][1] = nzn;
-        flag_store(&sm.data_ready[slot][par], (uint32_t)c + 1u);
+        s.nz0 = nz0;
+        s.nzn = nzn;
+        flag_store(&s.ready, (uint32_t)c + 1u);
     }
 }
 
@@ -354,37 +361,22 @@ struct ResolverBatch {
     uint64_t nw[NEAR + 1];
 };
 
-// Where chunk c's data sits: slot c mod A, parity (c / A) mod 2, and the
-// slot of chunk c - NEAR - 1, whose far words must be in before word c is
-// read.  Stepped from chunk to chunk instead of divided out.
-struct ResolverPos {
-    int slot, par, app_slot;
-    __device__ __forceinline__ void init(int c) {
-        slot = c % APPLIERS;
-        par = (c / APPLIERS) & 1;
-        app_slot = ((c - NEAR - 1) % APPLIERS + APPLIERS) % APPLIERS;
-    }
-    __device__ __forceinline__ void next() {
-        if (++slot == APPLIERS) {
-            slot = 0;
-            par ^= 1;
-        }
-        if (++app_slot == APPLIERS) app_slot = 0;
-    }
-};
+// Word c is complete once chunk c - LAG and every chunk before it is applied.
+constexpr int LAG = NEAR + 1;
 
-// The LDS performs the reads in order, so data read after a flag that is
-// already set is the data that flag announces.
-__device__ __forceinline__ void resolver_read(int c, const ResolverPos &q, const uint64_t *removed,
-                                              SweepSmem &sm, ResolverBatch &b) {
+// Chunk x's batch.  The LDS performs the reads in order, so data read after
+// a flag that is already set is the data that flag announces.
+__device__ __forceinline__ void resolver_read(int x, const uint64_t *removed, SweepSmem &sm,
+                                              ResolverBatch &b) {
     const int lane = threadIdx.x & 63;
-    b.f_data = flag_load(&sm.data_ready[q.slot][q.par]);
-    b.f_app = flag_load(&sm.applied[q.app_slot]);
-    b.nz0 = sm.summ[q.slot][q.par][0];
-    b.nzn = sm.summ[q.slot][q.par][1];
-    b.rem = removed[c];
+    const StageSlot &s = sm.stage[x & (RING - 1)];
+    b.f_data = flag_load(&s.ready);
+    b.f_app = flag_load(&sm.stage[(x - LAG) & (RING - 1)].applied);
+    b.nz0 = s.nz0;
+    b.nzn = s.nzn;
+    b.rem = removed[x];
 #pragma unroll
-    for (int j = 0; j <= NEAR; ++j) b.nw[j] = sm.near[q.slot][q.par][j][lane];
+    for (int j = 0; j <= NEAR; ++j) b.nw[j] = s.near[j][lane];
     compiler_barrier();
 }
 
@@ -393,10 +385,9 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f);
 
 // Resolver state carried from chunk to chunk in scalar registers.
 struct ResolverState {
-    ResolverPos at;      // chunk c
-    ResolverPos ahead;   // chunk c + 2, whose batch is read while c is settled
     uint64_t carry1;     // kept rows' words for tile c (chunks c - 1 and c - 2)
     uint64_t carry2;     // kept rows' words for tile c + 1 (chunk c - 1)
+    uint64_t last_valid; // rows of the last chunk that exist
     bool stale_next;     // chunk c + 1's batch must be read again (see resolve_one)
     uint32_t total;      // boxes kept before chunk c
 };
@@ -408,7 +399,7 @@ struct ResolverState {
 // c's and chunk c + 1's words for it travel in registers (carry2, then
 // carry1), the words of chunks c - 1 and c - 2 for it were ORed into LDS
 // (atomics) before this read is issued, and the far words of chunks up to
-// c + 2 - NEAR - 1 are in once the applied flag read with it says so and no
+// c + 2 - LAG are in once the applied flag read with it says so and no
 // earlier batch had to wait (a batch read before such a wait is read again).
 // Reading two chunks ahead keeps LDS latency, and this chunk's own LDS
 // writes, off the path from one chunk to the next.
@@ -417,20 +408,20 @@ __device__ __forceinline__ bool resolve_one(const SweepArgs &a, uint64_t *remove
                                             int c, ResolverState &st, ResolverBatch &cur,
                                             ResolverBatch &ahead) {
     const int lane = threadIdx.x & 63;
-    constexpr int LAG = NEAR + 1;
     const uint32_t app_need = c >= LAG ? (uint32_t)(c - LAG) + 1u : 0u;
-    // A batch is complete only if every chunk up to c - NEAR - 1 had been
-    // applied when it was read; its own flag covers the last of them, and
-    // the earlier ones were covered by the earlier batches' flags.  When a
-    // flag was not yet set, the waits below happen after chunk c + 1's
-    // batch was read, so that batch may miss far words of chunk c - NEAR - 1
-    // and is read again at the next chunk.
+    // A batch is complete only if every chunk up to c - LAG had been applied
+    // when it was read; its own flag covers the last of them, and the
+    // earlier ones were covered by the earlier batches' flags.  When a flag
+    // was not yet set, the waits below happen after chunk c + 1's batch was
+    // read, so that batch may miss far words of chunk c - LAG and is read
+    // again at the next chunk.
     const bool late = cur.f_data < (uint32_t)c + 1u || cur.f_app < app_need;
     if (late || st.stale_next) {
-        if (!wait_flag<FUSED>(&sm.data_ready[st.at.slot][st.at.par], (uint32_t)c + 1u, sm, a.ctrl))
+        if (!wait_flag<FUSED>(&sm.stage[c & (RING - 1)].ready, (uint32_t)c + 1u, sm, a.ctrl))
             return false;
-        if (!wait_flag<FUSED>(&sm.applied[st.at.app_slot], app_need, sm, a.ctrl)) return false;
-        resolver_read(c, st.at, removed, sm, cur);
+        if (!wait_flag<FUSED>(&sm.stage[(c - LAG) & (RING - 1)].applied, app_need, sm, a.ctrl))
+            return false;
+        resolver_read(c, removed, sm, cur);
         wait_lds();
     }
     st.stale_next = late;
@@ -438,12 +429,9 @@ __device__ __forceinline__ bool resolve_one(const SweepArgs &a, uint64_t *remove
     // spare words and the staging slots are a ring), so that the number of
     // LDS accesses in flight is the same on every path through the loop and
     // the compiler's waits for a batch do not wait for later accesses.
-    st.ahead.next();
-    resolver_read(c + 2, st.ahead, removed, sm, ahead);
-    const int slot = st.at.slot;
-    st.at.next();
+    resolver_read(c + 2, removed, sm, ahead);
 
-    const uint64_t valid = rows_valid(c, a.n);
+    const uint64_t valid = c == a.words - 1 ? st.last_valid : ~0ull;
     uint64_t rem = uniform64(cur.rem) | st.carry1;
     uint64_t cand = ~rem & uniform64(cur.nz0) & valid;
     if (cand) {
@@ -472,13 +460,11 @@ __device__ __forceinline__ bool resolve_one(const SweepArgs &a, uint64_t *remove
     }
     st.carry1 = c1;
     st.carry2 = c2;
-    // lane 0 publishes; the other lanes store to their own sink words
-    uint64_t *rem_at = lane == 0 ? &removed[c] : &sm.sink_rem[lane];
-    uint32_t *off_at = lane == 0 ? &sm.k_off[c & (KOFF_RING - 1)] : &sm.sink_off[lane];
-    uint32_t *flag_at = lane == 0 ? &sm.k_ready[slot] : &sm.sink_flag[lane];
-    *rem_at = rem;
-    *off_at = st.total;
-    flag_store(flag_at, (uint32_t)c + 1u);
+    if (lane == 0) {
+        removed[c] = rem;
+        sm.k_off[c & (KOFF_RING - 1)] = st.total;
+        flag_store(&sm.resolved, (uint32_t)c + 1u);
+    }
     st.total += (uint32_t)__popcll(kept);
     return true;
 }
@@ -493,15 +479,14 @@ template <bool FUSED>
 __device__ void resolve_chunks(const SweepArgs &a, uint64_t *removed, SweepSmem &sm) {
     const int W = a.words;
     ResolverState st;
-    st.at.init(0);
-    st.ahead.init(1);  // advanced to chunk 2 before its first read
     st.carry1 = 0ull;
     st.carry2 = 0ull;
+    st.last_valid = rows_valid(W - 1, a.n);
     st.stale_next = false;
     st.total = 0u;
     ResolverBatch b0, b1, b2;
-    resolver_read(0, st.at, removed, sm, b0);
-    resolver_read(1, st.ahead, removed, sm, b1);
+    resolver_read(0, removed, sm, b0);
+    resolver_read(1, removed, sm, b1);
     // Every path into the loop arrives with these batches in registers, so
     // the reads in flight inside the loop are only those issued there.
     wait_lds();
@@ -560,7 +545,6 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
                              int q) {
     const int lane = threadIdx.x & 63;
     const int W = a.words;
-    const int slot = q - 1;
     const int A = APPLIERS;
     int c = q - 1;
     if (c >= W) return;
@@ -569,7 +553,7 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
     // prologue: chunk c staged, its entries and chunk c + A's first level issued
     if (!load_level1<FUSED>(a, c, l1, sm)) return;
     wait_loads();
-    stage_level1(l1, c, slot, 0, sm);
+    stage_level1(l1, c, sm);
     uint32_t count = __builtin_amdgcn_readfirstlane(l1.count);
     load_entries<FUSED>(a, c, rounds_of(count), e);
     if (c + A < W && !load_level1<FUSED>(a, c + A, l1, sm)) return;
@@ -577,11 +561,11 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
         wait_loads();
         uint32_t count_next = 0;
         if (c + A < W) {
-            stage_level1(l1, c + A, slot, ((c + A) / A) & 1, sm);
+            stage_level1(l1, c + A, sm);
             count_next = __builtin_amdgcn_readfirstlane(l1.count);
             if (c + 2 * A < W && !load_level1<FUSED>(a, c + 2 * A, l1, sm)) return;
         }
-        if (!wait_flag<FUSED, APPLIER_SLEEP>(&sm.k_ready[slot], (uint32_t)c + 1u, sm, a.ctrl))
+        if (!wait_flag<FUSED, APPLIER_SLEEP>(&sm.resolved, (uint32_t)c + 1u, sm, a.ctrl))
             return;
         // the resolver wrote the chunk's final removed word and the count
         // of boxes kept before it ahead of the flag
@@ -612,7 +596,7 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
                 }
             }
         }
-        if (lane == 0) flag_store(&sm.applied[slot], (uint32_t)c + 1u);
+        if (lane == 0) flag_store(&sm.stage[c & (RING - 1)].applied, (uint32_t)c + 1u);
         if (c + A < W) load_entries<FUSED>(a, c + A, rounds_of(count_next), e);
         count = count_next;
     }
@@ -628,13 +612,12 @@ __device__ __forceinline__ void sweep_body(const SweepArgs &a, uint64_t *removed
     const int stride = a.grouped ? a.ctrl->band_stride : a.mstride;
 
     for (int w = tid; w < W + NEAR_TILES; w += NT) removed[w] = 0ull;
-    if (tid < APPLIERS) {
-        sm.data_ready[tid][0] = 0u;
-        sm.data_ready[tid][1] = 0u;
-        sm.k_ready[tid] = 0u;
-        sm.applied[tid] = 0u;
+    if (tid < RING) {
+        sm.stage[tid].ready = 0u;
+        sm.stage[tid].applied = 0u;
     }
     if (tid == 0) {
+        sm.resolved = 0u;
         sm.abort = 0u;
         sm.done_upto = 0u;
     }
