@@ -108,9 +108,6 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
 }
 
 constexpr int APPLIERS = NWAVES - 1;
-constexpr int KOFF_RING = 8;
-static_assert(KOFF_RING >= NEAR_TILES + 2 && (KOFF_RING & (KOFF_RING - 1)) == 0,
-              "the offset ring must outlast the resolver's lead over the appliers");
 // Bounded waits: about a second of polling before a wait gives up.
 constexpr uint32_t SPIN_LIMIT = 1u << 23;
 
@@ -119,34 +116,46 @@ constexpr int RMAX = 16;
 
 constexpr int NEAR = NEAR_TILES;
 static_assert(NEAR >= 2, "the resolver carries the words for the next two tiles in registers");
+// Word c is complete once chunk c - LAG and every chunk before it is applied.
+constexpr int LAG = NEAR + 1;
 
 // Appliers have slack; their polling shares the LDS with the resolver.
 constexpr int APPLIER_SLEEP = 1;
 
-// Chunk c's staged data sits in ring slot c mod RING.  An applier stages
-// chunk x after it has seen its previous chunk, x - A, settled, which came
-// after the resolver settled x - 2A (A = APPLIERS); the slot's previous
-// chunk, x - RING, is settled and read for the last time by then.
+// Chunk c's data sits in ring slot c mod RING.  An applier stages chunk x
+// after it has seen its previous chunk, x - A, settled, which came after the
+// resolver settled x - 2A (A = APPLIERS); the slot's previous chunk, x - RING,
+// is settled and read for the last time by then.  The settled word and
+// offset the resolver leaves for chunk c are read by chunk c's applier before
+// it reports chunk c applied, and the resolver reaches chunk c + RING only
+// after that report.
 constexpr int RING = 16;
-static_assert(RING >= 2 * APPLIERS && (RING & (RING - 1)) == 0,
+static_assert(RING >= 2 * APPLIERS && RING > LAG && (RING & (RING - 1)) == 0,
               "the staging ring must outlast an applier's lead over the resolver");
 
 struct StageSlot {
     uint64_t near[NEAR + 1][64];  // lane k: row 64c + k's words for tiles c .. c + NEAR
-    // rows whose diagonal word is nonzero, rows with a nonzero word for one
-    // of the next NEAR tiles
-    uint64_t nz0, nzn;
-    uint32_t ready;    // chunk + 1 once the words above are staged
-    uint32_t applied;  // chunk + 1 once the chunk's far words are ORed in
+    uint64_t nzn;  // rows with a nonzero word for one of the next NEAR tiles
+    // Both c + 1 when set, read together as one 64-bit word: ready once the
+    // words above are staged, app_lag once chunk c - LAG is applied (its
+    // applier writes it here, so one read tells the resolver both).
+    uint32_t ready, app_lag;
+};
+
+struct Settled {
+    uint64_t rem;    // settled removed word of the chunk
+    uint32_t k_off;  // boxes kept before the chunk (one image)
+    uint32_t pad;
 };
 
 struct SweepSmem {
     StageSlot stage[RING];
-    // boxes kept before chunk c, at k_off[c % KOFF_RING] (one image): when the
-    // resolver publishes chunk c, every chunk up to c - NEAR - 1 has been
-    // applied, so the ring slot's previous chunk has been read
-    uint32_t k_off[KOFF_RING];
-    uint32_t resolved;   // chunks settled: removed[c] is final below this
+    // settled[c mod RING] is chunk c's; the resolver's lanes other than lane
+    // 0 direct their copies of those writes to settled[RING + lane] and
+    // resolved[lane] (every lane stores, so the stores need no branch and
+    // the number of LDS accesses per chunk is fixed)
+    Settled settled[RING + 64];
+    uint32_t resolved[64];  // [0]: chunks settled
     uint32_t kept_total;
     uint32_t abort;
     uint32_t done_upto;  // fused kernel: row tiles below this are known finished
@@ -279,10 +288,8 @@ __device__ __forceinline__ void stage_level1(const Level1 &l, int c, SweepSmem &
     uint64_t ahead = 0ull;
 #pragma unroll
     for (int j = 1; j <= NEAR; ++j) ahead |= l.near[j];
-    const uint64_t nz0 = __ballot(l.near[0] != 0ull);
     const uint64_t nzn = __ballot(ahead != 0ull);
     if (lane == 0) {
-        s.nz0 = nz0;
         s.nzn = nzn;
         flag_store(&s.ready, (uint32_t)c + 1u);
     }
@@ -352,31 +359,36 @@ __device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// What the resolver reads from LDS for one chunk, issued as one batch: the
-// two hand-over flags, the chunk's summary masks and removed word (the same
-// for every lane) and lane k's staged words for row 64c + k.
-struct ResolverBatch {
-    uint32_t f_data, f_app;
-    uint64_t nz0, nzn, rem;
+// What the resolver reads from LDS for one chunk, in two parts.  The staged
+// part (lane k's words for row 64c + k, the summary mask and the ready flag)
+// is read two chunks ahead.  The removed word and the flag that says it is
+// complete are read one chunk ahead, which gives the appliers a chunk more
+// to OR far words in.
+struct StagedBatch {
+    uint32_t ready;
+    uint64_t nzn;
     uint64_t nw[NEAR + 1];
 };
+struct WordBatch {
+    uint32_t app_lag;
+    uint64_t rem;
+};
 
-// Word c is complete once chunk c - LAG and every chunk before it is applied.
-constexpr int LAG = NEAR + 1;
-
-// Chunk x's batch.  The LDS performs the reads in order, so data read after
-// a flag that is already set is the data that flag announces.
-__device__ __forceinline__ void resolver_read(int x, const uint64_t *removed, SweepSmem &sm,
-                                              ResolverBatch &b) {
+// The LDS performs the reads in order, so data read after a flag that is
+// already set is the data that flag announces.
+__device__ __forceinline__ void read_staged(int x, SweepSmem &sm, StagedBatch &b) {
     const int lane = threadIdx.x & 63;
     const StageSlot &s = sm.stage[x & (RING - 1)];
-    b.f_data = flag_load(&s.ready);
-    b.f_app = flag_load(&sm.stage[(x - LAG) & (RING - 1)].applied);
-    b.nz0 = s.nz0;
+    b.ready = flag_load(&s.ready);
     b.nzn = s.nzn;
-    b.rem = removed[x];
 #pragma unroll
     for (int j = 0; j <= NEAR; ++j) b.nw[j] = s.near[j][lane];
+    compiler_barrier();
+}
+__device__ __forceinline__ void read_word(int x, const uint64_t *removed, SweepSmem &sm,
+                                          WordBatch &b) {
+    b.app_lag = flag_load(&sm.stage[x & (RING - 1)].app_lag);
+    b.rem = removed[x];
     compiler_barrier();
 }
 
@@ -385,55 +397,57 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f);
 
 // Resolver state carried from chunk to chunk in scalar registers.
 struct ResolverState {
-    uint64_t carry1;     // kept rows' words for tile c (chunks c - 1 and c - 2)
-    uint64_t carry2;     // kept rows' words for tile c + 1 (chunk c - 1)
-    uint64_t last_valid; // rows of the last chunk that exist
-    bool stale_next;     // chunk c + 1's batch must be read again (see resolve_one)
-    uint32_t total;      // boxes kept before chunk c
+    uint64_t carry1;  // kept rows' words for tile c (chunks c - 1 and c - 2)
+    uint64_t carry2;  // kept rows' words for tile c + 1 (chunk c - 1)
+    bool dead;        // a wait gave up: the remaining chunks are skipped
+    uint32_t total;   // boxes kept before chunk c
 };
 
-// Settle chunk c from its batch cur, after issuing the reads of chunk c + 2
-// into ahead.  Returns false if a wait gave up.
+// Settle chunk c from its staged batch cur and its word batch wb, after
+// issuing the reads of word c + 1 (into wb) and of chunk c + 2's staged
+// batch (into ahead).
 //
-// Word c + 2 is read before chunk c is settled.  That is safe because chunk
-// c's and chunk c + 1's words for it travel in registers (carry2, then
-// carry1), the words of chunks c - 1 and c - 2 for it were ORed into LDS
-// (atomics) before this read is issued, and the far words of chunks up to
-// c + 2 - LAG are in once the applied flag read with it says so and no
-// earlier batch had to wait (a batch read before such a wait is read again).
-// Reading two chunks ahead keeps LDS latency, and this chunk's own LDS
+// Word c + 1 is read before chunk c is settled.  That is safe because chunk
+// c's and chunk c - 1's words for it travel in registers (carry2, then
+// carry1), the words of chunks c - 2 and c - 3 for it were ORed into LDS
+// (atomics) before the read is issued, and the far words of chunks up to
+// c + 1 - LAG are in once the flag read with it says so: the flags of the
+// chunks before have been checked (or waited for) before this read is
+// issued.  Reading ahead keeps LDS latency, and this chunk's own LDS
 // writes, off the path from one chunk to the next.
 template <bool FUSED>
-__device__ __forceinline__ bool resolve_one(const SweepArgs &a, uint64_t *removed, SweepSmem &sm,
-                                            int c, ResolverState &st, ResolverBatch &cur,
-                                            ResolverBatch &ahead) {
+__device__ __forceinline__ void resolve_one(const SweepArgs &a, uint64_t *removed, SweepSmem &sm,
+                                            int c, ResolverState &st, StagedBatch &cur,
+                                            StagedBatch &ahead, WordBatch &wb) {
     const int lane = threadIdx.x & 63;
-    const uint32_t app_need = c >= LAG ? (uint32_t)(c - LAG) + 1u : 0u;
-    // A batch is complete only if every chunk up to c - LAG had been applied
-    // when it was read; its own flag covers the last of them, and the
-    // earlier ones were covered by the earlier batches' flags.  When a flag
-    // was not yet set, the waits below happen after chunk c + 1's batch was
-    // read, so that batch may miss far words of chunk c - LAG and is read
-    // again at the next chunk.
-    const bool late = cur.f_data < (uint32_t)c + 1u || cur.f_app < app_need;
-    if (late || st.stale_next) {
-        if (!wait_flag<FUSED>(&sm.stage[c & (RING - 1)].ready, (uint32_t)c + 1u, sm, a.ctrl))
-            return false;
-        if (!wait_flag<FUSED>(&sm.stage[(c - LAG) & (RING - 1)].applied, app_need, sm, a.ctrl))
-            return false;
-        resolver_read(c, removed, sm, cur);
+    const uint32_t want = (uint32_t)c + 1u;
+    // s_waitcnt lgkmcnt(8): this chunk's batches are in.  Every chunk issues
+    // the next word batch (2 reads), a staged batch (5 reads) and its
+    // publishing writes (3), so word c was followed by chunk c - 1's staged
+    // batch and writes.
+    __builtin_amdgcn_s_waitcnt(0xC07F | (8 << 8));
+    // (the flags are the same in every lane: tested in scalar registers, so
+    // the compiler keeps the loop's branches uniform)
+    const uint32_t ready = __builtin_amdgcn_readfirstlane(cur.ready);
+    const uint32_t app = __builtin_amdgcn_readfirstlane(wb.app_lag);
+    if (__builtin_expect((ready != want) | (app != want), 0)) {
+        StageSlot &s = sm.stage[c & (RING - 1)];
+        const bool ok = wait_flag<FUSED>(&s.ready, want, sm, a.ctrl) &&
+                        wait_flag<FUSED>(&s.app_lag, want, sm, a.ctrl);
+        if (!__builtin_amdgcn_readfirstlane((int)ok)) st.dead = true;
+        read_staged(c, sm, cur);
+        read_word(c, removed, sm, wb);
         wait_lds();
     }
-    st.stale_next = late;
+    // rows past n are marked removed from the start; their words are zero
+    uint64_t rem = uniform64(wb.rem) | st.carry1;
     // Issued for every chunk, also past the last one (removed[] has NEAR >= 2
     // spare words and the staging slots are a ring), so that the number of
-    // LDS accesses in flight is the same on every path through the loop and
-    // the compiler's waits for a batch do not wait for later accesses.
-    resolver_read(c + 2, removed, sm, ahead);
+    // LDS accesses in flight is the same on every path through the loop.
+    read_word(c + 1, removed, sm, wb);
+    read_staged(c + 2, sm, ahead);
 
-    const uint64_t valid = c == a.words - 1 ? st.last_valid : ~0ull;
-    uint64_t rem = uniform64(cur.rem) | st.carry1;
-    uint64_t cand = ~rem & uniform64(cur.nz0) & valid;
+    uint64_t cand = ~rem & __ballot(cur.nw[0] != 0ull);
     if (cand) {
         const uint64_t d = cur.nw[0];
         const uint64_t nz = cand;
@@ -444,7 +458,7 @@ __device__ __forceinline__ bool resolve_one(const SweepArgs &a, uint64_t *remove
             cand = ~rem & nz & above;
         } while (cand);
     }
-    const uint64_t kept = ~rem & valid;
+    const uint64_t kept = ~rem;
     uint64_t c1 = st.carry2, c2 = 0ull;
     if (kept & uniform64(cur.nzn)) {
         const bool mine = (kept >> lane) & 1ull;
@@ -460,42 +474,61 @@ __device__ __forceinline__ bool resolve_one(const SweepArgs &a, uint64_t *remove
     }
     st.carry1 = c1;
     st.carry2 = c2;
-    if (lane == 0) {
-        removed[c] = rem;
-        sm.k_off[c & (KOFF_RING - 1)] = st.total;
-        flag_store(&sm.resolved, (uint32_t)c + 1u);
-    }
+    Settled &out = sm.settled[lane == 0 ? (c & (RING - 1)) : RING + lane];
+    out.rem = rem;
+    out.k_off = st.total;
+    flag_store(&sm.resolved[lane], want);
     st.total += (uint32_t)__popcll(kept);
-    return true;
 }
 
 // Resolver: settle the chunks in order.  A chunk in which no surviving row
 // has a nonzero diagonal word, and no kept row a nonzero word for the next
-// NEAR tiles (most chunks, when overlaps are sparse), costs only its summary
-// masks and removed word.  Otherwise the kept rows' words for tiles c + 1 and
-// c + 2 are ORed across the wave into registers, those for tiles c + 3 ..
-// c + NEAR into LDS with atomics.
+// NEAR tiles (most chunks, when overlaps are sparse), costs only its flags,
+// summary mask and removed word.  Otherwise the kept rows' words for tiles
+// c + 1 and c + 2 are ORed across the wave into registers, those for tiles
+// c + 3 .. c + NEAR into LDS with atomics.
 template <bool FUSED>
 __device__ void resolve_chunks(const SweepArgs &a, uint64_t *removed, SweepSmem &sm) {
     const int W = a.words;
     ResolverState st;
     st.carry1 = 0ull;
     st.carry2 = 0ull;
-    st.last_valid = rows_valid(W - 1, a.n);
-    st.stale_next = false;
+    st.dead = false;
     st.total = 0u;
-    ResolverBatch b0, b1, b2;
-    resolver_read(0, removed, sm, b0);
-    resolver_read(1, removed, sm, b1);
+    StagedBatch b0, b1, b2;
+    WordBatch wb;
+    read_staged(0, sm, b0);
+    read_staged(1, sm, b1);
+    read_word(0, removed, sm, wb);
     // Every path into the loop arrives with these batches in registers, so
     // the reads in flight inside the loop are only those issued there.
     wait_lds();
-    // three chunks per trip, so the three batches trade roles without copies
-    for (int c = 0; c < W; c += 3) {
-        if (!resolve_one<FUSED>(a, removed, sm, c, st, b0, b2)) return;
-        if (c + 1 < W && !resolve_one<FUSED>(a, removed, sm, c + 1, st, b1, b0)) return;
-        if (c + 2 < W && !resolve_one<FUSED>(a, removed, sm, c + 2, st, b2, b1)) return;
+    // The first W mod 3 chunks, so that the loop settles three per trip to
+    // the end: every path through its body then issues the same LDS
+    // accesses, the compiler's waits stay exact and the batches keep their
+    // registers from trip to trip.
+    const int lead = W % 3;
+    if (lead >= 1) resolve_one<FUSED>(a, removed, sm, 0, st, b0, b2, wb);
+    if (lead >= 2) resolve_one<FUSED>(a, removed, sm, 1, st, b1, b0, wb);
+    if (lead) {
+        // read the loop's first batches afresh (each read is complete if
+        // its own flag says so: every earlier flag has been checked)
+        wait_lds();
+        read_staged(lead, sm, b0);
+        read_staged(lead + 1, sm, b1);
+        read_word(lead, removed, sm, wb);
+        wait_lds();
     }
+    // three chunks per trip, so the three staged batches trade roles
+    // without copies
+    for (int c = lead; c < W; c += 3) {
+        resolve_one<FUSED>(a, removed, sm, c, st, b0, b2, wb);
+        resolve_one<FUSED>(a, removed, sm, c + 1, st, b1, b0, wb);
+        resolve_one<FUSED>(a, removed, sm, c + 2, st, b2, b1, wb);
+        // after giving up, every wait ends at once: a few chunks more are harmless
+        if (st.dead) return;
+    }
+    if (st.dead) return;
     sm.kept_total = st.total;  // every lane stores the same value
 }
 
@@ -565,16 +598,15 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
             count_next = __builtin_amdgcn_readfirstlane(l1.count);
             if (c + 2 * A < W && !load_level1<FUSED>(a, c + 2 * A, l1, sm)) return;
         }
-        if (!wait_flag<FUSED, APPLIER_SLEEP>(&sm.resolved, (uint32_t)c + 1u, sm, a.ctrl))
+        if (!wait_flag<FUSED, APPLIER_SLEEP>(&sm.resolved[0], (uint32_t)c + 1u, sm, a.ctrl))
             return;
-        // the resolver wrote the chunk's final removed word and the count
-        // of boxes kept before it ahead of the flag
-        const uint64_t kept = ~uniform64(removed[c]) & rows_valid(c, a.n);
-        if (!a.grouped && ((kept >> lane) & 1ull)) {
-            const uint64_t below = (1ull << lane) - 1ull;
-            const uint32_t at = sm.k_off[c & (KOFF_RING - 1)] + (uint32_t)__popcll(kept & below);
-            a.keep_out[at] = (int64_t)e.ord;
-        }
+        // The resolver wrote the chunk's settled word and the count of boxes
+        // kept before it ahead of the counter.  Both are read before the
+        // chunk is reported applied: after that the resolver may reuse the
+        // slot.
+        const Settled &s = sm.settled[c & (RING - 1)];
+        const uint64_t kept = ~uniform64(s.rem);
+        const uint32_t k_off = s.k_off;
         if (kept) {
             if (count > (uint32_t)TILE_LIST_CAP) {
                 // dense rows are plain stores of the mask stage, not visible
@@ -596,7 +628,13 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
                 }
             }
         }
-        if (lane == 0) flag_store(&sm.stage[c & (RING - 1)].applied, (uint32_t)c + 1u);
+        if (lane == 0) flag_store(&sm.stage[(c + LAG) & (RING - 1)].app_lag, (uint32_t)(c + LAG) + 1u);
+        // the outputs: off the resolver's path
+        if (lane == 0) a.kept[c] = kept;
+        if (!a.grouped && ((kept >> lane) & 1ull)) {
+            const uint64_t below = (1ull << lane) - 1ull;
+            a.keep_out[k_off + (uint32_t)__popcll(kept & below)] = (int64_t)e.ord;
+        }
         if (c + A < W) load_entries<FUSED>(a, c + A, rounds_of(count_next), e);
         count = count_next;
     }
@@ -611,13 +649,15 @@ __device__ __forceinline__ void sweep_body(const SweepArgs &a, uint64_t *removed
     const int W = a.words, n = a.n;
     const int stride = a.grouped ? a.ctrl->band_stride : a.mstride;
 
-    for (int w = tid; w < W + NEAR_TILES; w += NT) removed[w] = 0ull;
+    // rows past n start out removed, so no chunk ever keeps them
+    for (int w = tid; w < W + NEAR_TILES; w += NT) removed[w] = w == W - 1 ? ~rows_valid(w, n) : 0ull;
     if (tid < RING) {
         sm.stage[tid].ready = 0u;
-        sm.stage[tid].applied = 0u;
+        // chunks below LAG wait for no earlier chunk
+        sm.stage[tid].app_lag = tid < LAG ? (uint32_t)tid + 1u : 0u;
     }
     if (tid == 0) {
-        sm.resolved = 0u;
+        sm.resolved[0] = 0u;
         sm.abort = 0u;
         sm.done_upto = 0u;
     }
@@ -629,8 +669,7 @@ __device__ __forceinline__ void sweep_body(const SweepArgs &a, uint64_t *removed
     __syncthreads();
     if (sm.abort) return;
 
-    // kept bitmap = complement of removed, limited to existing boxes
-    for (int w = tid; w < W; w += NT) a.kept[w] = ~removed[w] & rows_valid(w, n);
+    // the appliers wrote the kept bitmap
     if (a.grouped) return;
     // one image: the appliers have written the output
     if (tid == 0) {
