@@ -159,6 +159,7 @@ struct SweepSmem {
     uint32_t kept_total;
     uint32_t abort;
     uint32_t done_upto;  // fused kernel: row tiles below this are known finished
+    uint32_t poller;     // fused kernel: 1 while a wave reads the mask's counters
 };
 
 // Hand-over flags.  Everything handed over between waves lives in LDS, and
@@ -218,33 +219,44 @@ __device__ __forceinline__ bool wait_flag(const uint32_t *flag, uint32_t target,
 // Fused kernel: wait until every mask work item of row tile c has finished
 // (each adds 64 to done[c] after its stores have completed).  Row tiles
 // finish roughly in order, so the waves share a frontier in LDS (every tile
-// below sm.done_upto has finished); a wave that must look reads the counts
-// of the 64 tiles from the frontier on, one per lane, and moves the frontier
-// past those that finished in a row.  Data a wave reads after learning of a
-// finished tile from the frontier is visible to it as well: the mask's
-// stores were visible device-wide before its count was raised.
+// below sm.done_upto has finished).  One wave at a time reads the counts of
+// the 64 tiles from the frontier on, one per lane, and moves the frontier
+// past those that finished in a row; the others watch the frontier.  (Device-
+// scope reads of the counters that the mask's waves are raising slow down the
+// mask waves on this wave's XCD, several times over when several waves poll.)
+// Data a wave reads after learning of a finished tile from the frontier is
+// visible to it as well: the mask's stores were visible device-wide before
+// its count was raised.
 __device__ __forceinline__ bool wait_tile_done(const SweepArgs &a, int c, SweepSmem &sm) {
     const int lane = threadIdx.x & 63;
     uint32_t spins = 0;
     for (;;) {
         const uint32_t base = flag_load(&sm.done_upto);
         if ((uint32_t)c < base) break;
-        const int t = (int)base + lane;
-        bool fin = false;
-        if (t < a.words) {
-            const uint32_t items = (64u << a.done_shift) * (uint32_t)(a.strip_groups - t / a.strip);
-            fin = __hip_atomic_load(&a.done[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-                  items;
-        }
-        const uint64_t m = __ballot(fin);
-        const uint32_t run = m == ~0ull ? 64u : (uint32_t)__builtin_ctzll(~m);
-        if (run) {
-            // every lane stores the same maximum: no lane-divergent region
+        // claim the polling role (every lane asks; the LDS grants one)
+        uint32_t expected = 0u;
+        const bool claimed = lane == 0 && __hip_atomic_compare_exchange_strong(
+                                              &sm.poller, &expected, 1u, __ATOMIC_RELAXED,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__ballot(claimed)) {
+            const int t = (int)flag_load(&sm.done_upto) + lane;
+            bool fin = false;
+            if (t < a.words) {
+                const uint32_t items =
+                    (64u << a.done_shift) * (uint32_t)(a.strip_groups - t / a.strip);
+                fin = __hip_atomic_load(&a.done[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                      items;
+            }
+            const uint64_t m = __ballot(fin);
+            const uint32_t run = m == ~0ull ? 64u : (uint32_t)__builtin_ctzll(~m);
+            // every lane stores the same values: no lane-divergent region
             // inside a loop whose exit the wave takes together
-            __hip_atomic_fetch_max(&sm.done_upto, base + run, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-            if ((uint32_t)c < base + run) break;
-            continue;
+            if (run)
+                __hip_atomic_fetch_max(&sm.done_upto, (uint32_t)(t - lane) + run, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            flag_store(&sm.poller, 0u);
+            if ((uint32_t)c < (uint32_t)(t - lane) + run) break;
+            if (run) continue;
         }
         if (flag_load(&sm.abort)) return false;
         if (++spins > SPIN_LIMIT) {
@@ -660,6 +672,7 @@ __device__ __forceinline__ void sweep_body(const SweepArgs &a, uint64_t *removed
         sm.resolved[0] = 0u;
         sm.abort = 0u;
         sm.done_upto = 0u;
+        sm.poller = 0u;
     }
     __syncthreads();
 
