@@ -45,8 +45,9 @@ constexpr int STRIP_GROUPED = 4;
 constexpr int RADIX_THREADS = 256;
 constexpr int RADIX_E = 16;
 constexpr int RADIX_TILE = RADIX_THREADS * RADIX_E;
-// One image of at most this many boxes is sorted by one workgroup.
-constexpr int SMALL_SORT_MAX = 8192;
+// One image of at most this many boxes is sorted by ranking: every box
+// counts the boxes that precede it (the keys of all boxes fit in LDS).
+constexpr int RANK_SORT_MAX = 16384;
 // 8-bit digit passes: 4 on the score key, then (grouped input) 4 on the
 // class key and 4 on the image.
 constexpr int RADIX_PASSES = 12;

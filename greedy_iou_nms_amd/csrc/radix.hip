@@ -12,8 +12,10 @@
 // order inside; the order after the score passes is kept as the plain score
 // order for the final compaction.
 //
-//   small_sort_kernel   one image of at most 8192 boxes: everything below in
-//                       one workgroup, the keys kept in LDS between passes.
+//   rank_sort_kernel    one image of at most 16384 boxes: every box's sorted
+//                       position counted directly (n^2 comparisons), the
+//                       sorted-box gather, the input checks and the per-call
+//                       initialisation, in one launch.
 //   radix_keys_kernel   one workgroup per tile of 4096 boxes: the keys (score;
 //                       grouped: class key and image of every box), each
 //                       tile's histograms of every digit (digit counts do not
@@ -246,143 +248,149 @@ __device__ __forceinline__ void scan256(const uint32_t *v, uint32_t *out) {
     out[4 * lane + 3] = ex + h0 + h1 + h2;
 }
 
-// ---------------------------------------------------------------- small sort
+// ---------------------------------------------------------------- rank sort
 
-// One image of at most SMALL_SORT_MAX boxes: keys, the four score passes,
-// the sorted-box gather and the per-call initialisation in one workgroup,
-// with the keys held in LDS between passes.  This replaces five launches
-// (and their look-back round trips) with one.  The passes rank exactly as
-// radix_pass_kernel does (waves, then elements, then lanes walk the
-// positions in order), so the order is the same stable one.
-// SE elements per thread: the smallest power of two with 1024 SE >= n, so
-// that small inputs do not rank empty slots.
-constexpr int SMALL_THREADS = 1024;
-constexpr int SMALL_WAVES = SMALL_THREADS / 64;
-static_assert(SMALL_SORT_MAX == 8 * SMALL_THREADS, "small sort tiling");
+// One image of at most RANK_SORT_MAX boxes, in one launch.  The stable order
+// puts box j before box i iff s_j > s_i, or s_j == s_i and j < i (float
+// comparisons order scores exactly as the radix keys do: -0 equals +0), so
+// box i's sorted position is the number of boxes j that satisfy that.  For j
+// in an earlier 64-box chunk than i this is s_j >= s_i, in a later chunk
+// s_j > s_i, and in i's own chunk the index decides ties.  A NaN score is an
+// error, but the positions must still be a permutation (later kernels index
+// with them): NaN counts as -infinity.  Comparing a raw s_j with the
+// sanitised s_i gives that already, except that for a box whose s_i is
+// -infinity (or NaN) every box of an earlier chunk precedes it, NaN or not.  One workgroup per chunk; its waves split the chunks among
+// them, each reading the scores of a chunk with scalar loads (the same
+// values for every lane) and comparing them with the lane's own score; wave
+// 0 adds the waves' counts and writes the sorted order, boxes and areas.
+// n^2 comparisons cost less than four passes over few tiles while n is
+// small.  An extra workgroup checks every score and box and writes the
+// control block beside them; every workgroup takes a share of the per-call
+// initialisation.
+constexpr int RANK_THREADS = 1024;
+constexpr int RANK_WAVES = RANK_THREADS / 64;
+constexpr int RANK_PER_THREAD = RANK_SORT_MAX / RANK_THREADS;  // inputs each thread checks
+static_assert(RANK_PER_THREAD * RANK_THREADS == RANK_SORT_MAX && RANK_PER_THREAD % 4 == 0,
+              "rank sort tiling");
 
-struct SmallSortSmem {
-    uint32_t wcnt[SMALL_WAVES][256];  // per wave: digit counts, then their prefix
-    uint32_t tot[256];
-    uint32_t tbase[256];
-    uint32_t key[SMALL_SORT_MAX];
-    uint32_t val[SMALL_SORT_MAX];
-    uint32_t err;
-    uint32_t unordered;
-};
+// Scores read through the constant address space, which lets the compiler
+// use scalar loads where the address is the same for every lane.
+typedef const __attribute__((address_space(4))) float *const_scores_t;
 
-template <int SE>
-__global__ __launch_bounds__(SMALL_THREADS) void small_sort_kernel(KeysArgs a,
-                                                                   const float4 *boxes) {
-    __shared__ SmallSortSmem sm;
-    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+__global__ __launch_bounds__(RANK_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void rank_sort_kernel(KeysArgs a,
+                                                                 const float4 *boxes) {
+    __shared__ uint32_t part[RANK_WAVES][64];
+    __shared__ uint32_t err_sh, unordered_sh;
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(wave_id());
     const Work &w = a.w;
-    if (tid == 0) {
-        sm.err = 0u;
-        sm.unordered = 0u;
-    }
-    const int base = wave * 64 * SE + lane;  // position of element 0 of this lane
-    uint32_t k[SE], v[SE], rk[SE];
-    uint32_t err = 0;
-#pragma unroll
-    for (int e = 0; e < SE; ++e) {
-        const int i = base + e * 64;
-        const float sc = i < a.n ? a.scores[i] : 0.0f;
-        if (sc != sc) err |= ERR_NONFINITE;
-        k[e] = score_key(sc);
-        v[e] = (uint32_t)i;
-    }
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 8 * pass;
-        for (int j = lane; j < 256; j += 64) sm.wcnt[wave][j] = 0u;
-#pragma unroll
-        for (int e = 0; e < SE; ++e) {
-            const bool valid = base + e * 64 < a.n;
-            const uint32_t d = (k[e] >> shift) & 255u;
-            uint64_t peers = __ballot(valid);
-#pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const bool bit = (d >> b) & 1u;
-                const uint64_t m = __ballot(bit);
-                peers &= bit ? m : ~m;
-            }
-            const uint32_t r_in = __builtin_amdgcn_mbcnt_hi(
-                (uint32_t)(peers >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
-            const uint32_t before = sm.wcnt[wave][d];
-            rk[e] = before + r_in;
-            // the lowest lane of each digit group advances the wave's count;
-            // the read above precedes this write in the wave's LDS order
-            if (valid && r_in == 0) sm.wcnt[wave][d] = before + (uint32_t)__popcll(peers);
+    const int n = a.n;
+    per_call_init<false>(a, blockIdx.x * RANK_THREADS + tid, gridDim.x * RANK_THREADS);
+
+    if (blockIdx.x == 0) {
+        // Workgroup 0 checks the whole input (the sort-only test export
+        // passes no boxes), every load in flight together, and writes the
+        // control block.
+        if (tid == 0) {
+            err_sh = 0u;
+            unordered_sh = 0u;
         }
-        __syncthreads();
-        if (tid < 256) {
-            uint32_t run = 0;
+        // Loads from clamped indices, with no branch around them, so that a
+        // round's loads are all in flight together; entries past n are then
+        // ignored.
+        uint32_t err = 0;
+        bool finite = true, ordered = true;
+        constexpr int H = RANK_PER_THREAD / 4;  // four rounds keep the registers few
+        if (n > 0) {
 #pragma unroll
-            for (int wv = 0; wv < SMALL_WAVES; ++wv) {
-                const uint32_t c = sm.wcnt[wv][tid];
-                sm.wcnt[wv][tid] = run;
-                run += c;
-            }
-            sm.tot[tid] = run;
-        }
-        __syncthreads();
-        if (wave == 0) scan256(sm.tot, sm.tbase);
-        __syncthreads();
+            for (int h = 0; h < 4; ++h) {
+                float sv[H];
+                float4 bb[H];
 #pragma unroll
-        for (int e = 0; e < SE; ++e) {
-            if (base + e * 64 < a.n) {
-                const uint32_t d = (k[e] >> shift) & 255u;
-                const uint32_t slot = sm.tbase[d] + sm.wcnt[wave][d] + rk[e];
-                sm.key[slot] = k[e];
-                sm.val[slot] = v[e];
+                for (int e = 0; e < H; ++e) {
+                    const int j = min(tid + (h * H + e) * RANK_THREADS, n - 1);
+                    sv[e] = a.scores[j];
+                    if (boxes != nullptr) bb[e] = boxes[j];
+                }
+#pragma unroll
+                for (int e = 0; e < H; ++e) {
+                    if (tid + (h * H + e) * RANK_THREADS >= n) continue;
+                    if (sv[e] != sv[e]) err |= ERR_NONFINITE;
+                    if (boxes == nullptr) continue;
+                    const float4 b = bb[e];
+                    finite = finite && isfinite(b.x) && isfinite(b.y) && isfinite(b.z) &&
+                             isfinite(b.w);
+                    const float ar = (b.z - b.x) * (b.w - b.y);
+                    ordered = ordered && b.x < b.z && b.y < b.w && ar > 0.0f && ar < INFINITY;
+                }
             }
         }
         __syncthreads();
+        if (!finite) err |= ERR_NONFINITE;
+        if (err) atomicOr(&err_sh, err);
+        if (!ordered) atomicOr(&unordered_sh, 1u);
+        __syncthreads();
+        if (tid == 0) {
+            Ctrl *c = w.ctrl;
+            c->error = err_sh;
+            c->flags = unordered_sh ? 0u : FLAG_ORDERED_BOXES;
+            c->count = 0;
+            c->num_items = item_base_full(a.words, a.words, a.strip);
+            c->band_stride = a.mstride;
+            c->num_segments = 1;
+            c->sweep_done = 0u;
+        }
+        return;
+    }
+
+    // Workgroup 1 + k ranks boxes 64 k .. 64 k + 63.
+    const int chunks = (n + 63) >> 6;
+    const int chunk = blockIdx.x - 1;
+    const int i = 64 * chunk + lane;
+    const const_scores_t sc = (const_scores_t)a.scores;
+    const float s_raw = i < n ? a.scores[i] : 0.0f;
+    const float si = s_raw != s_raw ? -INFINITY : s_raw;
+    // the box wave 0 will place, loaded now
+    const float4 bi = wave == 0 && boxes != nullptr && i < n ? boxes[i]
+                                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t cnt_early = 0, cnt = 0, early_chunks = 0;
+    for (int c = wave; c < chunks; c += RANK_WAVES) {
+        const const_scores_t sp = sc + 64 * c;
+        const int len = min(64, n - 64 * c);
+        if (c != chunk && len == 64) {
+            if (c < chunk) {
+                ++early_chunks;
 #pragma unroll
-        for (int e = 0; e < SE; ++e) {
-            const int j = base + e * 64;
-            if (j < a.n) {
-                k[e] = sm.key[j];
-                v[e] = sm.val[j];
+                for (int t = 0; t < 64; ++t) cnt_early += (uint32_t)(sp[t] >= si);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 64; ++t) cnt += (uint32_t)(sp[t] > si);
+            }
+        } else {
+            // this workgroup's own chunk, or the last, partial one (never
+            // an earlier one): lane t holds score 64 c + t
+            float mine = lane < len ? a.scores[64 * c + lane] : 0.0f;
+            if (mine != mine) mine = -INFINITY;
+#pragma unroll 1
+            for (int t = 0; t < len; ++t) {
+                const float sj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), t));
+                const bool before = c > chunk ? sj > si : (sj > si || (sj == si && t < lane));
+                cnt += (uint32_t)before;
             }
         }
-        __syncthreads();
     }
-    // sorted position base + 64 e holds input index v[e]: the order and
-    // (when boxes are given: the sort-only test export passes none) the
-    // sorted boxes and their areas, all box loads issued before any store
-    float4 b[SE];
-#pragma unroll
-    for (int e = 0; e < SE; ++e)
-        b[e] = boxes != nullptr && base + e * 64 < a.n ? boxes[v[e]]
-                                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-    bool finite = true, ordered = true;
-#pragma unroll
-    for (int e = 0; e < SE; ++e) {
-        const int j = base + e * 64;
-        if (j >= a.n) continue;
-        w.order[j] = (int32_t)v[e];
-        if (boxes == nullptr) continue;
-        const float4 bj = b[e];
-        finite = finite && isfinite(bj.x) && isfinite(bj.y) && isfinite(bj.z) && isfinite(bj.w);
-        const float ar = (bj.z - bj.x) * (bj.w - bj.y);
-        ordered = ordered && bj.x < bj.z && bj.y < bj.w && ar > 0.0f && ar < INFINITY;
-        w.sb[j] = bj;
-        w.area[j] = ar;
-    }
-    if (!finite) err |= ERR_NONFINITE;
-    if (err) atomicOr(&sm.err, err);
-    if (!ordered) atomicOr(&sm.unordered, 1u);
-    per_call_init<false>(a, tid, SMALL_THREADS);
+    cnt += si == -INFINITY ? 64u * early_chunks : cnt_early;
+    part[wave][lane] = cnt;
     __syncthreads();
-    if (tid == 0) {
-        Ctrl *c = w.ctrl;
-        c->error = sm.err;
-        c->flags = sm.unordered ? 0u : FLAG_ORDERED_BOXES;
-        c->count = 0;
-        c->num_items = item_base_full(a.words, a.words, a.strip);
-        c->band_stride = a.mstride;
-        c->num_segments = 1;
-        c->sweep_done = 0u;
+    if (wave == 0 && i < n) {
+        uint32_t r = 0;
+#pragma unroll
+        for (int v = 0; v < RANK_WAVES; ++v) r += part[v][lane];
+        w.order[r] = i;
+        if (boxes != nullptr) {
+            w.sb[r] = bi;
+            w.area[r] = (bi.z - bi.x) * (bi.w - bi.y);
+        }
     }
 }
 
@@ -865,17 +873,10 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
     ka.tiles = tiles;
     ka.grouped = P.grouped ? 1 : 0;
     ka.w = w;
-    if (!P.grouped && P.n <= SMALL_SORT_MAX) {
+    if (!P.grouped && P.n <= RANK_SORT_MAX) {
         const float4 *bx = reinterpret_cast<const float4 *>(P.boxes);
-        const dim3 g(1), b(SMALL_THREADS);
-        if (P.n <= SMALL_THREADS)
-            hipLaunchKernelGGL(small_sort_kernel<1>, g, b, 0, stream, ka, bx);
-        else if (P.n <= 2 * SMALL_THREADS)
-            hipLaunchKernelGGL(small_sort_kernel<2>, g, b, 0, stream, ka, bx);
-        else if (P.n <= 4 * SMALL_THREADS)
-            hipLaunchKernelGGL(small_sort_kernel<4>, g, b, 0, stream, ka, bx);
-        else
-            hipLaunchKernelGGL(small_sort_kernel<8>, g, b, 0, stream, ka, bx);
+        hipLaunchKernelGGL(rank_sort_kernel, dim3((unsigned)L.words + 1u), dim3(RANK_THREADS), 0,
+                           stream, ka, bx);
         return hipGetLastError();
     }
     if (P.grouped)

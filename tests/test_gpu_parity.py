@@ -106,10 +106,10 @@ def test_degenerate_boxes_take_the_division_path():
     _check(w)
 
 
-@pytest.mark.parametrize("n", [8192, 8193])
+@pytest.mark.parametrize("n", [8192, 8193, 16384, 16385])
 def test_sort_boundary_sizes_with_ties(n):
-    # the largest one-workgroup sort and the smallest multi-workgroup one,
-    # with few score levels so that the stable order decides
+    # around the largest ranking sort and the smallest radix sort, with few
+    # score levels so that the stable order decides
     w = workloads.random_small(800 + n, n, canvas=4.0 * np.sqrt(n) + 30, score_levels=8)
     _check(w)
 

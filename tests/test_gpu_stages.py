@@ -3,6 +3,7 @@ the race and state checks of the LeetCUDA page (bugs 1 and 2): repeated runs
 must be identical, and the result must not depend on what the workspace held
 before the call."""
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -20,10 +21,10 @@ def _g():
 
 # ---------------------------------------------------------------- sort
 
-# one-workgroup sort up to 8192 (1, 2, 4 or 8 keys per thread), multi-workgroup
-# from 8193
-@pytest.mark.parametrize("n", [1, 2, 100, 1024, 1025, 2048, 2049, 4096, 4097, 8191, 8192, 8193,
-                               65536])
+# ranking sort up to 16384 (one workgroup per 64 boxes; sizes around the
+# 64-box chunks), radix passes over tiles of 4096 from 16385
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 100, 1024, 1025, 2048, 2049, 4096, 4097, 8191,
+                               8192, 8193, 16383, 16384, 16385, 65536])
 def test_sort_order_is_stable_descending(n):
     dev = device()
     rng = np.random.default_rng(n)
@@ -35,6 +36,31 @@ def test_sort_order_is_stable_descending(n):
     want = np.argsort(-scores, kind="stable")
     np.testing.assert_array_equal(order.cpu().numpy(), want)
     np.testing.assert_array_equal(sorder.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("n", [100, 1000, 8192, 16384, 16385])
+def test_sort_with_nan_scores_reports_and_still_permutes(n):
+    # A NaN score is an error, but the kernels after the sort index memory
+    # with the sorted order, so it must still be a permutation of 0 .. n-1.
+    import ctypes
+    g = _g()
+    dev = device()
+    rng = np.random.default_rng(7 + n)
+    scores = rng.random(n).astype(np.float32)
+    scores[rng.integers(0, n, max(1, n // 20))] = np.nan
+    scores[rng.integers(0, n, max(1, n // 20))] = -np.inf
+    scores[rng.integers(0, n, max(1, n // 50))] = np.float32(-np.nan)
+    s = to_dev(scores, dev)
+    note("sort with NaN n=%d" % n)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        buf = torch.empty(g.workspace_size(n, 0, False), dtype=torch.uint8, device=dev)
+        order = torch.full((n,), -1, dtype=torch.int32, device=dev)
+        st = g._lib.nms_debug_order(g._ptr(s), n, None, None, 0, g._ptr(order), None,
+                                    g._ptr(buf), buf.numel(), ctypes.c_void_p(stream))
+        torch.cuda.synchronize(dev)
+    assert st == 3  # NMS_NONFINITE_INPUT
+    np.testing.assert_array_equal(np.sort(order.cpu().numpy()), np.arange(n))
 
 
 def test_sort_order_extreme_scores():
