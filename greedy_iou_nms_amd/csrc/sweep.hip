@@ -111,8 +111,12 @@ constexpr int APPLIERS = NWAVES - 1;
 // Bounded waits: about a second of polling before a wait gives up.
 constexpr uint32_t SPIN_LIMIT = 1u << 23;
 
-// Entries of a row tile's list held in registers: RMAX rounds of 64.
-constexpr int RMAX = 16;
+// Entries of a row tile's list held in registers: rounds of 64.  The plain
+// sweep holds the whole list (its one workgroup has registers to spare); the
+// fused sweep shares its kernel's register budget with the mask and holds
+// half, reading the rest when the kept set is known.
+template <bool FUSED>
+constexpr int rmax() { return FUSED ? 16 : TILE_LIST_CAP / 64; }
 
 constexpr int NEAR = NEAR_TILES;
 static_assert(NEAR >= 2, "the resolver carries the words for the next two tiles in registers");
@@ -308,9 +312,10 @@ __device__ __forceinline__ void stage_level1(const Level1 &l, int c, SweepSmem &
 }
 
 // The tile's list entries, round i holding entry 64 i + lane.
+template <int R>
 struct Entries {
-    uint32_t wk[RMAX];
-    uint64_t val[RMAX];
+    uint32_t wk[R];
+    uint64_t val[R];
     int32_t ord;  // order[64c + lane]: input index of the lane's box
 };
 
@@ -320,12 +325,13 @@ __device__ __forceinline__ int rounds_of(uint32_t count) {
 }
 
 template <bool FUSED>
-__device__ __forceinline__ void load_entries(const SweepArgs &a, int c, int rounds, Entries &e) {
+__device__ __forceinline__ void load_entries(const SweepArgs &a, int c, int rounds,
+                                             Entries<rmax<FUSED>()> &e) {
     const size_t base = (size_t)c * TILE_LIST_CAP + (threadIdx.x & 63);
     // written by the sort, before this launch: a plain load
     e.ord = a.order[64 * c + (threadIdx.x & 63)];
 #pragma unroll
-    for (int i = 0; i < RMAX; ++i) {
+    for (int i = 0; i < rmax<FUSED>(); ++i) {
         if (i < rounds) {
             e.wk[i] = get<FUSED>(&a.tent_wk[base + 64 * i]);
             e.val[i] = get<FUSED>(&a.tent_val[base + 64 * i]);
@@ -342,14 +348,14 @@ __device__ __forceinline__ void apply_entry(uint32_t wk, uint64_t val, bool live
 // Apply rounds I, I+1, ... < rounds of the register-held entries.  Nested
 // uniform branches (rather than a loop) keep every register index constant
 // and skip the rounds that do not exist.
-template <int I>
-__device__ __forceinline__ void apply_rounds(const Entries &e, int rounds, uint32_t count,
+template <int I, int R>
+__device__ __forceinline__ void apply_rounds(const Entries<R> &e, int rounds, uint32_t count,
                                              uint64_t kept, int c, uint64_t *removed) {
-    if constexpr (I < RMAX) {
+    if constexpr (I < R) {
         if (I < rounds) {
             const uint32_t lane = threadIdx.x & 63;
             apply_entry(e.wk[I], e.val[I], 64u * I + lane < count, kept, c, removed);
-            apply_rounds<I + 1>(e, rounds, count, kept, c, removed);
+            apply_rounds<I + 1, R>(e, rounds, count, kept, c, removed);
         }
     }
 }
@@ -594,7 +600,7 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
     int c = q - 1;
     if (c >= W) return;
     Level1 l1;
-    Entries e;
+    Entries<rmax<FUSED>()> e;
     // prologue: chunk c staged, its entries and chunk c + A's first level issued
     if (!load_level1<FUSED>(a, c, l1, sm)) return;
     wait_loads();
@@ -630,10 +636,10 @@ __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, 
                 apply_dense(a, c, stride, kept, removed);
             } else {
                 const int rounds = rounds_of(count);
-                apply_rounds<0>(e, rounds, count, kept, c, removed);
+                apply_rounds<0, rmax<FUSED>()>(e, rounds, count, kept, c, removed);
                 // rounds beyond the registers: load and apply them now
                 const size_t base = (size_t)c * TILE_LIST_CAP + lane;
-                for (int i = RMAX; i < rounds; ++i) {
+                for (int i = rmax<FUSED>(); i < rounds; ++i) {
                     const uint32_t wk = get<FUSED>(&a.tent_wk[base + 64 * i]);
                     const uint64_t val = get<FUSED>(&a.tent_val[base + 64 * i]);
                     apply_entry(wk, val, (uint32_t)(64 * i + lane) < count, kept, c, removed);
