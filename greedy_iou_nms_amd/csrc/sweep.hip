@@ -415,10 +415,14 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f);
 
 // Resolver state carried from chunk to chunk in scalar registers.
 struct ResolverState {
-    uint64_t carry1;  // kept rows' words for tile c (chunks c - 1 and c - 2)
-    uint64_t carry2;  // kept rows' words for tile c + 1 (chunk c - 1)
+    uint64_t carry;   // kept rows' words for tile c (chunk c - 1)
     bool dead;        // a wait gave up: the remaining chunks are skipped
     uint32_t total;   // boxes kept before chunk c
+    // 0, in a register the compiler cannot see into: added to the address
+    // of the kept rows' ORs into LDS, which then go out as one instruction
+    // from every lane (the LDS unit combines the lanes) instead of a loop
+    // over the lanes that the compiler makes of an atomic with one address
+    int zero;
 };
 
 // Settle chunk c from its staged batch cur and its word batch wb, after
@@ -426,12 +430,11 @@ struct ResolverState {
 // batch (into ahead).
 //
 // Word c + 1 is read before chunk c is settled.  That is safe because chunk
-// c's and chunk c - 1's words for it travel in registers (carry2, then
-// carry1), the words of chunks c - 2 and c - 3 for it were ORed into LDS
-// (atomics) before the read is issued, and the far words of chunks up to
-// c + 1 - LAG are in once the flag read with it says so: the flags of the
-// chunks before have been checked (or waited for) before this read is
-// issued.  Reading ahead keeps LDS latency, and this chunk's own LDS
+// c's words for it travel in registers (carry), the words of chunks c - 1 ..
+// c + 1 - NEAR for it were ORed into LDS (atomics) before the read is
+// issued, and the far words of chunks up to c + 1 - LAG are in once the flag
+// read with it says so: the flags of the chunks before have been checked (or
+// waited for) before this read is issued.  Reading ahead keeps LDS latency, and this chunk's own LDS
 // writes, off the path from one chunk to the next.
 template <bool FUSED>
 __device__ __forceinline__ void resolve_one(const SweepArgs &a, uint64_t *removed, SweepSmem &sm,
@@ -458,7 +461,7 @@ __device__ __forceinline__ void resolve_one(const SweepArgs &a, uint64_t *remove
         wait_lds();
     }
     // rows past n are marked removed from the start; their words are zero
-    uint64_t rem = uniform64(wb.rem) | st.carry1;
+    uint64_t rem = uniform64(wb.rem) | st.carry;
     // Issued for every chunk, also past the last one (removed[] has NEAR >= 2
     // spare words and the staging slots are a ring), so that the number of
     // LDS accesses in flight is the same on every path through the loop.
@@ -477,21 +480,19 @@ __device__ __forceinline__ void resolve_one(const SweepArgs &a, uint64_t *remove
         } while (cand);
     }
     const uint64_t kept = ~rem;
-    uint64_t c1 = st.carry2, c2 = 0ull;
+    uint64_t c1 = 0ull;
     if (kept & uniform64(cur.nzn)) {
         const bool mine = (kept >> lane) & 1ull;
-        // wave-wide ORs only where some kept row has a nonzero word
-        if (__ballot(mine && cur.nw[1] != 0ull)) c1 |= wave_or64(mine ? cur.nw[1] : 0ull);
-        if (__ballot(mine && cur.nw[2] != 0ull)) c2 = wave_or64(mine ? cur.nw[2] : 0ull);
+        // a wave-wide OR only where some kept row has a nonzero word
+        if (__ballot(mine && cur.nw[1] != 0ull)) c1 = wave_or64(mine ? cur.nw[1] : 0ull);
         if (mine) {
             // removed has NEAR spare words past the end for the last chunks
 #pragma unroll
-            for (int j = 3; j <= NEAR; ++j)
-                if (cur.nw[j] != 0ull) atomicOr(&removed[c + j], cur.nw[j]);
+            for (int j = 2; j <= NEAR; ++j)
+                if (cur.nw[j] != 0ull) atomicOr(&removed[c + j + st.zero], cur.nw[j]);
         }
     }
-    st.carry1 = c1;
-    st.carry2 = c2;
+    st.carry = c1;
     Settled &out = sm.settled[lane == 0 ? (c & (RING - 1)) : RING + lane];
     out.rem = rem;
     out.k_off = st.total;
@@ -502,17 +503,17 @@ __device__ __forceinline__ void resolve_one(const SweepArgs &a, uint64_t *remove
 // Resolver: settle the chunks in order.  A chunk in which no surviving row
 // has a nonzero diagonal word, and no kept row a nonzero word for the next
 // NEAR tiles (most chunks, when overlaps are sparse), costs only its flags,
-// summary mask and removed word.  Otherwise the kept rows' words for tiles
-// c + 1 and c + 2 are ORed across the wave into registers, those for tiles
-// c + 3 .. c + NEAR into LDS with atomics.
+// summary mask and removed word.  Otherwise the kept rows' words for tile
+// c + 1 are ORed across the wave into a register, those for tiles c + 2 ..
+// c + NEAR into LDS with atomics.
 template <bool FUSED>
 __device__ void resolve_chunks(const SweepArgs &a, uint64_t *removed, SweepSmem &sm) {
     const int W = a.words;
     ResolverState st;
-    st.carry1 = 0ull;
-    st.carry2 = 0ull;
+    st.carry = 0ull;
     st.dead = false;
     st.total = 0u;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(st.zero));
     StagedBatch b0, b1, b2;
     WordBatch wb;
     read_staged(0, sm, b0);
