@@ -129,12 +129,15 @@ MaskArgs make_mask_args(const Problem &P, const Layout &L, int64_t slots) {
     a.exact_ok = th.exact_ok ? 1 : 0;
     a.pinf = INFINITY;
     a.ninf = -INFINITY;
-    // Too few pairs to give every slot one: split them into up to 4 groups
-    // of rows.  Grouped input has short bands, and the bound here counts
-    // full rows, so its pairs are always split.
+    // Too few pairs to give every slot one: split them into up to 16 groups
+    // of rows while the items still fit the resident waves.  An item costs
+    // a few memory round trips whatever its rows, and items of one row tile
+    // share its list's counter, so items past the slots cost more than they
+    // save.  Grouped input has short bands, and the bound here counts full
+    // rows, so its pairs are always split.
     const int64_t pairs = mask_items_upper_bound(P, L);
     a.qshift = 0;
-    while (a.qshift < 2 && (pairs << a.qshift) < slots) ++a.qshift;
+    while (a.qshift < 4 && (pairs << (a.qshift + 1)) <= slots) ++a.qshift;
     if (P.grouped) a.qshift = 2;
     return a;
 }
