@@ -273,6 +273,8 @@ def main():
                     help="time only the N=65536 workload as the library runs it (for profiler runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run device copies of BYTES bytes (counter calibration)")
+    ap.add_argument("--trace-config", type=int, default=0, metavar="K",
+                    help="only time workload K (1..5) as the library runs it (for profiler runs)")
     ap.add_argument("--valu-rates", action="store_true",
                     help="only run the VALU issue-rate probe built next to the library")
     args = ap.parse_args()
@@ -289,6 +291,13 @@ def main():
         return
 
     import workloads
+
+    if args.trace_config:
+        wt = workloads.config(args.trace_config, seed=0)
+        rt = _measure(wt, args.steps, args.warmup)
+        print(json.dumps({"workload": wt.name, "n": wt.n, "steps": args.steps,
+                          "ms_per_call": rt["call_ms"], "stage_ms": rt["stage_ms"]}))
+        return
 
     w = workloads.config(5, seed=0)
     r = _measure(w, args.steps, args.warmup)
