@@ -161,16 +161,36 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
     const int rpi = 64 >> a.qshift;
     const int pair = item >> a.qshift;
     const int k_lo = (item & ((1 << a.qshift) - 1)) * rpi;
-    // row tile of this pair: the largest r with item_base[r] <= pair
+    // Row tile of this pair: the largest r whose first pair is <= pair.  One
+    // image: every row tile covers all strips from its own to the last, so
+    // the first pair of row tile r has a closed form (a triangle of strips)
+    // and the search is register arithmetic; grouped input searches the
+    // plan's table.
     int lo = 0, hi = a.words - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (m_.item_base[mid] <= pair) lo = mid;
-        else hi = mid - 1;
+    int32_t base_r;
+    if (!GROUPED) {
+        const int G = (a.words + S - 1) / S;
+        auto first_pair = [&](int rr) {
+            const int g = rr / S, u = rr % S;
+            return S * (g * G - g * (g - 1) / 2) + u * (G - g);
+        };
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (first_pair(mid) <= pair) lo = mid;
+            else hi = mid - 1;
+        }
+        base_r = first_pair(lo);
+    } else {
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (m_.item_base[mid] <= pair) lo = mid;
+            else hi = mid - 1;
+        }
+        base_r = m_.item_base[lo];
     }
     const int r = lo;
     const int s0 = r / S;
-    const int c0 = (s0 + (pair - m_.item_base[r])) * S;
+    const int c0 = (s0 + (pair - base_r)) * S;
     const int cend = m_.tile_cend[r];
     const int p0 = 64 * r;
     const int tile_rows = a.n - p0 < 64 ? a.n - p0 : 64;

@@ -125,3 +125,17 @@ def test_above_fusion_limit_uses_separate_launches():
     fused, sep, _, _, _ = _both(w)
     np.testing.assert_array_equal(fused, want)
     np.testing.assert_array_equal(sep, want)
+
+
+def test_largest_accepted_size():
+    # NMS_MAX_BOXES = 512000: 8000 row tiles, the plain sweep's removed
+    # bitmap at its largest (64 KB of LDS beside the staging ring)
+    n = 512000
+    boxes, scores, want = _pairs_on_a_grid(n, 5)
+    w = workloads.Workload("pairs", boxes, scores, 0.5)
+    note("largest size n=%d" % n)
+    import greedy_iou_nms_amd as g
+    dev = device()
+    got = g.nms(to_dev(boxes, dev), to_dev(scores, dev), 0.5).cpu().numpy()
+    np.testing.assert_array_equal(got, want)
+    del w
