@@ -113,10 +113,10 @@ constexpr uint32_t SPIN_LIMIT = 1u << 23;
 
 // Entries of a row tile's list held in registers: rounds of 64.  The plain
 // sweep holds the whole list (its one workgroup has registers to spare); the
-// fused sweep shares its kernel's register budget with the mask and holds
-// half, reading the rest when the kept set is known.
+// fused sweep shares its kernel's register budget with the mask and holds a
+// quarter, reading the rest when the kept set is known.
 template <bool FUSED>
-constexpr int rmax() { return FUSED ? 16 : TILE_LIST_CAP / 64; }
+constexpr int rmax() { return FUSED ? 8 : TILE_LIST_CAP / 64; }
 
 constexpr int NEAR = NEAR_TILES;
 static_assert(NEAR >= 2, "the resolver carries the words for the next two tiles in registers");
@@ -785,7 +785,7 @@ __global__ __launch_bounds__(GS_THREADS) void group_sweep_kernel(GroupSweepArgs 
 // computed.  No mask wave ever waits for anything, so every item completes
 // whatever the order in which workgroups are scheduled.
 // (two workgroups per compute unit, 4 waves per SIMD: at most 128 registers)
-__global__ __launch_bounds__(NT, 4) void mask_sweep_kernel(
+__global__ __launch_bounds__(NT, 6) void mask_sweep_kernel(
     maskcore::MaskArgs ma, const Ctrl *ctrl, const float4 *__restrict__ sb,
     const float *__restrict__ area, const int32_t *__restrict__ tile_cend,
     const int32_t *__restrict__ item_base, uint64_t *__restrict__ mask,
@@ -942,24 +942,26 @@ hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_
     return hipGetLastError();
 }
 
-// Workgroups of the fused kernel resident per CU, for the largest removed
-// bitmap the fused kernel takes (asked once per device: the query costs more
-// than a launch).  Two at most: the kernel's registers allow no more.
+// Workgroups of the fused kernel resident per CU for a given dynamic LDS
+// size (asked once per device and KiB of LDS: the query costs more than a
+// launch).  The registers allow three; a large removed bitmap leaves LDS for
+// two.
 int fused_blocks_per_cu(size_t lds) {
-    static int cached[64] = {0};
+    constexpr int BUCKETS = (FUSE_MAX_WORDS + NEAR_TILES) * 8 / 1024 + 1;
+    static int cached[64][BUCKETS] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cached[dev] == 0) {
-        const size_t worst = (size_t)(FUSE_MAX_WORDS + NEAR_TILES) * sizeof(uint64_t);
+    int b = (int)((lds + 1023) / 1024);
+    if (b >= BUCKETS) b = BUCKETS - 1;
+    if (cached[dev][b] == 0) {
         int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mask_sweep_kernel, NT, worst) !=
-                hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mask_sweep_kernel, NT,
+                                                         (size_t)b * 1024) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
-        cached[dev] = per_cu;
+        cached[dev][b] = per_cu;
     }
-    (void)lds;
-    return cached[dev];
+    return cached[dev][b];
 }
 
 hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
