@@ -147,6 +147,88 @@ __device__ __forceinline__ uint64_t column_valid(int c, int n) {
     return rem >= 64 ? ~0ull : ((1ull << rem) - 1ull);
 }
 
+// The rows k_lo .. k_hi - 1 of a work item in the division-free modes (t > 0,
+// ordered boxes).  With t > 0 a pair whose intersection is exactly 0 never
+// suppresses, and most pairs do not overlap, so each group of TG tiles first
+// asks whether any lane may overlap in any of them, and only then are the
+// tiles tested one by one; a tile where no lane may overlap is skipped, and
+// words that stay 0 need no write (they start at 0).  Two forms of the
+// question:
+//  * SIGN: a pair can overlap only if rx2 - cx1, cx2 - rx1, ry2 - cy1 and
+//    cy2 - ry1 are all >= 0 (when one is negative, the column box's clamped
+//    extent in that axis is empty).  Float subtraction of finite values keeps
+//    the sign of the exact difference (a tie gives +0), so the four
+//    differences ORed have a clear sign bit for every pair that may overlap;
+//    a tile that passes computes its intersection, union and test.  Four
+//    subtractions and three ORs per pair, all of the cheap issue class.
+//  * otherwise the intersections themselves, ORed (all are >= 0), and kept
+//    for the tiles that pass: more work per pair but a shorter chain of
+//    dependent instructions where a tile passes.
+// Outside the item that holds the diagonal tile every column tile lies after
+// the row's tile, and columns that take no part (tiles past the band, padding
+// past n) hold an empty box at 0, whose intersection is exactly 0, so no mask
+// is applied there.  In the diagonal item (DIAG) only columns after row k vote
+// in the diagonal tile, and tiles before the row's tile are masked out.
+template <int S, bool GROUPED, int MODE, bool DIAG, bool SIGN>
+__device__ __forceinline__ void fast_rows(const MaskArgs &a, const MaskPtrs &m_, int p0, int k_lo,
+                                          int k_hi, const float (&cx1)[S], const float (&cy1)[S],
+                                          const float (&cx2)[S], const float (&cy2)[S],
+                                          const float (&ca)[S], const uint32_t (&cg)[S],
+                                          const uint64_t (&tmask)[S], int t_diag,
+                                          uint32_t (&out_lo)[S], uint32_t (&out_hi)[S]) {
+    constexpr int TG = 4;
+    for (int k = k_lo; k < k_hi; ++k) {
+        const int p = p0 + k;
+        const float4 rb = m_.sb[p];
+        const float rx1 = rb.x;
+        const float ry1 = rb.y;
+        const float rx2 = rb.z;
+        const float ry2 = rb.w;
+        const float ra = m_.area[p];
+        const uint32_t rg = GROUPED ? m_.seg[p] : 0u;
+        const uint64_t dmask = k == 63 ? 0ull : (~0ull << (k + 1));
+#pragma unroll
+        for (int t0 = 0; t0 < S; t0 += TG) {
+            // SIGN: sign words of the differences; otherwise the intersections
+            uint32_t sgn[TG];
+            float inter[TG];
+            uint32_t acc = SIGN ? ~0u : 0u;
+#pragma unroll
+            for (int j = 0; j < TG; ++j) {
+                const int t = t0 + j;
+                if (SIGN) {
+                    sgn[j] = __float_as_uint(rx2 - cx1[t]) | __float_as_uint(cx2[t] - rx1) |
+                             __float_as_uint(ry2 - cy1[t]) | __float_as_uint(cy2[t] - ry1);
+                    acc &= sgn[j];
+                } else {
+                    inter[j] = intersection(rx1, ry1, rx2, ry2, cx1[t], cy1[t], cx2[t], cy2[t]);
+                    acc |= __float_as_uint(inter[j]);
+                }
+            }
+            // SIGN: the AND has a clear sign bit when some tile's OR has;
+            // otherwise the OR of non-negative intersections is 0 when all are
+            if (__ballot(SIGN ? (int32_t)acc >= 0 : acc != 0u) == 0ull) continue;
+#pragma unroll
+            for (int j = 0; j < TG; ++j) {
+                const int t = t0 + j;
+                uint64_t touch = __ballot(SIGN ? (int32_t)sgn[j] >= 0 : inter[j] > 0.0f);
+                if (DIAG) touch &= tmask[t] & ((t == t_diag) ? dmask : ~0ull);
+                if (touch) {
+                    const float in =
+                        SIGN ? intersection(rx1, ry1, rx2, ry2, cx1[t], cy1[t], cx2[t], cy2[t])
+                             : inter[j];
+                    const float uni = (ra + ca[t]) - in;
+                    bool pred = exceeds<MODE>(in, uni, a.t, a.mid);
+                    if (GROUPED) pred = pred && (cg[t] == rg);
+                    const uint64_t m = __ballot(pred) & touch;
+                    out_lo[t] = write_lane(out_lo[t], (uint32_t)m, k);
+                    out_hi[t] = write_lane(out_hi[t], (uint32_t)(m >> 32), k);
+                }
+            }
+        }
+    }
+}
+
 // One work item.  COHERENT (the fused mask + sweep kernel): the near words
 // and list entries, which the sweep reads while other items are still
 // running, are written with device-scope stores, and once they have all
@@ -225,18 +307,18 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
 #pragma unroll
     for (int t = 0; t < S; ++t) out_lo[t] = out_hi[t] = 0u;
 
-    for (int k = k_lo; k < k_hi; ++k) {
-        const int p = p0 + k;
-        const float4 rb = m_.sb[p];
-        const float rx1 = rb.x;
-        const float ry1 = rb.y;
-        const float rx2 = rb.z;
-        const float ry2 = rb.w;
-        const float ra = m_.area[p];
-        const uint32_t rg = GROUPED ? m_.seg[p] : 0u;
-        // in the diagonal tile only boxes after row k vote
-        const uint64_t dmask = k == 63 ? 0ull : (~0ull << (k + 1));
-        if (MODE == MODE_LITERAL) {
+    if (MODE == MODE_LITERAL) {
+        for (int k = k_lo; k < k_hi; ++k) {
+            const int p = p0 + k;
+            const float4 rb = m_.sb[p];
+            const float rx1 = rb.x;
+            const float ry1 = rb.y;
+            const float rx2 = rb.z;
+            const float ry2 = rb.w;
+            const float ra = m_.area[p];
+            const uint32_t rg = GROUPED ? m_.seg[p] : 0u;
+            // in the diagonal tile only boxes after row k vote
+            const uint64_t dmask = k == 63 ? 0ull : (~0ull << (k + 1));
 #pragma unroll
             for (int t = 0; t < S; ++t) {
                 const uint64_t live = tmask[t] & ((t == t_diag) ? dmask : ~0ull);
@@ -247,40 +329,28 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
                 out_lo[t] = write_lane(out_lo[t], (uint32_t)m, k);
                 out_hi[t] = write_lane(out_hi[t], (uint32_t)(m >> 32), k);
             }
+        }
+    } else {
+        // Few work items (qshift > 0) leave the GPU mostly idle and the item's
+        // latency decides: the intersections come first, as the pass test
+        // needs them anyway.  With many items the issue rate decides, and the
+        // sign test costs fewer and cheaper instructions.
+        const bool diag = t_diag >= 0 && t_diag < S;
+        if (a.qshift == 0) {
+            if (diag)
+                fast_rows<S, GROUPED, MODE, true, true>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2, cy2,
+                                                        ca, cg, tmask, t_diag, out_lo, out_hi);
+            else
+                fast_rows<S, GROUPED, MODE, false, true>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2, cy2,
+                                                         ca, cg, tmask, t_diag, out_lo, out_hi);
         } else {
-            // With t > 0 a pair without overlap (intersection exactly 0)
-            // never suppresses, and most pairs do not overlap.  The
-            // intersections of TG tiles are computed first; only when one of
-            // them is nonzero in some lane (their bit patterns ORed: all are
-            // non-negative) do that group's unions and threshold tests run.
-            // Words that stay 0 need no write (they start at 0).
-            constexpr int TG = 4;
-#pragma unroll
-            for (int t0 = 0; t0 < S; t0 += TG) {
-                float inter[TG];
-                uint32_t any = 0u;
-#pragma unroll
-                for (int j = 0; j < TG; ++j) {
-                    const int t = t0 + j;
-                    inter[j] = intersection(rx1, ry1, rx2, ry2, cx1[t], cy1[t], cx2[t], cy2[t]);
-                    any |= __float_as_uint(inter[j]);
-                }
-                if (__ballot(any != 0u) == 0ull) continue;
-#pragma unroll
-                for (int j = 0; j < TG; ++j) {
-                    const int t = t0 + j;
-                    const uint64_t live = tmask[t] & ((t == t_diag) ? dmask : ~0ull);
-                    const uint64_t touch = __ballot(inter[j] > 0.0f) & live;
-                    if (touch) {
-                        const float uni = (ra + ca[t]) - inter[j];
-                        bool pred = exceeds<MODE>(inter[j], uni, a.t, a.mid);
-                        if (GROUPED) pred = pred && (cg[t] == rg);
-                        const uint64_t m = __ballot(pred) & touch;
-                        out_lo[t] = write_lane(out_lo[t], (uint32_t)m, k);
-                        out_hi[t] = write_lane(out_hi[t], (uint32_t)(m >> 32), k);
-                    }
-                }
-            }
+            if (diag)
+                fast_rows<S, GROUPED, MODE, true, false>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2, cy2,
+                                                         ca, cg, tmask, t_diag, out_lo, out_hi);
+            else
+                fast_rows<S, GROUPED, MODE, false, false>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2,
+                                                          cy2, ca, cg, tmask, t_diag, out_lo,
+                                                          out_hi);
         }
     }
     if (mine) {

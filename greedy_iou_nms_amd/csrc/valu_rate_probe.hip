@@ -137,6 +137,30 @@ __global__ __launch_bounds__(256) void name(float *out, float s) {              
 #define OR8 "v_or_b32 %0, %8, %0\nv_or_b32 %1, %8, %1\nv_or_b32 %2, %8, %2\nv_or_b32 %3, %8, %3\nv_or_b32 %4, %8, %4\nv_or_b32 %5, %8, %5\nv_or_b32 %6, %8, %6\nv_or_b32 %7, %8, %7\n"
 U32_KERNEL(k_addc, ADDC8)
 U32_KERNEL(k_or, OR8)
+// two-operand (VOP2) and three-operand (VOP3) forms over the 8 registers
+#define OP2_8(I) I " %0, %8, %0\n" I " %1, %8, %1\n" I " %2, %8, %2\n" I " %3, %8, %3\n" \
+                 I " %4, %8, %4\n" I " %5, %8, %5\n" I " %6, %8, %6\n" I " %7, %8, %7\n"
+#define OP3_8(I) I " %0, %8, %0, %8\n" I " %1, %8, %1, %8\n" I " %2, %8, %2, %8\n"         \
+                 I " %3, %8, %3, %8\n" I " %4, %8, %4, %8\n" I " %5, %8, %5, %8\n"         \
+                 I " %6, %8, %6, %8\n" I " %7, %8, %7, %8\n"
+#define CMP_8(I) I " vcc, %8, %0\n" I " vcc, %8, %1\n" I " vcc, %8, %2\n" I " vcc, %8, %3\n" \
+                 I " vcc, %8, %4\n" I " vcc, %8, %5\n" I " vcc, %8, %6\n" I " vcc, %8, %7\n"
+#define CND_8 "v_cndmask_b32 %0, %0, %8, vcc\nv_cndmask_b32 %1, %1, %8, vcc\n"               \
+              "v_cndmask_b32 %2, %2, %8, vcc\nv_cndmask_b32 %3, %3, %8, vcc\n"               \
+              "v_cndmask_b32 %4, %4, %8, vcc\nv_cndmask_b32 %5, %5, %8, vcc\n"               \
+              "v_cndmask_b32 %6, %6, %8, vcc\nv_cndmask_b32 %7, %7, %8, vcc\n"
+U32_KERNEL(k_max_i32, OP2_8("v_max_i32"))
+U32_KERNEL(k_min_u32, OP2_8("v_min_u32"))
+U32_KERNEL(k_add_u32, OP2_8("v_add_u32"))
+U32_KERNEL(k_sub_u32, OP2_8("v_sub_u32"))
+U32_KERNEL(k_and_b32, OP2_8("v_and_b32"))
+U32_KERNEL(k_lshl_b32, OP2_8("v_lshlrev_b32"))
+U32_KERNEL(k_med3_i32, OP3_8("v_med3_i32"))
+U32_KERNEL(k_max3_i32, OP3_8("v_max3_i32"))
+U32_KERNEL(k_sub_f32_e64, OP2_8("v_sub_f32_e64"))
+U32_KERNEL(k_cmp_gt_i32, CMP_8("v_cmp_gt_i32"))
+U32_KERNEL(k_cmp_gt_f32, CMP_8("v_cmp_gt_f32"))
+U32_KERNEL(k_cndmask, CND_8)
 
 // rcp f32 (transcendental)
 __global__ __launch_bounds__(256) void k_rcp_f32(float *out, float s) {
@@ -177,6 +201,12 @@ int main() {
 {"v_rcp_f32", k_rcp_f32, nullptr},
         {"v_mul_f64", nullptr, k_mul_f64}, {"v_add_f64", nullptr, k_add_f64},
         {"v_cmp_gt_f64", nullptr, k_cmp_f64},
+        {"v_max_i32", k_max_i32, nullptr}, {"v_min_u32", k_min_u32, nullptr},
+        {"v_add_u32", k_add_u32, nullptr}, {"v_sub_u32", k_sub_u32, nullptr},
+        {"v_and_b32", k_and_b32, nullptr}, {"v_lshlrev_b32", k_lshl_b32, nullptr},
+        {"v_med3_i32", k_med3_i32, nullptr}, {"v_max3_i32", k_max3_i32, nullptr},
+        {"v_sub_f32_e64", k_sub_f32_e64, nullptr}, {"v_cmp_gt_i32", k_cmp_gt_i32, nullptr},
+        {"v_cmp_gt_f32", k_cmp_gt_f32, nullptr}, {"v_cndmask_b32", k_cndmask, nullptr},
     };
     for (int bpc : {4, 8}) {  // workgroups of 4 waves per CU: 4 -> 4 waves/SIMD, 8 -> 8
         const int blocks = cus * bpc;
