@@ -111,12 +111,13 @@ constexpr int APPLIERS = NWAVES - 1;
 // Bounded waits: about a second of polling before a wait gives up.
 constexpr uint32_t SPIN_LIMIT = 1u << 23;
 
-// Entries of a row tile's list held in registers: rounds of 64.  The plain
-// sweep holds the whole list (its one workgroup has registers to spare); the
-// fused sweep shares its kernel's register budget with the mask and holds a
-// quarter, reading the rest when the kept set is known.
+// Entries of a row tile's list held in registers: rounds of 64, in each of
+// an applier's two register sets.  The plain sweep holds the whole list (its
+// one workgroup has registers to spare); the fused sweep shares its kernel's
+// register budget with the mask and holds 384 entries, reading the rest when
+// the kept set is known.
 template <bool FUSED>
-constexpr int rmax() { return FUSED ? 8 : TILE_LIST_CAP / 64; }
+constexpr int rmax() { return FUSED ? 6 : TILE_LIST_CAP / 64; }
 
 constexpr int NEAR = NEAR_TILES;
 static_assert(NEAR >= 2, "the resolver carries the words for the next two tiles in registers");
@@ -588,74 +589,91 @@ __device__ void apply_dense(const SweepArgs &a, int c, int stride, uint64_t kept
     }
 }
 
-// Applier q (1..APPLIERS): chunks q-1, q-1+APPLIERS, ...  Loads run two
-// levels ahead: while chunk c is waiting for its kept set, the first level
-// (diagonal words, list length) of chunk c + 2A and the entries of chunk
-// c + A are in flight (A = APPLIERS).
+// One chunk of an applier: chunk c's entries are in `cur`, chunk c + A's
+// first level in `l1`.  Stages chunk c + A for the resolver and issues the
+// loads of its entries (into `nxt`) and of chunk c + 2A's first level, all
+// before waiting for chunk c's kept set, so that the memory latency of the
+// next chunk overlaps the wait.  Returns false if the sweep gave up.
+template <bool FUSED>
+__device__ __forceinline__ bool apply_one(const SweepArgs &a, int stride, uint64_t *removed,
+                                          SweepSmem &sm, int c, uint32_t &count, Level1 &l1,
+                                          const Entries<rmax<FUSED>()> &cur,
+                                          Entries<rmax<FUSED>()> &nxt) {
+    const int lane = threadIdx.x & 63;
+    const int W = a.words;
+    const int A = APPLIERS;
+    wait_loads();
+    uint32_t count_next = 0;
+    if (c + A < W) {
+        stage_level1(l1, c + A, sm);
+        count_next = __builtin_amdgcn_readfirstlane(l1.count);
+        load_entries<FUSED>(a, c + A, rounds_of(count_next), nxt);
+        if (c + 2 * A < W && !load_level1<FUSED>(a, c + 2 * A, l1, sm)) return false;
+    }
+    if (!wait_flag<FUSED, APPLIER_SLEEP>(&sm.resolved[0], (uint32_t)c + 1u, sm, a.ctrl))
+        return false;
+    // The resolver wrote the chunk's settled word and the count of boxes
+    // kept before it ahead of the counter.  Both are read before the chunk
+    // is reported applied: after that the resolver may reuse the slot.
+    const Settled &s = sm.settled[c & (RING - 1)];
+    const uint64_t kept = ~uniform64(s.rem);
+    const uint32_t k_off = s.k_off;
+    if (kept) {
+        if (count > (uint32_t)TILE_LIST_CAP) {
+            // dense rows are plain stores of the mask stage, not visible to
+            // the fused sweep: leave the work to the plain sweep
+            if (FUSED) {
+                give_up<true>(sm, a.ctrl);
+                return false;
+            }
+            apply_dense(a, c, stride, kept, removed);
+        } else {
+            const int rounds = rounds_of(count);
+            apply_rounds<0, rmax<FUSED>()>(cur, rounds, count, kept, c, removed);
+            // rounds beyond the registers: load and apply them now
+            const size_t base = (size_t)c * TILE_LIST_CAP + lane;
+            for (int i = rmax<FUSED>(); i < rounds; ++i) {
+                const uint32_t wk = get<FUSED>(&a.tent_wk[base + 64 * i]);
+                const uint64_t val = get<FUSED>(&a.tent_val[base + 64 * i]);
+                apply_entry(wk, val, (uint32_t)(64 * i + lane) < count, kept, c, removed);
+            }
+        }
+    }
+    if (lane == 0) flag_store(&sm.stage[(c + LAG) & (RING - 1)].app_lag, (uint32_t)(c + LAG) + 1u);
+    // the outputs: off the resolver's path
+    if (lane == 0) a.kept[c] = kept;
+    if (!a.grouped && ((kept >> lane) & 1ull)) {
+        const uint64_t below = (1ull << lane) - 1ull;
+        a.keep_out[k_off + (uint32_t)__popcll(kept & below)] = (int64_t)cur.ord;
+    }
+    count = count_next;
+    return true;
+}
+
+// Applier q (1..APPLIERS): chunks q-1, q-1+APPLIERS, ...  Loads run ahead:
+// while chunk c waits for its kept set, the entries of chunk c + A and the
+// first level (near words, list length) of chunk c + 2A are in flight
+// (A = APPLIERS).  Two register sets of entries alternate between chunks.
 template <bool FUSED>
 __device__ void apply_chunks(const SweepArgs &a, int stride, uint64_t *removed, SweepSmem &sm,
                              int q) {
-    const int lane = threadIdx.x & 63;
     const int W = a.words;
     const int A = APPLIERS;
     int c = q - 1;
     if (c >= W) return;
     Level1 l1;
-    Entries<rmax<FUSED>()> e;
+    Entries<rmax<FUSED>()> ea, eb;
     // prologue: chunk c staged, its entries and chunk c + A's first level issued
     if (!load_level1<FUSED>(a, c, l1, sm)) return;
     wait_loads();
     stage_level1(l1, c, sm);
     uint32_t count = __builtin_amdgcn_readfirstlane(l1.count);
-    load_entries<FUSED>(a, c, rounds_of(count), e);
+    load_entries<FUSED>(a, c, rounds_of(count), ea);
     if (c + A < W && !load_level1<FUSED>(a, c + A, l1, sm)) return;
-    for (; c < W; c += A) {
-        wait_loads();
-        uint32_t count_next = 0;
-        if (c + A < W) {
-            stage_level1(l1, c + A, sm);
-            count_next = __builtin_amdgcn_readfirstlane(l1.count);
-            if (c + 2 * A < W && !load_level1<FUSED>(a, c + 2 * A, l1, sm)) return;
-        }
-        if (!wait_flag<FUSED, APPLIER_SLEEP>(&sm.resolved[0], (uint32_t)c + 1u, sm, a.ctrl))
-            return;
-        // The resolver wrote the chunk's settled word and the count of boxes
-        // kept before it ahead of the counter.  Both are read before the
-        // chunk is reported applied: after that the resolver may reuse the
-        // slot.
-        const Settled &s = sm.settled[c & (RING - 1)];
-        const uint64_t kept = ~uniform64(s.rem);
-        const uint32_t k_off = s.k_off;
-        if (kept) {
-            if (count > (uint32_t)TILE_LIST_CAP) {
-                // dense rows are plain stores of the mask stage, not visible
-                // to the fused sweep: leave the work to the plain sweep
-                if (FUSED) {
-                    give_up<true>(sm, a.ctrl);
-                    return;
-                }
-                apply_dense(a, c, stride, kept, removed);
-            } else {
-                const int rounds = rounds_of(count);
-                apply_rounds<0, rmax<FUSED>()>(e, rounds, count, kept, c, removed);
-                // rounds beyond the registers: load and apply them now
-                const size_t base = (size_t)c * TILE_LIST_CAP + lane;
-                for (int i = rmax<FUSED>(); i < rounds; ++i) {
-                    const uint32_t wk = get<FUSED>(&a.tent_wk[base + 64 * i]);
-                    const uint64_t val = get<FUSED>(&a.tent_val[base + 64 * i]);
-                    apply_entry(wk, val, (uint32_t)(64 * i + lane) < count, kept, c, removed);
-                }
-            }
-        }
-        if (lane == 0) flag_store(&sm.stage[(c + LAG) & (RING - 1)].app_lag, (uint32_t)(c + LAG) + 1u);
-        // the outputs: off the resolver's path
-        if (lane == 0) a.kept[c] = kept;
-        if (!a.grouped && ((kept >> lane) & 1ull)) {
-            const uint64_t below = (1ull << lane) - 1ull;
-            a.keep_out[k_off + (uint32_t)__popcll(kept & below)] = (int64_t)e.ord;
-        }
-        if (c + A < W) load_entries<FUSED>(a, c + A, rounds_of(count_next), e);
-        count = count_next;
+    for (; c < W; c += 2 * A) {
+        if (!apply_one<FUSED>(a, stride, removed, sm, c, count, l1, ea, eb)) return;
+        if (c + A >= W) return;
+        if (!apply_one<FUSED>(a, stride, removed, sm, c + A, count, l1, eb, ea)) return;
     }
 }
 
