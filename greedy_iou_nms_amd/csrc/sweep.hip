@@ -112,12 +112,15 @@ constexpr int APPLIERS = NWAVES - 1;
 constexpr uint32_t SPIN_LIMIT = 1u << 23;
 
 // Entries of a row tile's list held in registers: rounds of 64, in each of
-// an applier's two register sets.  The plain sweep holds the whole list (its
-// one workgroup has registers to spare); the fused sweep shares its kernel's
-// register budget with the mask and holds 384 entries, reading the rest when
-// the kept set is known.
+// an applier's two register sets; the rest is read when the kept set is
+// known.  The plain sweep's one workgroup has registers to spare and holds
+// 1536 entries (217 VGPRs: a build holding the whole 2048-entry list
+// compiled to exactly 256 VGPRs and gave wrong kept sets in about 5 % of the
+// calls on 8192 clustered boxes, where the 1536- and 1024-entry builds gave
+// none in 300 calls each); the fused sweep shares its kernel's register
+// budget with the mask and holds 384.
 template <bool FUSED>
-constexpr int rmax() { return FUSED ? 6 : TILE_LIST_CAP / 64; }
+constexpr int rmax() { return FUSED ? 6 : 24; }
 
 constexpr int NEAR = NEAR_TILES;
 static_assert(NEAR >= 2, "the resolver carries the words for the next two tiles in registers");
