@@ -43,7 +43,7 @@ constexpr int STRIP_GROUPED = 4;
 // Multi-workgroup radix sort (one image): a workgroup of RADIX_THREADS ranks
 // one tile of RADIX_TILE keys per pass.
 constexpr int RADIX_THREADS = 256;
-constexpr int RADIX_E = 16;
+constexpr int RADIX_E = 8;
 constexpr int RADIX_TILE = RADIX_THREADS * RADIX_E;
 // One image of at most this many boxes is sorted by ranking: every box
 // counts the boxes that precede it (the keys of all boxes fit in LDS).

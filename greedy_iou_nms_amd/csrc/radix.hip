@@ -16,7 +16,7 @@
 //                       position counted directly (n^2 comparisons), the
 //                       sorted-box gather, the input checks and the per-call
 //                       initialisation, in one launch.
-//   radix_keys_kernel   one workgroup per tile of 4096 boxes: the keys (score;
+//   radix_keys_kernel   one workgroup per tile of 2048 boxes: the keys (score;
 //                       grouped: class key and image of every box), each
 //                       tile's histograms of every digit (digit counts do not
 //                       depend on the order, so one read serves all passes),
