@@ -884,7 +884,13 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
     else
         hipLaunchKernelGGL(radix_keys_kernel<false>, dim3(tiles), dim3(NT), 0, stream, ka);
     hipError_t e = hipGetLastError();
-    const int passes = P.grouped ? RADIX_PASSES : 4;
+    // The image index of a box is below num_images, so the image digits
+    // above those needed for num_images - 1 are 0 for every box: those
+    // passes would be skipped anyway and are not launched at all (a skipped
+    // pass still costs a launch).  The class key's range is not known here.
+    int image_digits = 0;
+    for (int64_t m = (int64_t)P.num_images - 1; m > 0; m >>= 8) ++image_digits;
+    const int passes = P.grouped ? 8 + image_digits : 4;
     if (e == hipSuccess && P.grouped) {
         PlanArgs pa;
         pa.n = P.n;
