@@ -55,6 +55,7 @@ struct MatrixArgs {
     const double *__restrict__ mlo;
     const double *__restrict__ mhi;
     uint64_t *mdrop;
+    const Ctrl *ctrl;
     int n, words, qshift;
     float t;
     double sigma;
@@ -107,6 +108,18 @@ __device__ __forceinline__ float overlap(float rx1, float ry1, float rx2, float 
     return fmaxf(inter / uni, 0.0f);
 }
 
+// Sign words of the four edge differences, ORed: a clear sign bit is
+// necessary for a positive intersection (boxes are ordered, and a float
+// difference keeps the sign of the exact one, a tie giving +0), so a pair
+// whose word has its sign bit set has O = 0.
+__device__ __forceinline__ uint32_t may_overlap(float rx1, float ry1, float rx2, float ry2,
+                                                float cx1, float cy1, float cx2, float cy2) {
+    return __float_as_uint(rx2 - cx1) | __float_as_uint(cx2 - rx1) |
+           __float_as_uint(ry2 - cy1) | __float_as_uint(cy2 - ry1);
+}
+
+constexpr int MG = 4;  // child tiles per may-overlap question
+
 struct Children {
     float x1[MS], y1[MS], x2[MS], y2[MS], a[MS];
     uint64_t valid[MS];  // lanes that are real children of this item's tile
@@ -130,6 +143,48 @@ __device__ __forceinline__ void load_children(const MatrixArgs &a, const Item &i
     }
 }
 
+// Running maxima of one item's rows.  A pair with no overlap has O = 0 and
+// leaves a maximum (which starts at 0) as it is, so each group of MG child
+// tiles first asks whether any lane may overlap in any of them, and only the
+// tiles where some lane may overlap compute their IoUs.  In the diagonal
+// item (DIAG) only children after the father count in the diagonal tile;
+// elsewhere every child tile lies after the father's tile, and lanes that
+// are no child hold an empty box (O = 0).
+template <bool DIAG>
+__device__ __forceinline__ void max_rows(const MatrixArgs &a, const Item &it, const Children &ch,
+                                         float (&m)[MS]) {
+    const int lane = threadIdx.x & 63;
+    const int t_diag = it.r - it.c0;
+    for (int k = it.k_lo; k < it.k_hi; ++k) {
+        const int p = 64 * it.r + k;
+        const float4 rb = a.sb[p];
+        const float ra = a.area[p];
+        const bool after = lane > k;
+#pragma unroll
+        for (int t0 = 0; t0 < MS; t0 += MG) {
+            uint32_t sgn[MG];
+            uint32_t all = ~0u;
+#pragma unroll
+            for (int j = 0; j < MG; ++j) {
+                const int t = t0 + j;
+                sgn[j] = may_overlap(rb.x, rb.y, rb.z, rb.w, ch.x1[t], ch.y1[t], ch.x2[t],
+                                     ch.y2[t]);
+                all &= sgn[j];
+            }
+            if (__ballot((int32_t)all >= 0) == 0ull) continue;
+#pragma unroll
+            for (int j = 0; j < MG; ++j) {
+                const int t = t0 + j;
+                if (__ballot((int32_t)sgn[j] >= 0) == 0ull) continue;
+                const float o = overlap(rb.x, rb.y, rb.z, rb.w, ra, ch.x1[t], ch.y1[t],
+                                        ch.x2[t], ch.y2[t], ch.a[t]);
+                const float mo = fmaxf(m[t], o);
+                m[t] = (!DIAG || t != t_diag || after) ? mo : m[t];
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(MT) void matrix_overlap_max_kernel(MatrixArgs a, int num_items) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -142,19 +197,8 @@ __global__ __launch_bounds__(MT) void matrix_overlap_max_kernel(MatrixArgs a, in
         float m[MS];
 #pragma unroll
         for (int t = 0; t < MS; ++t) m[t] = 0.0f;
-        for (int k = it.k_lo; k < it.k_hi; ++k) {
-            const int p = 64 * it.r + k;
-            const float4 rb = a.sb[p];
-            const float ra = a.area[p];
-            const bool after = lane > k;  // in the diagonal tile only children after p
-#pragma unroll
-            for (int t = 0; t < MS; ++t) {
-                const float o = overlap(rb.x, rb.y, rb.z, rb.w, ra, ch.x1[t], ch.y1[t],
-                                        ch.x2[t], ch.y2[t], ch.a[t]);
-                const float mo = fmaxf(m[t], o);
-                m[t] = (t != t_diag || after) ? mo : m[t];
-            }
-        }
+        if (t_diag >= 0 && t_diag < MS) max_rows<true>(a, it, ch, m);
+        else max_rows<false>(a, it, ch, m);
 #pragma unroll
         for (int t = 0; t < MS; ++t) {
             // omax holds non-negative floats, whose bit patterns order as
@@ -165,11 +209,81 @@ __global__ __launch_bounds__(MT) void matrix_overlap_max_kernel(MatrixArgs a, in
     }
 }
 
+// The decay test of one pair for the MS child tiles of tile t: D = omax[p]^2
+// - O^2 against the child's bounds, the literal expression inside the
+// margin; returns the lanes that drop.
+__device__ __forceinline__ uint64_t decay_drops(const MatrixArgs &a, const Item &it,
+                                                const Children &ch, int t, float4 rb, float ra,
+                                                double A, double lo, double hi, uint64_t live,
+                                                double t64) {
+    const int lane = threadIdx.x & 63;
+    const float o = overlap(rb.x, rb.y, rb.z, rb.w, ra, ch.x1[t], ch.y1[t], ch.x2[t], ch.y2[t],
+                            ch.a[t]);
+    const double od = (double)o;
+    const double D = __builtin_fma(-od, od, A);
+    uint64_t sure = __ballot(D < lo);
+    const uint64_t unsure = __ballot(D < hi) & ~sure;
+    if (unsure & live) {
+        // within the margin: the literal expression
+        const int q = 64 * (it.c0 + t) + lane;
+        bool hit = false;
+        if ((unsure >> lane) & 1ull) {
+            const double x = (A - od * od) / a.sigma;
+            hit = exp(x) * (double)a.mscore[q] < t64;
+        }
+        sure |= __ballot(hit);
+    }
+    return sure & live;
+}
+
+// The rows of one item.  SKIP: no child of this call has a negative score at
+// or above t, so a pair with no overlap never drops its child: it has D =
+// omax[p]^2 >= 0 and exp(D / sigma) s_q >= s_q >= t for s_q >= 0, and
+// children below t are dropped by the keep step anyway.  Groups of MG child
+// tiles where no lane may overlap are then skipped, as in the maximum.
+template <bool SKIP>
+__device__ __forceinline__ void decay_rows(const MatrixArgs &a, const Item &it,
+                                           const Children &ch, const double (&lo)[MS],
+                                           const double (&hi)[MS], uint64_t (&drop)[MS]) {
+    const double t64 = (double)a.t;
+    const int t_diag = it.r - it.c0;
+    for (int k = it.k_lo; k < it.k_hi; ++k) {
+        const int p = 64 * it.r + k;
+        const float4 rb = a.sb[p];
+        const float ra = a.area[p];
+        const float om = __uint_as_float(a.momax[p]);
+        const double A = (double)om * (double)om;  // exact: 24 x 24 bits
+        const uint64_t after = k == 63 ? 0ull : (~0ull << (k + 1));
+#pragma unroll
+        for (int t0 = 0; t0 < MS; t0 += MG) {
+            uint32_t sgn[MG];
+            if (SKIP) {
+                uint32_t all = ~0u;
+#pragma unroll
+                for (int j = 0; j < MG; ++j) {
+                    const int t = t0 + j;
+                    sgn[j] = may_overlap(rb.x, rb.y, rb.z, rb.w, ch.x1[t], ch.y1[t], ch.x2[t],
+                                         ch.y2[t]);
+                    all &= sgn[j];
+                }
+                if (__ballot((int32_t)all >= 0) == 0ull) continue;
+            }
+#pragma unroll
+            for (int j = 0; j < MG; ++j) {
+                const int t = t0 + j;
+                if (SKIP && __ballot((int32_t)sgn[j] >= 0) == 0ull) continue;
+                const uint64_t live = ch.valid[t] & (t == t_diag ? after : ~0ull);
+                drop[t] |= decay_drops(a, it, ch, t, rb, ra, A, lo[t], hi[t], live, t64);
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(MT) void matrix_decay_kernel(MatrixArgs a, int num_items) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int slots = gridDim.x * MWAVES;
-    const double t64 = (double)a.t;
+    const bool skip = !(a.ctrl->flags & FLAG_MATRIX_ZERO_PAIRS_MATTER);
     for (int item = blockIdx.x * MWAVES + wave; item < num_items; item += slots) {
         const Item it = decode(a, item);
         Children ch;
@@ -182,39 +296,11 @@ __global__ __launch_bounds__(MT) void matrix_decay_kernel(MatrixArgs a, int num_
             lo[t] = a.mlo[q];
             hi[t] = a.mhi[q];
         }
-        const int t_diag = it.r - it.c0;
         uint64_t drop[MS];
 #pragma unroll
         for (int t = 0; t < MS; ++t) drop[t] = 0ull;
-        for (int k = it.k_lo; k < it.k_hi; ++k) {
-            const int p = 64 * it.r + k;
-            const float4 rb = a.sb[p];
-            const float ra = a.area[p];
-            const float om = __uint_as_float(a.momax[p]);
-            const double A = (double)om * (double)om;  // exact: 24 x 24 bits
-            const uint64_t after = k == 63 ? 0ull : (~0ull << (k + 1));
-#pragma unroll
-            for (int t = 0; t < MS; ++t) {
-                const float o = overlap(rb.x, rb.y, rb.z, rb.w, ra, ch.x1[t], ch.y1[t],
-                                        ch.x2[t], ch.y2[t], ch.a[t]);
-                const double od = (double)o;
-                const double D = __builtin_fma(-od, od, A);
-                uint64_t sure = __ballot(D < lo[t]);
-                uint64_t unsure = __ballot(D < hi[t]) & ~sure;
-                const uint64_t live = ch.valid[t] & (t == t_diag ? after : ~0ull);
-                if (unsure & live) {
-                    // within the margin: the literal expression
-                    const int q = 64 * (it.c0 + t) + lane;
-                    bool hit = false;
-                    if ((unsure >> lane) & 1ull) {
-                        const double x = (A - od * od) / a.sigma;
-                        hit = exp(x) * (double)a.mscore[q] < t64;
-                    }
-                    sure |= __ballot(hit);
-                }
-                drop[t] |= sure & live;
-            }
-        }
+        if (skip) decay_rows<true>(a, it, ch, lo, hi, drop);
+        else decay_rows<false>(a, it, ch, lo, hi, drop);
 #pragma unroll
         for (int t = 0; t < MS; ++t)
             if (drop[t] && lane == 0) atomicOr(&a.mdrop[it.c0 + t], drop[t]);
@@ -243,7 +329,7 @@ __global__ __launch_bounds__(256) void matrix_prep_kernel(PrepArgs a) {
     if (p >= a.npad) return;
     double lo = -INFINITY, hi = -INFINITY;
     float s = 0.0f;
-    bool bad = false;
+    bool bad = false, neg = false;
     if (p < a.n) {
         const int32_t i = a.order[p];
         s = a.scores[i];
@@ -259,8 +345,10 @@ __global__ __launch_bounds__(256) void matrix_prep_kernel(PrepArgs a) {
                 lo = bound - margin;
                 hi = bound + margin;
             } else if (sd < 0.0) {
-                // t <= s < 0: every pair by the literal expression
+                // t <= s < 0: every pair by the literal expression, and a
+                // father with no overlap can drop the child
                 hi = INFINITY;
+                neg = true;
             }
             // s >= 0 >= t (s = 0 or t <= 0 < s): no candidate falls below t
         }
@@ -271,6 +359,9 @@ __global__ __launch_bounds__(256) void matrix_prep_kernel(PrepArgs a) {
     a.mhi[p] = hi;
     const uint64_t any_bad = __ballot(bad);
     if (any_bad && (threadIdx.x & 63) == 0) atomicOr(&a.ctrl->error, ERR_BAD_BOXES);
+    const uint64_t any_neg = __ballot(neg);
+    if (any_neg && (threadIdx.x & 63) == 0)
+        atomicOr(&a.ctrl->flags, FLAG_MATRIX_ZERO_PAIRS_MATTER);
 }
 
 __global__ __launch_bounds__(256) void matrix_keep_kernel(const float *mscore,
@@ -292,6 +383,7 @@ MatrixArgs make_args(const Problem &P, const Layout &L, const Work &w, double si
     a.mlo = w.mlo;
     a.mhi = w.mhi;
     a.mdrop = w.mdrop;
+    a.ctrl = w.ctrl;
     a.n = P.n;
     a.words = (int)L.words;
     a.t = P.thresh;

@@ -17,6 +17,9 @@ constexpr uint32_t ERR_BAD_BOXES = 8u;  // Matrix NMS: a box with x1 > x2 or y1 
 // Ctrl::flags bits.
 // every box has x1 < x2, y1 < y2 and a finite area > 0
 constexpr uint32_t FLAG_ORDERED_BOXES = 1u;
+// Matrix NMS: some child with a negative score at or above the threshold,
+// for which a father with no overlap can still decide the decay test.
+constexpr uint32_t FLAG_MATRIX_ZERO_PAIRS_MATTER = 2u;
 
 // Per-call control block at the start of the workspace.  The sort kernel
 // initialises it; later kernels read plan fields and raise error bits.  The

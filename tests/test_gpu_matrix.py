@@ -106,6 +106,18 @@ def test_signed_scores_and_thresholds():
         _check(w.boxes, scores, t, 0.5, "signed")
 
 
+@pytest.mark.parametrize("t", [-0.5, -0.9])
+def test_negative_scores_dropped_by_fathers_without_overlap(t):
+    # A child with t <= s < 0 can be dropped by a father it does not
+    # overlap at all (exp(omax^2 / sigma) s falls below t), so those pairs
+    # cannot be skipped; half the scores are negative here and the boxes
+    # spread enough that most pairs do not overlap.
+    rng = np.random.default_rng(93)
+    w = workloads.random_small(93, 1500, canvas=400.0)
+    scores = rng.uniform(-1.0, 1.0, 1500).astype(np.float32)
+    _check(w.boxes, scores, t, 0.5, "negative scores, sparse")
+
+
 def test_ten_runs_identical():
     import greedy_iou_nms_amd as g
     w = workloads.config(2, 1)
