@@ -209,6 +209,13 @@ __global__ __launch_bounds__(MT) void matrix_overlap_max_kernel(MatrixArgs a, in
     }
 }
 
+// The literal test of a pair inside the margin, out of line: inlined, the
+// binary64 exp's registers raised the decay kernel to 155 VGPRs (3 waves per
+// SIMD); with the call (rarely taken) and a 4-wave hint it fits 128.
+__device__ __attribute__((noinline)) bool literal_drop(double x, double s, double t) {
+    return exp(x) * s < t;
+}
+
 // The decay test of one pair for the MS child tiles of tile t: D = omax[p]^2
 // - O^2 against the child's bounds, the literal expression inside the
 // margin; returns the lanes that drop.
@@ -229,7 +236,7 @@ __device__ __forceinline__ uint64_t decay_drops(const MatrixArgs &a, const Item 
         bool hit = false;
         if ((unsure >> lane) & 1ull) {
             const double x = (A - od * od) / a.sigma;
-            hit = exp(x) * (double)a.mscore[q] < t64;
+            hit = literal_drop(x, (double)a.mscore[q], t64);
         }
         sure |= __ballot(hit);
     }
@@ -279,7 +286,8 @@ __device__ __forceinline__ void decay_rows(const MatrixArgs &a, const Item &it,
     }
 }
 
-__global__ __launch_bounds__(MT) void matrix_decay_kernel(MatrixArgs a, int num_items) {
+__global__ __launch_bounds__(MT) __attribute__((amdgpu_waves_per_eu(4))) void matrix_decay_kernel(
+    MatrixArgs a, int num_items) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int slots = gridDim.x * MWAVES;
