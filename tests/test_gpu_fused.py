@@ -46,6 +46,21 @@ def test_fused_ragged_sizes(n):
     np.testing.assert_array_equal(sep, want)
 
 
+def test_fused_with_two_workgroups_per_cu():
+    # 2501 row tiles: the removed bitmap (20 KB) beside the sweep's 42.8 KB
+    # of LDS leaves room for two workgroups per CU instead of three, so the
+    # fused launch takes its other occupancy and splits its items for it.
+    # Too large for the oracle in seconds: the fused result must equal the
+    # separate launches', which the oracle pins at the other sizes.
+    n = 64 * 2500 + 5
+    w = workloads.random_small(4242, n, canvas=60.0 + n / 8.0)
+    note("fused two workgroups per CU n=%d" % n)
+    fused, sep, plain, _, _ = _both(w)
+    assert fused.size > 0
+    np.testing.assert_array_equal(fused, sep)
+    np.testing.assert_array_equal(plain, sep)
+
+
 def test_fused_size_with_inverted_boxes():
     # a few boxes with x2 < x1 and y2 < y1 (positive area) send the whole
     # call to the literal division test, at a size the fused launch takes
