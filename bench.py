@@ -283,8 +283,8 @@ def main():
         probe = os.path.join(ROOT, "greedy_iou_nms_amd", "valu_rate_probe")
         sys.exit(subprocess.run([probe]).returncode)
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs on a single MI355X "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs the whole path on "
+              "a single MI355X (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         _copy_calibration(args.copy_calibration)
