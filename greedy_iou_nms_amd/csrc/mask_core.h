@@ -176,7 +176,10 @@ __device__ __forceinline__ void fast_rows(const MaskArgs &a, const MaskPtrs &m_,
                                           const float (&ca)[S], const uint32_t (&cg)[S],
                                           const uint64_t (&tmask)[S], int t_diag,
                                           uint32_t (&out_lo)[S], uint32_t (&out_hi)[S]) {
-    constexpr int TG = 4;
+    // tiles per question: measured at 65,536 boxes, the sign form is
+    // fastest asking per 2 tiles (0.357 ms; 0.368 per 4, 0.405 per 8, 0.385
+    // per tile), the intersection form per 4
+    constexpr int TG = SIGN ? 2 : 4;
     for (int k = k_lo; k < k_hi; ++k) {
         const int p = p0 + k;
         const float4 rb = m_.sb[p];
