@@ -118,7 +118,10 @@ __device__ __forceinline__ uint32_t may_overlap(float rx1, float ry1, float rx2,
            __float_as_uint(ry2 - cy1) | __float_as_uint(cy2 - ry1);
 }
 
-constexpr int MG = 4;  // child tiles per may-overlap question
+// child tiles per may-overlap question (measured at 65,536 boxes: the
+// maximum takes 0.30-0.33 ms asking per 2 tiles, 0.37-0.39 per 4 and
+// 0.31-0.32 per tile, where the decay step is slower)
+constexpr int MG = 2;
 
 struct Children {
     float x1[MS], y1[MS], x2[MS], y2[MS], a[MS];
