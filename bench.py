@@ -8,8 +8,10 @@ memory.  Prints one JSON line:
   value          boxes/s over the timed steps (whole job, one GPU)
   roofline       the dominant kernel of the timed steps (at this size the
                  fused IoU-mask launch, whose sweep workgroup runs beside the
-                 mask) against the chip's fp32 VALU issue rate, timed with HIP
-                 events on the launch stream
+                 mask) against the published fp32 vector peak (157.3 TFLOP/s),
+                 counting 13 algorithmic fp32 operations per box pair for every
+                 pair of the triangle, timed with HIP events on the launch
+                 stream
   mask_kernel_alone, sweep_alone
                  the mask and the sweep as separate launches (a few extra
                  steps), so each is measured on its own line
@@ -20,12 +22,13 @@ memory.  Prints one JSON line:
   matrix_nms     Matrix NMS (Gaussian decay, score threshold 0.1, sigma 0.5)
                  on the boxes and scores of both workloads: call time, stage
                  times, pair evaluations per second of its two pairwise
-                 kernels and their fraction of the VALU issue peak; parity
-                 with the CPU oracle at N = 8192
+                 kernels and their dense-equivalent fraction of the fp32
+                 vector peak; parity with the CPU oracle at N = 8192
+  near_threshold_pairs
+                 pairs the oracle evaluated with |IoU - t| <= 1e-6, per
+                 workload (from the oracle run of the cpu_baseline leg)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --valu-rates
-         (cycles per wave64 instruction of the VALU classes the kernels use)
        python bench.py --copy-calibration BYTES
          (device-to-device copies of a known size, run under rocprofv3 --pmc
           to scale the FETCH_SIZE / WRITE_SIZE counters to bytes)
@@ -43,12 +46,14 @@ if ROOT not in sys.path:
 # fp32 ops per box pair counted as the algorithmic work of the IoU test:
 # 4 max/min, 2 sub, 2 clamps, 1 mul, 1 add, 1 sub, 1 div, 1 compare
 OPS_PER_PAIR = 13
-# fp32 vector peak counted in operations (an FMA counts as one): the published
-# 157.3 TFLOP/s is 256 CUs x 4 SIMDs x 32 lanes x 2 (FMA) x 2.4 GHz, so plain
-# fp32 add / sub / mul issue at 256 x 4 x 32 x 2.4 GHz = 78.6 T ops/s (one
-# wave64 instruction per 2 cycles per SIMD; `bench.py --valu-rates` measures
-# it, and the 4-cycle classes: min/max/med3, conversions, fp64, lane writes)
-VALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
+# MI355X's published fp32 vector peak (dense), TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+# The rate at which plain fp32 add / sub / mul and bitwise ops issue (one
+# wave64 instruction per 2 cycles per SIMD: 256 x 4 x 32 x 2.4 GHz), quoted
+# beside the published peak as a side figure only.
+FP32_ISSUE_RATE_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
+COUNTED = ("algorithmic fp32 operations of the IoU test, 13 per box pair, over every pair "
+           "of the triangle (pairs the overlap pre-test rejects count as done)")
 HBM_PEAK_GBS = 8000.0
 # column tiles per mask work item for one image: a row's words are written
 # from the start of the strip holding its own tile
@@ -243,7 +248,10 @@ def _measure_matrix(w, steps, warmup):
                              ("decay", "decay", MATRIX_DECAY_INSTR)):
         rate = pairs / (st[key] * 1e-3)
         res[name + "_pairs_per_s"] = rate
-        res[name + "_valu_frac"] = instr * rate / (VALU_PEAK_TOPS * 1e12)
+        # dense-equivalent: every pair counted, also those the kernel skips
+        # because they cannot overlap, so this is not executed utilisation
+        res[name + "_dense_equivalent_frac_of_157tf"] = (
+            instr * rate / (FP32_VECTOR_PEAK_TFLOPS * 1e12))
     return res, keep
 
 
@@ -275,13 +283,7 @@ def main():
                     help="only run device copies of BYTES bytes (counter calibration)")
     ap.add_argument("--trace-config", type=int, default=0, metavar="K",
                     help="only time workload K (1..5) as the library runs it (for profiler runs)")
-    ap.add_argument("--valu-rates", action="store_true",
-                    help="only run the VALU issue-rate probe built next to the library")
     args = ap.parse_args()
-    if args.valu_rates:
-        import subprocess
-        probe = os.path.join(ROOT, "greedy_iou_nms_amd", "valu_rate_probe")
-        sys.exit(subprocess.run([probe]).returncode)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library runs the whole path on "
               "a single MI355X (--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -330,16 +332,18 @@ def main():
                   "beside it)",
         "bound": "alu",
         "achieved": achieved,
-        "peak": VALU_PEAK_TOPS,
+        "peak": FP32_VECTOR_PEAK_TFLOPS,
         "unit": "TFLOP/s",
-        "frac": achieved / VALU_PEAK_TOPS,
+        "counted": COUNTED,
+        "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
         "traffic": traffic,
         "traffic_detail": traffic_detail,
         "algorithmic_bytes": alg_bytes,
         "ops_per_pair": OPS_PER_PAIR,
         "pairs_per_launch": pairs,
         "launch_ms": launch_ms,
-        "frac_of_fp32_vector_157tf": achieved / 157.3,
+        "side_frac_of_fp32_issue_rate_78tops": achieved / FP32_ISSUE_RATE_TOPS,
+        "executed_valu": "profiles/valu_mask_kernels_n65536_large_mixed.md",
         "mask_bytes_written_gbs": alg_bytes / (launch_ms * 1e-3) / 1e9,
     }
 
@@ -351,8 +355,8 @@ def main():
         m_ach = OPS_PER_PAIR * pairs / (m_ms * 1e-3) / 1e12
         line["mask_kernel_alone"] = {
             "kernel": "mask_kernel (separate launch)", "launch_ms": m_ms, "achieved": m_ach,
-            "peak": VALU_PEAK_TOPS, "unit": "TFLOP/s", "frac": m_ach / VALU_PEAK_TOPS,
-            "steps": sep_steps,
+            "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "counted": COUNTED,
+            "frac": m_ach / FP32_VECTOR_PEAK_TFLOPS, "steps": sep_steps,
         }
         sw_ms = s["stage_ms"]["sweep"]
         dense = _sweep_dense_bytes(w, s["keep"])
@@ -361,7 +365,7 @@ def main():
             "dense_equivalent_bytes": dense, "dense_equivalent_gbs": dense / (sw_ms * 1e-3) / 1e9,
             "us_per_row_tile": 1000.0 * sw_ms / ((w.n + 63) // 64), "steps": sep_steps,
         }
-        valu_ms = 1000.0 * OPS_PER_PAIR * pairs / (VALU_PEAK_TOPS * 1e12)
+        valu_ms = 1000.0 * OPS_PER_PAIR * pairs / (FP32_VECTOR_PEAK_TFLOPS * 1e12)
         hbm_ms = 1000.0 * alg_bytes / (HBM_PEAK_GBS * 1e9)
         roof_ms = max(valu_ms, hbm_ms)
         line["e2e_roofline"] = {
@@ -390,7 +394,7 @@ def main():
 
         import oracle
         t0 = time.perf_counter()
-        want = oracle.c_nms(w.boxes, w.scores, w.iou_threshold)
+        want, border5 = oracle.c_nms(w.boxes, w.scores, w.iou_threshold, return_borderline=True)
         cpu_s = time.perf_counter() - t0
         line["cpu_baseline"] = {
             "value": w.n / cpu_s, "unit": "boxes/s", "cores": 1, "kind": "oracle",
@@ -399,6 +403,13 @@ def main():
                                         len(os.sched_getaffinity(0))),
         }
         line["parity_vs_oracle"] = bool(np.array_equal(r["keep"], want))
+        near = {w.name: border5}
+        if "n8192" in line:
+            want2, border2 = oracle.c_nms(w2.boxes, w2.scores, w2.iou_threshold,
+                                          return_borderline=True)
+            near[w2.name] = border2
+            line["n8192"]["parity_vs_oracle"] = bool(np.array_equal(r2["keep"], want2))
+        line["near_threshold_pairs"] = near
     print(json.dumps(line), flush=True)
 
 

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "NMSError", "STAGES", "nms", "nms_profiled", "workspace_size", "Workspace",
-    "debug_order", "debug_mask", "debug_decide", "library_path",
+    "debug_order", "debug_mask", "debug_decide", "debug_plan", "library_path",
     "MATRIX_STAGES", "matrix_nms", "matrix_nms_profiled", "matrix_workspace_size",
 ]
 
@@ -71,6 +71,8 @@ def _load():
     lib.nms_debug_mask.restype = ctypes.c_int
     lib.nms_debug_decide.argtypes = [c_vp, c_vp, c_i64, c_f, ctypes.c_int, c_vp, c_vp]
     lib.nms_debug_decide.restype = ctypes.c_int
+    lib.nms_debug_plan.argtypes = [c_i64, c_i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)]
+    lib.nms_debug_plan.restype = ctypes.c_int
     lib.nms_matrix_workspace_size.argtypes = [c_i64, ctypes.POINTER(c_sz)]
     lib.nms_matrix_workspace_size.restype = ctypes.c_int
     matrix = [c_vp, c_vp, c_i64, c_f, ctypes.c_double, c_vp, p_i64, c_vp, c_sz, c_vp]
@@ -163,6 +165,26 @@ def _check_inputs(boxes, scores, class_ids, batch_offsets):
 PROFILE_NO_FUSION = 1  # nms_f32_profiled flag: mask and sweep as separate launches
 
 
+def _check_out(out: Optional[torch.Tensor], n: int, device: torch.device) -> torch.Tensor:
+    """The output buffer: a fresh int64 tensor, or the caller's ``out``,
+    which the library fills through a raw pointer with 8 bytes per kept box,
+    so it must be a contiguous int64 tensor on ``device`` with room for n
+    entries."""
+    if out is None:
+        return torch.empty(max(n, 1), dtype=torch.int64, device=device)
+    if not isinstance(out, torch.Tensor):
+        raise TypeError("out must be a torch tensor")
+    if out.dtype != torch.int64:
+        raise TypeError("out must be an int64 tensor (got %s)" % out.dtype)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if out.device != device:
+        raise ValueError("out must be on the device of boxes (%s, got %s)" % (device, out.device))
+    if out.numel() < n:
+        raise ValueError("out holds %d entries; %d boxes need %d" % (out.numel(), n, n))
+    return out
+
+
 def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, profiled,
          fuse=True):
     boxes, scores, class_ids, batch_offsets, num_images = _check_inputs(
@@ -174,8 +196,7 @@ def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out,
         nbytes = workspace_size(n, num_images, class_ids is not None)
         ws = workspace if workspace is not None else _default_workspace(device, stream)
         buf = ws.get(nbytes, device)
-        if out is None or out.numel() < max(n, 1) or out.device != device:
-            out = torch.empty(max(n, 1), dtype=torch.int64, device=device)
+        out = _check_out(out, n, device)
         count = ctypes.c_int64(0)
         args = [_ptr(boxes), _ptr(scores), n, ctypes.c_float(float(iou_threshold)),
                 _ptr(class_ids), _ptr(batch_offsets), num_images, _ptr(out),
@@ -253,6 +274,17 @@ def debug_mask(boxes, scores, iou_threshold, class_ids=None, batch_offsets=None)
     return mask[:n, :words], order[:n]
 
 
+PLAN_FIELDS = ("mask_qshift", "fused", "fused_qshift", "rank_sort")
+
+
+def debug_plan(n: int, num_images: int = 0, has_classes: bool = False) -> Dict[str, int]:
+    """The launch plan ``nms`` and ``debug_mask`` take for n boxes on the
+    current device (see NMS_PLAN_* in include/greedy_nms.h)."""
+    plan = (ctypes.c_int32 * 8)()
+    _check(_lib.nms_debug_plan(int(n), int(num_images), int(bool(has_classes)), plan))
+    return {name: int(plan[i]) for i, name in enumerate(PLAN_FIELDS)}
+
+
 def debug_decide(inter: torch.Tensor, uni: torch.Tensor, iou_threshold: float,
                  positive_areas: bool) -> torch.Tensor:
     """The mask kernel's threshold test on given (intersection, union)
@@ -288,8 +320,7 @@ def _run_matrix(boxes, scores, score_threshold, sigma, workspace, out, profiled)
         nbytes = matrix_workspace_size(n)
         ws = workspace if workspace is not None else _default_workspace(device, stream)
         buf = ws.get(nbytes, device)
-        if out is None or out.numel() < max(n, 1) or out.device != device:
-            out = torch.empty(max(n, 1), dtype=torch.int64, device=device)
+        out = _check_out(out, n, device)
         count = ctypes.c_int64(0)
         args = [_ptr(boxes), _ptr(scores), n, ctypes.c_float(float(score_threshold)),
                 ctypes.c_double(float(sigma)), _ptr(out), ctypes.byref(count), _ptr(buf),

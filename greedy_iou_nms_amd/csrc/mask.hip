@@ -155,14 +155,22 @@ int64_t mask_items_upper_bound(const Problem &P, const Layout &L) {
 
 }  // namespace maskcore
 
+// Slots that the split of small inputs aims at: 16 waves per CU.  The
+// kernel's registers allow 6 waves per SIMD (24 per CU), but splitting for 24
+// cost the clustered 8192-box case 4.5 us (0.033 -> 0.037 ms) and gained 4096
+// boxes 1 us; splitting for 8 cost both (0.049, 0.021 ms).
+static maskcore::MaskArgs separate_mask_args(const Problem &P, const Layout &L) {
+    const int64_t slots = (int64_t)device_cu_count() * 16;
+    return maskcore::make_mask_args(P, L, slots);
+}
+
+int separate_mask_qshift(const Problem &P, const Layout &L) {
+    return separate_mask_args(P, L).qshift;
+}
+
 hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStream_t stream) {
     const int waves_per_block = MASK_THREADS / 64;
-    // Slots that the split of small inputs aims at: 16 waves per CU.  The
-    // kernel's registers allow 6 waves per SIMD (24 per CU), but splitting
-    // for 24 cost the clustered 8192-box case 4.5 us (0.033 -> 0.037 ms) and
-    // gained 4096 boxes 1 us; splitting for 8 cost both (0.049, 0.021 ms).
-    const int64_t slots = (int64_t)device_cu_count() * 16;
-    const maskcore::MaskArgs a = maskcore::make_mask_args(P, L, slots);
+    const maskcore::MaskArgs a = separate_mask_args(P, L);
     const int64_t items_ub = maskcore::mask_items_upper_bound(P, L) << a.qshift;
     // one work item per wave: the GPU starts workgroups as earlier ones
     // leave, which evens out waves that progress at different rates

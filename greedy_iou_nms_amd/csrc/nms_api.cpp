@@ -3,6 +3,7 @@
 // of {error bits, flags, kept count} that ends every call.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -120,21 +121,6 @@ struct Readback {
     int32_t num_items;
 };
 
-// A small pinned host buffer per thread for the read-back (pageable memory
-// would force a staged copy).  It is never freed: the HIP runtime may already
-// be gone when thread-local destructors run at exit.
-Readback *pinned_readback() {
-    thread_local Readback *buf = nullptr;
-    thread_local bool tried = false;
-    if (!tried) {
-        tried = true;
-        void *p = nullptr;
-        if (hipHostMalloc(&p, sizeof(Readback), hipHostMallocDefault) == hipSuccess)
-            buf = static_cast<Readback *>(p);
-    }
-    return buf;
-}
-
 nms_status check_common(int64_t n, float thresh, const int64_t *offsets, int64_t num_images) {
     if (n < 0 || std::isnan(thresh)) return NMS_INVALID_ARG;
     if (offsets == nullptr && num_images > 1) return NMS_INVALID_ARG;
@@ -161,18 +147,56 @@ Problem make_problem(const float *boxes, const float *scores, int64_t n, float t
 
 nms_status hip_status(hipError_t e) { return e == hipSuccess ? NMS_OK : NMS_HIP_ERROR; }
 
+// Pinned host buffers for the read-back.  A copy into pageable memory goes
+// through the runtime's staging and costs tens of microseconds more per
+// call.  Calls take a buffer from this pool and give it back; a buffer is
+// allocated (hipHostMalloc) only when every existing one is in use, at most
+// READBACK_POOL of them, and they are kept until the process ends (freeing
+// them at exit could run after the HIP runtime is gone; the slots are plain
+// atomics, so no code of this library runs at exit).  Past READBACK_POOL
+// concurrent calls the copy goes to pageable memory.
+constexpr int READBACK_POOL = 64;
+std::atomic<Readback *> g_readback_free[READBACK_POOL];
+std::atomic<int> g_readback_made{0};
+
+Readback *take_readback() {
+    for (int i = 0; i < READBACK_POOL; ++i) {
+        Readback *p = g_readback_free[i].exchange(nullptr, std::memory_order_acquire);
+        if (p) return p;
+    }
+    if (g_readback_made.fetch_add(1, std::memory_order_relaxed) >= READBACK_POOL) {
+        g_readback_made.fetch_sub(1, std::memory_order_relaxed);
+        return nullptr;
+    }
+    void *p = nullptr;
+    if (hipHostMalloc(&p, sizeof(Readback), hipHostMallocDefault) != hipSuccess) {
+        g_readback_made.fetch_sub(1, std::memory_order_relaxed);
+        return nullptr;
+    }
+    return static_cast<Readback *>(p);
+}
+
+void give_readback(Readback *p) {
+    for (int i = 0; i < READBACK_POOL; ++i) {
+        Readback *expected = nullptr;
+        if (g_readback_free[i].compare_exchange_strong(expected, p, std::memory_order_release,
+                                                       std::memory_order_relaxed))
+            return;
+    }
+    // unreachable: at most READBACK_POOL buffers exist, each in one slot or in use
+}
+
 // Copies the control block back (the call's only device-to-host transfer)
-// and synchronises the stream.
-nms_status read_back(const Work &w, hipStream_t stream, Readback *out) {
-    Readback *pin = pinned_readback();
-    hipError_t e;
+// and synchronises the stream.  pool: through a pinned buffer of the pool;
+// otherwise straight into *out (pageable), which allocates nothing.
+nms_status read_back(const Work &w, hipStream_t stream, Readback *out, bool pool = true) {
+    Readback *pin = pool ? take_readback() : nullptr;
+    Readback *dst = pin ? pin : out;
+    hipError_t e = hipMemcpyAsync(dst, w.ctrl, sizeof(Readback), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (pin) {
-        e = hipMemcpyAsync(pin, w.ctrl, sizeof(Readback), hipMemcpyDeviceToHost, stream);
-        if (e == hipSuccess) e = hipStreamSynchronize(stream);
         if (e == hipSuccess) *out = *pin;
-    } else {
-        e = hipMemcpyAsync(out, w.ctrl, sizeof(Readback), hipMemcpyDeviceToHost, stream);
-        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        give_readback(pin);
     }
     return hip_status(e);
 }
@@ -465,6 +489,24 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
     st = read_back(w, stream, &rb);
     if (st != NMS_OK) return st;
     return device_error(rb.error);
+}
+
+nms_status nms_debug_plan(int64_t n, int64_t num_images, int has_classes, int32_t *plan) {
+    if (plan == nullptr || n < 0 || num_images < 0) return NMS_INVALID_ARG;
+    if (n > NMS_MAX_BOXES) return NMS_TOO_LARGE;
+    for (int i = 0; i < NMS_PLAN_FIELDS; ++i) plan[i] = -1;
+    if (n == 0) return NMS_OK;
+    Layout L;
+    make_layout(n, &L);
+    Problem P = make_problem(nullptr, nullptr, n, 0.5f, nullptr, nullptr, num_images);
+    P.grouped = has_classes != 0 || num_images > 1;
+    P.strip = P.grouped ? STRIP_GROUPED : STRIP_SINGLE;
+    const bool fused = !P.grouped && L.words >= FUSE_MIN_WORDS && L.words <= FUSE_MAX_WORDS;
+    plan[NMS_PLAN_MASK_QSHIFT] = separate_mask_qshift(P, L);
+    plan[NMS_PLAN_FUSED] = fused ? 1 : 0;
+    plan[NMS_PLAN_FUSED_QSHIFT] = fused ? fused_mask_qshift(P, L) : -1;
+    plan[NMS_PLAN_RANK_SORT] = (!P.grouped && n <= RANK_SORT_MAX) ? 1 : 0;
+    return NMS_OK;
 }
 
 nms_status nms_debug_decide(const float *inter, const float *uni, int64_t count,

@@ -203,6 +203,10 @@ hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, i
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
+// Row-group split (log2) the mask launch takes on the current device: as a
+// separate launch, and as the fused mask + sweep launch.
+int separate_mask_qshift(const Problem &P, const Layout &L);
+int fused_mask_qshift(const Problem &P, const Layout &L);
 hipError_t launch_compact(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
                           hipStream_t stream);
 // Grouped input: sweep every segment with its own wave.  launch_sweep must

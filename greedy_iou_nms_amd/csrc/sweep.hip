@@ -114,13 +114,27 @@ constexpr uint32_t SPIN_LIMIT = 1u << 23;
 // Entries of a row tile's list held in registers: rounds of 64, in each of
 // an applier's two register sets; the rest is read when the kept set is
 // known.  The plain sweep's one workgroup has registers to spare and holds
-// 1536 entries (217 VGPRs: a build holding the whole 2048-entry list
-// compiled to exactly 256 VGPRs and gave wrong kept sets in about 5 % of the
-// calls on 8192 clustered boxes, where the 1536- and 1024-entry builds gave
-// none in 300 calls each); the fused sweep shares its kernel's register
-// budget with the mask and holds 384.
+// 1536 entries (217 VGPRs); the fused sweep shares its kernel's register
+// budget with the mask and holds 384.  A build holding the whole 2048-entry
+// list (256 VGPRs, no spills, no scratch, the resolver's code identical
+// instruction for instruction) gave wrong kept sets in about 5 % of the calls
+// on 8192 clustered boxes; the 1536- and 1024-entry builds gave none in 300
+// calls each.  That build issued up to 71 vector loads per applier wave
+// without a wait, more than the wave's vector-memory counter holds (see
+// VMCNT_CAPACITY below); the sizes are kept under both limits.
 template <bool FUSED>
 constexpr int rmax() { return FUSED ? 6 : 24; }
+
+// An applier issues, without a wait in between, the loads of one register
+// set (two per round: word index and value) and of the next chunk's first
+// level (NEAR + 1 words, the list length, the order entry).  The wave's
+// vector-memory counter holds at most 63 outstanding instructions; the
+// 2048-entry build that gave wrong kept sets was the only one that issued
+// more (71), so the count is kept under the counter's capacity.
+constexpr int VMCNT_CAPACITY = 63;
+static_assert(2 * rmax<false>() + (NEAR_TILES + 1) + 2 <= VMCNT_CAPACITY &&
+                  2 * rmax<true>() + (NEAR_TILES + 1) + 2 <= VMCNT_CAPACITY,
+              "an applier's loads in flight must fit the vector-memory counter");
 
 constexpr int NEAR = NEAR_TILES;
 static_assert(NEAR >= 2, "the resolver carries the words for the next two tiles in registers");
@@ -131,12 +145,15 @@ constexpr int LAG = NEAR + 1;
 constexpr int APPLIER_SLEEP = 1;
 
 // Chunk c's data sits in ring slot c mod RING.  An applier stages chunk x
-// after it has seen its previous chunk, x - A, settled, which came after the
-// resolver settled x - 2A (A = APPLIERS); the slot's previous chunk, x - RING,
-// is settled and read for the last time by then.  The settled word and
-// offset the resolver leaves for chunk c are read by chunk c's applier before
-// it reports chunk c applied, and the resolver reaches chunk c + RING only
-// after that report.
+// (A = APPLIERS) before it waits for chunk x - A, so the last settlement it
+// has seen is that of x - 2A, its chunk before last.  The resolver reads a
+// chunk's slot while settling the chunk two before it and, if the data was
+// late, while settling the chunk itself; so once x - 2A is settled the slot's
+// previous chunk, x - RING <= x - 2A, is read for the last time.  The settled
+// word and offset the resolver leaves for chunk c are read by chunk c's
+// applier before it reports chunk c applied, and the resolver reaches chunk
+// c + LAG < c + RING only after that report.  (tests/test_sweep_protocol.py
+// runs a model of this hand-over under random interleavings.)
 constexpr int RING = 16;
 static_assert(RING >= 2 * APPLIERS && RING > LAG && (RING & (RING - 1)) == 0,
               "the staging ring must outlast an applier's lead over the resolver");
@@ -985,17 +1002,24 @@ int fused_blocks_per_cu(size_t lds) {
     return cached[dev][b];
 }
 
+// one work item per mask wave; the number of resident waves only sets how
+// finely the pairs are split
+static maskcore::MaskArgs fused_mask_args(const Problem &P, const Layout &L) {
+    const size_t lds = (size_t)(L.words + NEAR_TILES) * sizeof(uint64_t);
+    const int per_cu = fused_blocks_per_cu(lds);
+    const int64_t cap = (int64_t)device_cu_count() * per_cu - 1;
+    return maskcore::make_mask_args(P, L, (cap > 1 ? cap : 1) * NWAVES);
+}
+
+int fused_mask_qshift(const Problem &P, const Layout &L) { return fused_mask_args(P, L).qshift; }
+
 hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
                              hipStream_t stream) {
     if (P.grouped || L.words < FUSE_MIN_WORDS || L.words > FUSE_MAX_WORDS)
         return hipErrorInvalidValue;
     const SweepArgs sa = make_sweep_args(P, L, w, keep_out);
-    // one work item per mask wave; the number of resident waves only sets
-    // how finely the pairs are split
     const size_t lds = (size_t)(L.words + NEAR_TILES) * sizeof(uint64_t);
-    const int per_cu = fused_blocks_per_cu(lds);
-    const int64_t cap = (int64_t)device_cu_count() * per_cu - 1;
-    const maskcore::MaskArgs ma = maskcore::make_mask_args(P, L, (cap > 1 ? cap : 1) * NWAVES);
+    const maskcore::MaskArgs ma = fused_mask_args(P, L);
     const int64_t pairs = maskcore::mask_items_upper_bound(P, L);
     const int64_t items = pairs << ma.qshift;
     int64_t blocks = (items + NWAVES - 1) / NWAVES;

@@ -26,9 +26,19 @@
  *
  * Memory.  Every pointer argument named "device" is HIP device memory on the
  * current device; the caller allocates and owns every buffer (inputs, output,
- * workspace).  The library allocates nothing, keeps no pointer after a call
- * returns and holds no device state between calls, so calls on different
- * streams with distinct workspaces may run concurrently.
+ * workspace).  The library allocates no device memory, keeps no pointer to a
+ * caller's buffer after a call returns and holds no device state between
+ * calls, so calls on different streams with distinct workspaces may run
+ * concurrently.  What the library does allocate, and keeps:
+ *   - pinned host buffers of 16 bytes (hipHostMalloc) for the read-back of
+ *     the kept count and the device-detected errors: a process-wide pool
+ *     of at most 64, one per call running at that moment, allocated when
+ *     every existing one is in use and kept until the process ends (past 64
+ *     concurrent calls the read-back goes to pageable memory instead);
+ *   - per profiled call (the *_profiled variants), HIP events, created and
+ *     destroyed inside the call.
+ * No library code runs at process exit (no static or thread-local object
+ * has a destructor).
  *
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  All work
  * is enqueued on it; each nms_* compute call returns after one
@@ -95,6 +105,11 @@ typedef enum nms_status {
  *                (dominated by the n * ceil(n/64) * 8-byte suppression
  *                bitmask), so no device synchronisation is needed.
  * Returns NMS_OK, NMS_INVALID_ARG (bytes NULL, n < 0) or NMS_TOO_LARGE.
+ * Why a bound from n alone: sizing a buffer from the data costs a device
+ * round trip before the work can start ("LeetCUDA 12-histogram", its binding
+ * section: the max() read back to size the histogram is a forced device
+ * synchronisation, which a caller-chosen size avoids).  Our reading: the
+ * caller sizes the workspace once from n and reuses it.
  */
 nms_status nms_workspace_size(int64_t n, int64_t num_images, int has_classes, size_t *bytes);
 
@@ -144,19 +159,26 @@ nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
                             size_t workspace_bytes, void *stream, float *stage_ms,
                             int flags);
 
-/* Human-readable name of a status ("NMS_OK", ...); never NULL. */
+/* Human-readable name of a status ("NMS_OK", ...); never NULL; the
+ * returned string is static.  Our reading: the pages' bindings raise
+ * exceptions on bad arguments (the device and dtype checks of "LeetCUDA
+ * 12-histogram"'s binding section), which cannot cross a C ABI, so every
+ * failure is a status code with a name. */
 const char *nms_status_string(nms_status status);
 
 /* ---- test-only exports: copy out one stage's intermediate result ---- */
 
 /*
- * nms_debug_order -- run the sort stage only.
+ * nms_debug_order -- run the sort stage only ("LeetCUDA 14-nms", algorithm
+ * step 1: a stable descending sort, equal scores in input order; the order is
+ * what bug 3's map-back needs).
  *   order_out        device, n int32: input index at each sorted position
  *                    (grouped input: ascending image, then class, then
  *                    descending score, then ascending index).
  *   score_order_out  device, n int32 or NULL: the plain score order
  *                    (descending score, ascending index).
- * Other arguments as for nms_f32.
+ * Other arguments as for nms_f32; returns as nms_f32 (NMS_NONFINITE_INPUT
+ * for a NaN score, with order_out still a permutation).
  */
 nms_status nms_debug_order(const float *scores, int64_t n, const int32_t *class_ids,
                            const int64_t *batch_offsets, int64_t num_images,
@@ -165,13 +187,17 @@ nms_status nms_debug_order(const float *scores, int64_t n, const int32_t *class_
 
 /*
  * nms_debug_mask -- run sort, gather and the IoU-mask stage, then expand the
- * mask into a dense row-major array.
- *   mask_out   device, n * ceil(n/64) uint64: word c of row p (sorted
- *              position p) has bit l set iff box q = 64c + l satisfies
- *              p < q < n, q in p's group and IoU > iou_thresh.  Words the
- *              kernel never computes (below the diagonal tile, beyond the
- *              group's last tile) read 0.
+ * mask into a dense row-major array.  The layout is the suppression bitmask
+ * of "LeetCUDA 14-nms", Phase 1 (its alignment rule 2: bit k of word w in
+ * every row stands for sorted box w * width + k, and boxes at or before the
+ * row vote 0), with 64-bit words instead of the page's 32-bit ones.
+ *   mask_out   device, n * ceil(n/64) uint64, row stride ceil(n/64) words:
+ *              word c of row p (sorted position p) has bit l set iff box
+ *              q = 64c + l satisfies p < q < n, q in p's group and
+ *              IoU > iou_thresh.  Words the kernel never computes (below
+ *              the diagonal tile, beyond the group's last tile) read 0.
  *   order_out  device, n int32 or NULL: the sorted order the rows refer to.
+ * Other arguments and returns as for nms_f32.
  */
 nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
                           float iou_thresh, const int32_t *class_ids,
@@ -179,8 +205,32 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
                           uint64_t *mask_out, int32_t *order_out, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/* nms_debug_plan fields. */
+#define NMS_PLAN_MASK_QSHIFT 0   /* log2 of the row groups a mask item of the   */
+                                 /* separate mask launch is split into (0: the  */
+                                 /* sign-test form of the overlap question)     */
+#define NMS_PLAN_FUSED 1         /* 1: nms_f32 runs mask and sweep in one launch */
+#define NMS_PLAN_FUSED_QSHIFT 2  /* the fused launch's split, -1 if not fused   */
+#define NMS_PLAN_RANK_SORT 3     /* 1: the one-launch ranking sort, 0: radix    */
+#define NMS_PLAN_FIELDS 8
+
 /*
- * nms_debug_decide -- the IoU-mask kernel's threshold test alone.
+ * nms_debug_plan -- the launch plan nms_f32 and nms_debug_mask take for n
+ * boxes on the current device, without running anything.
+ *   plan   host, NMS_PLAN_FIELDS int32: the fields above (unused ones -1;
+ *          all -1 for n = 0).
+ * Returns NMS_OK, NMS_INVALID_ARG (plan NULL, n < 0, num_images < 0) or
+ * NMS_TOO_LARGE.  Our reading: the pages time whole calls only; the plan is
+ * exported so that tests can show which kernel form produced a result.
+ */
+nms_status nms_debug_plan(int64_t n, int64_t num_images, int has_classes, int32_t *plan);
+
+/*
+ * nms_debug_decide -- the IoU-mask kernel's threshold test alone: the strict
+ * "IoU > threshold" of "LeetCUDA 14-nms" (introduction) on given
+ * intersection and union values, decided as the mask kernel decides it (its
+ * division-free form is this library's own and must agree with the float32
+ * quotient bit for bit, which this export lets a test check).
  *   inter, uni  device, count floats each: an intersection and a union value.
  *   out         device, count bytes: 1 iff the test "inter / uni > t" holds
  *               as the mask kernel decides it.

@@ -171,3 +171,29 @@ def test_matrix_host_argument_checks():
     assert _mcall(lib, 5, ws=FAKE + 64)[0] == "NMS_INVALID_ARG"
     assert _mcall(lib, 5, ws_bytes=100) == ("NMS_WORKSPACE_TOO_SMALL", 0)
     assert _mcall(lib, 512001)[0] == "NMS_TOO_LARGE"
+
+
+def test_binding_rejects_unusable_output_buffers():
+    """The binding hands `out` to the library as a raw int64 pointer: a
+    tensor of another dtype, a strided view, a tensor on another device or
+    one too small for n boxes must be refused before any device work."""
+    import torch
+
+    import greedy_iou_nms_amd as g
+
+    dev = torch.device("cpu")   # the check itself needs no GPU
+    good = torch.empty(10, dtype=torch.int64)
+    assert g._check_out(good, 10, dev) is good
+    assert g._check_out(None, 10, dev).dtype == torch.int64
+    with pytest.raises(TypeError):
+        g._check_out(torch.empty(10, dtype=torch.int32), 10, dev)
+    with pytest.raises(TypeError):
+        g._check_out(torch.empty(20, dtype=torch.float32), 10, dev)
+    with pytest.raises(ValueError):
+        g._check_out(torch.empty(20, dtype=torch.int64)[::2], 10, dev)
+    with pytest.raises(ValueError):
+        g._check_out(torch.empty(9, dtype=torch.int64), 10, dev)
+    with pytest.raises(ValueError):
+        g._check_out(good, 10, torch.device("meta"))
+    with pytest.raises(TypeError):
+        g._check_out([0] * 10, 10, dev)

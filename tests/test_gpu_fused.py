@@ -50,8 +50,9 @@ def test_fused_with_two_workgroups_per_cu():
     # 2501 row tiles: the removed bitmap (20 KB) beside the sweep's 42.8 KB
     # of LDS leaves room for two workgroups per CU instead of three, so the
     # fused launch takes its other occupancy and splits its items for it.
-    # Too large for the oracle in seconds: the fused result must equal the
-    # separate launches', which the oracle pins at the other sizes.
+    # The oracle comparison at this size is in test_gpu_coverage.py (on
+    # disjoint clusters); here the three launch forms must agree on the
+    # uniform boxes.
     n = 64 * 2500 + 5
     w = workloads.random_small(4242, n, canvas=60.0 + n / 8.0)
     note("fused two workgroups per CU n=%d" % n)

@@ -167,7 +167,7 @@ def test_literal_division_path_on_special_values():
 
 # ---------------------------------------------------------------- races and state
 
-@pytest.mark.parametrize("cfg", [2, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_ten_runs_identical(cfg):
     w = workloads.config(cfg, 0)
     note("determinism cfg=%d" % cfg)
