@@ -17,7 +17,7 @@ from typing import Dict, Optional, Tuple
 import torch
 
 __all__ = [
-    "NMSError", "STAGES", "nms", "nms_profiled", "workspace_size", "Workspace",
+    "NMSError", "STAGES", "nms", "nms_profiled", "nms_static", "workspace_size", "Workspace",
     "debug_order", "debug_mask", "debug_decide", "debug_plan", "library_path",
     "MATRIX_STAGES", "matrix_nms", "matrix_nms_profiled", "matrix_workspace_size",
 ]
@@ -62,6 +62,8 @@ def _load():
     lib.nms_f32.restype = ctypes.c_int
     lib.nms_f32_profiled.argtypes = common + [ctypes.POINTER(ctypes.c_float), ctypes.c_int]
     lib.nms_f32_profiled.restype = ctypes.c_int
+    lib.nms_f32_static.argtypes = [c_vp, c_vp, c_i64, c_f, c_vp, c_vp, c_i64, c_vp, p_i64, c_vp]
+    lib.nms_f32_static.restype = ctypes.c_int
     lib.nms_status_string.argtypes = [ctypes.c_int]
     lib.nms_status_string.restype = ctypes.c_char_p
     lib.nms_debug_order.argtypes = [c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp]
@@ -221,6 +223,32 @@ def nms(boxes: torch.Tensor, scores: torch.Tensor, iou_threshold: float,
     ``class_ids`` and/or ``batch_offsets`` boxes suppress only boxes of the
     same (image, class); the result is one list in global score order."""
     return _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, False)
+
+
+STATIC_MAX_BOXES = 16384  # NMS_STATIC_MAX_BOXES
+
+
+def nms_static(boxes: torch.Tensor, scores: torch.Tensor, iou_threshold: float,
+               class_ids: Optional[torch.Tensor] = None,
+               batch_offsets: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``nms`` through ``nms_f32_static``: the library's static scratch
+    instead of a workspace (at most STATIC_MAX_BOXES boxes; calls that
+    overlap on one device race).  With ``out`` given, the call allocates
+    nothing on the device."""
+    boxes, scores, class_ids, batch_offsets, num_images = _check_inputs(
+        boxes, scores, class_ids, batch_offsets)
+    device = boxes.device
+    n = boxes.shape[0]
+    with torch.cuda.device(device):
+        stream = torch.cuda.current_stream(device).cuda_stream
+        out = _check_out(out, n, device)
+        count = ctypes.c_int64(0)
+        _check(_lib.nms_f32_static(_ptr(boxes), _ptr(scores), n,
+                                   ctypes.c_float(float(iou_threshold)), _ptr(class_ids),
+                                   _ptr(batch_offsets), num_images, _ptr(out),
+                                   ctypes.byref(count), ctypes.c_void_p(stream)))
+    return out[:count.value]
 
 
 def nms_profiled(boxes, scores, iou_threshold, class_ids=None, batch_offsets=None,

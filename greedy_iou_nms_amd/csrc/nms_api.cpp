@@ -231,7 +231,8 @@ struct EventSet {
 nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thresh,
                    const int32_t *class_ids, const int64_t *offsets, int64_t num_images,
                    int64_t *keep_out, int64_t *num_kept, void *workspace, size_t ws_bytes,
-                   void *stream_ptr, float *stage_ms, bool allow_fusion) {
+                   void *stream_ptr, float *stage_ms, bool allow_fusion,
+                   bool pinned_pool = true) {
     if (num_kept == nullptr) return NMS_INVALID_ARG;
     *num_kept = 0;
     if (stage_ms)
@@ -276,7 +277,7 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     if (e != hipSuccess) return NMS_HIP_ERROR;
 
     Readback rb;
-    st = read_back(w, stream, &rb);
+    st = read_back(w, stream, &rb, pinned_pool);
     if (st != NMS_OK) return st;
     st = device_error(rb.error);
     if (st != NMS_OK) return st;
@@ -350,6 +351,35 @@ nms_status run_matrix(const float *boxes, const float *scores, int64_t n, float 
     return NMS_OK;
 }
 
+// Scratch of nms_f32_static: the workspace of one call, in a file-scope
+// device array.  Each device the library runs on holds its own copy (the HIP
+// runtime allocates it with the code object); host code may not use the
+// array's name as an address, only the pointer hipGetSymbolAddress returns
+// for the device, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[NMS_STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void *> g_scratch_ptr[MAX_DEVICES];
+
+// The current device's scratch address, or nullptr (with *status set).
+void *static_scratch(nms_status *status) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+        *status = NMS_HIP_ERROR;
+        return nullptr;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // two threads may both look it up; they get the same address
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            *status = NMS_HIP_ERROR;
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 }  // namespace
 }  // namespace gnms
 
@@ -374,6 +404,27 @@ nms_status nms_f32(const float *boxes, const float *scores, int64_t n, float iou
                    size_t workspace_bytes, void *stream) {
     return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
                    num_kept, workspace, workspace_bytes, stream, nullptr, true);
+}
+
+nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, float iou_thresh,
+                          const int32_t *class_ids, const int64_t *batch_offsets,
+                          int64_t num_images, int64_t *keep_out, int64_t *num_kept,
+                          void *stream) {
+    if (num_kept == nullptr) return NMS_INVALID_ARG;
+    *num_kept = 0;
+    nms_status st = check_common(n, iou_thresh, batch_offsets, num_images);
+    if (st != NMS_OK) return st;
+    if (n > NMS_STATIC_MAX_BOXES) return NMS_TOO_LARGE;
+    if (n == 0) return NMS_OK;
+    Layout L;
+    make_layout(n, &L);
+    if (L.total > (size_t)NMS_STATIC_SCRATCH_BYTES) return NMS_TOO_LARGE;
+    void *ws = static_scratch(&st);
+    if (ws == nullptr) return st;
+    // the same kernels as nms_f32 on the static scratch; the read-back goes
+    // to the caller's stack (pageable), so nothing is allocated
+    return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
+                   num_kept, ws, (size_t)NMS_STATIC_SCRATCH_BYTES, stream, nullptr, true, false);
 }
 
 nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,

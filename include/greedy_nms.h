@@ -36,7 +36,9 @@
  *     every existing one is in use and kept until the process ends (past 64
  *     concurrent calls the read-back goes to pageable memory instead);
  *   - per profiled call (the *_profiled variants), HIP events, created and
- *     destroyed inside the call.
+ *     destroyed inside the call;
+ *   - for nms_f32_static, a statically sized device array in the library's
+ *     code object (see there).
  * No library code runs at process exit (no static or thread-local object
  * has a destructor).
  *
@@ -140,6 +142,33 @@ nms_status nms_f32(const float *boxes, const float *scores, int64_t n, float iou
                    const int32_t *class_ids, const int64_t *batch_offsets, int64_t num_images,
                    int64_t *keep_out, int64_t *num_kept, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/* Largest n nms_f32_static accepts, and the size of its static scratch. */
+#define NMS_STATIC_MAX_BOXES 16384
+#define NMS_STATIC_SCRATCH_BYTES (48u << 20)
+
+/*
+ * nms_f32_static -- nms_f32 without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  It runs the same kernels as
+ * nms_f32 on a scratch array that the library holds in its code object: a
+ * file-scope device array of NMS_STATIC_SCRATCH_BYTES, one per device the
+ * library runs on, allocated by the HIP runtime when the library's code is
+ * loaded on that device and held until the process ends.  The call itself
+ * allocates nothing: no hipMalloc, no hipHostMalloc (the kept count is
+ * copied into the caller's stack frame), no events.
+ *   boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images,
+ *   keep_out, num_kept, stream   as for nms_f32.
+ * Returns as nms_f32, and NMS_TOO_LARGE for n > NMS_STATIC_MAX_BOXES.
+ * Every call on one device shares that device's scratch, which keeps the
+ * last call's contents (the kernels need no particular contents on entry):
+ * calls that overlap on one device -- from two host threads, or on two
+ * streams -- race and must be serialised by the caller.
+ */
+nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, float iou_thresh,
+                          const int32_t *class_ids, const int64_t *batch_offsets,
+                          int64_t num_images, int64_t *keep_out, int64_t *num_kept,
+                          void *stream);
 
 /* nms_f32_profiled flags. */
 #define NMS_PROFILE_NO_FUSION 1  /* run the mask and the sweep as separate */
