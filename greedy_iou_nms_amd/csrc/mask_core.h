@@ -92,6 +92,8 @@ struct MaskArgs {
     // 64 >> qshift rows: with few row tiles, whole pairs would leave most of
     // the GPU idle while one wave works through 64 rows.
     int qshift;
+    // the sort wrote the quantised pre-test words (one image, radix passes)
+    int use_packs;
 };
 
 // Read-only inputs and the output of the mask kernel.  They are separate
@@ -121,6 +123,7 @@ struct MaskPtrs {
     uint32_t *__restrict__ tent_wk;
     uint64_t *__restrict__ tent_val;
     uint64_t *__restrict__ tnear;
+    const uint2 *__restrict__ spk;
 };
 
 // v_writelane_b32: lane `lane` of the returned VGPR value becomes `val` (an
@@ -173,7 +176,7 @@ template <int S, bool GROUPED, int MODE, bool DIAG, bool SIGN>
 __device__ __forceinline__ void fast_rows(const MaskArgs &a, const MaskPtrs &m_, int p0, int k_lo,
                                           int k_hi, const float (&cx1)[S], const float (&cy1)[S],
                                           const float (&cx2)[S], const float (&cy2)[S],
-                                          const float (&ca)[S], const uint32_t (&cg)[S],
+                                          const uint32_t (&cg)[S],
                                           const uint64_t (&tmask)[S], int t_diag,
                                           uint32_t (&out_lo)[S], uint32_t (&out_hi)[S]) {
     // tiles per question: measured at 65,536 boxes, the sign form is
@@ -220,7 +223,9 @@ __device__ __forceinline__ void fast_rows(const MaskArgs &a, const MaskPtrs &m_,
                     const float in =
                         SIGN ? intersection(rx1, ry1, rx2, ry2, cx1[t], cy1[t], cx2[t], cy2[t])
                              : inter[j];
-                    const float uni = (ra + ca[t]) - in;
+                    // the column's area by the sort's expression (not held)
+                    const float ca = (cx2[t] - cx1[t]) * (cy2[t] - cy1[t]);
+                    const float uni = (ra + ca) - in;
                     bool pred = exceeds<MODE>(in, uni, a.t, a.mid);
                     if (GROUPED) pred = pred && (cg[t] == rg);
                     const uint64_t m = __ballot(pred) & touch;
@@ -232,15 +237,91 @@ __device__ __forceinline__ void fast_rows(const MaskArgs &a, const MaskPtrs &m_,
     }
 }
 
+// The rows k_lo .. k_hi - 1 of a work item with the quantised pre-test
+// (one image, t > 0, ordered boxes, radix-sorted so the words exist).  Per
+// pair two integer subtractions and an OR (PACK_* in nms_internal.h): a set
+// bit 31 or 15 rules the overlap out.  Two tiles are asked at once: the AND
+// of their words can only lose bits, so a group where no lane is left with
+// both bits clear has no overlap in either tile (the AND may also keep a
+// group that has none, when the tiles are ruled out on different axes; the
+// per-tile question then finds nothing).  Only the pre-test words of the
+// columns are held in registers: a group that passes loads its two tiles'
+// float boxes (from the cache: every item of the column tile reads them)
+// and computes the float32 intersection and threshold test as fast_rows()
+// does, with the column's area recomputed by the sort's expression.
+template <int S, bool GROUPED, int MODE, bool DIAG>
+__device__ __forceinline__ void packed_rows(const MaskArgs &a, const MaskPtrs &m_, int p0, int c0,
+                                            int k_lo, int k_hi, const uint32_t (&clo)[S],
+                                            const uint32_t (&chi)[S], const uint64_t (&tmask)[S],
+                                            int t_diag, uint32_t (&out_lo)[S],
+                                            uint32_t (&out_hi)[S]) {
+    static_assert(!GROUPED, "grouped input has no pre-test words");
+    const int lane = threadIdx.x & 63;
+    for (int k = k_lo; k < k_hi; ++k) {
+        const int p = p0 + k;
+        const uint2 rp = m_.spk[p];
+        const uint64_t dmask = k == 63 ? 0ull : (~0ull << (k + 1));
+#pragma unroll
+        for (int t0 = 0; t0 < S; t0 += 2) {
+            const uint32_t u0 = (chi[t0] - rp.x) | (rp.y - clo[t0]);
+            const uint32_t u1 = (chi[t0 + 1] - rp.x) | (rp.y - clo[t0 + 1]);
+            if (__ballot(((u0 & u1) & PACK_SIGNS) == 0u) == 0ull) continue;
+            // columns of both tiles (padding past n and tiles outside the
+            // band never pass the pre-test, so their lanes stay out of touch)
+            const float4 cb0 = m_.sb[64 * (c0 + t0) + lane];
+            const float4 cb1 = m_.sb[64 * (c0 + t0 + 1) + lane];
+            const float4 rb = m_.sb[p];
+            const float ra = m_.area[p];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int t = t0 + j;
+                uint64_t touch = __ballot(((j == 0 ? u0 : u1) & PACK_SIGNS) == 0u);
+                if (DIAG) touch &= tmask[t] & ((t == t_diag) ? dmask : ~0ull);
+                if (touch) {
+                    const float4 cb = j == 0 ? cb0 : cb1;
+                    const float in = intersection(rb.x, rb.y, rb.z, rb.w, cb.x, cb.y, cb.z, cb.w);
+                    const float ca = (cb.z - cb.x) * (cb.w - cb.y);
+                    const float uni = (ra + ca) - in;
+                    const bool pred = exceeds<MODE>(in, uni, a.t, a.mid);
+                    const uint64_t m = __ballot(pred) & touch;
+                    out_lo[t] = write_lane(out_lo[t], (uint32_t)m, k);
+                    out_hi[t] = write_lane(out_hi[t], (uint32_t)(m >> 32), k);
+                }
+            }
+        }
+    }
+}
+
+// Fused launch: report a finished item of row tile `pending` (if any) by
+// adding to done[pending].  The data the sweep reads was written with
+// device-scope stores, which write through the XCD's L2; once they are
+// acknowledged (s_waitcnt vmcnt(0) also counts stores) they are visible to
+// device-scope loads on every XCD, so a reader that sees the count sees the
+// data.  No L2 write-back (a release fence) is needed: that is for plain
+// stores, and the sweep reads none of those.  Every lane adds 1, so a
+// finished pair counts 64 << qshift: a lane-0-only branch here would put a
+// lane-divergent region in the caller's loop.
+// (The row tile is made visibly uniform: with an address the compiler takes
+// for a per-lane one, the 64 lanes' additions go out as 64 atomics instead
+// of one.)
+__device__ __forceinline__ void report_done(uint32_t *done, int &pending) {
+    const int r = __builtin_amdgcn_readfirstlane(pending);
+    if (r < 0) return;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+    __hip_atomic_fetch_add(&done[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pending = -1;
+}
+
 // One work item.  COHERENT (the fused mask + sweep kernel): the near words
 // and list entries, which the sweep reads while other items are still
 // running, are written with device-scope stores, and once they have all
 // completed the item adds 64 to done[r] (one per lane), the count of
 // finished items of its row tile times 64.  Plain stores may sit in the L2 of this XCD, which the sweep's
 // XCD does not see.
-template <int S, bool GROUPED, int MODE, bool COHERENT>
+template <int S, bool GROUPED, int MODE, bool COHERENT, bool PACKED>
 __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_, int item,
-                                          int stride, uint32_t *done) {
+                                          int stride, uint32_t *done, int &pending) {
     const int lane = threadIdx.x & 63;
     // the item's pair and rows within it
     const int rpi = 64 >> a.qshift;
@@ -289,20 +370,29 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
     // than branching around them; their boxes are replaced by an empty box
     // at 0, whose intersection with anything is exactly 0 (like the padding
     // boxes past n), so they never look like an overlap.
-    float cx1[S], cy1[S], cx2[S], cy2[S], ca[S];
-    uint32_t cg[S];
+    // With the quantised pre-test the columns' pre-test words take the place
+    // of their areas (recomputed where a tile passes), which keeps the
+    // registers of the two forms the same.
+    static_assert(!PACKED || (!GROUPED && MODE != MODE_LITERAL), "pre-test words: one image");
+    float cx1[S], cy1[S], cx2[S], cy2[S];
+    uint32_t cg[S], clo[S], chi[S];
     uint64_t tmask[S];
 #pragma unroll
     for (int t = 0; t < S; ++t) {
         const int c = c0 + t;
         const bool active = c >= r && c < cend;
         const int q = active ? 64 * c + lane : lane;
-        const float4 b = active ? m_.sb[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-        cx1[t] = b.x;
-        cy1[t] = b.y;
-        cx2[t] = b.z;
-        cy2[t] = b.w;
-        ca[t] = m_.area[q];
+        if constexpr (PACKED) {
+            const uint2 pk = active ? m_.spk[q] : make_uint2(PACK_NONE_LO, PACK_NONE_HI);
+            clo[t] = pk.x;
+            chi[t] = pk.y;
+        } else {
+            const float4 b = active ? m_.sb[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            cx1[t] = b.x;
+            cy1[t] = b.y;
+            cx2[t] = b.z;
+            cy2[t] = b.w;
+        }
         if (GROUPED) cg[t] = m_.seg[q];
         tmask[t] = active ? column_valid(c, a.n) : 0ull;
     }
@@ -326,7 +416,8 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
             for (int t = 0; t < S; ++t) {
                 const uint64_t live = tmask[t] & ((t == t_diag) ? dmask : ~0ull);
                 bool pred = suppresses<MODE>(rx1, ry1, rx2, ry2, ra, cx1[t], cy1[t], cx2[t],
-                                             cy2[t], ca[t], a.t, a.mid, a.pinf, a.ninf);
+                                             cy2[t], (cx2[t] - cx1[t]) * (cy2[t] - cy1[t]),
+                                             a.t, a.mid, a.pinf, a.ninf);
                 if (GROUPED) pred = pred && (cg[t] == rg);
                 const uint64_t m = __ballot(pred) & live;
                 out_lo[t] = write_lane(out_lo[t], (uint32_t)m, k);
@@ -339,23 +430,37 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
         // needs them anyway.  With many items the issue rate decides, and the
         // sign test costs fewer and cheaper instructions.
         const bool diag = t_diag >= 0 && t_diag < S;
-        if (a.qshift == 0) {
+        if constexpr (PACKED) {
+            {
+                if (diag)
+                    packed_rows<S, GROUPED, MODE, true>(a, m_, p0, c0, k_lo, k_hi, clo, chi,
+                                                        tmask, t_diag, out_lo, out_hi);
+                else
+                    packed_rows<S, GROUPED, MODE, false>(a, m_, p0, c0, k_lo, k_hi, clo, chi,
+                                                         tmask, t_diag, out_lo, out_hi);
+            }
+        }
+        if constexpr (PACKED) {
+        } else if (a.qshift == 0) {
             if (diag)
                 fast_rows<S, GROUPED, MODE, true, true>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2, cy2,
-                                                        ca, cg, tmask, t_diag, out_lo, out_hi);
+                                                        cg, tmask, t_diag, out_lo, out_hi);
             else
                 fast_rows<S, GROUPED, MODE, false, true>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2, cy2,
-                                                         ca, cg, tmask, t_diag, out_lo, out_hi);
+                                                         cg, tmask, t_diag, out_lo, out_hi);
         } else {
             if (diag)
                 fast_rows<S, GROUPED, MODE, true, false>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2, cy2,
-                                                         ca, cg, tmask, t_diag, out_lo, out_hi);
+                                                         cg, tmask, t_diag, out_lo, out_hi);
             else
                 fast_rows<S, GROUPED, MODE, false, false>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2,
-                                                          cy2, ca, cg, tmask, t_diag, out_lo,
+                                                          cy2, cg, tmask, t_diag, out_lo,
                                                           out_hi);
         }
     }
+    // COHERENT: the previous item's count, once its stores are acknowledged
+    // (they have had this item's computation to complete)
+    if (COHERENT) report_done(done, pending);
     if (mine) {
         const int p = p0 + lane;
         uint64_t *dst = m_.mask + (size_t)p * (size_t)stride + (size_t)(c0 - s0 * S);
@@ -402,41 +507,66 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
             }
         }
     }
-    if (COHERENT) {
-        // The data the sweep reads was written with device-scope stores,
-        // which write through this XCD's L2; once they are acknowledged
-        // (s_waitcnt vmcnt(0) also counts stores) they are visible to
-        // device-scope loads on every XCD, so a reader that sees the count
-        // sees the data.  No L2 write-back (a release fence) is needed: that
-        // is for plain stores, and the sweep reads none of those.
-        // Every lane adds 1, so a finished pair counts 64 << qshift: a
-        // lane-0-only branch here would put a lane-divergent region at the
-        // end of the caller's loop.
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        asm volatile("" ::: "memory");
-        __hip_atomic_fetch_add(&done[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // the count is reported with the next item's stores, or after the loop
+    if (COHERENT) pending = r;
 }
 
 // The work items of one launch, handed out to waves in item order (row tile
 // by row tile): wave slot `first` of `slots` takes items first, first +
 // slots, ... (launches give every wave at most one item unless the item
 // count exceeds what a grid can hold)
-template <int S, bool GROUPED, bool COHERENT>
+//
+// PACKED_ONLY (the fused launch, which runs for one image of at least 512
+// row tiles, always radix-sorted and never split): the division-free modes
+// come only in the pre-test form, so the kernel holds no code, and reserves
+// no registers, for the other forms.
+//
+// queue (the fused launch): the workgroup owns the block of `slots` items
+// from `first` on, and each of its waves takes the block's next item from a
+// counter in LDS until none is left.  A workgroup's waves keep taking items
+// while one of them is still busy, where with one item per wave the
+// workgroup (eight waves) would hold its slot until its slowest wave ended.
+// Blocks start in workgroup order, so items still finish row tile by row
+// tile.  (One counter in device memory for all waves was tried: its atomics
+// serialise, and the launch took twice as long.)
+template <int S, bool GROUPED, bool COHERENT, bool PACKED_ONLY = false>
 __device__ __forceinline__ void mask_items(const MaskArgs &a, const MaskPtrs &m_,
                                            const Ctrl *__restrict__ ctrl, int first, int slots,
-                                           uint32_t *done) {
+                                           uint32_t *done, uint32_t *queue = nullptr) {
+    static_assert(!(PACKED_ONLY && GROUPED), "grouped input has no pre-test words");
     const int num_items = ctrl->num_items << a.qshift;
     const bool fast = (ctrl->flags & FLAG_ORDERED_BOXES) && a.exact_ok;
+    const bool packed = a.use_packs && a.qshift == 0;
     const int stride = GROUPED ? ctrl->band_stride : a.mstride;
-    for (int item = first; item < num_items; item += slots) {
+    // queue: a counter in LDS over the workgroup's block of `slots` items
+    // from `first` on
+    const int end = queue ? (first + slots < num_items ? first + slots : num_items) : num_items;
+    auto next_item = [&](int item) -> int {
+        if (queue == nullptr) return item + slots;
+        uint32_t got = 0;
+        if ((threadIdx.x & 63) == 0)
+            got = __hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return first + (int)__builtin_amdgcn_readfirstlane(got);
+    };
+    int pending = -1;  // COHERENT: row tile of a finished item not yet counted
+    for (int item = queue ? next_item(0) : first; item < end; item = next_item(item)) {
         if (fast) {
-            if (a.odd) mask_item<S, GROUPED, MODE_ODD, COHERENT>(a, m_, item, stride, done);
-            else mask_item<S, GROUPED, MODE_EVEN, COHERENT>(a, m_, item, stride, done);
+            if constexpr (!GROUPED) {
+                if (PACKED_ONLY || packed) {
+                    if (a.odd) mask_item<S, false, MODE_ODD, COHERENT, true>(a, m_, item, stride, done, pending);
+                    else mask_item<S, false, MODE_EVEN, COHERENT, true>(a, m_, item, stride, done, pending);
+                    continue;
+                }
+            }
+            if constexpr (!PACKED_ONLY) {
+                if (a.odd) mask_item<S, GROUPED, MODE_ODD, COHERENT, false>(a, m_, item, stride, done, pending);
+                else mask_item<S, GROUPED, MODE_EVEN, COHERENT, false>(a, m_, item, stride, done, pending);
+            }
         } else {
-            mask_item<S, GROUPED, MODE_LITERAL, COHERENT>(a, m_, item, stride, done);
+            mask_item<S, GROUPED, MODE_LITERAL, COHERENT, false>(a, m_, item, stride, done, pending);
         }
     }
+    if (COHERENT) report_done(done, pending);
 }
 
 // Kernel arguments of the mask stage, filled on the host; `slots` is the

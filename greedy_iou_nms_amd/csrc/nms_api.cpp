@@ -64,6 +64,8 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_mlo = take(np * 8);
     L.off_mhi = take(np * 8);
     L.off_mdrop = take((size_t)L.words * 8 + 8);
+    L.off_tile_ext = take((size_t)L.tiles * 16);
+    L.off_spk = take(np * 8);
     L.off_mask = take((size_t)n * (size_t)L.mstride * 8);
     L.total = off;
     *out = L;
@@ -109,6 +111,8 @@ Work carve(void *workspace, const Layout &L) {
     w.mlo = reinterpret_cast<double *>(b + L.off_mlo);
     w.mhi = reinterpret_cast<double *>(b + L.off_mhi);
     w.mdrop = reinterpret_cast<uint64_t *>(b + L.off_mdrop);
+    w.tile_ext = reinterpret_cast<float4 *>(b + L.off_tile_ext);
+    w.spk = reinterpret_cast<uint2 *>(b + L.off_spk);
     return w;
 }
 
@@ -264,8 +268,7 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     // One image of moderate size: the sweep runs inside the mask launch.  The
     // plain sweep launch still follows; it does nothing when the fused sweep
     // finished.
-    const bool fused = allow_fusion && !P.grouped && L.words >= FUSE_MIN_WORDS &&
-                       L.words <= FUSE_MAX_WORDS;
+    const bool fused = allow_fusion && fused_launch_applies(P, L);
     if (e == hipSuccess)
         e = fused ? launch_mask_sweep(P, L, w, keep_out, stream) : launch_mask(P, L, w, stream);
     if (e == hipSuccess) e = mark(3);
@@ -552,7 +555,7 @@ nms_status nms_debug_plan(int64_t n, int64_t num_images, int has_classes, int32_
     Problem P = make_problem(nullptr, nullptr, n, 0.5f, nullptr, nullptr, num_images);
     P.grouped = has_classes != 0 || num_images > 1;
     P.strip = P.grouped ? STRIP_GROUPED : STRIP_SINGLE;
-    const bool fused = !P.grouped && L.words >= FUSE_MIN_WORDS && L.words <= FUSE_MAX_WORDS;
+    const bool fused = fused_launch_applies(P, L);
     plan[NMS_PLAN_MASK_QSHIFT] = separate_mask_qshift(P, L);
     plan[NMS_PLAN_FUSED] = fused ? 1 : 0;
     plan[NMS_PLAN_FUSED_QSHIFT] = fused ? fused_mask_qshift(P, L) : -1;

@@ -81,6 +81,23 @@ constexpr int TILE_LIST_CAP = 2048;
 // into tnear so that the 64 rows of a tile read word j with one coalesced
 // load.  Words further right are applied by helper waves from the lists.
 constexpr int NEAR_TILES = 4;
+// Quantised overlap pre-test (one image sorted by radix passes).  Every
+// sorted box also gets two 32-bit words, each holding two 16-bit fields of
+// coordinates quantised to 0 .. QMAX on a grid over the extent of all boxes:
+//   lo = qx1 << 16 | (QMAX - qy1)          hi = qx2' << 16 | (0x8000 + QMAX - qy2')
+// where q rounds down and qx2' = q(x2) + 1, qy2' = q(y2) + 1.  For a row box
+// r and a column box c, the 32-bit differences hi_c - lo_r and hi_r - lo_c
+// compare both axes at once (the low field never borrows from the high one):
+// bit 31 is set iff the x fields are ordered, bit 15 iff the y fields are,
+// in the way that rules an overlap out.  Rounding never reverses an order,
+// so a pair whose boxes overlap (x2_c > x1_r, ...) never has one of these
+// bits set; a pair with a bit set cannot overlap.  Columns that take no part
+// hold PACK_NONE, which always has bit 15 set against any row.
+constexpr uint32_t PACK_QMAX = 32767u;
+constexpr uint32_t PACK_SIGNS = 0x80008000u;
+constexpr uint32_t PACK_NONE_LO = 0x00007FFFu;
+constexpr uint32_t PACK_NONE_HI = 0x0000FFFFu;
+
 // Largest grid (in threads) a launch uses; kernels loop over what lies past it.
 constexpr int64_t MAX_GRID_THREADS = (int64_t)1 << 31;
 
@@ -107,6 +124,7 @@ struct Layout {
     size_t off_gcls = 0, off_gimg = 0, off_pass_plan = 0, off_gbase = 0;
     size_t off_done = 0, off_seg_start = 0, off_start_bits = 0, off_block_cnt = 0;
     size_t off_momax = 0, off_mscore = 0, off_mlo = 0, off_mhi = 0, off_mdrop = 0;
+    size_t off_tile_ext = 0, off_spk = 0;
     // the suppression bitmask comes last: Matrix NMS uses everything before it
     size_t off_mask = 0, total = 0;
 };
@@ -161,6 +179,11 @@ struct Work {
     float *mscore;
     double *mlo, *mhi;
     uint64_t *mdrop;
+    // one image sorted by radix passes: per radix tile the extent of its
+    // boxes (min x1, min y1, max x2, max y2), and per sorted position the
+    // quantised words (lo, hi) of the overlap pre-test (see PACK_*)
+    float4 *tile_ext;
+    uint2 *spk;
 };
 
 Work carve(void *workspace, const Layout &L);
@@ -207,6 +230,9 @@ int device_cu_count();
 // separate launch, and as the fused mask + sweep launch.
 int separate_mask_qshift(const Problem &P, const Layout &L);
 int fused_mask_qshift(const Problem &P, const Layout &L);
+// nms_f32 runs mask and sweep in one launch (one image of FUSE_MIN_WORDS to
+// FUSE_MAX_WORDS row tiles whose mask takes the pre-test form).
+bool fused_launch_applies(const Problem &P, const Layout &L);
 hipError_t launch_compact(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
                           hipStream_t stream);
 // Grouped input: sweep every segment with its own wave.  launch_sweep must

@@ -100,6 +100,7 @@ __device__ __forceinline__ uint32_t image_of(const int64_t *off, int num_images,
 }
 
 struct KeysArgs {
+    const float4 *boxes;       // one image: for the extent of the boxes (may be null)
     const float *scores;
     const int32_t *class_ids;  // grouped input only (may be null)
     const int64_t *offsets;    // grouped input only (may be null)
@@ -140,6 +141,7 @@ __device__ __forceinline__ void per_call_init(const KeysArgs &a, int gid, int gs
             w.sb[p] = make_float4(0.f, 0.f, 0.f, 0.f);
             w.area[p] = 0.0f;
             if (GROUPED) w.seg[p] = 0xFFFFFFFFu;
+            else w.spk[p] = make_uint2(PACK_NONE_LO, PACK_NONE_HI);
         }
     }
 }
@@ -195,6 +197,45 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
                     atomicAdd(&hist[8 + d][(m >> (8 * d)) & 255u], 1u);
                 }
             }
+        }
+    }
+    if constexpr (!GROUPED) {
+        // extent of this tile's boxes (every coordinate), for the quantised
+        // overlap pre-test; non-finite values make the pre-test pass
+        // everything, and such input is reported as an error anyway
+        __shared__ float4 ext_sh[NT / 64];
+        float4 ex = make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
+        if (a.boxes) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int i = base + e * 64;
+                if (i < a.n) {
+                    const float4 b = a.boxes[i];
+                    ex.x = fminf(ex.x, fminf(b.x, b.z));
+                    ex.y = fminf(ex.y, fminf(b.y, b.w));
+                    ex.z = fmaxf(ex.z, fmaxf(b.x, b.z));
+                    ex.w = fmaxf(ex.w, fmaxf(b.y, b.w));
+                }
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            ex.x = fminf(ex.x, __shfl_xor(ex.x, o, 64));
+            ex.y = fminf(ex.y, __shfl_xor(ex.y, o, 64));
+            ex.z = fmaxf(ex.z, __shfl_xor(ex.z, o, 64));
+            ex.w = fmaxf(ex.w, __shfl_xor(ex.w, o, 64));
+        }
+        if (lane == 0) ext_sh[wave] = ex;
+        __syncthreads();
+        if (tid == 0) {
+            float4 t = ext_sh[0];
+            for (int v = 1; v < NT / 64; ++v) {
+                t.x = fminf(t.x, ext_sh[v].x);
+                t.y = fminf(t.y, ext_sh[v].y);
+                t.z = fmaxf(t.z, ext_sh[v].z);
+                t.w = fmaxf(t.w, ext_sh[v].w);
+            }
+            w.tile_ext[tile] = t;
         }
     }
     const int gid = tile * NT + tid, gsz = a.tiles * NT;
@@ -483,7 +524,36 @@ struct PassSmem {
     uint32_t tile;
     uint32_t err;
     uint32_t unordered;
+    float4 ext[NWAVES];
 };
+
+// The quantised pre-test words of one box (see PACK_* in nms_internal.h):
+// q(v) = min(floor((v - lo) * s), QMAX - 1), which never reverses an order;
+// the right and bottom edges take q + 1.
+struct PackScale {
+    float x0, y0, sx, sy;
+};
+
+__device__ __forceinline__ uint32_t quantise(float v, float lo, float s) {
+    const float q = fminf(fmaxf(floorf((v - lo) * s), 0.0f), (float)(PACK_QMAX - 1u));
+    return (uint32_t)q;
+}
+
+__device__ __forceinline__ uint2 pack_box(float4 b, const PackScale &ps) {
+    const uint32_t x1 = quantise(b.x, ps.x0, ps.sx), y1 = quantise(b.y, ps.y0, ps.sy);
+    const uint32_t x2 = quantise(b.z, ps.x0, ps.sx) + 1u, y2 = quantise(b.w, ps.y0, ps.sy) + 1u;
+    return make_uint2((x1 << 16) | (PACK_QMAX - y1), (x2 << 16) | (0x8000u + PACK_QMAX - y2));
+}
+
+// Grid step for an axis of extent lo .. hi: QMAX - 1 steps, or 0 (every
+// coordinate on step 0, so the pre-test rules nothing out) when the extent
+// is empty, not finite or too small for a finite step.
+__device__ __forceinline__ float pack_step(float lo, float hi) {
+    const float d = hi - lo;
+    if (!(d > 0.0f) || !(d < INFINITY)) return 0.0f;
+    const float s = (float)(PACK_QMAX - 1u) / d;
+    return s < INFINITY ? s : 0.0f;
+}
 
 // Passes 0-3 sort on the score key (read from the key buffer), 4-7 on the
 // class key, 8-11 on the image; the last two read the key of each element's
@@ -654,6 +724,39 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
     __syncthreads();
     const int count = a.n - tile * TILE < TILE ? a.n - tile * TILE : TILE;
     bool finite = true, ordered = true;
+    // one image: the grid of the quantised pre-test, from every tile's extent
+    const bool packs = pl.last && !a.grouped && a.boxes != nullptr;
+    PackScale ps{0.f, 0.f, 0.f, 0.f};
+    if (packs) {
+        float4 ex = make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
+        for (int t = tid; t < a.tiles; t += NT) {
+            const float4 te = w.tile_ext[t];
+            ex.x = fminf(ex.x, te.x);
+            ex.y = fminf(ex.y, te.y);
+            ex.z = fmaxf(ex.z, te.z);
+            ex.w = fmaxf(ex.w, te.w);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            ex.x = fminf(ex.x, __shfl_xor(ex.x, o, 64));
+            ex.y = fminf(ex.y, __shfl_xor(ex.y, o, 64));
+            ex.z = fmaxf(ex.z, __shfl_xor(ex.z, o, 64));
+            ex.w = fmaxf(ex.w, __shfl_xor(ex.w, o, 64));
+        }
+        if (lane == 0) sm.ext[wave] = ex;
+        __syncthreads();
+        ex = sm.ext[0];
+        for (int v = 1; v < NWAVES; ++v) {
+            ex.x = fminf(ex.x, sm.ext[v].x);
+            ex.y = fminf(ex.y, sm.ext[v].y);
+            ex.z = fmaxf(ex.z, sm.ext[v].z);
+            ex.w = fmaxf(ex.w, sm.ext[v].w);
+        }
+        ps.x0 = ex.x;
+        ps.y0 = ex.y;
+        ps.sx = pack_step(ex.x, ex.z);
+        ps.sy = pack_step(ex.y, ex.w);
+    }
     if (!pl.last) {
         for (int s = tid; s < count; s += NT) {
             const uint32_t key = sm.stage_k[s];
@@ -700,6 +803,7 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
                 ordered = ordered && bj.x < bj.z && bj.y < bj.w && ar > 0.0f && ar < INFINITY;
                 w.sb[pos[j]] = bj;
                 w.area[pos[j]] = ar;
+                if (packs) w.spk[pos[j]] = pack_box(bj, ps);
             }
         }
     }
@@ -861,6 +965,7 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
                              hipStream_t stream) {
     const int tiles = (int)L.tiles;
     KeysArgs ka;
+    ka.boxes = reinterpret_cast<const float4 *>(P.boxes);
     ka.scores = P.scores;
     ka.class_ids = P.class_ids;
     ka.offsets = P.offsets;

@@ -813,12 +813,17 @@ __global__ __launch_bounds__(GS_THREADS) void group_sweep_kernel(GroupSweepArgs 
     }
 }
 
+// Mask work items per workgroup of the fused launch: four per wave, taken
+// from the block's queue in LDS.
+constexpr int FUSED_BLOCK_ITEMS = 4 * NWAVES;
+
 // Mask and sweep in one launch (one image).  Workgroup 0 runs the sweep;
-// every wave of the other workgroups computes one mask work item.  The GPU
-// starts workgroups in order as earlier ones leave, so items start row tile
-// by row tile, and a wave that finishes early is replaced by the next
-// workgroup rather than idling at the end, as a fixed share of items per
-// wave would: waves of one compute unit do not progress at the same rate.
+// each of the other workgroups computes a block of FUSED_BLOCK_ITEMS mask
+// work items, its waves taking the block's items one at a time from a
+// counter in LDS.  The GPU starts workgroups in order as earlier ones
+// leave, so items start row tile by row tile, and a wave that finishes an
+// item early takes the next one rather than idling until its workgroup's
+// slowest wave is done.
 // The sweep follows the finished row tiles while later ones are still being
 // computed.  No mask wave ever waits for anything, so every item completes
 // whatever the order in which workgroups are scheduled.
@@ -829,7 +834,7 @@ __global__ __launch_bounds__(NT, 6) void mask_sweep_kernel(
     const int32_t *__restrict__ item_base, uint64_t *__restrict__ mask,
     uint32_t *__restrict__ tcount, uint32_t *__restrict__ tent_wk,
     uint64_t *__restrict__ tent_val, uint64_t *__restrict__ tnear, uint32_t *__restrict__ done,
-    SweepArgs sa) {
+    const uint2 *__restrict__ spk, SweepArgs sa) {
     extern __shared__ uint64_t removed[];
     __shared__ SweepSmem sm;
     if (blockIdx.x == 0) {
@@ -837,10 +842,14 @@ __global__ __launch_bounds__(NT, 6) void mask_sweep_kernel(
         return;
     }
     const maskcore::MaskPtrs m_{sb,     area,   nullptr, tile_cend, item_base,
-                                mask,   tcount, tent_wk, tent_val,  tnear};
+                                mask,   tcount, tent_wk, tent_val,  tnear,     spk};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    maskcore::mask_items<STRIP_SINGLE, false, true>(ma, m_, ctrl, (blockIdx.x - 1) * NWAVES + wave,
-                                                    (gridDim.x - 1) * NWAVES, done);
+    __shared__ uint32_t item_queue;
+    if (threadIdx.x == 0) item_queue = 0u;
+    __syncthreads();
+    (void)wave;
+    maskcore::mask_items<STRIP_SINGLE, false, true, true>(
+        ma, m_, ctrl, (blockIdx.x - 1) * FUSED_BLOCK_ITEMS, FUSED_BLOCK_ITEMS, done, &item_queue);
 }
 
 // ---------------------------------------------------------------- compaction
@@ -1013,24 +1022,31 @@ static maskcore::MaskArgs fused_mask_args(const Problem &P, const Layout &L) {
 
 int fused_mask_qshift(const Problem &P, const Layout &L) { return fused_mask_args(P, L).qshift; }
 
+bool fused_launch_applies(const Problem &P, const Layout &L) {
+    if (P.grouped || L.words < FUSE_MIN_WORDS || L.words > FUSE_MAX_WORDS) return false;
+    // the fused kernel holds only the pre-test form of the division-free test
+    const maskcore::MaskArgs ma = fused_mask_args(P, L);
+    return ma.use_packs && ma.qshift == 0;
+}
+
 hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
                              hipStream_t stream) {
-    if (P.grouped || L.words < FUSE_MIN_WORDS || L.words > FUSE_MAX_WORDS)
-        return hipErrorInvalidValue;
+    if (!fused_launch_applies(P, L)) return hipErrorInvalidValue;
     const SweepArgs sa = make_sweep_args(P, L, w, keep_out);
     const size_t lds = (size_t)(L.words + NEAR_TILES) * sizeof(uint64_t);
     const maskcore::MaskArgs ma = fused_mask_args(P, L);
     const int64_t pairs = maskcore::mask_items_upper_bound(P, L);
     const int64_t items = pairs << ma.qshift;
-    int64_t blocks = (items + NWAVES - 1) / NWAVES;
-    // (the grid's thread count must fit in 32 bits; waves loop past that)
-    if (blocks > MAX_GRID_THREADS / NT) blocks = MAX_GRID_THREADS / NT;
+    // one block of FUSED_BLOCK_ITEMS items per mask workgroup
+    int64_t blocks = (items + FUSED_BLOCK_ITEMS - 1) / FUSED_BLOCK_ITEMS;
+    // (the grid's thread count must fit in 32 bits)
+    if (blocks > MAX_GRID_THREADS / NT - 1) return hipErrorInvalidValue;
     if (blocks < 1) blocks = 1;
     SweepArgs sa2 = sa;
     sa2.done_shift = ma.qshift;  // a finished pair counts 64 << qshift
     hipLaunchKernelGGL(mask_sweep_kernel, dim3((unsigned)(blocks + 1)), dim3(NT), lds, stream, ma,
                        w.ctrl, w.sb, w.area, w.tile_cend, w.item_base, w.mask, w.tcount,
-                       w.tent_wk, w.tent_val, w.tnear, w.done, sa2);
+                       w.tent_wk, w.tent_val, w.tnear, w.done, w.spk, sa2);
     return hipGetLastError();
 }
 

@@ -53,12 +53,15 @@ def _clustered(n, seed, canvas, cluster=16, jitter=6.0, edge_ties=True):
                               scores.astype(np.float32), 0.5)
 
 
-@pytest.mark.parametrize("n,seed", [(16385, 0), (20011, 1)])
+# 14,000 boxes: sorted by ranking, the float sign test; 16,385 and more:
+# radix-sorted, the quantised pre-test
+@pytest.mark.parametrize("n,seed", [(14000, 2), (16385, 0), (20011, 1)])
 def test_mask_sign_path_matches_definition(n, seed):
     g = _g()
     device()
     plan = g.debug_plan(n)
     assert plan["mask_qshift"] == 0, plan   # the sign-test form
+    assert plan["rank_sort"] == (1 if n <= 16384 else 0), plan
     w = _clustered(n, seed, canvas=2000.0 * np.sqrt(n / 8192))
     note("mask sign path n=%d" % n)
     dev = device()
@@ -145,3 +148,35 @@ def test_matrix_nms_large_mixed_against_oracle():
     got = g.matrix_nms(to_dev(w.boxes, dev), to_dev(w.scores, dev), 0.1, 0.5).cpu().numpy()
     want = oracle.c_matrix_nms(w.boxes, w.scores, 0.1, 0.5)
     np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("kind", ["wide_range", "negative_far", "tiny_boxes"])
+def test_quantised_pretest_on_extreme_ranges(kind):
+    # The pre-test quantises coordinates to 15 bits over the extent of all
+    # boxes: a huge extent makes its grid coarse (it then rules out less),
+    # never wrong.  Word by word against the definition, and end to end.
+    g = _g()
+    dev = device()
+    n = 20011
+    rng = np.random.default_rng({"wide_range": 1, "negative_far": 2, "tiny_boxes": 3}[kind])
+    w = _clustered(n, 31, canvas=3000.0, edge_ties=False)
+    b = w.boxes.astype(np.float64)
+    if kind == "wide_range":
+        b[:50] += rng.uniform(-1e7, 1e7, (50, 1))          # a few boxes far out
+    elif kind == "negative_far":
+        b -= 5e6                                            # large negative coordinates
+    else:
+        c = b[:, :2] + (b[:, 2:] - b[:, :2]) / 2
+        s = rng.uniform(1e-3, 3e-3, (n, 1))
+        b = np.concatenate([c / 1000 - s, c / 1000 + s], axis=1)   # tiny boxes, tiny canvas
+    w = workloads.Workload(kind, b.astype(np.float32), w.scores, 0.5)
+    assert np.all(w.boxes[:, 0] < w.boxes[:, 2]) and np.all(w.boxes[:, 1] < w.boxes[:, 3])
+    note("quantised pre-test %s n=%d" % (kind, n))
+    m, order = g.debug_mask(to_dev(w.boxes, dev), to_dev(w.scores, dev), w.iou_threshold)
+    m = m.cpu().numpy().view(np.uint64)
+    order = order.cpu().numpy()
+    want = oracle.mask_rows(w.boxes, w.iou_threshold, order)
+    bad = np.argwhere(m != want)
+    assert bad.size == 0, "first differing (row, word): %s" % (bad[:5].tolist(),)
+    np.testing.assert_array_equal(gpu_nms(w.boxes, w.scores, w.iou_threshold),
+                                  oracle.c_nms(w.boxes, w.scores, w.iou_threshold))
