@@ -261,11 +261,23 @@ __device__ __forceinline__ void packed_rows(const MaskArgs &a, const MaskPtrs &m
         const int p = p0 + k;
         const uint2 rp = m_.spk[p];
         const uint64_t dmask = k == 63 ? 0ull : (~0ull << (k + 1));
+        // every tile's words first, and one question for the whole row: the
+        // smallest of the groups' ANDed sign bits is 0 where some group may
+        // overlap (most rows have none, and cost one branch)
+        uint32_t u[S], grp[S / 2];
+#pragma unroll
+        for (int t = 0; t < S; ++t) u[t] = (chi[t] - rp.x) | (rp.y - clo[t]);
+        uint32_t least = ~0u;
+#pragma unroll
+        for (int g = 0; g < S / 2; ++g) {
+            grp[g] = (u[2 * g] & u[2 * g + 1]) & PACK_SIGNS;
+            least = least < grp[g] ? least : grp[g];
+        }
+        if (__ballot(least == 0u) == 0ull) continue;
 #pragma unroll
         for (int t0 = 0; t0 < S; t0 += 2) {
-            const uint32_t u0 = (chi[t0] - rp.x) | (rp.y - clo[t0]);
-            const uint32_t u1 = (chi[t0 + 1] - rp.x) | (rp.y - clo[t0 + 1]);
-            if (__ballot(((u0 & u1) & PACK_SIGNS) == 0u) == 0ull) continue;
+            const uint32_t u0 = u[t0], u1 = u[t0 + 1];
+            if (__ballot(grp[t0 / 2] == 0u) == 0ull) continue;
             // columns of both tiles (padding past n and tiles outside the
             // band never pass the pre-test, so their lanes stay out of touch)
             const float4 cb0 = m_.sb[64 * (c0 + t0) + lane];
