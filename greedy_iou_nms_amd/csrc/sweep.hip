@@ -816,6 +816,19 @@ __global__ __launch_bounds__(GS_THREADS) void group_sweep_kernel(GroupSweepArgs 
 // Mask work items per workgroup of the fused launch: four per wave, taken
 // from the block's queue in LDS.
 constexpr int FUSED_BLOCK_ITEMS = 4 * NWAVES;
+// Workgroups go to the XCDs in turn (workgroup b to XCD b mod 8), and the
+// XCD that holds the sweep's workgroup computes its share of the mask more
+// slowly (measured: its last item ended 25 us after the others' at 65,536
+// boxes, about 7 %), so its workgroups take fewer items.
+constexpr int FUSED_XCDS = 8;
+constexpr int FUSED_BLOCK_ITEMS_SWEEP_XCD = FUSED_BLOCK_ITEMS - 2;
+
+// First item of mask workgroup b (b >= 1; workgroup 0 is the sweep).
+__host__ __device__ __forceinline__ int64_t fused_block_start(int64_t b) {
+    const int64_t before = b - 1, on_sweep_xcd = before / FUSED_XCDS;
+    return (before - on_sweep_xcd) * FUSED_BLOCK_ITEMS +
+           on_sweep_xcd * FUSED_BLOCK_ITEMS_SWEEP_XCD;
+}
 
 // Mask and sweep in one launch (one image).  Workgroup 0 runs the sweep;
 // each of the other workgroups computes a block of FUSED_BLOCK_ITEMS mask
@@ -849,7 +862,9 @@ __global__ __launch_bounds__(NT, 6) void mask_sweep_kernel(
     __syncthreads();
     (void)wave;
     maskcore::mask_items<STRIP_SINGLE, false, true, true>(
-        ma, m_, ctrl, (blockIdx.x - 1) * FUSED_BLOCK_ITEMS, FUSED_BLOCK_ITEMS, done, &item_queue);
+        ma, m_, ctrl, (int)fused_block_start(blockIdx.x),
+        (int)(fused_block_start(blockIdx.x + 1) - fused_block_start(blockIdx.x)), done,
+        &item_queue);
 }
 
 // ---------------------------------------------------------------- compaction
@@ -1037,8 +1052,9 @@ hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, i
     const maskcore::MaskArgs ma = fused_mask_args(P, L);
     const int64_t pairs = maskcore::mask_items_upper_bound(P, L);
     const int64_t items = pairs << ma.qshift;
-    // one block of FUSED_BLOCK_ITEMS items per mask workgroup
+    // one block of items per mask workgroup (fewer on the sweep's XCD)
     int64_t blocks = (items + FUSED_BLOCK_ITEMS - 1) / FUSED_BLOCK_ITEMS;
+    while (fused_block_start(blocks + 1) < items) ++blocks;
     // (the grid's thread count must fit in 32 bits)
     if (blocks > MAX_GRID_THREADS / NT - 1) return hipErrorInvalidValue;
     if (blocks < 1) blocks = 1;
