@@ -10,6 +10,7 @@ library has not been built.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import threading
 from typing import Dict, Optional, Tuple
@@ -60,6 +61,8 @@ def _load():
     common = [c_vp, c_vp, c_i64, c_f, c_vp, c_vp, c_i64, c_vp, p_i64, c_vp, c_sz, c_vp]
     lib.nms_f32.argtypes = common
     lib.nms_f32.restype = ctypes.c_int
+    lib.nms_f32_ex.argtypes = common + [ctypes.c_int]
+    lib.nms_f32_ex.restype = ctypes.c_int
     lib.nms_f32_profiled.argtypes = common + [ctypes.POINTER(ctypes.c_float), ctypes.c_int]
     lib.nms_f32_profiled.restype = ctypes.c_int
     lib.nms_f32_static.argtypes = [c_vp, c_vp, c_i64, c_f, c_vp, c_vp, c_i64, c_vp, p_i64, c_vp]
@@ -94,10 +97,41 @@ def _check(status: int) -> None:
 
 
 def workspace_size(n: int, num_images: int = 0, has_classes: bool = False) -> int:
+    return _workspace_size(int(n), int(num_images), bool(has_classes))
+
+
+@functools.lru_cache(maxsize=256)
+def _workspace_size(n: int, num_images: int, has_classes: bool) -> int:
+    # a bound from the sizes alone, so it can be remembered
     out = ctypes.c_size_t(0)
-    _check(_lib.nms_workspace_size(int(n), int(num_images), int(bool(has_classes)),
-                                   ctypes.byref(out)))
+    _check(_lib.nms_workspace_size(n, num_images, int(has_classes), ctypes.byref(out)))
     return int(out.value)
+
+
+def _raw_stream(device: torch.device) -> int:
+    """The current stream of ``device`` as a raw hipStream_t value."""
+    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if get is not None:
+        return int(get(device.index))
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class _OnDevice:
+    """``torch.cuda.device(device)`` only when it is not already current (the
+    switch costs a few microseconds per call)."""
+
+    def __init__(self, device: torch.device):
+        self.ctx = None if torch.cuda.current_device() == device.index else \
+            torch.cuda.device(device)
+
+    def __enter__(self):
+        if self.ctx is not None:
+            self.ctx.__enter__()
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            return self.ctx.__exit__(*exc)
+        return False
 
 
 class Workspace:
@@ -145,8 +179,10 @@ def _check_inputs(boxes, scores, class_ids, batch_offsets):
         raise ValueError("scores must have shape (N,)")
     if scores.device != boxes.device:
         raise ValueError("scores must be on the device of boxes")
-    boxes = boxes.contiguous()
-    scores = scores.contiguous()
+    if not boxes.is_contiguous():
+        boxes = boxes.contiguous()
+    if not scores.is_contiguous():
+        scores = scores.contiguous()
     if class_ids is not None:
         if class_ids.dtype != torch.int32 or class_ids.shape != (n,):
             raise TypeError("class_ids must be an int32 tensor of shape (N,)")
@@ -165,6 +201,8 @@ def _check_inputs(boxes, scores, class_ids, batch_offsets):
 
 
 PROFILE_NO_FUSION = 1  # nms_f32_profiled flag: mask and sweep as separate launches
+PROFILE_ONE_LAUNCH = 2  # nms_f32_profiled flag: the one-launch path for small inputs
+FLAG_ONE_LAUNCH = 1  # nms_f32_ex flag: the one-launch path for small inputs
 
 
 def _check_out(out: Optional[torch.Tensor], n: int, device: torch.device) -> torch.Tensor:
@@ -188,14 +226,14 @@ def _check_out(out: Optional[torch.Tensor], n: int, device: torch.device) -> tor
 
 
 def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, profiled,
-         fuse=True):
+         fuse=True, one_launch=False):
     boxes, scores, class_ids, batch_offsets, num_images = _check_inputs(
         boxes, scores, class_ids, batch_offsets)
     device = boxes.device
     n = boxes.shape[0]
-    with torch.cuda.device(device):
-        stream = torch.cuda.current_stream(device).cuda_stream
-        nbytes = workspace_size(n, num_images, class_ids is not None)
+    with _OnDevice(device):
+        stream = _raw_stream(device)
+        nbytes = _workspace_size(n, num_images, class_ids is not None)
         ws = workspace if workspace is not None else _default_workspace(device, stream)
         buf = ws.get(nbytes, device)
         out = _check_out(out, n, device)
@@ -206,7 +244,10 @@ def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out,
         stage = None
         if profiled:
             stage = (ctypes.c_float * len(STAGES))()
-            _check(_lib.nms_f32_profiled(*args, stage, 0 if fuse else PROFILE_NO_FUSION))
+            flags = (0 if fuse else PROFILE_NO_FUSION) | (PROFILE_ONE_LAUNCH if one_launch else 0)
+            _check(_lib.nms_f32_profiled(*args, stage, flags))
+        elif one_launch:
+            _check(_lib.nms_f32_ex(*args, FLAG_ONE_LAUNCH))
         else:
             _check(_lib.nms_f32(*args))
     keep = out[:count.value]
@@ -217,12 +258,16 @@ def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out,
 
 def nms(boxes: torch.Tensor, scores: torch.Tensor, iou_threshold: float,
         class_ids: Optional[torch.Tensor] = None, batch_offsets: Optional[torch.Tensor] = None,
-        workspace: Optional[Workspace] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        workspace: Optional[Workspace] = None, out: Optional[torch.Tensor] = None,
+        one_launch: bool = False) -> torch.Tensor:
     """Greedy IoU NMS.  Returns the kept input indices (int64, on the boxes'
     device) in descending score order, ties by ascending index.  With
     ``class_ids`` and/or ``batch_offsets`` boxes suppress only boxes of the
-    same (image, class); the result is one list in global score order."""
-    return _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, False)
+    same (image, class); the result is one list in global score order.
+    ``one_launch=True`` runs one image of at most 4096 boxes as a single
+    launch (``nms_f32_ex`` with NMS_FLAG_ONE_LAUNCH); the result is the same."""
+    return _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, False,
+                True, one_launch)
 
 
 STATIC_MAX_BOXES = 16384  # NMS_STATIC_MAX_BOXES
@@ -240,8 +285,8 @@ def nms_static(boxes: torch.Tensor, scores: torch.Tensor, iou_threshold: float,
         boxes, scores, class_ids, batch_offsets)
     device = boxes.device
     n = boxes.shape[0]
-    with torch.cuda.device(device):
-        stream = torch.cuda.current_stream(device).cuda_stream
+    with _OnDevice(device):
+        stream = _raw_stream(device)
         out = _check_out(out, n, device)
         count = ctypes.c_int64(0)
         _check(_lib.nms_f32_static(_ptr(boxes), _ptr(scores), n,
@@ -252,13 +297,17 @@ def nms_static(boxes: torch.Tensor, scores: torch.Tensor, iou_threshold: float,
 
 
 def nms_profiled(boxes, scores, iou_threshold, class_ids=None, batch_offsets=None,
-                 workspace=None, out=None, fuse=True) -> Tuple[torch.Tensor, Dict[str, float]]:
+                 workspace=None, out=None, fuse=True,
+                 one_launch=False) -> Tuple[torch.Tensor, Dict[str, float]]:
     """``nms`` plus per-stage GPU times in milliseconds (HIP events on the
     launch stream).  ``fuse=False`` runs the mask and the sweep as separate
     launches even where ``nms`` fuses them, so the mask kernel is timed
-    alone."""
+    alone; ``one_launch=True`` takes the one-launch path for small inputs
+    (timed as the mask stage)."""
+    if one_launch and not fuse:
+        raise ValueError("one_launch and fuse=False exclude each other")
     return _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, True,
-                fuse)
+                fuse, one_launch)
 
 
 def debug_order(scores: torch.Tensor, class_ids=None, batch_offsets=None):
@@ -268,8 +317,8 @@ def debug_order(scores: torch.Tensor, class_ids=None, batch_offsets=None):
     _, scores, class_ids, batch_offsets, num_images = _check_inputs(
         dummy, scores, class_ids, batch_offsets)
     device = scores.device
-    with torch.cuda.device(device):
-        stream = torch.cuda.current_stream(device).cuda_stream
+    with _OnDevice(device):
+        stream = _raw_stream(device)
         buf = torch.empty(max(workspace_size(n, num_images, class_ids is not None), 256),
                           dtype=torch.uint8, device=device)
         order = torch.empty(max(n, 1), dtype=torch.int32, device=device)
@@ -289,8 +338,8 @@ def debug_mask(boxes, scores, iou_threshold, class_ids=None, batch_offsets=None)
     n = boxes.shape[0]
     words = (n + 63) // 64
     device = boxes.device
-    with torch.cuda.device(device):
-        stream = torch.cuda.current_stream(device).cuda_stream
+    with _OnDevice(device):
+        stream = _raw_stream(device)
         buf = torch.empty(max(workspace_size(n, num_images, class_ids is not None), 256),
                           dtype=torch.uint8, device=device)
         mask = torch.empty((max(n, 1), max(words, 1)), dtype=torch.int64, device=device)
@@ -302,7 +351,7 @@ def debug_mask(boxes, scores, iou_threshold, class_ids=None, batch_offsets=None)
     return mask[:n, :words], order[:n]
 
 
-PLAN_FIELDS = ("mask_qshift", "fused", "fused_qshift", "rank_sort")
+PLAN_FIELDS = ("mask_qshift", "fused", "fused_qshift", "rank_sort", "small")
 
 
 def debug_plan(n: int, num_images: int = 0, has_classes: bool = False) -> Dict[str, int]:
@@ -343,8 +392,8 @@ def _run_matrix(boxes, scores, score_threshold, sigma, workspace, out, profiled)
     boxes, scores, _, _, _ = _check_inputs(boxes, scores, None, None)
     device = boxes.device
     n = boxes.shape[0]
-    with torch.cuda.device(device):
-        stream = torch.cuda.current_stream(device).cuda_stream
+    with _OnDevice(device):
+        stream = _raw_stream(device)
         nbytes = matrix_workspace_size(n)
         ws = workspace if workspace is not None else _default_workspace(device, stream)
         buf = ws.get(nbytes, device)

@@ -143,6 +143,7 @@ MaskArgs make_mask_args(const Problem &P, const Layout &L, int64_t slots) {
     if (P.grouped) a.qshift = 2;
     // the radix sort of one image writes the quantised pre-test words
     a.use_packs = (!P.grouped && P.n > RANK_SORT_MAX) ? 1 : 0;
+    a.items_known = 0;
     return a;
 }
 

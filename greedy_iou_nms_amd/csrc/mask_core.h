@@ -94,6 +94,10 @@ struct MaskArgs {
     int qshift;
     // the sort wrote the quantised pre-test words (one image, radix passes)
     int use_packs;
+    // > 0: the launch's pair count, known on the host (the one-launch path,
+    // where the control block is written by the same launch); 0: read it
+    // from the control block
+    int items_known;
 };
 
 // Read-only inputs and the output of the mask kernel.  They are separate
@@ -150,6 +154,37 @@ __device__ __forceinline__ uint64_t column_valid(int c, int n) {
     return rem >= 64 ? ~0ull : ((1ull << rem) - 1ull);
 }
 
+// Row boxes of a work item.  Normally each row's box and area are loaded
+// when the row is reached (uniform loads, which the standalone kernels serve
+// from the scalar cache).  LANE_ROWS: lane k loaded row k's box and area at
+// the start of the item, together with the column boxes, and each row is
+// broadcast from its lane: one round trip to memory per item instead of one
+// per row, for launches where the sorted boxes were written by the same
+// launch and the loads cannot take the scalar path.
+struct LaneRows {
+    float4 box;
+    float area;
+};
+
+template <bool LANE_ROWS>
+__device__ __forceinline__ void row_box(const MaskPtrs &m_, int p, int k, const LaneRows &lr,
+                                        float &x1, float &y1, float &x2, float &y2, float &ar) {
+    if constexpr (LANE_ROWS) {
+        x1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lr.box.x), k));
+        y1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lr.box.y), k));
+        x2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lr.box.z), k));
+        y2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lr.box.w), k));
+        ar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lr.area), k));
+    } else {
+        const float4 rb = m_.sb[p];
+        x1 = rb.x;
+        y1 = rb.y;
+        x2 = rb.z;
+        y2 = rb.w;
+        ar = m_.area[p];
+    }
+}
+
 // The rows k_lo .. k_hi - 1 of a work item in the division-free modes (t > 0,
 // ordered boxes).  With t > 0 a pair whose intersection is exactly 0 never
 // suppresses, and most pairs do not overlap, so each group of TG tiles first
@@ -172,25 +207,22 @@ __device__ __forceinline__ uint64_t column_valid(int c, int n) {
 // past n) hold an empty box at 0, whose intersection is exactly 0, so no mask
 // is applied there.  In the diagonal item (DIAG) only columns after row k vote
 // in the diagonal tile, and tiles before the row's tile are masked out.
-template <int S, bool GROUPED, int MODE, bool DIAG, bool SIGN>
+template <int S, bool GROUPED, int MODE, bool DIAG, bool SIGN, bool LANE_ROWS>
 __device__ __forceinline__ void fast_rows(const MaskArgs &a, const MaskPtrs &m_, int p0, int k_lo,
                                           int k_hi, const float (&cx1)[S], const float (&cy1)[S],
                                           const float (&cx2)[S], const float (&cy2)[S],
                                           const uint32_t (&cg)[S],
                                           const uint64_t (&tmask)[S], int t_diag,
-                                          uint32_t (&out_lo)[S], uint32_t (&out_hi)[S]) {
+                                          uint32_t (&out_lo)[S], uint32_t (&out_hi)[S],
+                                          const LaneRows &lr) {
     // tiles per question: measured at 65,536 boxes, the sign form is
     // fastest asking per 2 tiles (0.357 ms; 0.368 per 4, 0.405 per 8, 0.385
     // per tile), the intersection form per 4
     constexpr int TG = SIGN ? 2 : 4;
     for (int k = k_lo; k < k_hi; ++k) {
         const int p = p0 + k;
-        const float4 rb = m_.sb[p];
-        const float rx1 = rb.x;
-        const float ry1 = rb.y;
-        const float rx2 = rb.z;
-        const float ry2 = rb.w;
-        const float ra = m_.area[p];
+        float rx1, ry1, rx2, ry2, ra;
+        row_box<LANE_ROWS>(m_, p, k, lr, rx1, ry1, rx2, ry2, ra);
         const uint32_t rg = GROUPED ? m_.seg[p] : 0u;
         const uint64_t dmask = k == 63 ? 0ull : (~0ull << (k + 1));
 #pragma unroll
@@ -331,7 +363,7 @@ __device__ __forceinline__ void report_done(uint32_t *done, int &pending) {
 // completed the item adds 64 to done[r] (one per lane), the count of
 // finished items of its row tile times 64.  Plain stores may sit in the L2 of this XCD, which the sweep's
 // XCD does not see.
-template <int S, bool GROUPED, int MODE, bool COHERENT, bool PACKED>
+template <int S, bool GROUPED, int MODE, bool COHERENT, bool PACKED, bool LANE_ROWS = false>
 __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_, int item,
                                           int stride, uint32_t *done, int &pending) {
     const int lane = threadIdx.x & 63;
@@ -408,6 +440,12 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
         if (GROUPED) cg[t] = m_.seg[q];
         tmask[t] = active ? column_valid(c, a.n) : 0ull;
     }
+    LaneRows lr;
+    if constexpr (LANE_ROWS) {
+        static_assert(!PACKED, "lane rows: the float form only");
+        lr.box = m_.sb[p0 + lane];   // rows past n are the zero padding
+        lr.area = m_.area[p0 + lane];
+    }
     uint32_t out_lo[S], out_hi[S];
 #pragma unroll
     for (int t = 0; t < S; ++t) out_lo[t] = out_hi[t] = 0u;
@@ -415,12 +453,8 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
     if (MODE == MODE_LITERAL) {
         for (int k = k_lo; k < k_hi; ++k) {
             const int p = p0 + k;
-            const float4 rb = m_.sb[p];
-            const float rx1 = rb.x;
-            const float ry1 = rb.y;
-            const float rx2 = rb.z;
-            const float ry2 = rb.w;
-            const float ra = m_.area[p];
+            float rx1, ry1, rx2, ry2, ra;
+            row_box<LANE_ROWS>(m_, p, k, lr, rx1, ry1, rx2, ry2, ra);
             const uint32_t rg = GROUPED ? m_.seg[p] : 0u;
             // in the diagonal tile only boxes after row k vote
             const uint64_t dmask = k == 63 ? 0ull : (~0ull << (k + 1));
@@ -455,19 +489,22 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
         if constexpr (PACKED) {
         } else if (a.qshift == 0) {
             if (diag)
-                fast_rows<S, GROUPED, MODE, true, true>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2, cy2,
-                                                        cg, tmask, t_diag, out_lo, out_hi);
+                fast_rows<S, GROUPED, MODE, true, true, LANE_ROWS>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2,
+                                                                   cy2, cg, tmask, t_diag, out_lo,
+                                                                   out_hi, lr);
             else
-                fast_rows<S, GROUPED, MODE, false, true>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2, cy2,
-                                                         cg, tmask, t_diag, out_lo, out_hi);
+                fast_rows<S, GROUPED, MODE, false, true, LANE_ROWS>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2,
+                                                                    cy2, cg, tmask, t_diag, out_lo,
+                                                                    out_hi, lr);
         } else {
             if (diag)
-                fast_rows<S, GROUPED, MODE, true, false>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2, cy2,
-                                                         cg, tmask, t_diag, out_lo, out_hi);
+                fast_rows<S, GROUPED, MODE, true, false, LANE_ROWS>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2,
+                                                                    cy2, cg, tmask, t_diag, out_lo,
+                                                                    out_hi, lr);
             else
-                fast_rows<S, GROUPED, MODE, false, false>(a, m_, p0, k_lo, k_hi, cx1, cy1, cx2,
-                                                          cy2, cg, tmask, t_diag, out_lo,
-                                                          out_hi);
+                fast_rows<S, GROUPED, MODE, false, false, LANE_ROWS>(a, m_, p0, k_lo, k_hi, cx1, cy1,
+                                                                     cx2, cy2, cg, tmask, t_diag,
+                                                                     out_lo, out_hi, lr);
         }
     }
     // COHERENT: the previous item's count, once its stores are acknowledged
@@ -541,12 +578,12 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
 // Blocks start in workgroup order, so items still finish row tile by row
 // tile.  (One counter in device memory for all waves was tried: its atomics
 // serialise, and the launch took twice as long.)
-template <int S, bool GROUPED, bool COHERENT, bool PACKED_ONLY = false>
+template <int S, bool GROUPED, bool COHERENT, bool PACKED_ONLY = false, bool LANE_ROWS = false>
 __device__ __forceinline__ void mask_items(const MaskArgs &a, const MaskPtrs &m_,
                                            const Ctrl *__restrict__ ctrl, int first, int slots,
                                            uint32_t *done, uint32_t *queue = nullptr) {
     static_assert(!(PACKED_ONLY && GROUPED), "grouped input has no pre-test words");
-    const int num_items = ctrl->num_items << a.qshift;
+    const int num_items = (a.items_known > 0 ? a.items_known : ctrl->num_items) << a.qshift;
     const bool fast = (ctrl->flags & FLAG_ORDERED_BOXES) && a.exact_ok;
     const bool packed = a.use_packs && a.qshift == 0;
     const int stride = GROUPED ? ctrl->band_stride : a.mstride;
@@ -571,11 +608,16 @@ __device__ __forceinline__ void mask_items(const MaskArgs &a, const MaskPtrs &m_
                 }
             }
             if constexpr (!PACKED_ONLY) {
-                if (a.odd) mask_item<S, GROUPED, MODE_ODD, COHERENT, false>(a, m_, item, stride, done, pending);
-                else mask_item<S, GROUPED, MODE_EVEN, COHERENT, false>(a, m_, item, stride, done, pending);
+                if (a.odd)
+                    mask_item<S, GROUPED, MODE_ODD, COHERENT, false, LANE_ROWS>(a, m_, item, stride,
+                                                                                done, pending);
+                else
+                    mask_item<S, GROUPED, MODE_EVEN, COHERENT, false, LANE_ROWS>(a, m_, item, stride,
+                                                                                 done, pending);
             }
         } else {
-            mask_item<S, GROUPED, MODE_LITERAL, COHERENT, false>(a, m_, item, stride, done, pending);
+            mask_item<S, GROUPED, MODE_LITERAL, COHERENT, false, LANE_ROWS>(a, m_, item, stride, done,
+                                                                            pending);
         }
     }
     if (COHERENT) report_done(done, pending);

@@ -3,7 +3,11 @@
 // of {error bits, flags, kept count} that ends every call.
 #include <hip/hip_runtime.h>
 
+#include <unistd.h>
+
 #include <atomic>
+#include <chrono>
+#include <cstddef>
 #include <cmath>
 #include <cstring>
 
@@ -66,6 +70,7 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_mdrop = take((size_t)L.words * 8 + 8);
     L.off_tile_ext = take((size_t)L.tiles * 16);
     L.off_spk = take(np * 8);
+    L.off_arrive = take((size_t)(L.words + 1) * 8);
     L.off_mask = take((size_t)n * (size_t)L.mstride * 8);
     L.total = off;
     *out = L;
@@ -113,17 +118,34 @@ Work carve(void *workspace, const Layout &L) {
     w.mdrop = reinterpret_cast<uint64_t *>(b + L.off_mdrop);
     w.tile_ext = reinterpret_cast<float4 *>(b + L.off_tile_ext);
     w.spk = reinterpret_cast<uint2 *>(b + L.off_spk);
+    w.arrive = reinterpret_cast<uint64_t *>(b + L.off_arrive);
     return w;
 }
 
 namespace {
 
-struct Readback {
-    uint32_t error;
-    uint32_t flags;
-    int32_t count;
-    int32_t num_items;
-};
+static_assert(sizeof(Readback) <= sizeof(Ctrl) && offsetof(Readback, sweep_done) ==
+                                                   offsetof(Ctrl, sweep_done),
+              "a copy of the control block's head fills the read-back");
+
+// Epochs of the one-launch path for small inputs: a process-wide counter
+// from a random start (clock and process id through the splitmix64
+// finaliser), so that neither an earlier call's slots, of this process or
+// another, nor leftover memory pass for this call's.  A function-local
+// static of a trivially destructible type: nothing runs at exit.
+uint64_t mix64(uint64_t z) {
+    z += 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+uint64_t next_epoch() {
+    static std::atomic<uint64_t> counter{mix64(
+        (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+        ((uint64_t)getpid() << 40))};
+    return counter.fetch_add(1, std::memory_order_relaxed);
+}
 
 nms_status check_common(int64_t n, float thresh, const int64_t *offsets, int64_t num_images) {
     if (n < 0 || std::isnan(thresh)) return NMS_INVALID_ARG;
@@ -205,6 +227,51 @@ nms_status read_back(const Work &w, hipStream_t stream, Readback *out, bool pool
     return hip_status(e);
 }
 
+// A pinned buffer of the pool, held for one call and given back on every
+// way out; null when none is wanted or none is free.
+struct PinnedSlot {
+    Readback *p;
+    explicit PinnedSlot(bool want) : p(want ? take_readback() : nullptr) {}
+    ~PinnedSlot() {
+        if (p) give_readback(p);
+    }
+    PinnedSlot(const PinnedSlot &) = delete;
+    PinnedSlot &operator=(const PinnedSlot &) = delete;
+    Post post(uint64_t tag) const { return Post{p, tag}; }
+};
+
+// How long the host spins on a posted result before it blocks in
+// hipStreamSynchronize instead (a long call, or one queued behind other
+// work on the stream).
+constexpr double POST_SPIN_US = 2000.0;
+
+// The end of a call.  With a pinned buffer: wait until the call's last
+// kernel has posted its result there with `tag` (spinning, then blocking;
+// a kernel that ended without posting is an internal error).  Without one:
+// copy the control block's head back (pageable, allocates nothing) and
+// synchronise the stream.
+nms_status collect(const Work &w, hipStream_t stream, Readback *pin, uint64_t tag,
+                   Readback *out) {
+    if (pin == nullptr) {
+        hipError_t e = hipMemcpyAsync(out, w.ctrl, sizeof(Readback), hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        return hip_status(e);
+    }
+    const auto t0 = std::chrono::steady_clock::now();
+    while (__atomic_load_n(&pin->tag, __ATOMIC_ACQUIRE) != tag) {
+        const double us =
+            std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+        if (us > POST_SPIN_US) {
+            const hipError_t e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_status(e);
+            if (__atomic_load_n(&pin->tag, __ATOMIC_ACQUIRE) != tag) return NMS_HIP_ERROR;
+            break;
+        }
+    }
+    *out = *pin;
+    return NMS_OK;
+}
+
 nms_status device_error(uint32_t err) {
     if (err & ERR_INTERNAL) return NMS_HIP_ERROR;
     if (err & ERR_BAD_BOXES) return NMS_BAD_BOXES;
@@ -235,7 +302,7 @@ struct EventSet {
 nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thresh,
                    const int32_t *class_ids, const int64_t *offsets, int64_t num_images,
                    int64_t *keep_out, int64_t *num_kept, void *workspace, size_t ws_bytes,
-                   void *stream_ptr, float *stage_ms, bool allow_fusion,
+                   void *stream_ptr, float *stage_ms, bool allow_fusion, bool one_launch,
                    bool pinned_pool = true) {
     if (num_kept == nullptr) return NMS_INVALID_ARG;
     *num_kept = 0;
@@ -261,7 +328,47 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
         return stage_ms ? hipEventRecord(events.ev[i], stream) : hipSuccess;
     };
 
-    hipError_t e = mark(0);
+    // one_launch: only the mask stage ran (it holds the whole launch)
+    auto finish = [&](const Readback &rb, bool one_launch) -> nms_status {
+        const nms_status ds = device_error(rb.error);
+        if (ds != NMS_OK) return ds;
+        if (stage_ms) {
+            for (int i = 0; i < NMS_NUM_STAGES; ++i) {
+                if (one_launch && i != NMS_STAGE_MASK) continue;
+                float ms = 0.0f;
+                if (hipEventElapsedTime(&ms, events.ev[i], events.ev[i + 1]) != hipSuccess)
+                    return NMS_HIP_ERROR;
+                stage_ms[i] = ms;
+            }
+        }
+        *num_kept = rb.count;
+        return NMS_OK;
+    };
+
+    // The result comes back through a pinned buffer of the pool, posted by
+    // the call's last kernel; profiled calls copy it back and synchronise
+    // (their events must have completed).
+    const PinnedSlot slot(pinned_pool && stage_ms == nullptr);
+
+    hipError_t e = hipSuccess;
+    // One small image: the whole call in one launch (timed as the mask
+    // stage).  Its result stands once its sweep finished, and an input
+    // error stands as it is; otherwise the stages below run from the start.
+    if (one_launch && small_launch_applies(P)) {
+        const uint64_t tag = next_epoch();
+        for (int i = 0; i <= 2 && e == hipSuccess; ++i) e = mark(i);
+        if (e == hipSuccess)
+            e = launch_small(P, L, w, keep_out, next_epoch(), slot.post(tag), stream);
+        for (int i = 3; i <= NMS_NUM_STAGES && e == hipSuccess; ++i) e = mark(i);
+        if (e != hipSuccess) return NMS_HIP_ERROR;
+        Readback rb;
+        st = collect(w, stream, slot.p, tag, &rb);
+        if (st != NMS_OK) return st;
+        if (rb.sweep_done == 1u || rb.error != 0u) return finish(rb, true);
+    }
+
+    const uint64_t tag = next_epoch();
+    e = mark(0);
     if (e == hipSuccess) e = launch_radix_sort(P, L, w, stream);
     if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess) e = mark(2);
@@ -273,27 +380,20 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
         e = fused ? launch_mask_sweep(P, L, w, keep_out, stream) : launch_mask(P, L, w, stream);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess && P.grouped) e = launch_group_sweep(P, L, w, stream);
-    if (e == hipSuccess) e = launch_sweep(P, L, w, keep_out, stream);
+    // one image: the sweep is the last kernel and posts the result
+    if (e == hipSuccess)
+        e = launch_sweep(P, L, w, keep_out, stream,
+                         P.grouped ? Post{nullptr, 0} : slot.post(tag));
     if (e == hipSuccess) e = mark(4);
     if (e == hipSuccess && P.grouped) e = launch_compact(P, L, w, keep_out, stream);
+    if (e == hipSuccess && P.grouped) e = launch_publish(w, slot.post(tag), stream);
     if (e == hipSuccess) e = mark(5);
     if (e != hipSuccess) return NMS_HIP_ERROR;
 
     Readback rb;
-    st = read_back(w, stream, &rb, pinned_pool);
+    st = collect(w, stream, slot.p, tag, &rb);
     if (st != NMS_OK) return st;
-    st = device_error(rb.error);
-    if (st != NMS_OK) return st;
-    if (stage_ms) {
-        for (int i = 0; i < NMS_NUM_STAGES; ++i) {
-            float ms = 0.0f;
-            if (hipEventElapsedTime(&ms, events.ev[i], events.ev[i + 1]) != hipSuccess)
-                return NMS_HIP_ERROR;
-            stage_ms[i] = ms;
-        }
-    }
-    *num_kept = rb.count;
-    return NMS_OK;
+    return finish(rb, false);
 }
 
 // Matrix NMS: the same sort, then prep, overlap maximum, decay test, kept
@@ -332,13 +432,16 @@ nms_status run_matrix(const float *boxes, const float *scores, int64_t n, float 
     if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess) e = launch_matrix_overlap_max(P, L, w, stream);
     if (e == hipSuccess) e = mark(2);
+    const PinnedSlot slot(stage_ms == nullptr);
+    const uint64_t tag = next_epoch();
     if (e == hipSuccess) e = launch_matrix_decay(P, L, w, sigma, stream);
     if (e == hipSuccess) e = launch_compact(P, L, w, keep_out, stream);
+    if (e == hipSuccess) e = launch_publish(w, slot.post(tag), stream);
     if (e == hipSuccess) e = mark(3);
     if (e != hipSuccess) return NMS_HIP_ERROR;
 
     Readback rb;
-    nms_status st = read_back(w, stream, &rb);
+    nms_status st = collect(w, stream, slot.p, tag, &rb);
     if (st != NMS_OK) return st;
     st = device_error(rb.error);
     if (st != NMS_OK) return st;
@@ -406,7 +509,18 @@ nms_status nms_f32(const float *boxes, const float *scores, int64_t n, float iou
                    int64_t *keep_out, int64_t *num_kept, void *workspace,
                    size_t workspace_bytes, void *stream) {
     return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
-                   num_kept, workspace, workspace_bytes, stream, nullptr, true);
+                   num_kept, workspace, workspace_bytes, stream, nullptr, true, false);
+}
+
+nms_status nms_f32_ex(const float *boxes, const float *scores, int64_t n, float iou_thresh,
+                      const int32_t *class_ids, const int64_t *batch_offsets, int64_t num_images,
+                      int64_t *keep_out, int64_t *num_kept, void *workspace,
+                      size_t workspace_bytes, void *stream, int flags) {
+    if (num_kept != nullptr) *num_kept = 0;
+    if ((flags & ~NMS_FLAG_ONE_LAUNCH) != 0) return NMS_INVALID_ARG;
+    return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
+                   num_kept, workspace, workspace_bytes, stream, nullptr, true,
+                   (flags & NMS_FLAG_ONE_LAUNCH) != 0);
 }
 
 nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, float iou_thresh,
@@ -427,7 +541,8 @@ nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, fl
     // the same kernels as nms_f32 on the static scratch; the read-back goes
     // to the caller's stack (pageable), so nothing is allocated
     return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
-                   num_kept, ws, (size_t)NMS_STATIC_SCRATCH_BYTES, stream, nullptr, true, false);
+                   num_kept, ws, (size_t)NMS_STATIC_SCRATCH_BYTES, stream, nullptr, true, false,
+                   false);
 }
 
 nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
@@ -436,10 +551,11 @@ nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
                             int64_t *keep_out, int64_t *num_kept, void *workspace,
                             size_t workspace_bytes, void *stream, float *stage_ms,
                             int flags) {
-    if (stage_ms == nullptr || (flags & ~NMS_PROFILE_NO_FUSION) != 0) return NMS_INVALID_ARG;
+    const int known = NMS_PROFILE_NO_FUSION | NMS_PROFILE_ONE_LAUNCH;
+    if (stage_ms == nullptr || (flags & ~known) != 0 || flags == known) return NMS_INVALID_ARG;
     return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
                    num_kept, workspace, workspace_bytes, stream, stage_ms,
-                   (flags & NMS_PROFILE_NO_FUSION) == 0);
+                   (flags & NMS_PROFILE_NO_FUSION) == 0, (flags & NMS_PROFILE_ONE_LAUNCH) != 0);
 }
 
 nms_status nms_matrix_workspace_size(int64_t n, size_t *bytes) {
@@ -560,6 +676,7 @@ nms_status nms_debug_plan(int64_t n, int64_t num_images, int has_classes, int32_
     plan[NMS_PLAN_FUSED] = fused ? 1 : 0;
     plan[NMS_PLAN_FUSED_QSHIFT] = fused ? fused_mask_qshift(P, L) : -1;
     plan[NMS_PLAN_RANK_SORT] = (!P.grouped && n <= RANK_SORT_MAX) ? 1 : 0;
+    plan[NMS_PLAN_SMALL] = small_launch_applies(P) ? 1 : 0;
     return NMS_OK;
 }
 

@@ -38,6 +38,54 @@ struct Ctrl {
 };
 static_assert(sizeof(Ctrl) == 64, "Ctrl layout");
 
+// The head of the control block as the host reads it at the end of a call,
+// and the call's tag (see Post).  A plain copy of the control block fills
+// the first eight fields.
+struct Readback {
+    uint32_t error;
+    uint32_t flags;
+    int32_t count;
+    int32_t num_items;
+    int32_t band_stride;
+    int32_t num_segments;
+    uint32_t sweep_done;
+    int32_t reserved0;
+    uint64_t tag;
+};
+
+// Where the last kernel of a call posts the result: a pinned host buffer
+// (null: nothing is posted and the host copies the control block back) and
+// the call's tag.  The tag is stored last, with release semantics at system
+// scope, and the host spins on it: it then sees the other fields complete,
+// with no copy to enqueue and no stream synchronisation, which cost about
+// 8 us more per call on this GPU.
+struct Post {
+    Readback *dst;
+    uint64_t tag;
+};
+
+// One thread posts the control block's head.  Every store the host relies on
+// (the output indices) must have completed before: the kernel's waves wait
+// for their stores and meet at a barrier first.  valid = false posts a
+// result that says only "no result" (sweep_done 0, no error), for a kernel
+// that gave up before the control block was complete.
+__device__ __forceinline__ void post_result(const Post &p, const Ctrl *ctrl, bool valid = true) {
+    if (p.dst == nullptr) return;
+    auto ld = [](const auto *q) {
+        return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    Readback *d = p.dst;
+    d->error = valid ? ld(&ctrl->error) : 0u;
+    d->flags = valid ? ld(&ctrl->flags) : 0u;
+    d->count = valid ? ld(&ctrl->count) : 0;
+    d->num_items = valid ? ld(&ctrl->num_items) : 0;
+    d->band_stride = valid ? ld(&ctrl->band_stride) : 0;
+    d->num_segments = valid ? ld(&ctrl->num_segments) : 0;
+    d->sweep_done = valid ? ld(&ctrl->sweep_done) : 0u;
+    d->reserved0 = 0;
+    __hip_atomic_store(&d->tag, p.tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Column tiles per mask work item ("strip"): 16 for one image, 4 for grouped
 // input whose bands are only a few tiles wide.
 constexpr int STRIP_SINGLE = 8;
@@ -108,6 +156,9 @@ constexpr int64_t MAX_GRID_THREADS = (int64_t)1 << 31;
 // bitmap) would no longer fit beside two mask workgroups per CU.
 constexpr int FUSE_MIN_WORDS = 512;
 constexpr int FUSE_MAX_WORDS = 4096;
+// One image of at most this many boxes runs sort, mask, sweep and output in
+// one launch.
+constexpr int SMALL_MAX = 4096;
 
 // Workspace carve-up, computed on the host from n alone.
 struct Layout {
@@ -124,7 +175,7 @@ struct Layout {
     size_t off_gcls = 0, off_gimg = 0, off_pass_plan = 0, off_gbase = 0;
     size_t off_done = 0, off_seg_start = 0, off_start_bits = 0, off_block_cnt = 0;
     size_t off_momax = 0, off_mscore = 0, off_mlo = 0, off_mhi = 0, off_mdrop = 0;
-    size_t off_tile_ext = 0, off_spk = 0;
+    size_t off_tile_ext = 0, off_spk = 0, off_arrive = 0;
     // the suppression bitmask comes last: Matrix NMS uses everything before it
     size_t off_mask = 0, total = 0;
 };
@@ -184,6 +235,9 @@ struct Work {
     // quantised words (lo, hi) of the overlap pre-test (see PACK_*)
     float4 *tile_ext;
     uint2 *spk;
+    // one launch for small inputs: W + 1 slots, each the epoch of the last
+    // call whose preparing workgroup finished
+    uint64_t *arrive;
 };
 
 Work carve(void *workspace, const Layout &L);
@@ -215,8 +269,12 @@ hipError_t launch_matrix_overlap_max(const Problem &P, const Layout &L, const Wo
 hipError_t launch_matrix_decay(const Problem &P, const Layout &L, const Work &w, double sigma,
                                hipStream_t stream);
 hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStream_t stream);
+// post: set only when the sweep is the call's last kernel (one image).
 hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
-                        hipStream_t stream);
+                        hipStream_t stream, const Post &post = Post{nullptr, 0});
+// One workgroup posts the control block's head (after the call's last
+// kernel, where that kernel has many workgroups).
+hipError_t launch_publish(const Work &w, const Post &post, hipStream_t stream);
 // One image with FUSE_MIN_WORDS <= L.words <= FUSE_MAX_WORDS: mask and
 // sweep in one launch.
 // launch_sweep must still follow; it returns at once when the fused sweep
@@ -233,6 +291,13 @@ int fused_mask_qshift(const Problem &P, const Layout &L);
 // nms_f32 runs mask and sweep in one launch (one image of FUSE_MIN_WORDS to
 // FUSE_MAX_WORDS row tiles whose mask takes the pre-test form).
 bool fused_launch_applies(const Problem &P, const Layout &L);
+// One image of 1 .. SMALL_MAX boxes: the whole call in one launch.  The
+// result stands only if the control block's sweep_done reads 1 afterwards;
+// otherwise (a wait gave up, a tile's list overflowed) the call runs the
+// multi-launch path from the start.  epoch: new for every call.
+bool small_launch_applies(const Problem &P);
+hipError_t launch_small(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
+                        uint64_t epoch, const Post &post, hipStream_t stream);
 hipError_t launch_compact(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
                           hipStream_t stream);
 // Grouped input: sweep every segment with its own wave.  launch_sweep must

@@ -48,6 +48,7 @@
 
 #include "greedy_nms.h"
 #include "nms_internal.h"
+#include "rank_core.h"
 
 #pragma clang fp contract(off)
 
@@ -97,53 +98,6 @@ __device__ __forceinline__ uint32_t image_of(const int64_t *off, int num_images,
         else hi = mid - 1;
     }
     return (uint32_t)lo;
-}
-
-struct KeysArgs {
-    const float4 *boxes;       // one image: for the extent of the boxes (may be null)
-    const float *scores;
-    const int32_t *class_ids;  // grouped input only (may be null)
-    const int64_t *offsets;    // grouped input only (may be null)
-    int num_images;
-    int n, npad, words, strip, mstride, tiles, grouped;
-    Work w;
-};
-
-// Mask work items of row tile r when every row covers all column tiles up to
-// W: strips floor(r/S) .. ceil(W/S)-1; returns the first item of row tile r.
-__device__ __forceinline__ int32_t item_base_full(int r, int W, int S) {
-    const int G = (W + S - 1) / S;
-    const int g = r / S, u = r % S;
-    return (int32_t)(S * (g * G - g * (g - 1) / 2) + u * (G - g));
-}
-
-// Per-call initialisation, spread over the threads gid = 0 .. gsz - 1: the
-// side arrays the mask kernel only partly writes, the padding rows of the
-// sorted arrays, and (one image) the plan of the mask kernel (every row tile
-// covers all column tiles).
-template <bool GROUPED>
-__device__ __forceinline__ void per_call_init(const KeysArgs &a, int gid, int gsz) {
-    const Work &w = a.w;
-    for (int r = gid; r <= a.words; r += gsz) {
-        if (!GROUPED) w.item_base[r] = item_base_full(r, a.words, a.strip);
-        if (r < a.words) {
-            if (!GROUPED) w.tile_cend[r] = a.words;
-            w.tcount[r] = 0u;
-            w.done[r] = 0u;
-            if (GROUPED) w.kept[r] = 0ull;  // the grouped sweep ORs segments in
-        }
-    }
-    for (int p = gid; p < a.npad; p += gsz) {
-#pragma unroll
-        for (int j = 0; j <= NEAR_TILES; ++j) w.tnear[(size_t)j * a.npad + p] = 0ull;
-        if (p >= a.n) {
-            w.order[p] = 0;
-            w.sb[p] = make_float4(0.f, 0.f, 0.f, 0.f);
-            w.area[p] = 0.0f;
-            if (GROUPED) w.seg[p] = 0xFFFFFFFFu;
-            else w.spk[p] = make_uint2(PACK_NONE_LO, PACK_NONE_HI);
-        }
-    }
 }
 
 // Lanes add into HIST_COPIES interleaved copies of the histograms: keys of
@@ -291,148 +245,25 @@ __device__ __forceinline__ void scan256(const uint32_t *v, uint32_t *out) {
 
 // ---------------------------------------------------------------- rank sort
 
-// One image of at most RANK_SORT_MAX boxes, in one launch.  The stable order
-// puts box j before box i iff s_j > s_i, or s_j == s_i and j < i (float
-// comparisons order scores exactly as the radix keys do: -0 equals +0), so
-// box i's sorted position is the number of boxes j that satisfy that.  For j
-// in an earlier 64-box chunk than i this is s_j >= s_i, in a later chunk
-// s_j > s_i, and in i's own chunk the index decides ties.  A NaN score is an
-// error, but the positions must still be a permutation (later kernels index
-// with them): NaN counts as -infinity.  Comparing a raw s_j with the
-// sanitised s_i gives that already, except that for a box whose s_i is
-// -infinity (or NaN) every box of an earlier chunk precedes it, NaN or not.  One workgroup per chunk; its waves split the chunks among
-// them, each reading the scores of a chunk with scalar loads (the same
-// values for every lane) and comparing them with the lane's own score; wave
-// 0 adds the waves' counts and writes the sorted order, boxes and areas.
-// n^2 comparisons cost less than four passes over few tiles while n is
-// small.  An extra workgroup checks every score and box and writes the
-// control block beside them; every workgroup takes a share of the per-call
-// initialisation.
+// One image of at most RANK_SORT_MAX boxes, in one launch: one workgroup per
+// 64-box chunk counts the sorted positions of its boxes (n^2 comparisons cost
+// less than four passes over few tiles while n is small); an extra
+// workgroup checks every score and box and writes the control block beside
+// them; every workgroup takes a share of the per-call initialisation.
 constexpr int RANK_THREADS = 1024;
 constexpr int RANK_WAVES = RANK_THREADS / 64;
 constexpr int RANK_PER_THREAD = RANK_SORT_MAX / RANK_THREADS;  // inputs each thread checks
-static_assert(RANK_PER_THREAD * RANK_THREADS == RANK_SORT_MAX && RANK_PER_THREAD % 4 == 0,
-              "rank sort tiling");
+static_assert(RANK_PER_THREAD * RANK_THREADS == RANK_SORT_MAX, "rank sort tiling");
 
-// Scores read through the constant address space, which lets the compiler
-// use scalar loads where the address is the same for every lane.
-typedef const __attribute__((address_space(4))) float *const_scores_t;
-
-__global__ __launch_bounds__(RANK_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void rank_sort_kernel(KeysArgs a,
-                                                                 const float4 *boxes) {
+__global__ __launch_bounds__(RANK_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void rank_sort_kernel(
+    KeysArgs a, const float4 *boxes) {
     __shared__ uint32_t part[RANK_WAVES][64];
     __shared__ uint32_t err_sh, unordered_sh;
-    const int tid = threadIdx.x, lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(wave_id());
-    const Work &w = a.w;
-    const int n = a.n;
-    per_call_init<false>(a, blockIdx.x * RANK_THREADS + tid, gridDim.x * RANK_THREADS);
-
-    if (blockIdx.x == 0) {
-        // Workgroup 0 checks the whole input (the sort-only test export
-        // passes no boxes), every load in flight together, and writes the
-        // control block.
-        if (tid == 0) {
-            err_sh = 0u;
-            unordered_sh = 0u;
-        }
-        // Loads from clamped indices, with no branch around them, so that a
-        // round's loads are all in flight together; entries past n are then
-        // ignored.
-        uint32_t err = 0;
-        bool finite = true, ordered = true;
-        constexpr int H = RANK_PER_THREAD / 4;  // four rounds keep the registers few
-        if (n > 0) {
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                float sv[H];
-                float4 bb[H];
-#pragma unroll
-                for (int e = 0; e < H; ++e) {
-                    const int j = min(tid + (h * H + e) * RANK_THREADS, n - 1);
-                    sv[e] = a.scores[j];
-                    if (boxes != nullptr) bb[e] = boxes[j];
-                }
-#pragma unroll
-                for (int e = 0; e < H; ++e) {
-                    if (tid + (h * H + e) * RANK_THREADS >= n) continue;
-                    if (sv[e] != sv[e]) err |= ERR_NONFINITE;
-                    if (boxes == nullptr) continue;
-                    const float4 b = bb[e];
-                    finite = finite && isfinite(b.x) && isfinite(b.y) && isfinite(b.z) &&
-                             isfinite(b.w);
-                    const float ar = (b.z - b.x) * (b.w - b.y);
-                    ordered = ordered && b.x < b.z && b.y < b.w && ar > 0.0f && ar < INFINITY;
-                }
-            }
-        }
-        __syncthreads();
-        if (!finite) err |= ERR_NONFINITE;
-        if (err) atomicOr(&err_sh, err);
-        if (!ordered) atomicOr(&unordered_sh, 1u);
-        __syncthreads();
-        if (tid == 0) {
-            Ctrl *c = w.ctrl;
-            c->error = err_sh;
-            c->flags = unordered_sh ? 0u : FLAG_ORDERED_BOXES;
-            c->count = 0;
-            c->num_items = item_base_full(a.words, a.words, a.strip);
-            c->band_stride = a.mstride;
-            c->num_segments = 1;
-            c->sweep_done = 0u;
-        }
-        return;
-    }
-
-    // Workgroup 1 + k ranks boxes 64 k .. 64 k + 63.
-    const int chunks = (n + 63) >> 6;
-    const int chunk = blockIdx.x - 1;
-    const int i = 64 * chunk + lane;
-    const const_scores_t sc = (const_scores_t)a.scores;
-    const float s_raw = i < n ? a.scores[i] : 0.0f;
-    const float si = s_raw != s_raw ? -INFINITY : s_raw;
-    // the box wave 0 will place, loaded now
-    const float4 bi = wave == 0 && boxes != nullptr && i < n ? boxes[i]
-                                                             : make_float4(0.f, 0.f, 0.f, 0.f);
-    uint32_t cnt_early = 0, cnt = 0, early_chunks = 0;
-    for (int c = wave; c < chunks; c += RANK_WAVES) {
-        const const_scores_t sp = sc + 64 * c;
-        const int len = min(64, n - 64 * c);
-        if (c != chunk && len == 64) {
-            if (c < chunk) {
-                ++early_chunks;
-#pragma unroll
-                for (int t = 0; t < 64; ++t) cnt_early += (uint32_t)(sp[t] >= si);
-            } else {
-#pragma unroll
-                for (int t = 0; t < 64; ++t) cnt += (uint32_t)(sp[t] > si);
-            }
-        } else {
-            // this workgroup's own chunk, or the last, partial one (never
-            // an earlier one): lane t holds score 64 c + t
-            float mine = lane < len ? a.scores[64 * c + lane] : 0.0f;
-            if (mine != mine) mine = -INFINITY;
-#pragma unroll 1
-            for (int t = 0; t < len; ++t) {
-                const float sj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), t));
-                const bool before = c > chunk ? sj > si : (sj > si || (sj == si && t < lane));
-                cnt += (uint32_t)before;
-            }
-        }
-    }
-    cnt += si == -INFINITY ? 64u * early_chunks : cnt_early;
-    part[wave][lane] = cnt;
-    __syncthreads();
-    if (wave == 0 && i < n) {
-        uint32_t r = 0;
-#pragma unroll
-        for (int v = 0; v < RANK_WAVES; ++v) r += part[v][lane];
-        w.order[r] = i;
-        if (boxes != nullptr) {
-            w.sb[r] = bi;
-            w.area[r] = (bi.z - bi.x) * (bi.w - bi.y);
-        }
-    }
+    per_call_init<false>(a, blockIdx.x * RANK_THREADS + threadIdx.x, gridDim.x * RANK_THREADS);
+    // workgroup 0 checks the input (the sort-only test export passes no
+    // boxes); workgroup 1 + k ranks boxes 64 k .. 64 k + 63
+    if (blockIdx.x == 0) check_image<RANK_THREADS, RANK_PER_THREAD>(a, boxes, &err_sh, &unordered_sh);
+    else rank_chunk<RANK_WAVES>(a, boxes, blockIdx.x - 1, part);
 }
 
 struct PlanArgs {

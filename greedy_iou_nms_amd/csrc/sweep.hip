@@ -47,6 +47,7 @@
 // order.
 #include "mask_core.h"
 #include "nms_internal.h"
+#include "rank_core.h"
 
 namespace gnms {
 namespace {
@@ -70,6 +71,7 @@ struct SweepArgs {
     int n, words, npad, mstride, strip, grouped;
     int strip_groups;  // ceil(W / strip): mask work pairs of row tile 0
     int done_shift;    // fused: a finished pair adds 64 << done_shift to done[]
+    Post post;         // the call's result, when this sweep ends the call
 };
 
 // Reads of data the mask stage writes.  In the fused kernel the mask is still
@@ -736,14 +738,25 @@ __device__ __forceinline__ void sweep_body(const SweepArgs &a, uint64_t *removed
     }
 }
 
+// Waves of a workgroup that posts the call's result: every wave's stores
+// complete (s_waitcnt vmcnt(0)), then one thread posts.
+__device__ __forceinline__ void post_from_workgroup(const Post &p, const Ctrl *ctrl, bool valid) {
+    if (p.dst == nullptr) return;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (threadIdx.x == 0) post_result(p, ctrl, valid);
+}
+
 __global__ __launch_bounds__(NT) void sweep_kernel(SweepArgs a) {
     extern __shared__ uint64_t removed[];
     __shared__ SweepSmem sm;
     // the fused mask + sweep kernel, or the grouped sweep (which runs
-    // whenever every band fits its window), already produced the result
-    if (a.ctrl->sweep_done) return;
-    if (a.grouped && a.ctrl->band_stride <= GROUP_SWEEP_WIN) return;
-    sweep_body<false>(a, removed, sm);
+    // whenever every band fits its window), may already have produced the
+    // result
+    const bool done = a.ctrl->sweep_done ||
+                      (a.grouped && a.ctrl->band_stride <= GROUP_SWEEP_WIN);
+    if (!done) sweep_body<false>(a, removed, sm);
+    post_from_workgroup(a.post, a.ctrl, true);
 }
 
 // ---------------------------------------------------------------- grouped sweep
@@ -865,6 +878,138 @@ __global__ __launch_bounds__(NT, 6) void mask_sweep_kernel(
         ma, m_, ctrl, (int)fused_block_start(blockIdx.x),
         (int)(fused_block_start(blockIdx.x + 1) - fused_block_start(blockIdx.x)), done,
         &item_queue);
+}
+
+// ---------------------------------------------------------------- small inputs
+
+// One image of at most SMALL_MAX boxes in one launch: sort, mask, sweep and
+// output, so that a call costs one launch and the read-back (the page's
+// measured losses at 1024 and 2048 boxes come from fixed per-launch costs:
+// "LeetCUDA 14-nms", measured results).  Workgroups, in launch order:
+//   0 .. W - 1   rank the 64 boxes of chunk k (the ranking sort's code);
+//   W            checks the input and writes the control block;
+//   W + 1        the sweep, as in the fused launch;
+//   W + 2 ...    the mask, one work item per wave.
+// The first W + 1 share the per-call initialisation and never wait; each
+// then stores the call's epoch in its slot of `arrive`.  Every later
+// workgroup first waits until all W + 1 slots hold the epoch.  The GPU starts
+// workgroups in launch order, so a waiting workgroup waits only for ones
+// already started, which finish whatever else is resident; the sweep also
+// waits for mask items, which never wait for the sweep.  Every wait is
+// bounded: a wait that gives up leaves sweep_done clear, and so does a row
+// tile whose list overflowed (its dense rows are plain stores), and the host
+// then runs the multi-launch path from the start.
+//
+// The host gives every call a new 64-bit epoch (a process-wide counter from a
+// random start), so a slot left by an earlier call, or never written, does
+// not match; a match of all W + 1 slots by leftover memory is not a practical
+// concern.
+constexpr int SMALL_PER_THREAD = SMALL_MAX / NT;  // inputs each checking thread reads
+static_assert(SMALL_PER_THREAD * NT == SMALL_MAX && SMALL_MAX <= RANK_SORT_MAX,
+              "small-input tiling");
+static_assert(SMALL_MAX / 64 + 1 <= 128, "a wave polls at most two slots per lane");
+
+struct SmallArgs {
+    KeysArgs ka;
+    const float4 *boxes;
+    uint64_t *arrive;  // W + 1 slots
+    uint64_t epoch;
+    int prep;          // W + 1 preparing workgroups
+    int mask_waves;    // waves of the mask workgroups
+    Post post;         // posted by the sweep's workgroup
+};
+
+// Preparing workgroup: once every wave's device-scope stores have completed
+// (s_waitcnt vmcnt(0): they reached the memory all XCDs share), one store
+// of the epoch announces them.  (A release fence would also write back this
+// XCD's whole L2, which cost several microseconds per workgroup here.)
+__device__ __forceinline__ void announce(uint64_t *slot, uint64_t epoch) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(slot, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every preparing workgroup has announced its stores: wave 0
+// polls the slots (lane l reads slots l, l + 64); false if it took too long.
+__device__ __forceinline__ bool wait_prepared(const SmallArgs &s, uint32_t *ok_sh) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        uint32_t spins = 0;
+        bool ok = true;
+        for (;;) {
+            // both loads in flight together
+            const uint64_t v0 = lane < s.prep ? __hip_atomic_load(&s.arrive[lane], __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_AGENT)
+                                              : s.epoch;
+            const uint64_t v1 = lane + 64 < s.prep
+                                    ? __hip_atomic_load(&s.arrive[lane + 64], __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT)
+                                    : s.epoch;
+            if (__ballot(v0 != s.epoch || v1 != s.epoch) == 0ull) break;
+            if (++spins > SPIN_LIMIT) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane == 0) *ok_sh = ok ? 1u : 0u;
+    }
+    // No cache invalidation is needed after the wait: every cache was
+    // invalidated when the launch began, nothing reads the prepared data
+    // before this point, and the preparing workgroups' device-scope stores
+    // are in memory, so the first reads of those lines fetch the new values.
+    __syncthreads();
+    return *ok_sh != 0u;
+}
+
+// (at most 128 registers: the sweep's and the mask's code paths share them)
+__global__ __launch_bounds__(NT, 4) void small_nms_kernel(SmallArgs s, maskcore::MaskArgs ma,
+                                                          SweepArgs sa) {
+    extern __shared__ uint64_t removed[];
+    // the sweep's shared state, or a ranking workgroup's staged scores
+    __shared__ union {
+        SweepSmem sweep;
+        float scores[SMALL_MAX];
+    } u;
+    __shared__ uint32_t part[NWAVES][64];
+    __shared__ uint32_t err_sh, unordered_sh, ok_sh;
+    const int b = blockIdx.x;
+    if (b < s.prep) {
+        // the initialisation stores come last: a wait for a load (or for a
+        // register a load still writes) waits for every store issued
+        // before it, and device-scope stores take a round trip to memory
+        if (b == s.prep - 1) {
+            check_image<NT, SMALL_PER_THREAD, true>(s.ka, s.boxes, &err_sh, &unordered_sh);
+        } else {
+            RankStaged<NWAVES, SMALL_MAX> st;
+            rank_staged_load(s.ka, s.boxes, b, st);
+            rank_staged_finish(s.ka, s.boxes, b, st, u.scores, part);
+        }
+        per_call_init<false, true>(s.ka, b * NT + threadIdx.x, s.prep * NT);
+        announce(&s.arrive[b], s.epoch);
+        return;
+    }
+    const bool ready = wait_prepared(s, &ok_sh);
+    if (b == s.prep) {
+        // the sweep posts the call's result, or "no result" if the wait gave
+        // up (the control block may then be incomplete)
+        if (ready) sweep_body<true>(sa, removed, u.sweep);
+        post_from_workgroup(s.post, sa.ctrl, ready);
+        return;
+    }
+    if (!ready) return;
+    const Work &w = s.ka.w;
+    const maskcore::MaskPtrs m_{w.sb,     w.area,   nullptr,    w.tile_cend, w.item_base, w.mask,
+                                w.tcount, w.tent_wk, w.tent_val, w.tnear,     w.spk};
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    maskcore::mask_items<STRIP_SINGLE, false, true, false, true>(
+        ma, m_, w.ctrl, (b - s.prep - 1) * NWAVES + wave, s.mask_waves, w.done);
+}
+
+// The call's result, posted after the last kernel where that kernel has
+// many workgroups (stream order makes it wait for all of them).
+__global__ __launch_bounds__(64) void publish_kernel(Post p, const Ctrl *ctrl) {
+    if (threadIdx.x == 0) post_result(p, ctrl, true);
 }
 
 // ---------------------------------------------------------------- compaction
@@ -991,14 +1136,16 @@ SweepArgs make_sweep_args(const Problem &P, const Layout &L, const Work &w, int6
     a.done = w.done;
     a.strip_groups = (int)((L.words + P.strip - 1) / P.strip);
     a.done_shift = 0;
+    a.post = Post{nullptr, 0};
     return a;
 }
 
 }  // namespace
 
 hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
-                        hipStream_t stream) {
-    const SweepArgs a = make_sweep_args(P, L, w, keep_out);
+                        hipStream_t stream, const Post &post) {
+    SweepArgs a = make_sweep_args(P, L, w, keep_out);
+    a.post = post;
     const size_t lds = (size_t)(L.words + NEAR_TILES) * sizeof(uint64_t);
     hipLaunchKernelGGL(sweep_kernel, dim3(1), dim3(NT), lds, stream, a);
     return hipGetLastError();
@@ -1063,6 +1210,55 @@ hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, i
     hipLaunchKernelGGL(mask_sweep_kernel, dim3((unsigned)(blocks + 1)), dim3(NT), lds, stream, ma,
                        w.ctrl, w.sb, w.area, w.tile_cend, w.item_base, w.mask, w.tcount,
                        w.tent_wk, w.tent_val, w.tnear, w.done, w.spk, sa2);
+    return hipGetLastError();
+}
+
+hipError_t launch_publish(const Work &w, const Post &post, hipStream_t stream) {
+    if (post.dst == nullptr) return hipSuccess;
+    hipLaunchKernelGGL(publish_kernel, dim3(1), dim3(64), 0, stream, post, (const Ctrl *)w.ctrl);
+    return hipGetLastError();
+}
+
+bool small_launch_applies(const Problem &P) {
+    return !P.grouped && P.n >= 1 && P.n <= SMALL_MAX;
+}
+
+hipError_t launch_small(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
+                        uint64_t epoch, const Post &post, hipStream_t stream) {
+    if (!small_launch_applies(P)) return hipErrorInvalidValue;
+    SmallArgs s;
+    KeysArgs &ka = s.ka;
+    ka.boxes = reinterpret_cast<const float4 *>(P.boxes);
+    ka.scores = P.scores;
+    ka.class_ids = nullptr;
+    ka.offsets = nullptr;
+    ka.num_images = 1;
+    ka.n = P.n;
+    ka.npad = (int)L.npad;
+    ka.words = (int)L.words;
+    ka.strip = P.strip;
+    ka.mstride = (int)L.mstride;
+    ka.tiles = (int)L.tiles;
+    ka.grouped = 0;
+    ka.w = w;
+    s.boxes = ka.boxes;
+    s.arrive = w.arrive;
+    s.epoch = epoch;
+    s.prep = (int)L.words + 1;
+    s.post = post;
+    // one work item per wave; the pairs are split into row groups while the
+    // items fit 16 waves per CU
+    maskcore::MaskArgs ma = maskcore::make_mask_args(P, L, (int64_t)device_cu_count() * 16);
+    // every row tile covers all column tiles: the item count is known here
+    ma.items_known = (int)maskcore::mask_items_upper_bound(P, L);
+    const int64_t items = (int64_t)ma.items_known << ma.qshift;
+    const int64_t mask_blocks = (items + NWAVES - 1) / NWAVES;
+    s.mask_waves = (int)(mask_blocks * NWAVES);
+    SweepArgs sa = make_sweep_args(P, L, w, keep_out);
+    sa.done_shift = ma.qshift;  // a finished pair counts 64 << qshift
+    const size_t lds = (size_t)(L.words + NEAR_TILES) * sizeof(uint64_t);
+    hipLaunchKernelGGL(small_nms_kernel, dim3((unsigned)(s.prep + 1 + mask_blocks)), dim3(NT),
+                       lds, stream, s, ma, sa);
     return hipGetLastError();
 }
 

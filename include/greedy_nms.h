@@ -90,7 +90,9 @@ typedef enum nms_status {
 #define NMS_STAGE_GATHER 1   /* sorted box gather + areas + input checks     */
 #define NMS_STAGE_MASK 2     /* triangle-tiled IoU suppression bitmask; one  */
                              /* image of 32705 to 262144 boxes: mask and     */
-                             /* sweep in one launch (sweep overlaps mask)    */
+                             /* sweep in one launch (sweep overlaps mask);   */
+                             /* the one-launch path for small inputs: the    */
+                             /* whole call, timed here                       */
 #define NMS_STAGE_SWEEP 3    /* greedy sweep over the mask (+ compaction);   */
                              /* after the fused launch, only its completion  */
                              /* check (or the sweep, if a tile's list of     */
@@ -170,16 +172,43 @@ nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, fl
                           int64_t num_images, int64_t *keep_out, int64_t *num_kept,
                           void *stream);
 
+/* nms_f32_ex flags. */
+#define NMS_FLAG_ONE_LAUNCH 1    /* one image of 1 to 4096 boxes: the whole  */
+                                 /* call in a single launch                  */
+
+/*
+ * nms_f32_ex -- nms_f32 with launch-plan flags; flags 0 is nms_f32.
+ *   flags   0 or NMS_FLAG_ONE_LAUNCH (other bits: NMS_INVALID_ARG).
+ * NMS_FLAG_ONE_LAUNCH: one image of 1 to 4096 boxes runs sort, mask, sweep
+ * and output in one launch, against the fixed per-launch cost that the
+ * "LeetCUDA 14-nms" page (measured results) blames for its losses at 1024
+ * and 2048 boxes.  Its workgroups hand over through device memory (a
+ * bounded wait on the sort's workgroups, then per-row-tile counters as in
+ * the fused launch); if a wait gives up, or a row tile's list of nonzero
+ * mask words overflows, the call runs nms_f32's launches instead.  The
+ * result is identical either way.  Other inputs ignore the flag.  Our
+ * measurement: on MI355X a dependent launch on the same stream costs less
+ * than those hand-overs (the three launches of a 1024-box call span 17 us
+ * of GPU time, the one launch 25 us), so nms_f32 does not take it.
+ * Other arguments and returns as for nms_f32.
+ */
+nms_status nms_f32_ex(const float *boxes, const float *scores, int64_t n, float iou_thresh,
+                      const int32_t *class_ids, const int64_t *batch_offsets, int64_t num_images,
+                      int64_t *keep_out, int64_t *num_kept, void *workspace,
+                      size_t workspace_bytes, void *stream, int flags);
+
 /* nms_f32_profiled flags. */
 #define NMS_PROFILE_NO_FUSION 1  /* run the mask and the sweep as separate */
                                  /* launches (to time the mask kernel alone) */
+#define NMS_PROFILE_ONE_LAUNCH 2 /* as NMS_FLAG_ONE_LAUNCH (timed as the    */
+                                 /* mask stage)                              */
 
 /*
  * nms_f32_profiled -- nms_f32 with HIP events recorded on `stream` around
  * each stage.  stage_ms (host, NMS_NUM_STAGES floats) receives each stage's
  * elapsed GPU time in milliseconds (0 for a stage that did not run).  flags:
- * 0 or NMS_PROFILE_NO_FUSION (other bits: NMS_INVALID_ARG).  The result is
- * identical to nms_f32's either way.
+ * 0, NMS_PROFILE_NO_FUSION or NMS_PROFILE_ONE_LAUNCH (other bits, or both:
+ * NMS_INVALID_ARG).  The result is identical to nms_f32's either way.
  */
 nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
                             float iou_thresh, const int32_t *class_ids,
@@ -241,6 +270,8 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
 #define NMS_PLAN_FUSED 1         /* 1: nms_f32 runs mask and sweep in one launch */
 #define NMS_PLAN_FUSED_QSHIFT 2  /* the fused launch's split, -1 if not fused   */
 #define NMS_PLAN_RANK_SORT 3     /* 1: the one-launch ranking sort, 0: radix    */
+#define NMS_PLAN_SMALL 4         /* 1: the input may take the one-launch path */
+                                 /* (one image of 1 to 4096 boxes)             */
 #define NMS_PLAN_FIELDS 8
 
 /*

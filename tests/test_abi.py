@@ -35,7 +35,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for want in ("nms_f32", "nms_workspace_size", "nms_status_string", "nms_f32_profiled",
+    for want in ("nms_f32", "nms_f32_ex", "nms_workspace_size", "nms_status_string",
+                 "nms_f32_profiled",
                  "nms_debug_order", "nms_debug_mask", "nms_debug_decide",
                  "nms_matrix_workspace_size", "nms_matrix_f32", "nms_matrix_f32_profiled"):
         assert want in names
