@@ -53,7 +53,6 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_tnear = take(np * 8 * (NEAR_TILES + 1));
     L.off_hist_tile = take((size_t)L.tiles * RADIX_PASSES * 256 * 4);
     L.off_lb_status = take((size_t)RADIX_PASSES * L.tiles * 256 * 4);
-    L.off_tickets = take(RADIX_PASSES * 4);
     L.off_err_tile = take((size_t)L.tiles * 4);
     L.off_gcls = take(np * 4);
     L.off_gimg = take(np * 4);
@@ -100,7 +99,6 @@ Work carve(void *workspace, const Layout &L) {
     w.tnear = reinterpret_cast<uint64_t *>(b + L.off_tnear);
     w.hist_tile = reinterpret_cast<uint32_t *>(b + L.off_hist_tile);
     w.lb_status = reinterpret_cast<uint32_t *>(b + L.off_lb_status);
-    w.tickets = reinterpret_cast<uint32_t *>(b + L.off_tickets);
     w.err_tile = reinterpret_cast<uint32_t *>(b + L.off_err_tile);
     w.mask = reinterpret_cast<uint64_t *>(b + L.off_mask);
     w.done = reinterpret_cast<uint32_t *>(b + L.off_done);

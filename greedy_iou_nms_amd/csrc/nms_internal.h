@@ -171,7 +171,7 @@ struct Layout {
     size_t off_order = 0, off_score_order = 0, off_seg = 0, off_inv = 0;
     size_t off_sb = 0, off_area = 0, off_tile_cend = 0, off_item_base = 0, off_kept = 0;
     size_t off_tcount = 0, off_tent_wk = 0, off_tent_val = 0, off_tnear = 0;
-    size_t off_hist_tile = 0, off_lb_status = 0, off_tickets = 0, off_err_tile = 0;
+    size_t off_hist_tile = 0, off_lb_status = 0, off_err_tile = 0;
     size_t off_gcls = 0, off_gimg = 0, off_pass_plan = 0, off_gbase = 0;
     size_t off_done = 0, off_seg_start = 0, off_start_bits = 0, off_block_cnt = 0;
     size_t off_momax = 0, off_mscore = 0, off_mlo = 0, off_mhi = 0, off_mdrop = 0;
@@ -204,12 +204,11 @@ struct Work {
     uint64_t *tnear;
     uint64_t *mask;        // suppression bitmask rows
     // radix sort: per-tile digit histograms [tile][RADIX_PASSES][256],
-    // look-back status words [pass][tile][256], one ticket per pass, per-tile
+    // look-back status words [pass][tile][256], per-tile
     // error bits from key generation, the grouped keys of every input box
     // (class key, image), and per pass its plan and digit starts [pass][256]
     uint32_t *hist_tile;
     uint32_t *lb_status;
-    uint32_t *tickets;
     uint32_t *err_tile;
     uint32_t *gcls;
     uint32_t *gimg;

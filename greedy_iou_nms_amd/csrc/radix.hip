@@ -41,8 +41,8 @@
 //                       position, the band of column tiles of every row tile
 //                       and the mask work items.
 //
-// The look-back waits only on tiles that took their ticket earlier, which are
-// already running, and every wait is bounded: a wait that gives up raises an
+// The look-back waits only on lower-numbered tiles, whose workgroups the GPU
+// started earlier, and every wait is bounded: a wait that gives up raises an
 // internal error instead of hanging.
 #include <cmath>
 
@@ -217,7 +217,6 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
     }
     if (tid == 0) w.err_tile[tile] = err_sh;
     if (tile == 0 && tid == 0) {
-        for (int p = 0; p < RADIX_PASSES; ++p) w.tickets[p] = 0u;
         Ctrl *c = w.ctrl;
         c->error = 0u;
         c->flags = FLAG_ORDERED_BOXES;
@@ -352,7 +351,6 @@ struct PassSmem {
     uint32_t wpre[NWAVES][256];
     uint32_t stage_k[TILE];
     uint32_t stage_v[TILE];
-    uint32_t tile;
     uint32_t err;
     uint32_t unordered;
     float4 ext[NWAVES];
@@ -409,38 +407,17 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
     const uint32_t *src_v = pl.src ? w.vals1 : w.vals0;
     uint32_t *dst_k = pl.src ? w.keys0 : w.keys1;
     uint32_t *dst_v = pl.src ? w.vals0 : w.vals1;
+    // Tile t is workgroup t.  The GPU starts workgroups in order, so a tile
+    // only ever waits (in the look-back below) on tiles already running;
+    // the wait is bounded in any case.  (Numbering tiles by a ticket taken
+    // at the start would put a round trip to memory before every load.)
+    const int tile = blockIdx.x;
     if (tid == 0) {
-        // tiles are numbered in the order their workgroups start, so a tile
-        // only ever waits on tiles that are already running
-        sm.tile = atomicAdd(&w.tickets[a.pass], 1u);
         sm.err = 0u;
         sm.unordered = 0u;
     }
-    if (a.planned) {
-        sm.gbase[tid] = w.gbase[a.pass * 256 + tid];
-    } else {
-        // global start of each digit: all tiles' counts of this pass's digit,
-        // eight tiles' loads in flight at a time
-        const uint32_t *h = w.hist_tile + (size_t)a.pass * 256 + tid;
-        constexpr size_t TS = (size_t)RADIX_PASSES * 256;  // one tile's counts
-        uint32_t tot = 0;
-        int t = 0;
-        for (; t + 8 <= a.tiles; t += 8) {
-            uint32_t c[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] = h[(size_t)(t + j) * TS];
-            tot += ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
-        }
-        for (; t < a.tiles; ++t) tot += h[(size_t)t * TS];
-        sm.tcnt[tid] = tot;  // scratch until the scan below
-        __syncthreads();
-        if (wave == 0) scan256(sm.tcnt, sm.gbase);
-    }
-    __syncthreads();
-    const int tile = (int)sm.tile;
-    if (tid == 0 && pl.last && w.err_tile[tile]) atomicOr(&w.ctrl->error, w.err_tile[tile]);
-
-    // load and rank the tile
+    // the tile's values (and score keys) first: no load here depends on
+    // another, so they are all in flight together with the counts below
     const int wbase = tile * TILE + wave * 64 * E;
     uint32_t k[E], v[E], rk[E];
 #pragma unroll
@@ -449,6 +426,31 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
         v[e] = i < a.n ? src_v[i] : 0u;
         k[e] = kind == 0 && i < a.n ? src_k[i] : 0u;
     }
+    if (a.planned) {
+        sm.gbase[tid] = w.gbase[a.pass * 256 + tid];
+    } else {
+        // global start of each digit: all tiles' counts of this pass's
+        // digit, up to HROUND tiles' loads in flight at a time
+        constexpr int HROUND = 32;
+        const uint32_t *h = w.hist_tile + (size_t)a.pass * 256 + tid;
+        constexpr size_t TS = (size_t)RADIX_PASSES * 256;  // one tile's counts
+        uint32_t tot = 0;
+        for (int t0 = 0; t0 < a.tiles; t0 += HROUND) {
+            uint32_t c[HROUND];
+#pragma unroll
+            for (int j = 0; j < HROUND; ++j)
+                c[j] = t0 + j < a.tiles ? h[(size_t)(t0 + j) * TS] : 0u;
+#pragma unroll
+            for (int j = 0; j < HROUND; ++j) tot += c[j];
+        }
+        sm.tcnt[tid] = tot;  // scratch until the scan below
+        __syncthreads();
+        if (wave == 0) scan256(sm.tcnt, sm.gbase);
+    }
+    __syncthreads();
+    if (tid == 0 && pl.last && w.err_tile[tile]) atomicOr(&w.ctrl->error, w.err_tile[tile]);
+
+    // rank the tile
     if (kind != 0) {
         const uint32_t *gk = kind == 1 ? w.gcls : w.gimg;
 #pragma unroll
