@@ -61,9 +61,12 @@ MASK_STRIP = 8
 
 
 def _measure(w, steps, warmup, fuse=True):
-    """Time `steps` calls after `warmup` untimed ones.  Every call ends with
-    the library's read-back of the kept count (a stream synchronisation), so
-    the host clock around a call is its end-to-end time."""
+    """Time `steps` calls after `warmup` untimed ones, as a user calls the
+    library (``nms``: every call returns once its result is complete, so the
+    host clock around a call is its end-to-end time), then `steps` calls of
+    ``nms_profiled`` (HIP events on the launch stream around every stage) for
+    the stage times.  fuse=False: the mask and the sweep as separate
+    launches; every timed call is then a profiled one."""
     import numpy as np
     import torch
 
@@ -77,28 +80,37 @@ def _measure(w, steps, warmup, fuse=True):
     ws = g.Workspace(dev)
     out = torch.empty(w.n, dtype=torch.int64, device=dev)
 
-    def call():
+    def profiled():
         return g.nms_profiled(boxes, scores, w.iou_threshold, cls, offs, workspace=ws, out=out,
                               fuse=fuse)
 
+    def call():
+        if not fuse:
+            return profiled()[0]
+        return g.nms(boxes, scores, w.iou_threshold, cls, offs, workspace=ws, out=out)
+
     first = None
     for _ in range(warmup):
-        keep, _ = call()
+        keep = call()
         if first is None:
             first = keep.cpu().numpy().copy()
+        profiled()
     torch.cuda.synchronize()
-    stage_sum = {s: 0.0 for s in g.STAGES}
     call_ms = []
     t0 = time.perf_counter()
     for _ in range(steps):
         t1 = time.perf_counter()
-        keep, st = call()
+        keep = call()
         call_ms.append(1000.0 * (time.perf_counter() - t1))
-        for k, v in st.items():
-            stage_sum[k] += v
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     last = keep.cpu().numpy().copy()
+    stage_sum = {s: 0.0 for s in g.STAGES}
+    for _ in range(steps):
+        _, st = profiled()
+        for k, v in st.items():
+            stage_sum[k] += v
+    torch.cuda.synchronize()
     deterministic = first is None or bool(np.array_equal(first, last))
     return {
         "elapsed": elapsed,
@@ -283,6 +295,9 @@ def main():
                     help="only run device copies of BYTES bytes (counter calibration)")
     ap.add_argument("--trace-config", type=int, default=0, metavar="K",
                     help="only time workload K (1..5) as the library runs it (for profiler runs)")
+    ap.add_argument("--separate", action="store_true",
+                    help="with --main-only: the mask and the sweep as separate launches "
+                         "(for profiler runs of the mask kernel alone)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library runs the whole path on "
@@ -302,6 +317,12 @@ def main():
         return
 
     w = workloads.config(5, seed=0)
+    if args.separate:
+        rs = _measure(w, args.steps, args.warmup, fuse=False)
+        print(json.dumps({"workload": w.name, "n": w.n, "steps": args.steps,
+                          "separate_launches": True, "ms_per_call": rs["call_ms"],
+                          "stage_ms": rs["stage_ms"]}))
+        return
     r = _measure(w, args.steps, args.warmup)
     ms_per_step = 1000.0 * r["elapsed"] / args.steps
     pairs = _pairs(w)
