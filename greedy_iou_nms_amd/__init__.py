@@ -58,6 +58,8 @@ def _load():
     p_i64 = ctypes.POINTER(ctypes.c_int64)
     lib.nms_workspace_size.argtypes = [c_i64, c_i64, ctypes.c_int, ctypes.POINTER(c_sz)]
     lib.nms_workspace_size.restype = ctypes.c_int
+    lib.nms_workspace_size_lists.argtypes = [c_i64, ctypes.POINTER(c_sz)]
+    lib.nms_workspace_size_lists.restype = ctypes.c_int
     common = [c_vp, c_vp, c_i64, c_f, c_vp, c_vp, c_i64, c_vp, p_i64, c_vp, c_sz, c_vp]
     lib.nms_f32.argtypes = common
     lib.nms_f32.restype = ctypes.c_int
@@ -106,6 +108,16 @@ def _workspace_size(n: int, num_images: int, has_classes: bool) -> int:
     out = ctypes.c_size_t(0)
     _check(_lib.nms_workspace_size(n, num_images, int(has_classes), ctypes.byref(out)))
     return int(out.value)
+
+
+@functools.lru_cache(maxsize=256)
+def _workspace_size_lists(n: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.nms_workspace_size_lists(n, ctypes.byref(out)))
+    return int(out.value)
+
+
+_WORKSPACE_TOO_SMALL = 2  # NMS_WORKSPACE_TOO_SMALL
 
 
 def _raw_stream(device: torch.device) -> int:
@@ -233,23 +245,33 @@ def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out,
     n = boxes.shape[0]
     with _OnDevice(device):
         stream = _raw_stream(device)
-        nbytes = _workspace_size(n, num_images, class_ids is not None)
+        full = _workspace_size(n, num_images, class_ids is not None)
+        # one image: the workspace without the dense bitmask first (enough
+        # unless a row tile's list of nonzero words overflows; the library
+        # then asks for the full size, see nms_workspace_size_lists)
+        single = class_ids is None and num_images <= 1
+        nbytes = _workspace_size_lists(n) if single else full
         ws = workspace if workspace is not None else _default_workspace(device, stream)
-        buf = ws.get(nbytes, device)
         out = _check_out(out, n, device)
         count = ctypes.c_int64(0)
-        args = [_ptr(boxes), _ptr(scores), n, ctypes.c_float(float(iou_threshold)),
-                _ptr(class_ids), _ptr(batch_offsets), num_images, _ptr(out),
-                ctypes.byref(count), _ptr(buf), buf.numel(), ctypes.c_void_p(stream)]
-        stage = None
-        if profiled:
-            stage = (ctypes.c_float * len(STAGES))()
-            flags = (0 if fuse else PROFILE_NO_FUSION) | (PROFILE_ONE_LAUNCH if one_launch else 0)
-            _check(_lib.nms_f32_profiled(*args, stage, flags))
-        elif one_launch:
-            _check(_lib.nms_f32_ex(*args, FLAG_ONE_LAUNCH))
-        else:
-            _check(_lib.nms_f32(*args))
+        stage = (ctypes.c_float * len(STAGES))() if profiled else None
+        flags = (0 if fuse else PROFILE_NO_FUSION) | (PROFILE_ONE_LAUNCH if one_launch else 0)
+
+        def call(buf):
+            args = [_ptr(boxes), _ptr(scores), n, ctypes.c_float(float(iou_threshold)),
+                    _ptr(class_ids), _ptr(batch_offsets), num_images, _ptr(out),
+                    ctypes.byref(count), _ptr(buf), buf.numel(), ctypes.c_void_p(stream)]
+            if profiled:
+                return _lib.nms_f32_profiled(*args, stage, flags)
+            if one_launch:
+                return _lib.nms_f32_ex(*args, FLAG_ONE_LAUNCH)
+            return _lib.nms_f32(*args)
+
+        buf = ws.get(nbytes, device)
+        status = call(buf)
+        if status == _WORKSPACE_TOO_SMALL and buf.numel() < full:
+            status = call(ws.get(full, device))
+        _check(status)
     keep = out[:count.value]
     if profiled:
         return keep, {name: float(stage[i]) for i, name in enumerate(STAGES)}

@@ -144,6 +144,7 @@ MaskArgs make_mask_args(const Problem &P, const Layout &L, int64_t slots) {
     // the radix sort of one image writes the quantised pre-test words
     a.use_packs = (!P.grouped && P.n > RANK_SORT_MAX) ? 1 : 0;
     a.items_known = 0;
+    a.dense = P.dense ? 1 : 0;
     return a;
 }
 

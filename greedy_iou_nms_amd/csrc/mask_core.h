@@ -98,6 +98,8 @@ struct MaskArgs {
     // where the control block is written by the same launch); 0: read it
     // from the control block
     int items_known;
+    // write dense rows (every band word) besides the lists
+    int dense;
 };
 
 // Read-only inputs and the output of the mask kernel.  They are separate
@@ -512,11 +514,13 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
     if (COHERENT) report_done(done, pending);
     if (mine) {
         const int p = p0 + lane;
-        uint64_t *dst = m_.mask + (size_t)p * (size_t)stride + (size_t)(c0 - s0 * S);
-        uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+        if (a.dense) {
+            uint64_t *dst = m_.mask + (size_t)p * (size_t)stride + (size_t)(c0 - s0 * S);
+            uint4 *d4 = reinterpret_cast<uint4 *>(dst);
 #pragma unroll
-        for (int t = 0; t < S; t += 2)
-            d4[t / 2] = make_uint4(out_lo[t], out_hi[t], out_lo[t + 1], out_hi[t + 1]);
+            for (int t = 0; t < S; t += 2)
+                d4[t / 2] = make_uint4(out_lo[t], out_hi[t], out_lo[t + 1], out_hi[t + 1]);
+        }
         // transposed copies of the words for tiles r .. r + NEAR_TILES
 #pragma unroll
         for (int t = 0; t < S; ++t) {

@@ -166,6 +166,7 @@ Problem make_problem(const float *boxes, const float *scores, int64_t n, float t
     P.num_images = offsets ? (int)num_images : 1;
     P.grouped = class_ids != nullptr || offsets != nullptr;
     P.strip = P.grouped ? STRIP_GROUPED : STRIP_SINGLE;
+    P.dense = P.grouped;
     return P;
 }
 
@@ -315,9 +316,10 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
         return NMS_INVALID_ARG;
     Layout L;
     make_layout(n, &L);
-    if (ws_bytes < L.total) return NMS_WORKSPACE_TOO_SMALL;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-    const Problem P = make_problem(boxes, scores, n, thresh, class_ids, offsets, num_images);
+    // one image runs without dense mask rows first (see Problem::dense)
+    Problem P = make_problem(boxes, scores, n, thresh, class_ids, offsets, num_images);
+    if (ws_bytes < (P.dense ? L.total : L.off_mask)) return NMS_WORKSPACE_TOO_SMALL;
     const Work w = carve(workspace, L);
 
     EventSet events;
@@ -326,13 +328,13 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
         return stage_ms ? hipEventRecord(events.ev[i], stream) : hipSuccess;
     };
 
-    // one_launch: only the mask stage ran (it holds the whole launch)
-    auto finish = [&](const Readback &rb, bool one_launch) -> nms_status {
+    // only_mask: only the mask stage ran (the one launch, timed there)
+    auto finish = [&](const Readback &rb, bool only_mask) -> nms_status {
         const nms_status ds = device_error(rb.error);
         if (ds != NMS_OK) return ds;
         if (stage_ms) {
             for (int i = 0; i < NMS_NUM_STAGES; ++i) {
-                if (one_launch && i != NMS_STAGE_MASK) continue;
+                if (only_mask && i != NMS_STAGE_MASK) continue;
                 float ms = 0.0f;
                 if (hipEventElapsedTime(&ms, events.ev[i], events.ev[i + 1]) != hipSuccess)
                     return NMS_HIP_ERROR;
@@ -365,6 +367,7 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
         if (rb.sweep_done == 1u || rb.error != 0u) return finish(rb, true);
     }
 
+    for (;;) {
     const uint64_t tag = next_epoch();
     e = mark(0);
     if (e == hipSuccess) e = launch_radix_sort(P, L, w, stream);
@@ -391,7 +394,11 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     Readback rb;
     st = collect(w, stream, slot.p, tag, &rb);
     if (st != NMS_OK) return st;
-    return finish(rb, false);
+    if (P.dense || (rb.flags & FLAG_NEEDS_DENSE) == 0u || rb.error != 0u) return finish(rb, false);
+    // a row tile's list overflowed: again, with dense rows, if they fit
+    if (ws_bytes < L.total) return NMS_WORKSPACE_TOO_SMALL;
+    P.dense = true;
+    }
 }
 
 // Matrix NMS: the same sort, then prep, overlap maximum, decay test, kept
@@ -499,6 +506,15 @@ nms_status nms_workspace_size(int64_t n, int64_t num_images, int has_classes, si
     Layout L;
     make_layout(n, &L);
     *bytes = L.total;
+    return NMS_OK;
+}
+
+nms_status nms_workspace_size_lists(int64_t n, size_t *bytes) {
+    if (bytes == nullptr || n < 0) return NMS_INVALID_ARG;
+    if (n > NMS_MAX_BOXES) return NMS_TOO_LARGE;
+    Layout L;
+    make_layout(n, &L);
+    *bytes = L.off_mask;
     return NMS_OK;
 }
 
@@ -644,8 +660,8 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
     make_layout(n, &L);
     if (workspace_bytes < L.total) return NMS_WORKSPACE_TOO_SMALL;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-    const Problem P =
-        make_problem(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images);
+    Problem P = make_problem(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images);
+    P.dense = true;  // the export reads the dense rows
     const Work w = carve(workspace, L);
     hipError_t e = launch_radix_sort(P, L, w, stream);
     if (e == hipSuccess) e = launch_mask(P, L, w, stream);

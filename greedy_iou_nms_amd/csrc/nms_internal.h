@@ -20,6 +20,10 @@ constexpr uint32_t FLAG_ORDERED_BOXES = 1u;
 // Matrix NMS: some child with a negative score at or above the threshold,
 // for which a father with no overlap can still decide the decay test.
 constexpr uint32_t FLAG_MATRIX_ZERO_PAIRS_MATTER = 2u;
+// One image without dense mask rows: a row tile had more nonzero mask words
+// than its list holds, so the sweep stopped without a result; the call has
+// to run again with dense rows.
+constexpr uint32_t FLAG_NEEDS_DENSE = 4u;
 
 // Per-call control block at the start of the workspace.  The sort kernel
 // initialises it; later kernels read plan fields and raise error bits.  The
@@ -251,6 +255,12 @@ struct Problem {
     int num_images;
     bool grouped;          // class_ids or more than one image
     int strip;             // STRIP_SINGLE or STRIP_GROUPED
+    // The mask kernel writes dense rows (every band word) besides the lists
+    // of nonzero words.  Grouped input always (its sweep reads them); one
+    // image only when a row tile's list overflows, after a first run
+    // without them stopped (FLAG_NEEDS_DENSE).  Without dense rows the
+    // workspace ends where the dense rows would begin (Layout::off_mask).
+    bool dense;
 };
 
 // Stage launchers; all enqueue on `stream` and return the launch status.

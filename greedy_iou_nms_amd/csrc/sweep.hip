@@ -71,6 +71,7 @@ struct SweepArgs {
     int n, words, npad, mstride, strip, grouped;
     int strip_groups;  // ceil(W / strip): mask work pairs of row tile 0
     int done_shift;    // fused: a finished pair adds 64 << done_shift to done[]
+    int dense;         // the mask kernel wrote dense rows (see Problem::dense)
     Post post;         // the call's result, when this sweep ends the call
 };
 
@@ -210,11 +211,14 @@ __device__ __forceinline__ void flag_store(uint32_t *p, uint32_t v) {
 }
 
 // sm.abort values.  ABORT_ERROR: a wait gave up (internal error raised).
+// ABORT_NEEDS_DENSE: a tile's list overflowed and there are no dense rows
+// (FLAG_NEEDS_DENSE raised: the call runs again with them).
 // ABORT_BAIL: the fused sweep stops without a result (a tile's list
 // overflowed, or the mask took too long) and the plain sweep kernel that
 // follows it does the work.
 constexpr uint32_t ABORT_ERROR = 1u;
 constexpr uint32_t ABORT_BAIL = 2u;
+constexpr uint32_t ABORT_NEEDS_DENSE = 3u;
 
 // Give up: the fused sweep bails out quietly, the plain sweep reports an
 // internal error.
@@ -646,6 +650,15 @@ __device__ __forceinline__ bool apply_one(const SweepArgs &a, int stride, uint64
             // the fused sweep: leave the work to the plain sweep
             if (FUSED) {
                 give_up<true>(sm, a.ctrl);
+                return false;
+            }
+            // no dense rows this time: stop, and have the call run again
+            // with them
+            if (!a.dense) {
+                if (lane == 0) {
+                    flag_store(&sm.abort, ABORT_NEEDS_DENSE);
+                    atomicOr(&a.ctrl->flags, FLAG_NEEDS_DENSE);
+                }
                 return false;
             }
             apply_dense(a, c, stride, kept, removed);
@@ -1136,6 +1149,7 @@ SweepArgs make_sweep_args(const Problem &P, const Layout &L, const Work &w, int6
     a.done = w.done;
     a.strip_groups = (int)((L.words + P.strip - 1) / P.strip);
     a.done_shift = 0;
+    a.dense = P.dense ? 1 : 0;
     a.post = Post{nullptr, 0};
     return a;
 }

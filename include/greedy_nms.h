@@ -118,6 +118,27 @@ typedef enum nms_status {
 nms_status nms_workspace_size(int64_t n, int64_t num_images, int has_classes, size_t *bytes);
 
 /*
+ * nms_workspace_size_lists -- a smaller workspace for one image of n boxes:
+ * everything but the dense suppression bitmask: about 530 bytes per box,
+ * most of it the lists of nonzero mask words (24 KiB per 64 boxes), against
+ * n * ceil(n/64) * 8 more bytes for the bitmask (35 MB instead of 572 MB at
+ * 65,536 boxes, 273 MB instead of 33 GB at 512,000).
+ *   n       number of boxes (0 <= n <= NMS_MAX_BOXES); *bytes receives it.
+ * Returns NMS_OK, NMS_INVALID_ARG (bytes NULL, n < 0) or NMS_TOO_LARGE.
+ * For one image nms_f32 never writes the dense bitmask unless it must: the
+ * sweep reads only the lists of nonzero words of each 64-row tile ("LeetCUDA
+ * 14-nms", measured results: the blocked bitmask its authors name as the
+ * next step to cut the mask's memory).  A tile with more nonzero words than
+ * its list holds (2048: each of its boxes overlapping boxes in 32 or more
+ * other tiles on average) needs the dense rows; nms_f32 then runs the call
+ * again with them if its workspace holds nms_workspace_size() bytes, and
+ * otherwise returns NMS_WORKSPACE_TOO_SMALL (nothing else changes; call
+ * again with the larger workspace).  Grouped input always needs
+ * nms_workspace_size() bytes.
+ */
+nms_status nms_workspace_size_lists(int64_t n, size_t *bytes);
+
+/*
  * nms_f32 -- greedy IoU NMS (see the file comment for the exact result).
  *   boxes          device, n*4 floats, row k = (x1, y1, x2, y2) of box k;
  *                  16-byte aligned.
@@ -131,8 +152,10 @@ nms_status nms_workspace_size(int64_t n, int64_t num_images, int has_classes, si
  *   keep_out       device, capacity n int64: receives the kept input indices
  *                  in descending score order (ties: ascending index).
  *   num_kept       host: receives the number of kept boxes.
- *   workspace      device scratch of at least nms_workspace_size() bytes,
- *                  256-byte aligned; its contents on entry do not matter.
+ *   workspace      device scratch of at least nms_workspace_size() bytes
+ *                  (one image: nms_workspace_size_lists() bytes will do
+ *                  unless the input is dense, see there), 256-byte aligned;
+ *                  its contents on entry do not matter.
  *   stream         hipStream_t or NULL.
  * Sorting follows "LeetCUDA 14-nms" step 1 (stable, descending); the
  * bitmask layout follows its Phase 1 (bit k of word w of row i means sorted
