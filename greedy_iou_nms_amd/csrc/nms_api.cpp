@@ -1,6 +1,8 @@
 // Host side of libgreedy_nms: argument checks, workspace carve-up, stage
-// launches on the caller's stream, and the single device-to-host read-back
-// of {error bits, flags, kept count} that ends every call.
+// launches on the caller's stream, and the end of every call: the result
+// {error bits, flags, kept count} that the last kernel posts into pinned
+// host memory (or, without a pinned buffer, one device-to-host copy and a
+// stream synchronisation).
 #include <hip/hip_runtime.h>
 
 #include <unistd.h>

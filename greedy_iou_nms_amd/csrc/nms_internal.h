@@ -27,7 +27,7 @@ constexpr uint32_t FLAG_NEEDS_DENSE = 4u;
 
 // Per-call control block at the start of the workspace.  The sort kernel
 // initialises it; later kernels read plan fields and raise error bits.  The
-// first 16 bytes are copied back to the host at the end of a call.
+// first 32 bytes (Readback) reach the host at the end of a call.
 struct Ctrl {
     uint32_t error;
     uint32_t flags;

@@ -30,11 +30,12 @@
  * caller's buffer after a call returns and holds no device state between
  * calls, so calls on different streams with distinct workspaces may run
  * concurrently.  What the library does allocate, and keeps:
- *   - pinned host buffers of 16 bytes (hipHostMalloc) for the read-back of
- *     the kept count and the device-detected errors: a process-wide pool
- *     of at most 64, one per call running at that moment, allocated when
- *     every existing one is in use and kept until the process ends (past 64
- *     concurrent calls the read-back goes to pageable memory instead);
+ *   - pinned host buffers of 40 bytes (hipHostMalloc) into which a call's
+ *     last kernel posts the kept count, the device-detected errors and the
+ *     call's tag: a process-wide pool of at most 64, one per call running at
+ *     that moment, allocated when every existing one is in use and kept
+ *     until the process ends (past 64 concurrent calls the call copies the
+ *     control block back into pageable memory instead);
  *   - per profiled call (the *_profiled variants), HIP events, created and
  *     destroyed inside the call;
  *   - for nms_f32_static, a statically sized device array in the library's
@@ -43,9 +44,15 @@
  * has a destructor).
  *
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  All work
- * is enqueued on it; each nms_* compute call returns after one
- * hipStreamSynchronize, which makes *num_kept (a host pointer) valid.  Inputs
- * must not change until the call returns.
+ * is enqueued on it.  Each nms_* compute call returns once its result is
+ * complete: its last kernel posts the result into a pinned buffer of the
+ * pool and the host spins on it (for up to 2 ms, then it blocks in
+ * hipStreamSynchronize); the profiled variants, nms_f32_static and calls
+ * past the pool copy the control block back and synchronise the stream
+ * instead.  Either way, when the call returns *num_kept (a host pointer)
+ * is valid and every write of the call to keep_out and the workspace has
+ * completed (its last kernel may still be retiring; it writes nothing
+ * more).  Inputs must not change until the call returns.
  *
  * Errors.  No exception crosses the ABI.  Every call returns an nms_status;
  * on any status other than NMS_OK, *num_kept (when given) is 0 and keep_out is
@@ -67,7 +74,9 @@ typedef enum nms_status {
     /* A null pointer with n > 0, n < 0, iou_thresh NaN, num_images
      * inconsistent with batch_offsets, or a misaligned boxes pointer. */
     NMS_INVALID_ARG = 1,
-    /* workspace_bytes is below what nms_workspace_size reports. */
+    /* workspace_bytes is below what nms_workspace_size reports (one image:
+     * below nms_workspace_size_lists, or below nms_workspace_size for an
+     * input that needs the dense bitmask). */
     NMS_WORKSPACE_TOO_SMALL = 2,
     /* A NaN score or a non-finite box coordinate (detected on the device). */
     NMS_NONFINITE_INPUT = 3,
