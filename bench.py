@@ -283,6 +283,51 @@ def _workload_line(w, r):
     }
 
 
+def _table(steps, warmup):
+    """Per workload: the library's call time and stage times, pair rates,
+    exact parity with the oracle, 10 identical results in a row, and the
+    oracle's own time (single-threaded)."""
+    import numpy as np
+    import torch
+
+    import greedy_iou_nms_amd as g
+    import oracle
+    import workloads
+
+    dev = torch.device("cuda:0")
+    for idx in (1, 2, 3, 4, 5):
+        w = workloads.config(idx, seed=0)
+        r = _measure(w, steps, warmup)
+        pairs = _pairs(w)
+        ms = r["call_ms"]["median"]
+        mask_ms = r["stage_ms"]["mask"]
+        b = torch.from_numpy(w.boxes).to(dev)
+        sc = torch.from_numpy(w.scores).to(dev)
+        cl = None if w.class_ids is None else torch.from_numpy(w.class_ids).to(dev)
+        of = None if w.batch_offsets is None else torch.from_numpy(w.batch_offsets).to(dev)
+        runs = [g.nms(b, sc, w.iou_threshold, cl, of).cpu().numpy() for _ in range(10)]
+        t0 = time.perf_counter()
+        want, border = oracle.c_nms(w.boxes, w.scores, w.iou_threshold, w.class_ids,
+                                    w.batch_offsets, return_borderline=True)
+        cpu_s = time.perf_counter() - t0
+        single = w.class_ids is None and w.batch_offsets is None
+        line = {
+            "config": idx, "workload": w.name, "n": w.n, "kept": int(r["keep"].size),
+            "ms_per_call": r["call_ms"], "boxes_per_s": w.n / (ms * 1e-3),
+            "stage_ms": r["stage_ms"], "pairs": pairs,
+            "iou_per_s_mask_stage": pairs / (mask_ms * 1e-3),
+            "iou_per_s_call": pairs / (ms * 1e-3),
+            "mask_stage_frac_of_157tf": OPS_PER_PAIR * pairs / (mask_ms * 1e-3) /
+                                        (FP32_VECTOR_PEAK_TFLOPS * 1e12),
+            "mask_dense_equivalent_gbs": (_mask_algorithmic_bytes(w) / (mask_ms * 1e-3) / 1e9
+                                          if single else None),
+            "parity_vs_oracle": bool(np.array_equal(r["keep"], want)),
+            "ten_runs_identical": all(np.array_equal(x, runs[0]) for x in runs),
+            "oracle_s_one_thread": cpu_s, "near_threshold_pairs": int(border),
+        }
+        print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +340,9 @@ def main():
                     help="only run device copies of BYTES bytes (counter calibration)")
     ap.add_argument("--trace-config", type=int, default=0, metavar="K",
                     help="only time workload K (1..5) as the library runs it (for profiler runs)")
+    ap.add_argument("--table", action="store_true",
+                    help="one JSON line per workload 1..5: call time, stage times, pair rates, "
+                         "parity with the oracle, 10-run determinism, oracle time")
     ap.add_argument("--separate", action="store_true",
                     help="with --main-only: the mask and the sweep as separate launches "
                          "(for profiler runs of the mask kernel alone)")
@@ -308,6 +356,10 @@ def main():
         return
 
     import workloads
+
+    if args.table:
+        _table(args.steps, args.warmup)
+        return
 
     if args.trace_config:
         wt = workloads.config(args.trace_config, seed=0)
