@@ -100,6 +100,21 @@ __device__ __forceinline__ uint64_t read_lane64(uint64_t v, int k) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Settle the rows of one 64-row chunk in order.  cand: the rows still clear
+// whose word d (lane k holds row k's word for the chunk's own tile) is
+// nonzero; rows with a zero word remove nothing inside the chunk.  The
+// lowest candidate is kept and ORs its word into rem, which may remove later
+// candidates; then the next.  Returns rem.
+__device__ __forceinline__ uint64_t settle_rows(uint64_t d, uint64_t rem, uint64_t cand) {
+    while (cand) {
+        const int k = __builtin_ctzll(cand);
+        rem |= read_lane64(d, k);
+        cand &= cand - 1ull;  // row k settled
+        cand &= ~rem;         // rows it removed
+    }
+    return rem;
+}
+
 __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -495,17 +510,7 @@ __device__ __forceinline__ void resolve_one(const SweepArgs &a, uint64_t *remove
     read_word(c + 1, removed, sm, wb);
     read_staged(c + 2, sm, ahead);
 
-    uint64_t cand = ~rem & __ballot(cur.nw[0] != 0ull);
-    if (cand) {
-        const uint64_t d = cur.nw[0];
-        const uint64_t nz = cand;
-        do {
-            const int k = __builtin_ctzll(cand);
-            rem |= read_lane64(d, k);
-            const uint64_t above = k == 63 ? 0ull : (~0ull << (k + 1));
-            cand = ~rem & nz & above;
-        } while (cand);
-    }
+    rem = settle_rows(cur.nw[0], rem, ~rem & __ballot(cur.nw[0] != 0ull));
     const uint64_t kept = ~rem;
     uint64_t c1 = 0ull;
     if (kept & uniform64(cur.nzn)) {
@@ -814,14 +819,7 @@ __global__ __launch_bounds__(GS_THREADS) void group_sweep_kernel(GroupSweepArgs 
             const uint64_t d = in_seg ? row[t] : 0ull;
             uint64_t rem = uniform64(rw[t % GROUP_SWEEP_WIN]);
             const uint64_t valid = __ballot(in_seg);
-            uint64_t cand = ~rem & __ballot(d != 0ull) & valid;
-            const uint64_t nz = cand;
-            while (cand) {
-                const int kk = __builtin_ctzll(cand);
-                rem |= read_lane64(d, kk);
-                const uint64_t above = kk == 63 ? 0ull : (~0ull << (kk + 1));
-                cand = ~rem & nz & above;
-            }
+            rem = settle_rows(d, rem, ~rem & __ballot(d != 0ull) & valid);
             const uint64_t kept = ~rem & valid;
             const bool mine = (kept >> lane) & 1ull;
             for (int u = t + 1; u <= tl; ++u) {
