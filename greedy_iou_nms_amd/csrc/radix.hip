@@ -283,18 +283,20 @@ __global__ __launch_bounds__(PLAN_THREADS) void radix_plan_kernel(PlanArgs a) {
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const Work &w = a.w;
     // digit totals over all tiles, (pass, digit) pairs spread over the
-    // threads, the tiles' counts loaded several at a time
+    // threads, up to HROUND tiles' counts in flight at a time (each round
+    // of dependent loads is a trip to memory)
+    constexpr int HROUND = 32;
     for (int j = tid; j < a.passes * 256; j += PLAN_THREADS) {
         uint32_t t = 0;
-        int tl = 0;
-        for (; tl + 4 <= a.tiles; tl += 4) {
-            const uint32_t c0 = w.hist_tile[(size_t)(tl + 0) * RADIX_PASSES * 256 + j];
-            const uint32_t c1 = w.hist_tile[(size_t)(tl + 1) * RADIX_PASSES * 256 + j];
-            const uint32_t c2 = w.hist_tile[(size_t)(tl + 2) * RADIX_PASSES * 256 + j];
-            const uint32_t c3 = w.hist_tile[(size_t)(tl + 3) * RADIX_PASSES * 256 + j];
-            t += (c0 + c1) + (c2 + c3);
+        for (int t0 = 0; t0 < a.tiles; t0 += HROUND) {
+            uint32_t c[HROUND];
+#pragma unroll
+            for (int q = 0; q < HROUND; ++q)
+                c[q] = t0 + q < a.tiles ? w.hist_tile[(size_t)(t0 + q) * RADIX_PASSES * 256 + j]
+                                        : 0u;
+#pragma unroll
+            for (int q = 0; q < HROUND; ++q) t += c[q];
         }
-        for (; tl < a.tiles; ++tl) t += w.hist_tile[(size_t)tl * RADIX_PASSES * 256 + j];
         tot[j >> 8][j & 255] = t;
     }
     __syncthreads();
