@@ -27,7 +27,7 @@ LIB = os.path.join(HERE, "libgreedy_nms.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["radix.hip", "mask.hip", "sweep.hip", "matrix.hip", "nms_api.cpp"]
+SOURCES = ["radix.hip", "team_sort.hip", "mask.hip", "sweep.hip", "matrix.hip", "nms_api.cpp"]
 
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-x", "hip",

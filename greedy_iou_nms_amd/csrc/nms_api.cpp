@@ -72,6 +72,8 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_tile_ext = take((size_t)L.tiles * 16);
     L.off_spk = take(np * 8);
     L.off_arrive = take((size_t)(L.words + 1) * 8);
+    L.off_team = n <= TEAM_MAX_N ? take(team_ws_bytes(team_layout_members(n))) : 0;
+    L.off_team_ring = n <= TEAM_MAX_N ? take((size_t)3 * 2 * 8 * np) : 0;
     L.off_mask = take((size_t)n * (size_t)L.mstride * 8);
     L.total = off;
     *out = L;
@@ -119,6 +121,8 @@ Work carve(void *workspace, const Layout &L) {
     w.tile_ext = reinterpret_cast<float4 *>(b + L.off_tile_ext);
     w.spk = reinterpret_cast<uint2 *>(b + L.off_spk);
     w.arrive = reinterpret_cast<uint64_t *>(b + L.off_arrive);
+    w.team = L.off_team ? reinterpret_cast<uint64_t *>(b + L.off_team) : nullptr;
+    w.team_ring = L.off_team_ring ? reinterpret_cast<uint64_t *>(b + L.off_team_ring) : nullptr;
     return w;
 }
 
@@ -169,6 +173,7 @@ Problem make_problem(const float *boxes, const float *scores, int64_t n, float t
     P.grouped = class_ids != nullptr || offsets != nullptr;
     P.strip = P.grouped ? STRIP_GROUPED : STRIP_SINGLE;
     P.dense = P.grouped;
+    P.team_sort = true;
     return P;
 }
 
@@ -304,7 +309,7 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
                    const int32_t *class_ids, const int64_t *offsets, int64_t num_images,
                    int64_t *keep_out, int64_t *num_kept, void *workspace, size_t ws_bytes,
                    void *stream_ptr, float *stage_ms, bool allow_fusion, bool one_launch,
-                   bool pinned_pool = true) {
+                   bool pinned_pool = true, bool team_sort = true) {
     if (num_kept == nullptr) return NMS_INVALID_ARG;
     *num_kept = 0;
     if (stage_ms)
@@ -321,6 +326,7 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     // one image runs without dense mask rows first (see Problem::dense)
     Problem P = make_problem(boxes, scores, n, thresh, class_ids, offsets, num_images);
+    P.team_sort = team_sort;
     if (ws_bytes < (P.dense ? L.total : L.off_mask)) return NMS_WORKSPACE_TOO_SMALL;
     const Work w = carve(workspace, L);
 
@@ -372,7 +378,7 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     for (;;) {
     const uint64_t tag = next_epoch();
     e = mark(0);
-    if (e == hipSuccess) e = launch_radix_sort(P, L, w, stream);
+    if (e == hipSuccess) e = launch_radix_sort(P, L, w, next_epoch(), stream);
     if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess) e = mark(2);
     // One image of moderate size: the sweep runs inside the mask launch.  The
@@ -434,7 +440,7 @@ nms_status run_matrix(const float *boxes, const float *scores, int64_t n, float 
         return stage_ms ? hipEventRecord(events.ev[i], stream) : hipSuccess;
     };
     hipError_t e = mark(0);
-    if (e == hipSuccess) e = launch_radix_sort(P, L, w, stream);
+    if (e == hipSuccess) e = launch_radix_sort(P, L, w, next_epoch(), stream);
     if (e == hipSuccess) e = launch_matrix_prep(P, L, w, sigma, stream);
     if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess) e = launch_matrix_overlap_max(P, L, w, stream);
@@ -533,10 +539,10 @@ nms_status nms_f32_ex(const float *boxes, const float *scores, int64_t n, float 
                       int64_t *keep_out, int64_t *num_kept, void *workspace,
                       size_t workspace_bytes, void *stream, int flags) {
     if (num_kept != nullptr) *num_kept = 0;
-    if ((flags & ~NMS_FLAG_ONE_LAUNCH) != 0) return NMS_INVALID_ARG;
+    if ((flags & ~(NMS_FLAG_ONE_LAUNCH | NMS_FLAG_PASS_SORT)) != 0) return NMS_INVALID_ARG;
     return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
                    num_kept, workspace, workspace_bytes, stream, nullptr, true,
-                   (flags & NMS_FLAG_ONE_LAUNCH) != 0);
+                   (flags & NMS_FLAG_ONE_LAUNCH) != 0, true, (flags & NMS_FLAG_PASS_SORT) == 0);
 }
 
 nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, float iou_thresh,
@@ -567,11 +573,14 @@ nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
                             int64_t *keep_out, int64_t *num_kept, void *workspace,
                             size_t workspace_bytes, void *stream, float *stage_ms,
                             int flags) {
-    const int known = NMS_PROFILE_NO_FUSION | NMS_PROFILE_ONE_LAUNCH;
-    if (stage_ms == nullptr || (flags & ~known) != 0 || flags == known) return NMS_INVALID_ARG;
+    const int known = NMS_PROFILE_NO_FUSION | NMS_PROFILE_ONE_LAUNCH | NMS_PROFILE_PASS_SORT;
+    const int both = NMS_PROFILE_NO_FUSION | NMS_PROFILE_ONE_LAUNCH;
+    if (stage_ms == nullptr || (flags & ~known) != 0 || (flags & both) == both)
+        return NMS_INVALID_ARG;
     return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
                    num_kept, workspace, workspace_bytes, stream, stage_ms,
-                   (flags & NMS_PROFILE_NO_FUSION) == 0, (flags & NMS_PROFILE_ONE_LAUNCH) != 0);
+                   (flags & NMS_PROFILE_NO_FUSION) == 0, (flags & NMS_PROFILE_ONE_LAUNCH) != 0,
+                   true, (flags & NMS_PROFILE_PASS_SORT) == 0);
 }
 
 nms_status nms_matrix_workspace_size(int64_t n, size_t *bytes) {
@@ -628,7 +637,7 @@ nms_status nms_debug_order(const float *scores, int64_t n, const int32_t *class_
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     const Problem P = make_problem(nullptr, scores, n, 0.5f, class_ids, batch_offsets, num_images);
     const Work w = carve(workspace, L);
-    hipError_t e = launch_radix_sort(P, L, w, stream);
+    hipError_t e = launch_radix_sort(P, L, w, next_epoch(), stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(order_out, w.order, (size_t)n * 4, hipMemcpyDeviceToDevice, stream);
     if (e == hipSuccess && score_order_out) {
@@ -665,7 +674,7 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
     Problem P = make_problem(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images);
     P.dense = true;  // the export reads the dense rows
     const Work w = carve(workspace, L);
-    hipError_t e = launch_radix_sort(P, L, w, stream);
+    hipError_t e = launch_radix_sort(P, L, w, next_epoch(), stream);
     if (e == hipSuccess) e = launch_mask(P, L, w, stream);
     if (e == hipSuccess) e = launch_expand_mask(P, L, w, mask_out, stream);
     if (e == hipSuccess && order_out)
@@ -693,6 +702,7 @@ nms_status nms_debug_plan(int64_t n, int64_t num_images, int has_classes, int32_
     plan[NMS_PLAN_FUSED_QSHIFT] = fused ? fused_mask_qshift(P, L) : -1;
     plan[NMS_PLAN_RANK_SORT] = (!P.grouped && n <= RANK_SORT_MAX) ? 1 : 0;
     plan[NMS_PLAN_SMALL] = small_launch_applies(P) ? 1 : 0;
+    plan[NMS_PLAN_TEAM_SORT] = L.off_team != 0 && team_sort_applies(P) ? 1 : 0;
     return NMS_OK;
 }
 

@@ -106,6 +106,33 @@ constexpr int RANK_SORT_MAX = 16384;
 // 8-bit digit passes: 4 on the score key, then (grouped input) 4 on the
 // class key and 4 on the image.
 constexpr int RADIX_PASSES = 12;
+// The radix sort in one launch (team_sort.hip): up to TEAM_MAX resident
+// workgroups of TEAM_THREADS threads, each ranking a tile of up to
+// TEAM_EMAX boxes per thread in every pass; blocks beside the team check.
+constexpr int TEAM_THREADS = 1024;
+constexpr int TEAM_MAX = 32;
+constexpr int TEAM_EMAX = 8;
+constexpr int64_t TEAM_MAX_N = (int64_t)TEAM_MAX * TEAM_THREADS * TEAM_EMAX;
+// Checker blocks per team member at most (the team's XCD and up to seven
+// others).
+constexpr int TEAM_CHECKERS_PER_MEMBER = 7;
+// Team members the workspace of n boxes provides for: the most any device
+// can use (tiles of at least TEAM_THREADS boxes).
+constexpr int64_t team_layout_members(int64_t n) {
+    return n < 1 ? 0 : ((n + TEAM_THREADS - 1) / TEAM_THREADS < TEAM_MAX
+                            ? (n + TEAM_THREADS - 1) / TEAM_THREADS
+                            : TEAM_MAX);
+}
+// Bytes of the team's tagged words for tl members (carved by team_work in
+// team_sort.hip in this order): tile counts and prefixes [tl][RADIX_PASSES
+// * 256], totals [RADIX_PASSES * 256], per-pass tile counts [RADIX_PASSES]
+// [tl][256], done and extent slots [tl][16], checker slots
+// [tl * TEAM_CHECKERS_PER_MEMBER][16].
+constexpr size_t team_ws_bytes(int64_t tl) {
+    return 8 * ((size_t)2 * tl * RADIX_PASSES * 256 + (size_t)RADIX_PASSES * 256 +
+                (size_t)RADIX_PASSES * tl * 256 + (size_t)2 * tl * 16 +
+                (size_t)tl * TEAM_CHECKERS_PER_MEMBER * 16);
+}
 
 // Per radix pass, decided on the device from the digit counts.
 struct RadixPassPlan {
@@ -180,6 +207,8 @@ struct Layout {
     size_t off_done = 0, off_seg_start = 0, off_start_bits = 0, off_block_cnt = 0;
     size_t off_momax = 0, off_mscore = 0, off_mlo = 0, off_mhi = 0, off_mdrop = 0;
     size_t off_tile_ext = 0, off_spk = 0, off_arrive = 0;
+    size_t off_team = 0;       // 0: no team sort for this n
+    size_t off_team_ring = 0;  // the team's pass buffers: 3 x 2 x npad tagged words
     // the suppression bitmask comes last: Matrix NMS uses everything before it
     size_t off_mask = 0, total = 0;
 };
@@ -241,6 +270,10 @@ struct Work {
     // one launch for small inputs: W + 1 slots, each the epoch of the last
     // call whose preparing workgroup finished
     uint64_t *arrive;
+    // the radix sort in one launch: the team's tagged words and its ring of
+    // pass buffers (null when the layout has none)
+    uint64_t *team;
+    uint64_t *team_ring;
 };
 
 Work carve(void *workspace, const Layout &L);
@@ -261,13 +294,22 @@ struct Problem {
     // without them stopped (FLAG_NEEDS_DENSE).  Without dense rows the
     // workspace ends where the dense rows would begin (Layout::off_mask).
     bool dense;
+    // The sort may run in one launch (team_sort_applies); false: one launch
+    // per radix pass, as for inputs too large for the team.
+    bool team_sort;
 };
 
 // Stage launchers; all enqueue on `stream` and return the launch status.
 // launch_radix_sort sorts, gathers the sorted boxes and (grouped input)
 // plans the segments and the mask work.
-hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
+hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w, uint64_t epoch,
                              hipStream_t stream);
+// The sort in one launch (team_sort.hip) applies: grouped input of up to
+// TEAM_MAX_N boxes, or one image of RANK_SORT_MAX + 1 to TEAM_MAX_N boxes,
+// on a device with room for the team on one XCD.  epoch: new for every call.
+bool team_sort_applies(const Problem &P);
+hipError_t launch_team_sort(const Problem &P, const Layout &L, const Work &w, uint64_t epoch,
+                            hipStream_t stream);
 // Matrix NMS after the sort (matrix.hip): scores, bounds and checks; the
 // largest overlap of every box with its fathers; the decay test; the kept
 // bitmap (then launch_compact writes the output).

@@ -49,11 +49,14 @@
 #include "greedy_nms.h"
 #include "nms_internal.h"
 #include "rank_core.h"
+#include "sort_core.h"
 
 #pragma clang fp contract(off)
 
 namespace gnms {
 namespace {
+
+using namespace sortcore;
 
 constexpr int NT = RADIX_THREADS;
 constexpr int NWAVES = NT / 64;
@@ -65,45 +68,6 @@ constexpr uint32_t LB_INCLUSIVE = 2u << 30;  // count of this tile and all befor
 constexpr uint32_t LB_COUNT = (1u << 30) - 1u;
 constexpr uint32_t LB_SPIN_LIMIT = 1u << 22;
 constexpr int LB_WINDOW = 16;
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
-
-__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-    }
-    return v;
-}
-
-__device__ __forceinline__ uint32_t score_key(float s) {
-    uint32_t u = __float_as_uint(s);
-    if (u == 0x80000000u) u = 0u;
-    const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ~asc;
-}
-
-// signed class id -> unsigned key with the same order
-__device__ __forceinline__ uint32_t class_key(int32_t c) { return (uint32_t)c ^ 0x80000000u; }
-
-// Image of input box i: the largest m < num_images with off[m] <= i.
-__device__ __forceinline__ uint32_t image_of(const int64_t *off, int num_images, int64_t i) {
-    int lo = 0, hi = num_images - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= i) lo = mid;
-        else hi = mid - 1;
-    }
-    return (uint32_t)lo;
-}
-
-// Lanes add into HIST_COPIES interleaved copies of the histograms: keys of
-// real scores share their top digits (the float exponent), and atomics of
-// many lanes on one LDS word serialise.
-constexpr int HIST_COPIES = 4;
 
 // One image needs the score digits only (a third of the LDS to clear).
 template <bool GROUPED>
@@ -229,19 +193,6 @@ __global__ __launch_bounds__(NT) void radix_keys_kernel(KeysArgs a) {
     per_call_init<GROUPED>(a, gid, gsz);
 }
 
-// Exclusive scan of v[0..256) into out[] by one wave (4 per lane).
-__device__ __forceinline__ void scan256(const uint32_t *v, uint32_t *out) {
-    const int lane = lane_id();
-    const uint32_t h0 = v[4 * lane], h1 = v[4 * lane + 1], h2 = v[4 * lane + 2],
-                   h3 = v[4 * lane + 3];
-    const uint32_t s = h0 + h1 + h2 + h3;
-    const uint32_t ex = wave_incl_sum(s) - s;
-    out[4 * lane] = ex;
-    out[4 * lane + 1] = ex + h0;
-    out[4 * lane + 2] = ex + h0 + h1;
-    out[4 * lane + 3] = ex + h0 + h1 + h2;
-}
-
 // ---------------------------------------------------------------- rank sort
 
 // One image of at most RANK_SORT_MAX boxes, in one launch: one workgroup per
@@ -357,34 +308,6 @@ struct PassSmem {
     uint32_t unordered;
     float4 ext[NWAVES];
 };
-
-// The quantised pre-test words of one box (see PACK_* in nms_internal.h):
-// q(v) = min(floor((v - lo) * s), QMAX - 1), which never reverses an order;
-// the right and bottom edges take q + 1.
-struct PackScale {
-    float x0, y0, sx, sy;
-};
-
-__device__ __forceinline__ uint32_t quantise(float v, float lo, float s) {
-    const float q = fminf(fmaxf(floorf((v - lo) * s), 0.0f), (float)(PACK_QMAX - 1u));
-    return (uint32_t)q;
-}
-
-__device__ __forceinline__ uint2 pack_box(float4 b, const PackScale &ps) {
-    const uint32_t x1 = quantise(b.x, ps.x0, ps.sx), y1 = quantise(b.y, ps.y0, ps.sy);
-    const uint32_t x2 = quantise(b.z, ps.x0, ps.sx) + 1u, y2 = quantise(b.w, ps.y0, ps.sy) + 1u;
-    return make_uint2((x1 << 16) | (PACK_QMAX - y1), (x2 << 16) | (0x8000u + PACK_QMAX - y2));
-}
-
-// Grid step for an axis of extent lo .. hi: QMAX - 1 steps, or 0 (every
-// coordinate on step 0, so the pre-test rules nothing out) when the extent
-// is empty, not finite or too small for a finite step.
-__device__ __forceinline__ float pack_step(float lo, float hi) {
-    const float d = hi - lo;
-    if (!(d > 0.0f) || !(d < INFINITY)) return 0.0f;
-    const float s = (float)(PACK_QMAX - 1u) / d;
-    return s < INFINITY ? s : 0.0f;
-}
 
 // Passes 0-3 sort on the score key (read from the key buffer), 4-7 on the
 // class key, 8-11 on the image; the last two read the key of each element's
@@ -796,7 +719,7 @@ __global__ __launch_bounds__(GP_THREADS) void group_plan_kernel(GroupPlanArgs a)
 
 }  // namespace
 
-hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
+hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w, uint64_t epoch,
                              hipStream_t stream) {
     const int tiles = (int)L.tiles;
     KeysArgs ka;
@@ -819,11 +742,18 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
                            stream, ka, bx);
         return hipGetLastError();
     }
-    if (P.grouped)
+    hipError_t e = hipSuccess;
+    const bool team = P.team_sort && w.team != nullptr && team_sort_applies(P);
+    if (team) {
+        e = launch_team_sort(P, L, w, epoch, stream);
+        if (e != hipSuccess || !P.grouped) return e;
+    } else if (P.grouped) {
         hipLaunchKernelGGL(radix_keys_kernel<true>, dim3(tiles), dim3(NT), 0, stream, ka);
-    else
+        e = hipGetLastError();
+    } else {
         hipLaunchKernelGGL(radix_keys_kernel<false>, dim3(tiles), dim3(NT), 0, stream, ka);
-    hipError_t e = hipGetLastError();
+        e = hipGetLastError();
+    }
     // The image index of a box is below num_images, so the image digits
     // above those needed for num_images - 1 are 0 for every box: those
     // passes would be skipped anyway and are not launched at all (a skipped
@@ -831,7 +761,7 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
     int image_digits = 0;
     for (int64_t m = (int64_t)P.num_images - 1; m > 0; m >>= 8) ++image_digits;
     const int passes = P.grouped ? 8 + image_digits : 4;
-    if (e == hipSuccess && P.grouped) {
+    if (e == hipSuccess && P.grouped && !team) {
         PlanArgs pa;
         pa.n = P.n;
         pa.tiles = tiles;
@@ -840,7 +770,7 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w,
         hipLaunchKernelGGL(radix_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, pa);
         e = hipGetLastError();
     }
-    for (int pass = 0; pass < passes && e == hipSuccess; ++pass) {
+    for (int pass = 0; pass < passes && e == hipSuccess && !team; ++pass) {
         PassArgs pa;
         pa.boxes = reinterpret_cast<const float4 *>(P.boxes);
         pa.n = P.n;

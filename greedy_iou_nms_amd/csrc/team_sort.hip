@@ -1,0 +1,866 @@
+// Stage (a) in one launch: the stable LSD radix sort of radix.hip (same
+// keys, same 8-bit digit passes, same order of passes), run by a team of
+// workgroups that stay resident through every pass.  Each pass is one
+// round of the team instead of one kernel launch.
+//
+// Greedy NMS visits boxes by score, highest first, with equal scores in
+// input order ("LeetCUDA 14-nms", algorithm and data flow, step 1: a stable
+// sort).  Grouped input continues with stable passes on the class key and
+// then on the image ("YOLOv5 post-processing", section 2.2: boxes of
+// different classes never suppress one another).
+//
+// Why one launch: at 65,536 boxes a pass moves 0.5 MB, a few hundred
+// nanoseconds of HBM time, yet a pass launched as its own kernel took about
+// 13 us on this GPU, spent in dependent trips to memory (the tile's loads,
+// the look-back, the scatter) and in the kernel's start and end.  Here the
+// passes follow one another inside the launch, with no barrier between them.
+//
+// The team is blocks 0 .. T - 1 (T <= 32, one tile of E * 1024 boxes each),
+// which the GPU spreads over its XCDs; the blocks after them ("checkers")
+// do the work no pass waits for.  Every word one workgroup hands to another
+// goes through device-coherent (agent-scope) loads and stores, whose
+// bandwidth is per XCD: a team packed onto one XCD ran its exchanges at a
+// fraction of the speed.
+//
+//   phase 0   member t keys the input tile t (score key; grouped: class key
+//             and image), checks its boxes, counts the digits of every pass
+//             in LDS and publishes the counts and (one image) its boxes'
+//             extent.  Owners then sum groups of 8 columns over all tiles
+//             (each digit's total, and every tile's count of it in the tiles
+//             before), and every member reads the totals and its own
+//             prefixes back.  From the totals every member derives the same
+//             plan: a pass whose digit is the same for every key is skipped;
+//             the last pass that runs writes the outputs.
+//   passes    the first pass sorts the input tiles, whose digit offsets
+//             phase 0 gave.  Each later pass loads its tile from a ring of
+//             three buffers of tagged words (value, then the pass's key),
+//             waiting only for the words it reads; ranks it (64-lane
+//             ballots; waves, then elements, then lanes walk positions in
+//             order, which keeps the pass stable); publishes the tile's digit
+//             counts and sums those of the tiles before it; and writes the
+//             tile out in digit runs through LDS, each word tagged with the
+//             next pass's tag.  A ring buffer is rewritten only after every
+//             member has loaded the pass that last read it (its counts for
+//             that pass are out).
+//   last pass the sorted order, and (boxes given) the sorted boxes, areas
+//             and (one image) the quantised pre-test words; grouped input
+//             also the inverse permutation, and the score order after the
+//             last score pass.
+//   checkers  per-call initialisation for the later kernels and the check of
+//             the batch offsets.
+//
+// Every word one workgroup reads from another carries a tag from the call's
+// epoch (and, in the ring, the pass), so nothing an earlier call or pass
+// left passes for the one expected; every wait is bounded and a wait that
+// gives up raises ERR_INTERNAL.  Member 0 writes the control block last,
+// from what every workgroup reported.
+#include <cmath>
+
+#include "greedy_nms.h"
+#include "nms_internal.h"
+#include "rank_core.h"
+#include "sort_core.h"
+
+#pragma clang fp contract(off)
+
+namespace gnms {
+namespace {
+
+using namespace sortcore;
+
+constexpr int NT = TEAM_THREADS;
+constexpr int NW = NT / 64;
+constexpr uint32_t TEAM_SPIN_LIMIT = 1u << 18;
+constexpr int SLOT = 16;  // words between two workgroups' slots (128 bytes)
+
+// Device-coherent loads and stores (agent scope) for the words workgroups
+// hand to one another.
+template <typename T>
+__device__ __forceinline__ T ld_c(const T *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_c(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): every vector memory access of this wave so far has
+// completed (stores included: they have reached the memory all XCDs share).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t v) {
+    return (uint64_t)tag << 32 | v;
+}
+
+// Loads the tagged words p[j] (bit j of want) until each carries tag; their
+// values land in out[j].  False when the wait gave up.
+template <int K>
+__device__ __forceinline__ bool poll_words(const uint64_t *const *p, uint32_t want, uint32_t tag,
+                                           uint32_t (&out)[K]) {
+    uint32_t spins = 0;
+    while (want) {
+        uint64_t w[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) w[j] = (want >> j) & 1u ? ld_c(p[j]) : 0ull;
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            if (((want >> j) & 1u) && (uint32_t)(w[j] >> 32) == tag) {
+                out[j] = (uint32_t)w[j];
+                want &= ~(1u << j);
+            }
+        if (!want) break;
+        if (++spins > TEAM_SPIN_LIMIT) return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+}
+
+// The team's words in the workspace (Layout::off_team), for tl members at
+// most (the layout's team_layout_members).
+struct TeamWork {
+    int tl;
+    uint64_t *hist;  // [tl][RADIX_PASSES * 256]: member t's digit counts of its input tile
+    uint64_t *pre;   // [tl][RADIX_PASSES * 256]: counts in the input tiles before t
+    uint64_t *tot;   // [RADIX_PASSES * 256]: digit totals
+    uint64_t *cnt;   // [RADIX_PASSES][tl][256]: per pass, tile counts (look-back)
+    uint64_t *done;  // [tl][SLOT]: member t finished, with its error bits
+    uint64_t *ext;   // [tl][SLOT]: extent of member t's input boxes (words 0-3)
+    uint64_t *chk;   // [tl * TEAM_CHECKERS_PER_MEMBER][SLOT]: checker h finished: error bits
+    uint64_t *end;   // one past the last word
+};
+
+__host__ __device__ inline TeamWork team_work(uint64_t *base, int tl) {
+    TeamWork tw;
+    uint64_t *p = base;
+    tw.tl = tl;
+    tw.hist = p;
+    p += (size_t)tl * RADIX_PASSES * 256;
+    tw.pre = p;
+    p += (size_t)tl * RADIX_PASSES * 256;
+    tw.tot = p;
+    p += (size_t)RADIX_PASSES * 256;
+    tw.cnt = p;
+    p += (size_t)RADIX_PASSES * tl * 256;
+    tw.done = p;
+    p += (size_t)tl * SLOT;
+    tw.ext = p;
+    p += (size_t)tl * SLOT;
+    tw.chk = p;
+    p += (size_t)tl * TEAM_CHECKERS_PER_MEMBER * SLOT;
+    tw.end = p;
+    return tw;
+}
+
+struct TeamArgs {
+    KeysArgs ka;
+    int team;      // members (tiles of E * NT input boxes)
+    int checkers;  // blocks T .. T + checkers - 1 (0: the members do their work)
+    int passes;    // 4, or 8 + the image digits (grouped)
+    uint64_t epoch;
+    uint64_t *team_ws;
+    int tl;        // members the workspace provides for
+    // [3][2 * npad] words: the element at position i of a pass's input is
+    // (value) at 2 i and (key) at 2 i + 1, each with the pass's ring tag;
+    // pass j reads ring j % 3
+    uint64_t *ring;
+};
+
+// Grouped input of up to TEAM_LDS_OFFSETS - 1 images finds a box's image in
+// a copy of the batch offsets in LDS.
+constexpr int TEAM_LDS_OFFSETS = 2048;
+
+__device__ __forceinline__ uint32_t image_in(const int32_t *off, int num_images, int64_t i) {
+    int lo = 0, hi = num_images - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= i) lo = mid;
+        else hi = mid - 1;
+    }
+    return (uint32_t)lo;
+}
+
+// Tag of the ring words that pass number j (0, 1, ... among the passes that
+// run) reads: unique per call and pass.
+__device__ __forceinline__ uint32_t ring_tag(uint64_t epoch, int j) {
+    return (uint32_t)(epoch * 16u + (uint64_t)j);
+}
+
+// Checker error word: bit 31 = some box is not ordered.
+constexpr uint32_t UNORDERED_BIT = 0x80000000u;
+
+template <int E, bool GROUPED>
+struct TeamSmem {
+    static constexpr int S = E * NT;
+    static constexpr int DIGITS = GROUPED ? RADIX_PASSES : 4;
+    union {
+        uint32_t hc[HIST_COPIES][DIGITS][256];
+        struct {
+            uint32_t k[S];
+            uint32_t v[S];
+        } stage;
+    } u;
+    uint32_t gtot[DIGITS * 256];  // digit totals per pass
+    uint32_t gpre[DIGITS * 256];  // this tile's input-order prefixes per pass
+    uint32_t wcnt[NW][256];
+    uint32_t wpre[NW][256];
+    uint32_t gb[256];     // start of each digit in the pass's output
+    uint32_t tcnt[256];   // digit counts of this tile
+    uint32_t tbase[256];  // start of each digit's run in the staged tile
+    int32_t gsh[256];     // output position minus staged slot, per digit
+    uint32_t part[4][256];
+    float4 ext[NW];
+    PackScale ps;
+    uint32_t skip[RADIX_PASSES];
+    int32_t act[RADIX_PASSES];  // the passes that run, in order
+    int32_t nact;
+    uint32_t err, unordered;
+    // grouped input: the batch offsets (up to TEAM_LDS_OFFSETS - 1 images)
+    int32_t offs[GROUPED ? TEAM_LDS_OFFSETS : 1];
+};
+
+// ------------------------------------------------------------------ checkers
+
+// Work no pass waits for, spread over H blocks (h = 0 .. H - 1): a share of
+// the per-call initialisation for the later kernels, and the check of the
+// batch offsets.  Returns this thread's error bits.
+template <bool GROUPED>
+__device__ uint32_t team_check(const TeamArgs &a, int h, int H) {
+    const KeysArgs &ka = a.ka;
+    const int gid = h * NT + threadIdx.x, gsz = H * NT;
+    per_call_init<GROUPED>(ka, gid, gsz);
+    uint32_t err = 0;
+    if (GROUPED && ka.offsets) {
+        // batch offsets must rise from 0 to n
+        for (int m = gid; m <= ka.num_images; m += gsz) {
+            const int64_t o = ka.offsets[m];
+            bool bad = (m == 0 && o != 0) || (m == ka.num_images && o != (int64_t)ka.n);
+            if (m > 0 && o < ka.offsets[m - 1]) bad = true;
+            if (bad) err |= ERR_BAD_OFFSETS;
+        }
+    }
+    return err;
+}
+
+__device__ __forceinline__ float4 ext_min_max(float4 a, float4 b) {
+    return make_float4(fminf(a.x, b.x), fminf(a.y, b.y), fmaxf(a.z, b.z), fmaxf(a.w, b.w));
+}
+
+__device__ __forceinline__ float4 wave_ext(float4 ex) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        ex = ext_min_max(ex, make_float4(__shfl_xor(ex.x, o, 64), __shfl_xor(ex.y, o, 64),
+                                         __shfl_xor(ex.z, o, 64), __shfl_xor(ex.w, o, 64)));
+    return ex;
+}
+
+// ------------------------------------------------------------------ kernel
+
+template <int E, bool GROUPED>
+__global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
+    using Smem = TeamSmem<E, GROUPED>;
+    constexpr int S = Smem::S;
+    __shared__ Smem sm;
+    const KeysArgs &ka = a.ka;
+    const Work &w = ka.w;
+    const TeamWork tw = team_work(a.team_ws, a.tl);
+    const uint32_t tag = (uint32_t)a.epoch;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int T = a.team, P = a.passes, n = ka.n;
+    if (b >= T) {
+        // a checker: its error bits, once its work is done
+        if (tid == 0) sm.err = 0u;
+        __syncthreads();
+        const uint32_t e = team_check<GROUPED>(a, b - T, a.checkers);
+        if (e) atomicOr(&sm.err, e);
+        __syncthreads();
+        if (tid == 0) st_c(&tw.chk[(size_t)(b - T) * SLOT], tagged(tag, sm.err));
+        return;
+    }
+    // Members are blocks 0 .. T - 1, which the GPU spreads over its XCDs:
+    // the passes move data through device-coherent loads and stores, whose
+    // bandwidth is per XCD.
+    const int t = b;
+
+    // ---------------------------------------------------------- phase 0
+    if (tid == 0) {
+        sm.err = 0u;
+        sm.unordered = 0u;
+    }
+    __syncthreads();
+    if (a.checkers == 0) {
+        const uint32_t e = team_check<GROUPED>(a, t, T);
+        if (e) atomicOr(&sm.err, e);
+    }
+    const bool lds_offs = GROUPED && ka.offsets != nullptr && ka.num_images < TEAM_LDS_OFFSETS;
+    if (lds_offs)
+        for (int j = tid; j <= ka.num_images; j += NT) sm.offs[j] = (int32_t)ka.offsets[j];
+    for (int j = tid; j < HIST_COPIES * Smem::DIGITS * 256; j += NT) (&sm.u.hc[0][0][0])[j] = 0u;
+    const int wbase = t * S + wave * 64 * E + lane;  // element e: wbase + 64 e
+    float s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = wbase + e * 64;
+        s[e] = i < n ? ka.scores[i] : 0.0f;
+    }
+    // the tile's boxes: finite, ordered with a positive finite area, and
+    // (one image) their extent, on which the pre-test words are quantised
+    bool finite = true, ordered = true;
+    float4 ex = make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
+    if (ka.boxes != nullptr) {
+        float4 bx[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = wbase + e * 64;
+            bx[e] = i < n ? ka.boxes[i] : make_float4(0.f, 0.f, 1.f, 1.f);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (wbase + e * 64 >= n) continue;
+            const float4 q = bx[e];
+            finite = finite && isfinite(q.x) && isfinite(q.y) && isfinite(q.z) && isfinite(q.w);
+            const float ar = (q.z - q.x) * (q.w - q.y);
+            ordered = ordered && q.x < q.z && q.y < q.w && ar > 0.0f && ar < INFINITY;
+            ex = ext_min_max(ex, make_float4(fminf(q.x, q.z), fminf(q.y, q.w), fmaxf(q.x, q.z),
+                                             fmaxf(q.y, q.w)));
+        }
+    }
+    if (lds_offs) __syncthreads();
+    uint32_t sk[E], ck[E], ik[E];
+    uint32_t err = finite ? 0u : ERR_NONFINITE;
+    if (!ordered) atomicOr(&sm.unordered, 1u);
+    const bool packs = !GROUPED && ka.boxes != nullptr;
+    if (packs) {
+        ex = wave_ext(ex);
+        if (lane == 0) sm.ext[wave] = ex;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = wbase + e * 64;
+        if (s[e] != s[e] && i < n) err |= ERR_NONFINITE;
+        sk[e] = score_key(s[e]);
+        ck[e] = 0u;
+        ik[e] = 0u;
+        if constexpr (GROUPED) {
+            if (i < n) {
+                ck[e] = ka.class_ids ? class_key(ka.class_ids[i]) : 0u;
+                ik[e] = lds_offs    ? image_in(sm.offs, ka.num_images, i)
+                        : ka.offsets ? image_of(ka.offsets, ka.num_images, i)
+                                     : 0u;
+                st_c(&w.gcls[i], ck[e]);
+                st_c(&w.gimg[i], ik[e]);
+            }
+        }
+    }
+    __syncthreads();
+    {
+        uint32_t(*hist)[256] = sm.u.hc[lane % HIST_COPIES];
+        // A digit every valid lane of the wave shares (the high digits of a
+        // score, of a small class id, of the image) is one add of the lane
+        // count; others are one LDS atomic per lane.
+        auto count = [&](int pos, uint32_t d, uint64_t vm, int first) {
+            const uint32_t d0 = (uint32_t)__shfl((int)d, first, 64);
+            if (__ballot(((vm >> lane) & 1u) && d != d0) == 0ull) {
+                if (lane == first) atomicAdd(&sm.u.hc[0][pos][d0], (uint32_t)__popcll(vm));
+            } else if ((vm >> lane) & 1u) {
+                atomicAdd(&hist[pos][d], 1u);
+            }
+        };
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint64_t vm = __ballot(wbase + e * 64 < n);
+            if (vm == 0ull) continue;
+            const int first = __builtin_ctzll(vm);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) count(d, (sk[e] >> (8 * d)) & 255u, vm, first);
+            if constexpr (GROUPED) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    count(4 + d, (ck[e] >> (8 * d)) & 255u, vm, first);
+                    if (8 + d < P) count(8 + d, (ik[e] >> (8 * d)) & 255u, vm, first);
+                }
+            }
+        }
+    }
+    if (err) atomicOr(&sm.err, err);
+    __syncthreads();
+    const int cols = P * 256;
+    for (int j = tid; j < cols; j += NT) {
+        uint32_t sum = 0;
+#pragma unroll
+        for (int q = 0; q < HIST_COPIES; ++q) sum += (&sm.u.hc[q][0][0])[j];
+        st_c(&tw.hist[(size_t)t * RADIX_PASSES * 256 + j], tagged(tag, sum));
+    }
+    if (packs && tid == 0) {
+        float4 te = sm.ext[0];
+        for (int v = 1; v < NW; ++v) te = ext_min_max(te, sm.ext[v]);
+        uint64_t *x = tw.ext + (size_t)t * SLOT;
+        st_c(&x[0], tagged(tag, __float_as_uint(te.x)));
+        st_c(&x[1], tagged(tag, __float_as_uint(te.y)));
+        st_c(&x[2], tagged(tag, __float_as_uint(te.z)));
+        st_c(&x[3], tagged(tag, __float_as_uint(te.w)));
+    }
+    // Owners: member t sums the groups of 8 columns g = t, t + T, ... (a
+    // group fills a 64-byte line of a tile's counts).  Lanes l and l + 32
+    // hold two columns, lane l & 31 = tile; a 32-lane scan gives every
+    // tile's prefix, lane 31 the total.
+    bool ok = true;
+    {
+        const int tile = lane & 31;
+        const int col = tid >> 5;  // 0 .. 31: four groups per round
+        for (int g0 = 0; 8 * (t + T * g0) < cols; g0 += 4) {
+            const int c = 8 * (t + T * (g0 + (col >> 3))) + (col & 7);
+            uint32_t v = 0;
+            if (c < cols && tile < T) {
+                const uint64_t *const p[1] = {&tw.hist[(size_t)tile * RADIX_PASSES * 256 + c]};
+                uint32_t out[1] = {0};
+                if (!poll_words<1>(p, 1u, tag, out)) ok = false;
+                v = out[0];
+            }
+            uint32_t incl = v;
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) {
+                const uint32_t u = __shfl_up(incl, o, 32);
+                if (tile >= o) incl += u;
+            }
+            const uint32_t total = __shfl(incl, 31, 32);
+            if (c < cols && tile < T) {
+                st_c(&tw.pre[(size_t)tile * RADIX_PASSES * 256 + c], tagged(tag, incl - v));
+                if (tile == 0) st_c(&tw.tot[c], tagged(tag, total));
+            }
+        }
+    }
+    // every member: the totals, and its own tile's prefixes
+    {
+        constexpr int K = (RADIX_PASSES * 256 + NT - 1) / NT;  // columns per thread at most
+        const uint64_t *p[2 * K];
+        uint32_t want = 0;
+#pragma unroll
+        for (int q = 0; q < K; ++q) {
+            const int j = tid + q * NT;
+            const int jj = j < cols ? j : 0;
+            p[2 * q] = &tw.tot[jj];
+            p[2 * q + 1] = &tw.pre[(size_t)t * RADIX_PASSES * 256 + jj];
+            if (j < cols) want |= 3u << (2 * q);
+        }
+        uint32_t v[2 * K];
+#pragma unroll
+        for (int q = 0; q < 2 * K; ++q) v[q] = 0;
+        if (!poll_words<2 * K>(p, want, tag, v)) ok = false;
+#pragma unroll
+        for (int q = 0; q < K; ++q) {
+            const int j = tid + q * NT;
+            if (j < cols) {
+                sm.gtot[j] = v[2 * q];
+                sm.gpre[j] = v[2 * q + 1];
+            }
+        }
+    }
+    // one image: the extent of all boxes, from every member's slot
+    if (packs && wave == 0) {
+        float4 e4 = make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
+        if (lane < T) {
+            const uint64_t *x = tw.ext + (size_t)lane * SLOT;
+            const uint64_t *const p[4] = {x, x + 1, x + 2, x + 3};
+            uint32_t v[4] = {0, 0, 0, 0};
+            if (!poll_words<4>(p, 0xFu, tag, v)) ok = false;
+            e4 = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                             __uint_as_float(v[3]));
+        }
+        e4 = wave_ext(e4);
+        if (lane == 0) {
+            sm.ps.x0 = e4.x;
+            sm.ps.y0 = e4.y;
+            sm.ps.sx = pack_step(e4.x, e4.z);
+            sm.ps.sy = pack_step(e4.y, e4.w);
+        }
+    }
+    if (!ok) atomicOr(&sm.err, ERR_INTERNAL);
+    __syncthreads();
+    // the plan: a pass whose digit is the same for every key moves nothing
+    if (wave < P) {
+        const uint32_t un = (uint32_t)n;
+        const uint32_t *g = &sm.gtot[wave * 256];
+        const bool one = g[4 * lane] == un || g[4 * lane + 1] == un || g[4 * lane + 2] == un ||
+                         g[4 * lane + 3] == un;
+        const uint64_t any = __ballot(one);
+        if (lane == 0) sm.skip[wave] = any ? 1u : 0u;
+    }
+    __syncthreads();
+    int last = -1, last_score = -1;
+    for (int p = 0; p < P; ++p)
+        if (!sm.skip[p]) {
+            last = p;
+            if (p < 4) last_score = p;
+        }
+    // every key the same: the last pass runs anyway (it moves nothing) and
+    // writes the outputs
+    if (last < 0) last = P - 1;
+    if (tid == 0) {
+        int m = 0;
+        for (int p = 0; p < P; ++p)
+            if (!sm.skip[p] || p == last) sm.act[m++] = p;
+        sm.nact = m;
+    }
+    if (GROUPED && last_score < 0) {
+        // no score pass moves anything: the score order is the input order
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = wbase + e * 64;
+            if (i < n) w.score_order[i] = i;
+        }
+    }
+
+    // ---------------------------------------------------------- passes
+    __syncthreads();
+    const int count = n - t * S < S ? n - t * S : S;
+    const int nact = sm.nact;
+    const size_t ring_words = 2 * (size_t)ka.npad;
+    uint32_t k[E], v[E], rk[E];
+    for (int j = 0; j < nact; ++j) {
+        const int p = sm.act[j];
+        const int shift = 8 * (p & 3);
+        const int kind = p >> 2;  // 0 score, 1 class, 2 image
+        const bool is_last = j == nact - 1;
+        // the tile's values and keys: the first pass keeps phase 0's; later
+        // ones load the ring words of their positions once they carry this
+        // pass's tag (no barrier: each word says whether it is written)
+        if (j == 0) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                k[e] = kind == 0 ? sk[e] : kind == 1 ? ck[e] : ik[e];
+                v[e] = (uint32_t)(wbase + e * 64);
+            }
+        } else {
+            const uint64_t *rb = a.ring + (size_t)(j % 3) * ring_words;
+            const uint64_t *pp[2 * E];
+            uint32_t want = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int i = wbase + e * 64;
+                const int ii = i < n ? i : 0;
+                pp[2 * e] = &rb[2 * (size_t)ii];
+                pp[2 * e + 1] = &rb[2 * (size_t)ii + 1];
+                if (i < n) want |= 3u << (2 * e);
+            }
+            uint32_t wv[2 * E];
+#pragma unroll
+            for (int q = 0; q < 2 * E; ++q) wv[q] = 0u;
+            if (!poll_words<2 * E>(pp, want, ring_tag(a.epoch, j), wv))
+                atomicOr(&sm.err, ERR_INTERNAL);
+            // The values are input indices.  Only after a wait gave up could
+            // one be out of range; it is then replaced, and the call reports
+            // ERR_INTERNAL.
+            bool bad = false;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                v[e] = wv[2 * e];
+                k[e] = wv[2 * e + 1];
+                if (v[e] >= (uint32_t)n) {
+                    bad = true;
+                    v[e] = 0u;
+                }
+            }
+            if (bad) atomicOr(&sm.err, ERR_INTERNAL);
+        }
+        // rank the tile: lanes with the same digit, from one ballot per bit
+        // (a lane keeps the lanes whose bit equals its own)
+        for (int q = lane; q < 256; q += 64) sm.wcnt[wave][q] = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool valid = wbase + e * 64 < n;
+            const uint32_t d = (k[e] >> shift) & 255u;
+            const uint32_t nd = ~d;
+            const uint64_t vm = __ballot(valid);
+            uint32_t plo = (uint32_t)vm, phi = (uint32_t)(vm >> 32);
+#pragma unroll
+            for (int bit = 0; bit < 8; ++bit) {
+                // 0 where this lane's bit is set, all ones where it is clear
+                const uint32_t tm = (uint32_t)__builtin_amdgcn_sbfe((int)nd, bit, 1);
+                const uint64_t m = __ballot(tm == 0u);
+                plo &= (uint32_t)m ^ tm;
+                phi &= (uint32_t)(m >> 32) ^ tm;
+            }
+            const uint64_t peers = (uint64_t)phi << 32 | plo;
+            const uint32_t r_in = __builtin_amdgcn_mbcnt_hi(phi, __builtin_amdgcn_mbcnt_lo(plo, 0u));
+            const uint32_t before = sm.wcnt[wave][d];
+            rk[e] = before + r_in;
+            // the lowest lane of each digit group advances the wave's count;
+            // the read above precedes this write in the wave's LDS order
+            if (valid && r_in == 0) sm.wcnt[wave][d] = before + (uint32_t)__popcll(peers);
+        }
+        __syncthreads();
+        if (tid < 256) {
+            const int d = tid;
+            uint32_t run = 0;
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) {
+                const uint32_t c = sm.wcnt[wv][d];
+                sm.wpre[wv][d] = run;
+                run += c;
+            }
+            sm.tcnt[d] = run;
+            if (j > 0) st_c(&tw.cnt[((size_t)p * tw.tl + t) * 256 + d], tagged(tag, run));
+        }
+        if (wave == 0) scan256(&sm.gtot[p * 256], sm.gb);
+        __syncthreads();
+        // the tile's offset per digit among the earlier tiles
+        if (j == 0) {
+            if (tid < 256) sm.part[0][tid] = sm.gpre[p * 256 + tid];
+        } else {
+            // thread (q, d) sums the counts of tiles q, q + 4, ... below t
+            const int d = tid & 255, q = tid >> 8;
+            constexpr int KT = TEAM_MAX / 4;
+            const uint64_t *pp[KT];
+            uint32_t want = 0;
+#pragma unroll
+            for (int m = 0; m < KT; ++m) {
+                const int tt = q + 4 * m;
+                pp[m] = &tw.cnt[((size_t)p * tw.tl + (tt < t ? tt : 0)) * 256 + d];
+                if (tt < t) want |= 1u << m;
+            }
+            uint32_t c[KT];
+#pragma unroll
+            for (int m = 0; m < KT; ++m) c[m] = 0;
+            if (!poll_words<KT>(pp, want, tag, c)) atomicOr(&sm.err, ERR_INTERNAL);
+            uint32_t sum = 0;
+#pragma unroll
+            for (int m = 0; m < KT; ++m) sum += c[m];
+            sm.part[q][d] = sum;
+        }
+        if (wave == 0) scan256(sm.tcnt, sm.tbase);
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t ex = sm.part[0][tid];
+            if (j > 0) ex += sm.part[1][tid] + sm.part[2][tid] + sm.part[3][tid];
+            sm.gsh[tid] = (int32_t)(sm.gb[tid] + ex) - (int32_t)sm.tbase[tid];
+        }
+        // reorder the tile by digit in LDS
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (wbase + e * 64 < n) {
+                const uint32_t d = (k[e] >> shift) & 255u;
+                const uint32_t slot = sm.tbase[d] + sm.wpre[wave][d] + rk[e];
+                sm.u.stage.k[slot] = k[e];
+                sm.u.stage.v[slot] = v[e];
+            }
+        }
+        // The ring this pass writes was last read by pass j - 2: every
+        // member must have loaded that pass's tile, which its counts for
+        // that pass (published after the loads) show.
+        if (j >= 3 && !is_last && wave == 0) {
+            const int pr = sm.act[j - 2];
+            for (int tt = lane; tt < T; tt += 64) {
+                const uint64_t *const pw[1] = {&tw.cnt[((size_t)pr * tw.tl + tt) * 256]};
+                uint32_t c[1] = {0};
+                if (!poll_words<1>(pw, 1u, tag, c)) atomicOr(&sm.err, ERR_INTERNAL);
+            }
+        }
+        __syncthreads();
+        const bool score_order_here = GROUPED && p == last_score;
+        if (!is_last) {
+            // the next pass's key: the same key, or at a change of kind the
+            // class key or the image of the box
+            const int nk = sm.act[j + 1] >> 2;
+            uint64_t *wb = a.ring + (size_t)((j + 1) % 3) * ring_words;
+            const uint32_t tag_out = ring_tag(a.epoch, j + 1);
+            bool bad = false;
+            for (int s0 = tid; s0 < count; s0 += NT) {
+                const uint32_t key = sm.u.stage.k[s0];
+                const int pos = s0 + sm.gsh[(key >> shift) & 255u];
+                const uint32_t val = sm.u.stage.v[s0];
+                // in range unless a wait gave up (see above)
+                if ((uint32_t)pos >= (uint32_t)n) {
+                    bad = true;
+                    continue;
+                }
+                uint32_t nkey = key;
+                if (GROUPED && nk != kind) {
+                    if (nk == 1) nkey = ka.class_ids ? class_key(ka.class_ids[val]) : 0u;
+                    else nkey = lds_offs    ? image_in(sm.offs, ka.num_images, val)
+                                : ka.offsets ? image_of(ka.offsets, ka.num_images, val)
+                                             : 0u;
+                }
+                if (score_order_here) w.score_order[pos] = (int32_t)val;
+                st_c(&wb[2 * (size_t)pos], tagged(tag_out, val));
+                st_c(&wb[2 * (size_t)pos + 1], tagged(tag_out, nkey));
+            }
+            if (bad) atomicOr(&sm.err, ERR_INTERNAL);
+        } else {
+            const PackScale ps = sm.ps;
+            // The sorted order, and (boxes given: the sort-only export passes
+            // none) the sorted boxes with their areas.  All of a thread's box
+            // loads are issued before any of its stores.
+            int pos[E];
+            uint32_t val[E];
+            float4 bx[E];
+#pragma unroll
+            for (int q = 0; q < E; ++q) {
+                const int s0 = tid + q * NT;
+                pos[q] = -1;
+                val[q] = 0u;
+                if (s0 < count) {
+                    const uint32_t key = sm.u.stage.k[s0];
+                    const int pq = s0 + sm.gsh[(key >> shift) & 255u];
+                    // in range unless a wait gave up (see above)
+                    if ((uint32_t)pq < (uint32_t)n) {
+                        pos[q] = pq;
+                        val[q] = sm.u.stage.v[s0];
+                    } else {
+                        atomicOr(&sm.err, ERR_INTERNAL);
+                    }
+                }
+                bx[q] = ka.boxes != nullptr && pos[q] >= 0 ? ka.boxes[val[q]]
+                                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int q = 0; q < E; ++q) {
+                if (pos[q] < 0) continue;
+                if (score_order_here) w.score_order[pos[q]] = (int32_t)val[q];
+                w.order[pos[q]] = (int32_t)val[q];
+                if (GROUPED) w.inv[val[q]] = pos[q];
+                if (ka.boxes == nullptr) continue;
+                const float4 bj = bx[q];
+                w.sb[pos[q]] = bj;
+                w.area[pos[q]] = (bj.z - bj.x) * (bj.w - bj.y);
+                if (packs) w.spk[pos[q]] = pack_box(bj, ps);
+            }
+        }
+        // the next pass rewrites the staged tile and the counts
+        __syncthreads();
+    }
+
+    // ---------------------------------------------------------- report
+    __syncthreads();
+    if (tid == 0)
+        st_c(&tw.done[(size_t)t * SLOT],
+             tagged(tag, sm.err | (sm.unordered ? UNORDERED_BIT : 0u)));
+    if (t != 0) return;
+    // member 0: every member's and every checker's bits, then the control
+    // block
+    if (tid == 0) sm.part[0][0] = 0u;
+    __syncthreads();
+    for (int j = tid; j < T + a.checkers; j += NT) {
+        const uint64_t *const p[1] = {j < T ? &tw.done[(size_t)j * SLOT]
+                                            : &tw.chk[(size_t)(j - T) * SLOT]};
+        uint32_t out[1] = {0};
+        if (!poll_words<1>(p, 1u, tag, out)) out[0] = ERR_INTERNAL;
+        if (out[0]) atomicOr(&sm.part[0][0], out[0]);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t all = sm.part[0][0];
+        Ctrl *c = w.ctrl;
+        c->error = all & ~UNORDERED_BIT;
+        c->flags = (all & UNORDERED_BIT) ? 0u : FLAG_ORDERED_BOXES;
+        c->count = 0;
+        c->num_items = GROUPED ? 0 : item_base_full(ka.words, ka.words, ka.strip);
+        c->band_stride = ka.mstride;
+        c->num_segments = 1;
+        c->sweep_done = 0u;
+    }
+}
+
+// Elements per thread of a team of at most tmax members (tiles of e * NT
+// boxes) for n boxes; 0 when n is too large.
+int team_elems(int64_t n, int tmax) {
+    for (int e = 1; e <= TEAM_EMAX; e *= 2)
+        if ((n + (int64_t)e * NT - 1) / ((int64_t)e * NT) <= tmax) return e;
+    return 0;
+}
+
+// XCDs of the current device (cached per device; 1 when unknown).
+int device_xcc_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    if (cached[dev] == 0) {
+        int x = 0;
+        if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || x <= 0)
+            x = 1;
+        cached[dev] = x;
+    }
+    return cached[dev];
+}
+
+struct TeamShape {
+    int e, team, blocks;
+};
+
+// The team's shape on the current device: members are blocks 0 .. T - 1,
+// at most TEAM_MAX and at most one per XCD's worth of compute units, so that
+// every member is resident (one workgroup per compute unit); blocks T .. up
+// to T * (XCDs, at most 8) check.
+TeamShape team_shape(int64_t n) {
+    TeamShape s{0, 0, 0};
+    int xcc = device_xcc_count();
+    xcc = xcc < 1 ? 1 : (xcc > 8 ? 8 : xcc);
+    const int per_xcd = device_cu_count() / xcc;
+    const int tmax = per_xcd < TEAM_MAX ? per_xcd : TEAM_MAX;
+    if (tmax < 1 || n < 1) return s;
+    s.e = team_elems(n, tmax);
+    if (s.e > 0) {
+        s.team = (int)((n + (int64_t)s.e * NT - 1) / ((int64_t)s.e * NT));
+        s.blocks = s.team * xcc;
+    }
+    return s;
+}
+
+}  // namespace
+
+bool team_sort_applies(const Problem &P) {
+    if (P.n < 1 || P.n > TEAM_MAX_N) return false;
+    if (!P.grouped && P.n <= RANK_SORT_MAX) return false;
+    return team_shape(P.n).team > 0;
+}
+
+hipError_t launch_team_sort(const Problem &P, const Layout &L, const Work &w, uint64_t epoch,
+                            hipStream_t stream) {
+    const TeamShape s = team_shape(P.n);
+    const int tl = (int)team_layout_members(P.n);
+    if (s.team <= 0 || s.team > tl || L.off_team == 0 || w.team == nullptr)
+        return hipErrorInvalidValue;
+    // the carve must end where the layout's region ends
+    const TeamWork tw = team_work(w.team, tl);
+    if ((size_t)(tw.end - w.team) * 8 != team_ws_bytes(tl)) return hipErrorInvalidValue;
+    TeamArgs a;
+    KeysArgs &ka = a.ka;
+    ka.boxes = reinterpret_cast<const float4 *>(P.boxes);
+    ka.scores = P.scores;
+    ka.class_ids = P.class_ids;
+    ka.offsets = P.offsets;
+    ka.num_images = P.num_images;
+    ka.n = P.n;
+    ka.npad = (int)L.npad;
+    ka.words = (int)L.words;
+    ka.strip = P.strip;
+    ka.mstride = (int)L.mstride;
+    ka.tiles = s.team;
+    ka.grouped = P.grouped ? 1 : 0;
+    ka.w = w;
+    a.team = s.team;
+    a.checkers = s.blocks - s.team;
+    int image_digits = 0;
+    for (int64_t m = (int64_t)P.num_images - 1; m > 0; m >>= 8) ++image_digits;
+    a.passes = P.grouped ? 8 + image_digits : 4;
+    a.epoch = epoch;
+    a.team_ws = w.team;
+    a.tl = tl;
+    a.ring = w.team_ring;
+    if (a.ring == nullptr) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)s.blocks), block(NT);
+#define GNMS_TEAM_LAUNCH(EV)                                                         \
+    if (s.e == EV) {                                                                 \
+        if (P.grouped)                                                               \
+            hipLaunchKernelGGL((team_sort_kernel<EV, true>), grid, block, 0, stream, a); \
+        else                                                                         \
+            hipLaunchKernelGGL((team_sort_kernel<EV, false>), grid, block, 0, stream, a); \
+    }
+    GNMS_TEAM_LAUNCH(1)
+    GNMS_TEAM_LAUNCH(2)
+    GNMS_TEAM_LAUNCH(4)
+    GNMS_TEAM_LAUNCH(8)
+#undef GNMS_TEAM_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace gnms

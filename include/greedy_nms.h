@@ -207,10 +207,13 @@ nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, fl
 /* nms_f32_ex flags. */
 #define NMS_FLAG_ONE_LAUNCH 1    /* one image of 1 to 4096 boxes: the whole  */
                                  /* call in a single launch                  */
+#define NMS_FLAG_PASS_SORT 2     /* the radix sort as one launch per pass,   */
+                                 /* as for inputs above 262144 boxes         */
 
 /*
  * nms_f32_ex -- nms_f32 with launch-plan flags; flags 0 is nms_f32.
- *   flags   0 or NMS_FLAG_ONE_LAUNCH (other bits: NMS_INVALID_ARG).
+ *   flags   0, or NMS_FLAG_ONE_LAUNCH and/or NMS_FLAG_PASS_SORT (other bits:
+ *           NMS_INVALID_ARG).
  * NMS_FLAG_ONE_LAUNCH: one image of 1 to 4096 boxes runs sort, mask, sweep
  * and output in one launch, against the fixed per-launch cost that the
  * "LeetCUDA 14-nms" page (measured results) blames for its losses at 1024
@@ -222,6 +225,12 @@ nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, fl
  * measurement: on MI355X a dependent launch on the same stream costs less
  * than those hand-overs (the three launches of a 1024-box call span 17 us
  * of GPU time, the one launch 25 us), so nms_f32 does not take it.
+ * NMS_FLAG_PASS_SORT: grouped input, and one image of more than 16384 boxes,
+ * is sorted with one launch per radix pass, the form inputs of more than
+ * 262144 boxes always take, instead of by a team of workgroups that stay
+ * resident through every pass (one launch).  The result is identical; the
+ * flag exists to compare the two (our reading: the pages fix the sort's
+ * result, a stable descending order, not its form).
  * Other arguments and returns as for nms_f32.
  */
 nms_status nms_f32_ex(const float *boxes, const float *scores, int64_t n, float iou_thresh,
@@ -234,12 +243,14 @@ nms_status nms_f32_ex(const float *boxes, const float *scores, int64_t n, float 
                                  /* launches (to time the mask kernel alone) */
 #define NMS_PROFILE_ONE_LAUNCH 2 /* as NMS_FLAG_ONE_LAUNCH (timed as the    */
                                  /* mask stage)                              */
+#define NMS_PROFILE_PASS_SORT 4  /* as NMS_FLAG_PASS_SORT                    */
 
 /*
  * nms_f32_profiled -- nms_f32 with HIP events recorded on `stream` around
  * each stage.  stage_ms (host, NMS_NUM_STAGES floats) receives each stage's
  * elapsed GPU time in milliseconds (0 for a stage that did not run).  flags:
- * 0, NMS_PROFILE_NO_FUSION or NMS_PROFILE_ONE_LAUNCH (other bits, or both:
+ * 0, NMS_PROFILE_NO_FUSION or NMS_PROFILE_ONE_LAUNCH, either with
+ * NMS_PROFILE_PASS_SORT or not (other bits, or the first two together:
  * NMS_INVALID_ARG).  The result is identical to nms_f32's either way.
  */
 nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
@@ -304,6 +315,9 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
 #define NMS_PLAN_RANK_SORT 3     /* 1: the one-launch ranking sort, 0: radix    */
 #define NMS_PLAN_SMALL 4         /* 1: the input may take the one-launch path */
                                  /* (one image of 1 to 4096 boxes)             */
+#define NMS_PLAN_TEAM_SORT 5     /* 1: the radix sort runs in one launch (a team */
+                                 /* of resident workgroups), 0: one launch per  */
+                                 /* pass (or the ranking sort)                  */
 #define NMS_PLAN_FIELDS 8
 
 /*

@@ -76,8 +76,15 @@ def test_workspace_size_bound():
         words = (n + 63) // 64
         mask = n * (((words + 15) // 16) * 16) * 8
         # dense mask + O(n) scratch (sort buffers, sorted boxes, row lists,
-        # the per-box arrays of Matrix NMS)
-        assert mask <= b <= mask + 576 * n + 128 * 1024
+        # the per-box arrays of Matrix NMS) + the one-launch sort's words:
+        # per team member (one per 1024 boxes, at most 32) 12 x 256 counts
+        # and prefixes, 12 x 256 per-pass counts and 9 slots of 16 words,
+        # plus 12 x 256 totals, 8 bytes each; its pass buffers hold three
+        # times two 8-byte words per box (48 n bytes)
+        members = min(32, (n + 1023) // 1024)
+        team = 8 * (members * (2 * 12 * 256 + 12 * 256 + 9 * 16) + 12 * 256) + 48 * 64 * (
+            (n + 63) // 64)
+        assert mask <= b <= mask + 576 * n + 128 * 1024 + team
         assert b >= prev
         prev = b
     st, b = _ws(lib, 65536)
@@ -144,8 +151,10 @@ def test_matrix_workspace_is_linear_and_below_greedy():
     for n in (1, 1000, 65536, 512000):
         st, b = _mws(lib, n)
         assert st == 0 and b < _ws(lib, n)[1]
-        # no pairwise matrix: a few hundred bytes per box at most
-        assert b <= 576 * n + (1 << 20)
+        # no pairwise matrix: a few hundred bytes per box at most, plus the
+        # one-launch sort's pass buffers (48 bytes per box) and its words
+        # (under 2.5 MB)
+        assert b <= (576 + 48) * n + (1 << 20) + (5 << 19)
     assert _mws(lib, 512001)[0] == 5
     assert lib.nms_matrix_workspace_size(5, None) == 1
 
