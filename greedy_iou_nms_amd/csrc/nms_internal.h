@@ -111,7 +111,7 @@ constexpr int RADIX_PASSES = 12;
 // TEAM_EMAX boxes per thread in every pass; blocks beside the team check.
 constexpr int TEAM_THREADS = 1024;
 constexpr int TEAM_MAX = 32;
-constexpr int TEAM_EMAX = 8;
+constexpr int TEAM_EMAX = 4;
 constexpr int64_t TEAM_MAX_N = (int64_t)TEAM_MAX * TEAM_THREADS * TEAM_EMAX;
 // Checker blocks per team member at most (the team's XCD and up to seven
 // others).

@@ -12,6 +12,10 @@
 // order inside; the order after the score passes is kept as the plain score
 // order for the final compaction.
 //
+// Grouped input of up to 131072 boxes, and one image of 16385 to 131072,
+// take the same passes in one launch instead (team_sort.hip); the kernels
+// below sort the rest, and plan the segments of every grouped input.
+//
 //   rank_sort_kernel    one image of at most 16384 boxes: every box's sorted
 //                       position counted directly (n^2 comparisons), the
 //                       sorted-box gather, the input checks and the per-call
@@ -37,9 +41,9 @@
 //                       the inverse permutation.
 //   group_starts_kernel grouped input, all compute units: a bitmap of the
 //                       sorted positions where a new (image, class) group starts.
-//   group_plan_kernel   grouped input, one workgroup: segment of every sorted
-//                       position, the band of column tiles of every row tile
-//                       and the mask work items.
+//   group_plan_kernel   grouped input, a workgroup per 32 row tiles: segment
+//                       of every sorted position, the band of column tiles of
+//                       every row tile and the mask work items.
 //
 // The look-back waits only on lower-numbered tiles, whose workgroups the GPU
 // started earlier, and every wait is bounded: a wait that gives up raises an
@@ -580,6 +584,7 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
 
 constexpr int GP_THREADS = 1024;
 constexpr int GP_WAVES = GP_THREADS / 64;
+constexpr int GP_TILES = 32;  // row tiles a group-plan workgroup writes
 
 struct GroupPlanArgs {
     int n, words, npad, strip;
@@ -629,33 +634,60 @@ __device__ uint32_t gp_excl_sum(uint32_t v, GroupPlanSmem &sm, uint32_t *total) 
     return r;
 }
 
-// Sorted position of the last row of the segment holding sorted position p:
-// one before the next segment start after p (n - 1 if there is none).
-__device__ __forceinline__ int segment_end(const GroupPlanSmem &sm, int p, int n) {
-    const int nw = (n + 63) / 64;
-    int wi = p >> 6;
-    uint64_t bits = (p & 63) == 63 ? 0ull : (sm.start[wi] & (~0ull << ((p & 63) + 1)));
-    while (bits == 0ull) {
-        if (++wi >= nw) return n - 1;
-        bits = sm.start[wi];
+// Position of segment start k (0-based): the word holding it is the last
+// word with fewer starts before it than k + 1, then the bit inside it.
+__device__ __forceinline__ int start_position(const GroupPlanSmem &sm, int nw, uint32_t k) {
+    int lo = 0, hi = nw - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sm.wpre[mid] <= k) lo = mid;
+        else hi = mid - 1;
     }
-    return 64 * wi + __builtin_ctzll(bits) - 1;
+    uint64_t x = sm.start[lo];
+    uint32_t j = k - sm.wpre[lo];  // j-th set bit of x (0-based)
+    int pos = 0;
+#pragma unroll
+    for (int width = 32; width > 0; width >>= 1) {
+        const uint32_t c = (uint32_t)__popcll(x & ((1ull << width) - 1ull));
+        if (j >= c) {
+            j -= c;
+            x >>= width;
+            pos += width;
+        }
+    }
+    return 64 * lo + pos;
 }
 
-// Grouped input after the sort: segment ids, the band of every row tile (its
-// columns run through the tile holding the end of the segment that holds
-// the tile's last row), the work items of the mask kernel and the mask row
-// stride.
+// One past the last column tile of row tile r's band: its columns run
+// through the tile holding the end of the segment that holds the tile's
+// last row.
+__device__ __forceinline__ int band_end(const GroupPlanSmem &sm, int r, int n, int nw,
+                                        uint32_t segments) {
+    const int last = 64 * r + 63 < n - 1 ? 64 * r + 63 : n - 1;
+    const uint64_t bits = sm.start[last >> 6];
+    const uint32_t s =
+        sm.wpre[last >> 6] + (uint32_t)__popcll(bits & (~0ull >> (63 - (last & 63)))) - 1u;
+    const int end = s + 1u < segments ? start_position(sm, nw, s + 1u) - 1 : n - 1;
+    return (end >> 6) + 1;
+}
+
+// Grouped input after the sort: segment ids, the band of every row tile and
+// its mask work items, the mask row stride.  Workgroup b writes row tiles
+// [GP_TILES b, GP_TILES (b + 1)) and their rows; every workgroup derives the
+// prefixes it needs (segment starts before each word, work items before
+// each tile) from the whole start bitmap itself, which costs O(n / 64).
 __global__ __launch_bounds__(GP_THREADS) void group_plan_kernel(GroupPlanArgs a) {
     __shared__ GroupPlanSmem sm;
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const Work &w = a.w;
     const int n = a.n, W = a.words, S = a.strip;
     const int nw = (n + 63) / 64;
+    const int r0 = (int)blockIdx.x * GP_TILES;
+    const int r1 = r0 + GP_TILES < W ? r0 + GP_TILES : W;
     // the segment starts, from group_starts_kernel
     for (int wi = tid; wi < nw; wi += GP_THREADS) sm.start[wi] = w.start_bits[wi];
     __syncthreads();
-    // segment id of every position: starts up to and including it, minus one
+    // segment starts in the words before each word
     const int chunk = (nw + GP_THREADS - 1) / GP_THREADS;
     const int lo = tid * chunk < nw ? tid * chunk : nw;
     const int hi = lo + chunk < nw ? lo + chunk : nw;
@@ -668,34 +700,42 @@ __global__ __launch_bounds__(GP_THREADS) void group_plan_kernel(GroupPlanArgs a)
         before += (uint32_t)__popcll(sm.start[wi]);
     }
     __syncthreads();
-    for (int p = tid; p < n; p += GP_THREADS) {
-        const uint64_t bits = sm.start[p >> 6];
-        const int k = p & 63;
-        const uint32_t s = sm.wpre[p >> 6] + (uint32_t)__popcll(bits & (~0ull >> (63 - k))) - 1u;
-        w.seg[p] = s;
-        if ((bits >> k) & 1ull) w.seg_start[s] = p;
+    // segment id of this workgroup's rows: a wave per word, a lane per row
+    for (int wi = r0 + wave; wi < r1; wi += GP_WAVES) {
+        const int p = 64 * wi + lane;
+        if (p < n) {
+            const uint64_t bits = sm.start[wi];
+            const uint32_t sg = sm.wpre[wi] + (uint32_t)__popcll(bits & (~0ull >> (63 - lane))) - 1u;
+            w.seg[p] = sg;
+            if ((bits >> lane) & 1ull) w.seg_start[sg] = p;
+        }
     }
-    // band of every row tile and its work items
+    // the band and work items of every row tile (for the prefix), kept for
+    // this workgroup's tiles
     const int tchunk = (W + GP_THREADS - 1) / GP_THREADS;
     const int rlo = tid * tchunk < W ? tid * tchunk : W;
     const int rhi = rlo + tchunk < W ? rlo + tchunk : W;
     uint32_t items = 0, widest = 0;
-    int seg_end = -1;  // end of the segment found last (tiles come in order)
     for (int r = rlo; r < rhi; ++r) {
-        const int last = 64 * r + 63 < n - 1 ? 64 * r + 63 : n - 1;
-        if (last > seg_end) seg_end = segment_end(sm, last, n);
-        const int cend = (seg_end >> 6) + 1;
-        w.tile_cend[r] = cend;
+        const int cend = band_end(sm, r, n, nw, segments);
         const uint32_t it = (uint32_t)((cend + S - 1) / S - r / S);
         items += it;
         widest = it > widest ? it : widest;
     }
     uint32_t total_items = 0;
     uint32_t base = gp_excl_sum(items, sm, &total_items);
-    for (int r = rlo; r < rhi; ++r) {
-        w.item_base[r] = (int32_t)base;
-        base += (uint32_t)((w.tile_cend[r] + S - 1) / S - r / S);
+    if (rhi > r0 && rlo < r1) {
+        for (int r = rlo; r < rhi; ++r) {
+            const int cend = band_end(sm, r, n, nw, segments);
+            const uint32_t it = (uint32_t)((cend + S - 1) / S - r / S);
+            if (r >= r0 && r < r1) {
+                w.tile_cend[r] = cend;
+                w.item_base[r] = (int32_t)base;
+            }
+            base += it;
+        }
     }
+    if (blockIdx.x != 0) return;
     // the widest band sets the row stride of the mask
     uint32_t wmax = widest;
 #pragma unroll
@@ -793,7 +833,9 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w, u
                            stream, ga);
         e = hipGetLastError();
         if (e == hipSuccess) {
-            hipLaunchKernelGGL(group_plan_kernel, dim3(1), dim3(GP_THREADS), 0, stream, ga);
+            hipLaunchKernelGGL(group_plan_kernel,
+                               dim3((unsigned)((L.words + GP_TILES - 1) / GP_TILES)),
+                               dim3(GP_THREADS), 0, stream, ga);
             e = hipGetLastError();
         }
     }

@@ -91,27 +91,43 @@ __device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t v) {
     return (uint64_t)tag << 32 | v;
 }
 
-// Loads the tagged words p[j] (bit j of want) until each carries tag; their
-// values land in out[j].  False when the wait gave up.
+// Loads the tagged words a[m * stride] (and b[m * stride] when b is given),
+// for bit m of want, until each carries tag; their values land in va[m]
+// (vb[m]).  False when the wait gave up.  Addresses come from one base and a
+// stride, which keeps the registers few.
 template <int K>
-__device__ __forceinline__ bool poll_words(const uint64_t *const *p, uint32_t want, uint32_t tag,
-                                           uint32_t (&out)[K]) {
+__device__ __forceinline__ bool poll_words(const uint64_t *a, const uint64_t *b, size_t stride,
+                                           uint32_t want, uint32_t tag, uint32_t (&va)[K],
+                                           uint32_t (&vb)[K]) {
     uint32_t spins = 0;
     while (want) {
-        uint64_t w[K];
+        uint64_t wa[K], wb[K];
 #pragma unroll
-        for (int j = 0; j < K; ++j) w[j] = (want >> j) & 1u ? ld_c(p[j]) : 0ull;
+        for (int m = 0; m < K; ++m) {
+            const bool on = (want >> m) & 1u;
+            wa[m] = on ? ld_c(a + m * stride) : 0ull;
+            wb[m] = on && b != nullptr ? ld_c(b + m * stride) : ((uint64_t)tag << 32);
+        }
 #pragma unroll
-        for (int j = 0; j < K; ++j)
-            if (((want >> j) & 1u) && (uint32_t)(w[j] >> 32) == tag) {
-                out[j] = (uint32_t)w[j];
-                want &= ~(1u << j);
+        for (int m = 0; m < K; ++m)
+            if (((want >> m) & 1u) && (uint32_t)(wa[m] >> 32) == tag &&
+                (uint32_t)(wb[m] >> 32) == tag) {
+                va[m] = (uint32_t)wa[m];
+                vb[m] = (uint32_t)wb[m];
+                want &= ~(1u << m);
             }
         if (!want) break;
         if (++spins > TEAM_SPIN_LIMIT) return false;
         __builtin_amdgcn_s_sleep(1);
     }
     return true;
+}
+
+template <int K>
+__device__ __forceinline__ bool poll_words(const uint64_t *a, size_t stride, uint32_t want,
+                                           uint32_t tag, uint32_t (&va)[K]) {
+    uint32_t vb[K];
+    return poll_words<K>(a, nullptr, stride, want, tag, va, vb);
 }
 
 // The team's words in the workspace (Layout::off_team), for tl members at
@@ -306,22 +322,26 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
     // (one image) their extent, on which the pre-test words are quantised
     bool finite = true, ordered = true;
     float4 ex = make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
+    constexpr int CH = E < 4 ? E : 4;  // boxes or ring words in flight per thread
     if (ka.boxes != nullptr) {
-        float4 bx[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int i = wbase + e * 64;
-            bx[e] = i < n ? ka.boxes[i] : make_float4(0.f, 0.f, 1.f, 1.f);
+        for (int e0 = 0; e0 < E; e0 += CH) {
+        float4 bx[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int i = wbase + (e0 + c) * 64;
+            bx[c] = i < n ? ka.boxes[i] : make_float4(0.f, 0.f, 1.f, 1.f);
         }
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if (wbase + e * 64 >= n) continue;
-            const float4 q = bx[e];
+        for (int c = 0; c < CH; ++c) {
+            if (wbase + (e0 + c) * 64 >= n) continue;
+            const float4 q = bx[c];
             finite = finite && isfinite(q.x) && isfinite(q.y) && isfinite(q.z) && isfinite(q.w);
             const float ar = (q.z - q.x) * (q.w - q.y);
             ordered = ordered && q.x < q.z && q.y < q.w && ar > 0.0f && ar < INFINITY;
             ex = ext_min_max(ex, make_float4(fminf(q.x, q.z), fminf(q.y, q.w), fmaxf(q.x, q.z),
                                              fmaxf(q.y, q.w)));
+        }
         }
     }
     if (lds_offs) __syncthreads();
@@ -402,56 +422,63 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
     // Owners: member t sums the groups of 8 columns g = t, t + T, ... (a
     // group fills a 64-byte line of a tile's counts).  Lanes l and l + 32
     // hold two columns, lane l & 31 = tile; a 32-lane scan gives every
-    // tile's prefix, lane 31 the total.
+    // tile's prefix, lane 31 the total.  Four groups make a round; the loads
+    // of OWNER_ROUNDS rounds are in flight together.
     bool ok = true;
     {
+        constexpr int OWNER_ROUNDS = 4;
         const int tile = lane & 31;
         const int col = tid >> 5;  // 0 .. 31: four groups per round
-        for (int g0 = 0; 8 * (t + T * g0) < cols; g0 += 4) {
-            const int c = 8 * (t + T * (g0 + (col >> 3))) + (col & 7);
-            uint32_t v = 0;
-            if (c < cols && tile < T) {
-                const uint64_t *const p[1] = {&tw.hist[(size_t)tile * RADIX_PASSES * 256 + c]};
-                uint32_t out[1] = {0};
-                if (!poll_words<1>(p, 1u, tag, out)) ok = false;
-                v = out[0];
-            }
-            uint32_t incl = v;
+        for (int g0 = 0; 8 * (t + T * g0) < cols; g0 += 4 * OWNER_ROUNDS) {
+            // round r's column: c0 + 32 T r
+            const int c0 = 8 * (t + T * (g0 + (col >> 3))) + (col & 7);
+            uint32_t want = 0;
 #pragma unroll
-            for (int o = 1; o < 32; o <<= 1) {
-                const uint32_t u = __shfl_up(incl, o, 32);
-                if (tile >= o) incl += u;
-            }
-            const uint32_t total = __shfl(incl, 31, 32);
-            if (c < cols && tile < T) {
-                st_c(&tw.pre[(size_t)tile * RADIX_PASSES * 256 + c], tagged(tag, incl - v));
-                if (tile == 0) st_c(&tw.tot[c], tagged(tag, total));
+            for (int r = 0; r < OWNER_ROUNDS; ++r)
+                if (c0 + 32 * T * r < cols && tile < T) want |= 1u << r;
+            uint32_t v[OWNER_ROUNDS];
+#pragma unroll
+            for (int r = 0; r < OWNER_ROUNDS; ++r) v[r] = 0u;
+            if (want && !poll_words<OWNER_ROUNDS>(
+                            &tw.hist[(size_t)tile * RADIX_PASSES * 256 + c0], 32 * (size_t)T, want,
+                            tag, v))
+                ok = false;
+#pragma unroll
+            for (int r = 0; r < OWNER_ROUNDS; ++r) {
+                uint32_t incl = v[r];
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) {
+                    const uint32_t u = __shfl_up(incl, o, 32);
+                    if (tile >= o) incl += u;
+                }
+                const uint32_t total = __shfl(incl, 31, 32);
+                if ((want >> r) & 1u) {
+                    const int c = c0 + 32 * T * r;
+                    st_c(&tw.pre[(size_t)tile * RADIX_PASSES * 256 + c], tagged(tag, incl - v[r]));
+                    if (tile == 0) st_c(&tw.tot[c], tagged(tag, total));
+                }
             }
         }
     }
     // every member: the totals, and its own tile's prefixes
     {
         constexpr int K = (RADIX_PASSES * 256 + NT - 1) / NT;  // columns per thread at most
-        const uint64_t *p[2 * K];
         uint32_t want = 0;
 #pragma unroll
-        for (int q = 0; q < K; ++q) {
-            const int j = tid + q * NT;
-            const int jj = j < cols ? j : 0;
-            p[2 * q] = &tw.tot[jj];
-            p[2 * q + 1] = &tw.pre[(size_t)t * RADIX_PASSES * 256 + jj];
-            if (j < cols) want |= 3u << (2 * q);
-        }
-        uint32_t v[2 * K];
+        for (int q = 0; q < K; ++q)
+            if (tid + q * NT < cols) want |= 1u << q;
+        uint32_t vt[K], vp[K];
 #pragma unroll
-        for (int q = 0; q < 2 * K; ++q) v[q] = 0;
-        if (!poll_words<2 * K>(p, want, tag, v)) ok = false;
+        for (int q = 0; q < K; ++q) vt[q] = vp[q] = 0u;
+        if (!poll_words<K>(&tw.tot[tid], &tw.pre[(size_t)t * RADIX_PASSES * 256 + tid], NT, want,
+                           tag, vt, vp))
+            ok = false;
 #pragma unroll
         for (int q = 0; q < K; ++q) {
             const int j = tid + q * NT;
             if (j < cols) {
-                sm.gtot[j] = v[2 * q];
-                sm.gpre[j] = v[2 * q + 1];
+                sm.gtot[j] = vt[q];
+                sm.gpre[j] = vp[q];
             }
         }
     }
@@ -459,10 +486,8 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
     if (packs && wave == 0) {
         float4 e4 = make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
         if (lane < T) {
-            const uint64_t *x = tw.ext + (size_t)lane * SLOT;
-            const uint64_t *const p[4] = {x, x + 1, x + 2, x + 3};
             uint32_t v[4] = {0, 0, 0, 0};
-            if (!poll_words<4>(p, 0xFu, tag, v)) ok = false;
+            if (!poll_words<4>(tw.ext + (size_t)lane * SLOT, 1, 0xFu, tag, v)) ok = false;
             e4 = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
                              __uint_as_float(v[3]));
         }
@@ -531,30 +556,32 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
                 v[e] = (uint32_t)(wbase + e * 64);
             }
         } else {
-            const uint64_t *rb = a.ring + (size_t)(j % 3) * ring_words;
-            const uint64_t *pp[2 * E];
+            const uint64_t *rb = a.ring + (size_t)(j % 3) * ring_words + 2 * (size_t)wbase;
             uint32_t want = 0;
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int i = wbase + e * 64;
-                const int ii = i < n ? i : 0;
-                pp[2 * e] = &rb[2 * (size_t)ii];
-                pp[2 * e + 1] = &rb[2 * (size_t)ii + 1];
-                if (i < n) want |= 3u << (2 * e);
-            }
-            uint32_t wv[2 * E];
+            for (int e = 0; e < E; ++e)
+                if (wbase + e * 64 < n) want |= 1u << e;
 #pragma unroll
-            for (int q = 0; q < 2 * E; ++q) wv[q] = 0u;
-            if (!poll_words<2 * E>(pp, want, ring_tag(a.epoch, j), wv))
-                atomicOr(&sm.err, ERR_INTERNAL);
+            for (int e0 = 0; e0 < E; e0 += CH) {
+                uint32_t cv[CH], ck2[CH];
+#pragma unroll
+                for (int c = 0; c < CH; ++c) cv[c] = ck2[c] = 0u;
+                if (!poll_words<CH>(rb + 128 * e0, rb + 128 * e0 + 1, 128,
+                                    (want >> e0) & ((1u << CH) - 1u), ring_tag(a.epoch, j), cv,
+                                    ck2))
+                    atomicOr(&sm.err, ERR_INTERNAL);
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    v[e0 + c] = cv[c];
+                    k[e0 + c] = ck2[c];
+                }
+            }
             // The values are input indices.  Only after a wait gave up could
             // one be out of range; it is then replaced, and the call reports
             // ERR_INTERNAL.
             bool bad = false;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                v[e] = wv[2 * e];
-                k[e] = wv[2 * e + 1];
                 if (v[e] >= (uint32_t)n) {
                     bad = true;
                     v[e] = 0u;
@@ -610,18 +637,16 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
             // thread (q, d) sums the counts of tiles q, q + 4, ... below t
             const int d = tid & 255, q = tid >> 8;
             constexpr int KT = TEAM_MAX / 4;
-            const uint64_t *pp[KT];
             uint32_t want = 0;
 #pragma unroll
-            for (int m = 0; m < KT; ++m) {
-                const int tt = q + 4 * m;
-                pp[m] = &tw.cnt[((size_t)p * tw.tl + (tt < t ? tt : 0)) * 256 + d];
-                if (tt < t) want |= 1u << m;
-            }
+            for (int m = 0; m < KT; ++m)
+                if (q + 4 * m < t) want |= 1u << m;
             uint32_t c[KT];
 #pragma unroll
             for (int m = 0; m < KT; ++m) c[m] = 0;
-            if (!poll_words<KT>(pp, want, tag, c)) atomicOr(&sm.err, ERR_INTERNAL);
+            if (want && !poll_words<KT>(&tw.cnt[((size_t)p * tw.tl + q) * 256 + d], 4 * 256, want,
+                                        tag, c))
+                atomicOr(&sm.err, ERR_INTERNAL);
             uint32_t sum = 0;
 #pragma unroll
             for (int m = 0; m < KT; ++m) sum += c[m];
@@ -650,9 +675,9 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
         if (j >= 3 && !is_last && wave == 0) {
             const int pr = sm.act[j - 2];
             for (int tt = lane; tt < T; tt += 64) {
-                const uint64_t *const pw[1] = {&tw.cnt[((size_t)pr * tw.tl + tt) * 256]};
                 uint32_t c[1] = {0};
-                if (!poll_words<1>(pw, 1u, tag, c)) atomicOr(&sm.err, ERR_INTERNAL);
+                if (!poll_words<1>(&tw.cnt[((size_t)pr * tw.tl + tt) * 256], 0, 1u, tag, c))
+                    atomicOr(&sm.err, ERR_INTERNAL);
             }
         }
         __syncthreads();
@@ -690,12 +715,14 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
             // The sorted order, and (boxes given: the sort-only export passes
             // none) the sorted boxes with their areas.  All of a thread's box
             // loads are issued before any of its stores.
-            int pos[E];
-            uint32_t val[E];
-            float4 bx[E];
 #pragma unroll
-            for (int q = 0; q < E; ++q) {
-                const int s0 = tid + q * NT;
+            for (int q0 = 0; q0 < E; q0 += CH) {
+            int pos[CH];
+            uint32_t val[CH];
+            float4 bx[CH];
+#pragma unroll
+            for (int q = 0; q < CH; ++q) {
+                const int s0 = tid + (q0 + q) * NT;
                 pos[q] = -1;
                 val[q] = 0u;
                 if (s0 < count) {
@@ -713,7 +740,7 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
                                                            : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
-            for (int q = 0; q < E; ++q) {
+            for (int q = 0; q < CH; ++q) {
                 if (pos[q] < 0) continue;
                 if (score_order_here) w.score_order[pos[q]] = (int32_t)val[q];
                 w.order[pos[q]] = (int32_t)val[q];
@@ -723,6 +750,7 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
                 w.sb[pos[q]] = bj;
                 w.area[pos[q]] = (bj.z - bj.x) * (bj.w - bj.y);
                 if (packs) w.spk[pos[q]] = pack_box(bj, ps);
+            }
             }
         }
         // the next pass rewrites the staged tile and the counts
@@ -740,10 +768,10 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
     if (tid == 0) sm.part[0][0] = 0u;
     __syncthreads();
     for (int j = tid; j < T + a.checkers; j += NT) {
-        const uint64_t *const p[1] = {j < T ? &tw.done[(size_t)j * SLOT]
-                                            : &tw.chk[(size_t)(j - T) * SLOT]};
         uint32_t out[1] = {0};
-        if (!poll_words<1>(p, 1u, tag, out)) out[0] = ERR_INTERNAL;
+        if (!poll_words<1>(j < T ? &tw.done[(size_t)j * SLOT] : &tw.chk[(size_t)(j - T) * SLOT],
+                           0, 1u, tag, out))
+            out[0] = ERR_INTERNAL;
         if (out[0]) atomicOr(&sm.part[0][0], out[0]);
     }
     __syncthreads();
@@ -858,7 +886,6 @@ hipError_t launch_team_sort(const Problem &P, const Layout &L, const Work &w, ui
     GNMS_TEAM_LAUNCH(1)
     GNMS_TEAM_LAUNCH(2)
     GNMS_TEAM_LAUNCH(4)
-    GNMS_TEAM_LAUNCH(8)
 #undef GNMS_TEAM_LAUNCH
     return hipGetLastError();
 }

@@ -208,7 +208,7 @@ nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, fl
 #define NMS_FLAG_ONE_LAUNCH 1    /* one image of 1 to 4096 boxes: the whole  */
                                  /* call in a single launch                  */
 #define NMS_FLAG_PASS_SORT 2     /* the radix sort as one launch per pass,   */
-                                 /* as for inputs above 262144 boxes         */
+                                 /* as for inputs above 131072 boxes         */
 
 /*
  * nms_f32_ex -- nms_f32 with launch-plan flags; flags 0 is nms_f32.
@@ -227,7 +227,7 @@ nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, fl
  * of GPU time, the one launch 25 us), so nms_f32 does not take it.
  * NMS_FLAG_PASS_SORT: grouped input, and one image of more than 16384 boxes,
  * is sorted with one launch per radix pass, the form inputs of more than
- * 262144 boxes always take, instead of by a team of workgroups that stay
+ * 131072 boxes always take, instead of by a team of workgroups that stay
  * resident through every pass (one launch).  The result is identical; the
  * flag exists to compare the two (our reading: the pages fix the sort's
  * result, a stable descending order, not its form).

@@ -35,16 +35,17 @@ def _tied_scores(n, seed):
 
 def test_plan_names_the_team_sort():
     g = _g()
-    for n in (16385, 65536, 262144):
+    for n in (16385, 65536, 131072):
         assert g.debug_plan(n)["team_sort"] == 1, n
-    for n in (1, 16384, 262145, 512000):
+    for n in (1, 16384, 131073, 512000):
         assert g.debug_plan(n)["team_sort"] == 0, n
-    for n in (1, 1000, 16384, 64000, 262144):
+    for n in (1, 1000, 16384, 64000, 131072):
         assert g.debug_plan(n, 16, True)["team_sort"] == 1, n
-    assert g.debug_plan(262145, 2, True)["team_sort"] == 0
+    assert g.debug_plan(131073, 2, True)["team_sort"] == 0
 
 
-# tile sizes of 1024, 2048, 4096 and 8192 boxes per member, full and ragged
+# tile sizes of 1024, 2048 and 4096 boxes per member, full and ragged; above
+# 131072 the sort with one launch per pass
 @pytest.mark.parametrize("n", [16385, 20000, 32768, 32769, 65535, 65536, 65537, 100003, 131072,
                                131073, 262144])
 def test_one_image_order(n):
