@@ -183,6 +183,9 @@ struct TeamArgs {
 // Grouped input of up to TEAM_LDS_OFFSETS - 1 images finds a box's image in
 // a copy of the batch offsets in LDS.
 constexpr int TEAM_LDS_OFFSETS = 2048;
+// Grouped input whose images all hold at most IMAGE_CAP boxes has each
+// image's group order sorted in LDS by one checker block (see image_sort).
+constexpr int IMAGE_CAP = 4096;
 
 __device__ __forceinline__ uint32_t image_in(const int32_t *off, int num_images, int64_t i) {
     int lo = 0, hi = num_images - 1;
@@ -207,12 +210,18 @@ template <int E, bool GROUPED>
 struct TeamSmem {
     static constexpr int S = E * NT;
     static constexpr int DIGITS = GROUPED ? RADIX_PASSES : 4;
+    static constexpr int ICAP = GROUPED ? IMAGE_CAP : 1;
     union {
         uint32_t hc[HIST_COPIES][DIGITS][256];
         struct {
             uint32_t k[S];
             uint32_t v[S];
         } stage;
+        struct {  // one image's keys and its order, local indices
+            uint32_t skey[ICAP];
+            uint32_t ckey[ICAP];
+            uint32_t perm[2][ICAP];
+        } img;
     } u;
     uint32_t gtot[DIGITS * 256];  // digit totals per pass
     uint32_t gpre[DIGITS * 256];  // this tile's input-order prefixes per pass
@@ -229,6 +238,7 @@ struct TeamSmem {
     int32_t act[RADIX_PASSES];  // the passes that run, in order
     int32_t nact;
     uint32_t err, unordered;
+    uint32_t img_bad, img_max;
     // grouped input: the batch offsets (up to TEAM_LDS_OFFSETS - 1 images)
     int32_t offs[GROUPED ? TEAM_LDS_OFFSETS : 1];
 };
@@ -268,6 +278,172 @@ __device__ __forceinline__ float4 wave_ext(float4 ex) {
     return ex;
 }
 
+// ------------------------------------------------------------------ images
+
+// Grouped input: copies the batch offsets to LDS (no offsets: one image of
+// n boxes) when there are fewer than TEAM_LDS_OFFSETS images, and returns
+// whether every image may be sorted in LDS by itself: the offsets rise from
+// 0 to n and no image holds more than IMAGE_CAP boxes.  Every block of the
+// launch computes the same answer from the same offsets.
+template <class Smem>
+__device__ bool stage_offsets(const KeysArgs &ka, Smem &sm) {
+    const int tid = threadIdx.x;
+    const int images = ka.offsets ? ka.num_images : 1;
+    if (images >= TEAM_LDS_OFFSETS) return false;
+    if (tid == 0) {
+        sm.img_bad = 0u;
+        sm.img_max = 0u;
+    }
+    for (int j = tid; j <= images; j += NT)
+        sm.offs[j] = ka.offsets ? (int32_t)ka.offsets[j] : (j == 0 ? 0 : ka.n);
+    __syncthreads();
+    uint32_t bad = 0u, big = 0u;
+    for (int m = tid; m < images; m += NT) {
+        const int64_t lo = sm.offs[m], hi = sm.offs[m + 1];
+        if (hi < lo) bad = 1u;
+        else big = (uint32_t)(hi - lo) > big ? (uint32_t)(hi - lo) : big;
+    }
+    if (sm.offs[0] != 0 || sm.offs[images] != ka.n) bad = 1u;
+    if (bad) atomicOr(&sm.img_bad, 1u);
+    if (big) atomicMax(&sm.img_max, big);
+    __syncthreads();
+    return sm.img_bad == 0u && sm.img_max <= (uint32_t)IMAGE_CAP;
+}
+
+// Ranks E positions per thread (position wave * 64 E + 64 e + lane, of the
+// first `count`) by digit d[e]: rk[e] = positions before it in the same
+// wave with the same digit; sm.wcnt[wave][digit] = the wave's count.  The
+// lanes with the same digit come from one ballot per bit (a lane keeps the
+// lanes whose bit equals its own).
+template <int E, class Smem>
+__device__ __forceinline__ void rank_digits(Smem &sm, const uint32_t (&d)[E], int count,
+                                            uint32_t (&rk)[E]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int q = lane; q < 256; q += 64) sm.wcnt[wave][q] = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const bool valid = wave * 64 * E + e * 64 + lane < count;
+        const uint32_t nd = ~d[e];
+        const uint64_t vm = __ballot(valid);
+        uint32_t plo = (uint32_t)vm, phi = (uint32_t)(vm >> 32);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            // 0 where this lane's bit is set, all ones where it is clear
+            const uint32_t tm = (uint32_t)__builtin_amdgcn_sbfe((int)nd, bit, 1);
+            const uint64_t m = __ballot(tm == 0u);
+            plo &= (uint32_t)m ^ tm;
+            phi &= (uint32_t)(m >> 32) ^ tm;
+        }
+        const uint32_t r_in = __builtin_amdgcn_mbcnt_hi(phi, __builtin_amdgcn_mbcnt_lo(plo, 0u));
+        const uint32_t before = sm.wcnt[wave][d[e]];
+        rk[e] = before + r_in;
+        // the lowest lane of each digit group advances the wave's count; the
+        // read above precedes this write in the wave's LDS order
+        if (valid && r_in == 0)
+            sm.wcnt[wave][d[e]] = before + (uint32_t)(__popc(plo) + __popc(phi));
+    }
+}
+
+// One image m of at most IMAGE_CAP boxes, by one block: its boxes in group
+// order (class key, then score key, then input index: stable 8-bit passes
+// in LDS from input order, score digits first) at the image's own
+// positions [off[m], off[m + 1]), with the inverse permutation and the
+// sorted boxes and areas.  Digits every box of the image shares are
+// skipped.
+template <class Smem>
+__device__ void image_sort(const KeysArgs &ka, Smem &sm, int m) {
+    constexpr int EI = IMAGE_CAP / NT;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Work &w = ka.w;
+    const int base = sm.offs[m], cnt = sm.offs[m + 1] - base;
+    if (cnt <= 0) return;
+    auto &img = sm.u.img;
+    for (int j = tid; j < 8 * 256; j += NT) sm.gtot[j] = 0u;
+    __syncthreads();
+    // keys, and the digit counts of the eight digits (a digit every lane of
+    // a wave shares is one add)
+#pragma unroll
+    for (int e = 0; e < EI; ++e) {
+        const int v = e * NT + tid;
+        const bool valid = v < cnt;
+        const uint32_t sk = valid ? score_key(ka.scores[base + v]) : 0u;
+        const uint32_t ck = valid && ka.class_ids ? class_key(ka.class_ids[base + v]) : 0u;
+        if (valid) {
+            img.skey[v] = sk;
+            img.ckey[v] = ck;
+            img.perm[0][v] = (uint32_t)v;
+        }
+        const uint64_t vm = __ballot(valid);
+        if (vm == 0ull) continue;
+        const int first = __builtin_ctzll(vm);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t dg = ((q < 4 ? sk : ck) >> (8 * (q & 3))) & 255u;
+            const uint32_t d0 = (uint32_t)__shfl((int)dg, first, 64);
+            if (__ballot(valid && dg != d0) == 0ull) {
+                if (lane == first) atomicAdd(&sm.gtot[q * 256 + d0], (uint32_t)__popcll(vm));
+            } else if (valid) {
+                atomicAdd(&sm.gtot[q * 256 + dg], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    if (wave < 8) {
+        const uint32_t *g = &sm.gtot[wave * 256];
+        const uint32_t un = (uint32_t)cnt;
+        const bool one = g[4 * lane] == un || g[4 * lane + 1] == un || g[4 * lane + 2] == un ||
+                         g[4 * lane + 3] == un;
+        const uint64_t any = __ballot(one);
+        if (lane == 0) sm.skip[wave] = any ? 1u : 0u;
+    }
+    __syncthreads();
+    int cur = 0;
+    for (int q = 0; q < 8; ++q) {
+        if (sm.skip[q]) continue;
+        const int shift = 8 * (q & 3);
+        uint32_t v[EI], d[EI], rk[EI];
+#pragma unroll
+        for (int e = 0; e < EI; ++e) {
+            const int i = wave * 64 * EI + e * 64 + lane;
+            v[e] = i < cnt ? img.perm[cur][i] : 0u;
+            d[e] = i < cnt ? ((q < 4 ? img.skey[v[e]] : img.ckey[v[e]]) >> shift) & 255u : 0u;
+        }
+        rank_digits<EI>(sm, d, cnt, rk);
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t run = 0;
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) {
+                const uint32_t c = sm.wcnt[wv][tid];
+                sm.wpre[wv][tid] = run;
+                run += c;
+            }
+            sm.tcnt[tid] = run;
+        }
+        __syncthreads();
+        if (wave == 0) scan256(sm.tcnt, sm.tbase);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < EI; ++e)
+            if (wave * 64 * EI + e * 64 + lane < cnt)
+                img.perm[cur ^ 1][sm.tbase[d[e]] + sm.wpre[wave][d[e]] + rk[e]] = v[e];
+        __syncthreads();
+        cur ^= 1;
+    }
+    for (int r = tid; r < cnt; r += NT) {
+        const int pos = base + r;
+        const int i = base + (int)img.perm[cur][r];
+        w.order[pos] = i;
+        w.inv[i] = pos;
+        if (ka.boxes != nullptr) {
+            const float4 bj = ka.boxes[i];
+            w.sb[pos] = bj;
+            w.area[pos] = (bj.z - bj.x) * (bj.w - bj.y);
+        }
+    }
+    __syncthreads();  // the next image reuses the LDS
+}
+
 // ------------------------------------------------------------------ kernel
 
 template <int E, bool GROUPED>
@@ -281,13 +457,20 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
     const uint32_t tag = (uint32_t)a.epoch;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const int T = a.team, P = a.passes, n = ka.n;
+    const int T = a.team, n = ka.n;
     if (b >= T) {
         // a checker: its error bits, once its work is done
         if (tid == 0) sm.err = 0u;
         __syncthreads();
         const uint32_t e = team_check<GROUPED>(a, b - T, a.checkers);
         if (e) atomicOr(&sm.err, e);
+        if constexpr (GROUPED) {
+            // every image small enough: this block's share of the images
+            if (stage_offsets(ka, sm)) {
+                const int images = ka.offsets ? ka.num_images : 1;
+                for (int m = b - T; m < images; m += a.checkers) image_sort(ka, sm, m);
+            }
+        }
         __syncthreads();
         if (tid == 0) st_c(&tw.chk[(size_t)(b - T) * SLOT], tagged(tag, sm.err));
         return;
@@ -308,8 +491,12 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
         if (e) atomicOr(&sm.err, e);
     }
     const bool lds_offs = GROUPED && ka.offsets != nullptr && ka.num_images < TEAM_LDS_OFFSETS;
-    if (lds_offs)
-        for (int j = tid; j <= ka.num_images; j += NT) sm.offs[j] = (int32_t)ka.offsets[j];
+    // Grouped input whose images are all small: the checkers sort every
+    // image's group order in LDS (image_sort, with the boxes and the inverse
+    // permutation); the team sorts by score only, for the score order.
+    bool per_image = false;
+    if constexpr (GROUPED) per_image = stage_offsets(ka, sm);
+    const int P = per_image ? 4 : a.passes;
     for (int j = tid; j < HIST_COPIES * Smem::DIGITS * 256; j += NT) (&sm.u.hc[0][0][0])[j] = 0u;
     const int wbase = t * S + wave * 64 * E + lane;  // element e: wbase + 64 e
     float s[E];
@@ -344,7 +531,6 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
         }
         }
     }
-    if (lds_offs) __syncthreads();
     uint32_t sk[E], ck[E], ik[E];
     uint32_t err = finite ? 0u : ERR_NONFINITE;
     if (!ordered) atomicOr(&sm.unordered, 1u);
@@ -393,10 +579,12 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
 #pragma unroll
             for (int d = 0; d < 4; ++d) count(d, (sk[e] >> (8 * d)) & 255u, vm, first);
             if constexpr (GROUPED) {
+                if (P > 4) {
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    count(4 + d, (ck[e] >> (8 * d)) & 255u, vm, first);
-                    if (8 + d < P) count(8 + d, (ik[e] >> (8 * d)) & 255u, vm, first);
+                    for (int d = 0; d < 4; ++d) {
+                        count(4 + d, (ck[e] >> (8 * d)) & 255u, vm, first);
+                        if (8 + d < P) count(8 + d, (ik[e] >> (8 * d)) & 255u, vm, first);
+                    }
                 }
             }
         }
@@ -589,31 +777,12 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
             }
             if (bad) atomicOr(&sm.err, ERR_INTERNAL);
         }
-        // rank the tile: lanes with the same digit, from one ballot per bit
-        // (a lane keeps the lanes whose bit equals its own)
-        for (int q = lane; q < 256; q += 64) sm.wcnt[wave][q] = 0u;
+        // rank the tile
+        {
+            uint32_t dg[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const bool valid = wbase + e * 64 < n;
-            const uint32_t d = (k[e] >> shift) & 255u;
-            const uint32_t nd = ~d;
-            const uint64_t vm = __ballot(valid);
-            uint32_t plo = (uint32_t)vm, phi = (uint32_t)(vm >> 32);
-#pragma unroll
-            for (int bit = 0; bit < 8; ++bit) {
-                // 0 where this lane's bit is set, all ones where it is clear
-                const uint32_t tm = (uint32_t)__builtin_amdgcn_sbfe((int)nd, bit, 1);
-                const uint64_t m = __ballot(tm == 0u);
-                plo &= (uint32_t)m ^ tm;
-                phi &= (uint32_t)(m >> 32) ^ tm;
-            }
-            const uint64_t peers = (uint64_t)phi << 32 | plo;
-            const uint32_t r_in = __builtin_amdgcn_mbcnt_hi(phi, __builtin_amdgcn_mbcnt_lo(plo, 0u));
-            const uint32_t before = sm.wcnt[wave][d];
-            rk[e] = before + r_in;
-            // the lowest lane of each digit group advances the wave's count;
-            // the read above precedes this write in the wave's LDS order
-            if (valid && r_in == 0) sm.wcnt[wave][d] = before + (uint32_t)__popcll(peers);
+            for (int e = 0; e < E; ++e) dg[e] = (k[e] >> shift) & 255u;
+            rank_digits<E>(sm, dg, count, rk);
         }
         __syncthreads();
         if (tid < 256) {
@@ -743,6 +912,7 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
             for (int q = 0; q < CH; ++q) {
                 if (pos[q] < 0) continue;
                 if (score_order_here) w.score_order[pos[q]] = (int32_t)val[q];
+                if (per_image) continue;  // the checkers write the group order
                 w.order[pos[q]] = (int32_t)val[q];
                 if (GROUPED) w.inv[val[q]] = pos[q];
                 if (ka.boxes == nullptr) continue;

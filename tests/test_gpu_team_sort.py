@@ -107,6 +107,24 @@ def test_grouped_order(n, images, classes):
     np.testing.assert_array_equal(sorder.cpu().numpy(), swant)
 
 
+@pytest.mark.parametrize("sizes", [[4096, 100, 4096, 1], [4096, 4097], [0, 3000, 0, 2500],
+                                   [4096] * 20])
+def test_grouped_images_at_the_lds_limit(sizes):
+    # images of at most 4096 boxes are each sorted in LDS by one block; one
+    # larger image sends the whole input through the team's passes
+    dev = device()
+    n = int(sum(sizes))
+    rng = np.random.default_rng(len(sizes) + n)
+    scores = _tied_scores(n, n + 2)
+    cls = rng.integers(0, 90, n).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    note("team sort grouped, image sizes %s" % sizes[:4])
+    order, sorder = _g().debug_order(to_dev(scores, dev), to_dev(cls, dev), to_dev(offs, dev))
+    want, swant = _grouped_want(scores, cls, offs)
+    np.testing.assert_array_equal(order.cpu().numpy(), want)
+    np.testing.assert_array_equal(sorder.cpu().numpy(), swant)
+
+
 def test_grouped_every_key_equal():
     dev = device()
     n = 30000
