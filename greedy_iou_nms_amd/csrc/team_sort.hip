@@ -738,10 +738,19 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
         // ones load the ring words of their positions once they carry this
         // pass's tag (no barrier: each word says whether it is written)
         if (j == 0) {
+            // (a first pass on the class or the image, every score digit
+            // being shared, looks its keys up again rather than keep them)
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                k[e] = kind == 0 ? sk[e] : kind == 1 ? ck[e] : ik[e];
-                v[e] = (uint32_t)(wbase + e * 64);
+                const int i = wbase + e * 64;
+                v[e] = (uint32_t)i;
+                k[e] = sk[e];
+                if (GROUPED && kind != 0 && i < n) {
+                    if (kind == 1) k[e] = ka.class_ids ? class_key(ka.class_ids[i]) : 0u;
+                    else k[e] = lds_offs    ? image_in(sm.offs, ka.num_images, i)
+                                : ka.offsets ? image_of(ka.offsets, ka.num_images, i)
+                                             : 0u;
+                }
             }
         } else {
             const uint64_t *rb = a.ring + (size_t)(j % 3) * ring_words + 2 * (size_t)wbase;

@@ -152,6 +152,35 @@ def test_end_to_end_team_vs_pass_sort_vs_oracle(cfg, seed):
     np.testing.assert_array_equal(_nms(w, True), want)
 
 
+@pytest.mark.parametrize("images", [1, 2, 5, 32, 33])
+def test_merged_images_end_to_end(images):
+    # Images of at most 4096 boxes, each sorted on its own beside the team's
+    # score passes, some empty; scores in few levels, so equal scores across
+    # images are common: the earlier image's box (the smaller index) must
+    # come first in the output.
+    rng = np.random.default_rng(500 + images)
+    sizes = rng.integers(0, 900, images)
+    sizes[rng.integers(0, images)] = 0          # an empty image
+    n = int(sizes.sum())
+    base = workloads.random_small(600 + images, max(n, 1), canvas=300.0, score_levels=6,
+                                  classes=5)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    w = workloads.Workload("merge_%d" % images, base.boxes[:n], base.scores[:n], 0.5,
+                           base.class_ids[:n], offs)
+    note("merged images=%d n=%d" % (images, n))
+    want = oracle.c_nms(w.boxes, w.scores, w.iou_threshold, w.class_ids, w.batch_offsets)
+    np.testing.assert_array_equal(_nms(w, False), want)
+
+
+def test_one_image_with_classes_end_to_end():
+    # no batch offsets: one image of classes, sorted on its own if small
+    for n in (3000, 4096, 4097):
+        w = workloads.random_small(700 + n, n, canvas=200.0, score_levels=8, classes=12)
+        note("one image with classes n=%d" % n)
+        want = oracle.c_nms(w.boxes, w.scores, w.iou_threshold, w.class_ids, None)
+        np.testing.assert_array_equal(_nms(w, False), want)
+
+
 def test_one_large_group_end_to_end():
     # one image, one class, 40000 boxes: a grouped call whose band is wider
     # than the grouped sweep's window
