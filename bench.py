@@ -15,7 +15,7 @@ memory.  Prints one JSON line:
   mask_kernel_alone, sweep_alone
                  the mask and the sweep as separate launches (a few extra
                  steps), so each is measured on its own line
-  e2e_roofline   max(VALU time of all pairs, HBM time of the algorithmic
+  e2e_roofline   max(VALU time of all pairs, HBM time of the mask's algorithmic
                  bytes) over the measured median call time
   cpu_baseline   the CPU oracle on the same workload, on this host
   n8192          the same measurement on the N = 8192 clustered workload
@@ -156,9 +156,10 @@ def _traffic():
     return rec["fetch_bytes"] + rec["write_bytes"], detail
 
 
-def _mask_algorithmic_bytes(w):
-    """Bytes the mask kernel must move for one single-image call: every word
-    of the row band it writes, the sorted boxes and areas it reads once."""
+def _dense_band_bytes(w):
+    """Bytes of a mask kernel that writes every word of the row band (the
+    dense form, which this library writes only when a tile's list of nonzero
+    words overflows), plus the sorted boxes and areas read once."""
     n = w.n
     words = (n + 63) // 64
     strip = MASK_STRIP
@@ -167,6 +168,28 @@ def _mask_algorithmic_bytes(w):
         rows = min(64, n - 64 * r)
         total += rows * (words - (r // strip) * strip) * 8
     return total + 20 * n
+
+
+def _mask_nonzero_words(w):
+    """Nonzero 64-bit words of the suppression mask of one single-image
+    call, counted on the device from the library's dense export (outside any
+    timed region)."""
+    import torch
+    import greedy_iou_nms_amd as g
+    dev = torch.device("cuda:0")
+    m, _ = g.debug_mask(torch.from_numpy(w.boxes).to(dev), torch.from_numpy(w.scores).to(dev),
+                        w.iou_threshold)
+    nnz = int(torch.count_nonzero(m).item())
+    del m
+    torch.cuda.empty_cache()
+    return nnz
+
+
+def _mask_sparse_bytes(w, nnz):
+    """Bytes the mask must move for one single-image call when it writes
+    only the nonzero words: the sorted boxes and areas read once (20 B per
+    box) and every nonzero word written once with its column (12 B)."""
+    return 20 * w.n + 12 * nnz
 
 
 def _sweep_dense_bytes(w, keep):
@@ -319,7 +342,7 @@ def _table(steps, warmup):
             "iou_per_s_call": pairs / (ms * 1e-3),
             "mask_stage_frac_of_157tf": OPS_PER_PAIR * pairs / (mask_ms * 1e-3) /
                                         (FP32_VECTOR_PEAK_TFLOPS * 1e12),
-            "mask_dense_equivalent_gbs": (_mask_algorithmic_bytes(w) / (mask_ms * 1e-3) / 1e9
+            "mask_dense_equivalent_gbs": (_dense_band_bytes(w) / (mask_ms * 1e-3) / 1e9
                                           if single else None),
             "parity_vs_oracle": bool(np.array_equal(r["keep"], want)),
             "ten_runs_identical": all(np.array_equal(x, runs[0]) for x in runs),
@@ -381,7 +404,11 @@ def main():
     launch_ms = r["stage_ms"]["mask"]
     achieved = OPS_PER_PAIR * pairs / (launch_ms * 1e-3) / 1e12
     traffic, traffic_detail = _traffic()
-    alg_bytes = _mask_algorithmic_bytes(w)
+    dense_bytes = _dense_band_bytes(w)
+    # the nonzero words come from an extra export call: not in the profiled
+    # main-only runs, whose traces hold the timed kernels only
+    nnz = None if args.main_only else _mask_nonzero_words(w)
+    alg_bytes = None if nnz is None else _mask_sparse_bytes(w, nnz)
 
     line = {
         "metric": "NMS boxes/s and pairwise IoU/s at N=8192 and N=65536 (1 MI355X); % of roofline",
@@ -412,12 +439,15 @@ def main():
         "traffic": traffic,
         "traffic_detail": traffic_detail,
         "algorithmic_bytes": alg_bytes,
+        "algorithmic_bytes_counted": "20 B per box read (sorted box, area) + 12 B per nonzero "
+                                     "mask word written (value, column)",
+        "nonzero_mask_words": nnz,
+        "dense_band_bytes": dense_bytes,
         "ops_per_pair": OPS_PER_PAIR,
         "pairs_per_launch": pairs,
         "launch_ms": launch_ms,
         "side_frac_of_fp32_issue_rate_78tops": achieved / FP32_ISSUE_RATE_TOPS,
         "executed_valu": "profiles/valu_mask_kernels_n65536_large_mixed.md",
-        "mask_bytes_written_gbs": alg_bytes / (launch_ms * 1e-3) / 1e9,
     }
 
     if not args.main_only:
@@ -439,7 +469,7 @@ def main():
             "us_per_row_tile": 1000.0 * sw_ms / ((w.n + 63) // 64), "steps": sep_steps,
         }
         valu_ms = 1000.0 * OPS_PER_PAIR * pairs / (FP32_VECTOR_PEAK_TFLOPS * 1e12)
-        hbm_ms = 1000.0 * alg_bytes / (HBM_PEAK_GBS * 1e9)
+        hbm_ms = 1000.0 * (alg_bytes or 0) / (HBM_PEAK_GBS * 1e9)
         roof_ms = max(valu_ms, hbm_ms)
         line["e2e_roofline"] = {
             "roofline_ms": roof_ms, "valu_ms": valu_ms, "hbm_ms": hbm_ms,

@@ -15,7 +15,7 @@ import workloads  # noqa: E402
 def test_mask_bytes_small_case_by_hand():
     # 130 boxes: 3 row tiles, all in strip 0, so every row writes 3 words
     w = workloads.random_small(0, 130)
-    assert bench._mask_algorithmic_bytes(w) == 130 * 3 * 8 + 20 * 130
+    assert bench._dense_band_bytes(w) == 130 * 3 * 8 + 20 * 130
 
 
 def test_mask_bytes_strip_offsets():
@@ -23,8 +23,14 @@ def test_mask_bytes_strip_offsets():
     # 0 (20 words), 8..15 at column 8 (12 words), 16..19 at column 16 (4 words)
     assert bench.MASK_STRIP == 8
     w = workloads.random_small(0, 64 * 20)
-    assert bench._mask_algorithmic_bytes(w) == (64 * (8 * 20 + 8 * 12 + 4 * 4) * 8
+    assert bench._dense_band_bytes(w) == (64 * (8 * 20 + 8 * 12 + 4 * 4) * 8
                                                 + 20 * 64 * 20)
+
+
+def test_sparse_mask_bytes_by_hand():
+    # 130 boxes read once (20 B each) and 7 nonzero words written (12 B each)
+    w = workloads.random_small(0, 130)
+    assert bench._mask_sparse_bytes(w, 7) == 20 * 130 + 12 * 7
 
 
 def test_traffic_record_is_read_when_sources_match():

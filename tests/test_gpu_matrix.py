@@ -82,6 +82,13 @@ def test_large_mixed_prefix():
     _check(w.boxes[idx], w.scores[idx], 0.2, 0.5, "large_mixed subset")
 
 
+def test_full_size_workload():
+    # the 65536-box workload the benchmark times, whole: the sort takes the
+    # one-launch team form there (the oracle needs tens of seconds)
+    w = workloads.config(5, 0)
+    _check(w.boxes, w.scores, 0.1, 0.5, "large_mixed full")
+
+
 def test_ties_and_empty_boxes():
     w = workloads.random_small(91, 3000, canvas=150.0, score_levels=8)
     b = w.boxes.copy()
