@@ -272,69 +272,74 @@ __device__ __forceinline__ void fast_rows(const MaskArgs &a, const MaskPtrs &m_,
 }
 
 // The rows k_lo .. k_hi - 1 of a work item with the quantised pre-test
-// (one image, t > 0, ordered boxes, radix-sorted so the words exist).  Per
-// pair two integer subtractions and an OR (PACK_* in nms_internal.h): a set
-// bit 31 or 15 rules the overlap out.  Two tiles are asked at once: the AND
-// of their words can only lose bits, so a group where no lane is left with
-// both bits clear has no overlap in either tile (the AND may also keep a
-// group that has none, when the tiles are ruled out on different axes; the
-// per-tile question then finds nothing).  Only the pre-test words of the
-// columns are held in registers: a group that passes loads its two tiles'
-// float boxes (from the cache: every item of the column tile reads them)
-// and computes the float32 intersection and threshold test as fast_rows()
-// does, with the column's area recomputed by the sort's expression.
+// (one image, t > 0, ordered boxes, radix-sorted so the words exist).  First
+// the coarse question (COARSE_* in nms_internal.h): one subtraction per pair
+// asks all four coordinate orders at once, a set bit 7 in a byte rules the
+// overlap out.  Two tiles are asked together: the AND of their differences
+// can only lose bits, so a group where no lane is left with all four bits
+// clear has no overlap in either tile (the AND may keep a group that has
+// none, when the tiles are ruled out on different bytes; the questions
+// after it then find nothing).  Only the coarse column words are held in
+// registers.  A group that passes loads its two tiles' fine words (PACK_*:
+// per pair two subtractions and an OR, a set bit 31 or 15 rules the overlap
+// out) and, where a lane passes those, the float boxes, and computes the
+// float32 intersection and threshold test as fast_rows() does, with the
+// column's area recomputed by the sort's expression.  The loads come from
+// the cache: every item of the column tile reads them.
 template <int S, bool GROUPED, int MODE, bool DIAG>
 __device__ __forceinline__ void packed_rows(const MaskArgs &a, const MaskPtrs &m_, int p0, int c0,
-                                            int k_lo, int k_hi, const uint32_t (&clo)[S],
-                                            const uint32_t (&chi)[S], const uint64_t (&tmask)[S],
-                                            int t_diag, uint32_t (&out_lo)[S],
-                                            uint32_t (&out_hi)[S]) {
+                                            int k_lo, int k_hi, const uint32_t (&ccw)[S],
+                                            const uint64_t (&tmask)[S], int t_diag,
+                                            uint32_t (&out_lo)[S], uint32_t (&out_hi)[S]) {
     static_assert(!GROUPED, "grouped input has no pre-test words");
     const int lane = threadIdx.x & 63;
-    for (int k = k_lo; k < k_hi; ++k) {
+    const uint32_t *__restrict__ srow =
+        reinterpret_cast<const uint32_t *>(m_.spk + a.npad) + a.npad;
+    // One row: the coarse question for its 8 tiles, then, where some lane
+    // passes, the float test of the tiles that have such a lane.
+    auto row = [&](int k, uint32_t rw) {
         const int p = p0 + k;
-        const uint2 rp = m_.spk[p];
         const uint64_t dmask = k == 63 ? 0ull : (~0ull << (k + 1));
-        // every tile's words first, and one question for the whole row: the
-        // smallest of the groups' ANDed sign bits is 0 where some group may
-        // overlap (most rows have none, and cost one branch)
-        uint32_t u[S], grp[S / 2];
+        // one question for the whole row first: the smallest of the tiles'
+        // masked differences is 0 where some tile may overlap (most rows
+        // have none, and cost one branch)
+        uint32_t h[S];
 #pragma unroll
-        for (int t = 0; t < S; ++t) u[t] = (chi[t] - rp.x) | (rp.y - clo[t]);
-        uint32_t least = ~0u;
+        for (int t = 0; t < S; ++t) h[t] = (ccw[t] - rw) & COARSE_SIGNS;
+        uint32_t least = h[0];
 #pragma unroll
-        for (int g = 0; g < S / 2; ++g) {
-            grp[g] = (u[2 * g] & u[2 * g + 1]) & PACK_SIGNS;
-            least = least < grp[g] ? least : grp[g];
-        }
-        if (__ballot(least == 0u) == 0ull) continue;
+        for (int t = 1; t < S; ++t) least = least < h[t] ? least : h[t];
+        if (__ballot(least == 0u) == 0ull) return;
+        const float4 rb = m_.sb[p];
+        const float ra = m_.area[p];
 #pragma unroll
-        for (int t0 = 0; t0 < S; t0 += 2) {
-            const uint32_t u0 = u[t0], u1 = u[t0 + 1];
-            if (__ballot(grp[t0 / 2] == 0u) == 0ull) continue;
-            // columns of both tiles (padding past n and tiles outside the
-            // band never pass the pre-test, so their lanes stay out of touch)
-            const float4 cb0 = m_.sb[64 * (c0 + t0) + lane];
-            const float4 cb1 = m_.sb[64 * (c0 + t0 + 1) + lane];
-            const float4 rb = m_.sb[p];
-            const float ra = m_.area[p];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int t = t0 + j;
-                uint64_t touch = __ballot(((j == 0 ? u0 : u1) & PACK_SIGNS) == 0u);
-                if (DIAG) touch &= tmask[t] & ((t == t_diag) ? dmask : ~0ull);
-                if (touch) {
-                    const float4 cb = j == 0 ? cb0 : cb1;
-                    const float in = intersection(rb.x, rb.y, rb.z, rb.w, cb.x, cb.y, cb.z, cb.w);
-                    const float ca = (cb.z - cb.x) * (cb.w - cb.y);
-                    const float uni = (ra + ca) - in;
-                    const bool pred = exceeds<MODE>(in, uni, a.t, a.mid);
-                    const uint64_t m = __ballot(pred) & touch;
-                    out_lo[t] = write_lane(out_lo[t], (uint32_t)m, k);
-                    out_hi[t] = write_lane(out_hi[t], (uint32_t)(m >> 32), k);
-                }
+        for (int t = 0; t < S; ++t) {
+            uint64_t touch = __ballot(h[t] == 0u);
+            if (DIAG) touch &= tmask[t] & ((t == t_diag) ? dmask : ~0ull);
+            if (touch) {
+                // columns of the tile (padding past n and tiles outside the
+                // band never pass the pre-test, so their lanes stay out of
+                // touch)
+                const float4 cb = m_.sb[64 * (c0 + t) + lane];
+                const float in = intersection(rb.x, rb.y, rb.z, rb.w, cb.x, cb.y, cb.z, cb.w);
+                const float ca = (cb.z - cb.x) * (cb.w - cb.y);
+                const float uni = (ra + ca) - in;
+                const bool pred = exceeds<MODE>(in, uni, a.t, a.mid);
+                const uint64_t m = __ballot(pred) & touch;
+                out_lo[t] = write_lane(out_lo[t], (uint32_t)m, k);
+                out_hi[t] = write_lane(out_hi[t], (uint32_t)(m >> 32), k);
             }
         }
+    };
+    // Four rows per trip, their row words in one 16-byte load (k_lo is 0:
+    // the pre-test form is only used for whole row tiles).  Rows past n in
+    // the last group hold COARSE_NO_ROW and never pass.
+    for (int k = k_lo; k < k_hi; k += 4) {
+        const uint4 r4 = *reinterpret_cast<const uint4 *>(srow + p0 + k);
+        row(k, r4.x);
+        row(k + 1, r4.y);
+        row(k + 2, r4.z);
+        row(k + 3, r4.w);
     }
 }
 
@@ -416,12 +421,11 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
     // than branching around them; their boxes are replaced by an empty box
     // at 0, whose intersection with anything is exactly 0 (like the padding
     // boxes past n), so they never look like an overlap.
-    // With the quantised pre-test the columns' pre-test words take the place
-    // of their areas (recomputed where a tile passes), which keeps the
-    // registers of the two forms the same.
+    // With the quantised pre-test the columns' coarse pre-test words take the
+    // place of the boxes.
     static_assert(!PACKED || (!GROUPED && MODE != MODE_LITERAL), "pre-test words: one image");
     float cx1[S], cy1[S], cx2[S], cy2[S];
-    uint32_t cg[S], clo[S], chi[S];
+    uint32_t cg[S], clo[S];
     uint64_t tmask[S];
 #pragma unroll
     for (int t = 0; t < S; ++t) {
@@ -429,9 +433,10 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
         const bool active = c >= r && c < cend;
         const int q = active ? 64 * c + lane : lane;
         if constexpr (PACKED) {
-            const uint2 pk = active ? m_.spk[q] : make_uint2(PACK_NONE_LO, PACK_NONE_HI);
-            clo[t] = pk.x;
-            chi[t] = pk.y;
+            // the coarse column words (the fine ones are loaded where a
+            // group passes)
+            clo[t] = active ? reinterpret_cast<const uint32_t *>(m_.spk + a.npad)[q]
+                            : COARSE_NONE;
         } else {
             const float4 b = active ? m_.sb[q] : make_float4(0.f, 0.f, 0.f, 0.f);
             cx1[t] = b.x;
@@ -481,10 +486,10 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
         if constexpr (PACKED) {
             {
                 if (diag)
-                    packed_rows<S, GROUPED, MODE, true>(a, m_, p0, c0, k_lo, k_hi, clo, chi,
+                    packed_rows<S, GROUPED, MODE, true>(a, m_, p0, c0, k_lo, k_hi, clo,
                                                         tmask, t_diag, out_lo, out_hi);
                 else
-                    packed_rows<S, GROUPED, MODE, false>(a, m_, p0, c0, k_lo, k_hi, clo, chi,
+                    packed_rows<S, GROUPED, MODE, false>(a, m_, p0, c0, k_lo, k_hi, clo,
                                                          tmask, t_diag, out_lo, out_hi);
             }
         }

@@ -176,6 +176,24 @@ constexpr uint32_t PACK_QMAX = 32767u;
 constexpr uint32_t PACK_SIGNS = 0x80008000u;
 constexpr uint32_t PACK_NONE_LO = 0x00007FFFu;
 constexpr uint32_t PACK_NONE_HI = 0x0000FFFFu;
+// The coarse pre-test, asked first: the same grid cut to 7 bits (v = min(q >>
+// 8, 126), which never reverses an order either) and all four comparisons of
+// a pair in one 32-bit subtraction, one byte each.  A box's column word and
+// row word are
+//   col = (0xFF - vx2) | (0x7F + vx1) << 8 | (0xFF - vy2) << 16 | (0x7F + vy1) << 24
+//   row = (0x80 - vx1) | vx2 << 8          | (0x80 - vy1) << 16 | vy2 << 24
+// (v of the raw coordinates, right and bottom edges included).  Every byte of
+// col_c - row_r lies in 1 .. 0xFD, so no byte borrows from the next, and its
+// bit 7 is set iff vx1_r > vx2_c (byte 0), vx1_c > vx2_r (byte 1), or the same
+// for y: an order of the coordinates that rules the overlap out.  Columns that
+// take no part hold COARSE_NONE, whose byte 1 (0xFE) sets bit 7 against any
+// row (vx2 <= 126).
+constexpr uint32_t COARSE_SIGNS = 0x80808080u;
+constexpr uint32_t COARSE_NONE = 0x7F80FE80u;
+// Rows past n hold COARSE_NO_ROW: its byte 0 (1) sets bit 7 against every
+// column (byte 0 of a column word is at least 0x81, of COARSE_NONE 0x80 with
+// byte 1 set anyway), so a padding row never passes.
+constexpr uint32_t COARSE_NO_ROW = 0x00000001u;
 
 // Largest grid (in threads) a launch uses; kernels loop over what lies past it.
 constexpr int64_t MAX_GRID_THREADS = (int64_t)1 << 31;
@@ -264,9 +282,11 @@ struct Work {
     uint64_t *mdrop;
     // one image sorted by radix passes: per radix tile the extent of its
     // boxes (min x1, min y1, max x2, max y2), and per sorted position the
-    // quantised words (lo, hi) of the overlap pre-test (see PACK_*)
+    // quantised words (lo, hi) of the overlap pre-test (see PACK_*); scol
+    // and srow (npad words each, after spk): the coarse words (see COARSE_*)
     float4 *tile_ext;
     uint2 *spk;
+    uint32_t *scol, *srow;
     // one launch for small inputs: W + 1 slots, each the epoch of the last
     // call whose preparing workgroup finished
     uint64_t *arrive;

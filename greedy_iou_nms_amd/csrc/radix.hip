@@ -565,7 +565,12 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
                 ordered = ordered && bj.x < bj.z && bj.y < bj.w && ar > 0.0f && ar < INFINITY;
                 w.sb[pos[j]] = bj;
                 w.area[pos[j]] = ar;
-                if (packs) w.spk[pos[j]] = pack_box(bj, ps);
+                if (packs) {
+                    uint2 crs;
+                    w.spk[pos[j]] = pack_box(bj, ps, crs);
+                    w.scol[pos[j]] = crs.x;
+                    w.srow[pos[j]] = crs.y;
+                }
             }
         }
     }

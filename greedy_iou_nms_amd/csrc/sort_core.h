@@ -74,10 +74,18 @@ __device__ __forceinline__ uint32_t quantise(float v, float lo, float s) {
     return (uint32_t)q;
 }
 
-__device__ __forceinline__ uint2 pack_box(float4 b, const PackScale &ps) {
+__device__ __forceinline__ uint32_t coarse(uint32_t q) { return min(q >> 8, 126u); }
+
+// The fine words (returned) and the coarse words (col, row) of one box (see
+// PACK_* and COARSE_* in nms_internal.h).
+__device__ __forceinline__ uint2 pack_box(float4 b, const PackScale &ps, uint2 &crs) {
     const uint32_t x1 = quantise(b.x, ps.x0, ps.sx), y1 = quantise(b.y, ps.y0, ps.sy);
-    const uint32_t x2 = quantise(b.z, ps.x0, ps.sx) + 1u, y2 = quantise(b.w, ps.y0, ps.sy) + 1u;
-    return make_uint2((x1 << 16) | (PACK_QMAX - y1), (x2 << 16) | (0x8000u + PACK_QMAX - y2));
+    const uint32_t x2 = quantise(b.z, ps.x0, ps.sx), y2 = quantise(b.w, ps.y0, ps.sy);
+    const uint32_t vx1 = coarse(x1), vy1 = coarse(y1), vx2 = coarse(x2), vy2 = coarse(y2);
+    crs.x = (0xFFu - vx2) | (0x7Fu + vx1) << 8 | (0xFFu - vy2) << 16 | (0x7Fu + vy1) << 24;
+    crs.y = (0x80u - vx1) | vx2 << 8 | (0x80u - vy1) << 16 | vy2 << 24;
+    return make_uint2((x1 << 16) | (PACK_QMAX - y1),
+                      ((x2 + 1u) << 16) | (0x8000u + PACK_QMAX - (y2 + 1u)));
 }
 
 // Grid step for an axis of extent lo .. hi: QMAX - 1 steps, or 0 (every

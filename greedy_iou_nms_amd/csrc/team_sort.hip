@@ -928,7 +928,12 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
                 const float4 bj = bx[q];
                 w.sb[pos[q]] = bj;
                 w.area[pos[q]] = (bj.z - bj.x) * (bj.w - bj.y);
-                if (packs) w.spk[pos[q]] = pack_box(bj, ps);
+                if (packs) {
+                    uint2 crs;
+                    w.spk[pos[q]] = pack_box(bj, ps, crs);
+                    w.scol[pos[q]] = crs.x;
+                    w.srow[pos[q]] = crs.y;
+                }
             }
             }
         }

@@ -180,3 +180,55 @@ def test_quantised_pretest_on_extreme_ranges(kind):
     assert bad.size == 0, "first differing (row, word): %s" % (bad[:5].tolist(),)
     np.testing.assert_array_equal(gpu_nms(w.boxes, w.scores, w.iou_threshold),
                                   oracle.c_nms(w.boxes, w.scores, w.iou_threshold))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_coarse_pretest_cell_boundaries(seed):
+    # The coarse pre-test cuts the grid to 7 bits: on an extent of exactly
+    # 0 .. 32766 the fine grid step is 1 and a coarse cell is 256 wide.  Box
+    # edges sit on and within 2 of the cell edges, boxes touch (x2 of one on
+    # x1 of another) and shifted copies overlap across cells, so pairs in the
+    # same, adjacent and next-but-one cells all occur.  Word by word against
+    # the definition, and end to end.
+    g = _g()
+    dev = device()
+    rng = np.random.default_rng(40 + seed)
+    n = 20000
+    base = n // 2
+
+    def edge(cells, jit):
+        return 256.0 * cells + rng.choice(jit, cells.shape)
+
+    x1 = np.clip(edge(rng.integers(0, 120, base), [-2, -1, -0.5, 0, 0.5, 1, 2]), 0, None)
+    y1 = np.clip(edge(rng.integers(0, 120, base), [-2, -1, 0, 1, 2]), 0, None)
+    x2 = x1 + edge(rng.integers(1, 3, base), [-2, -1, 0, 1, 2])
+    y2 = y1 + edge(rng.integers(1, 3, base), [-2, -1, 0, 1, 2])
+    a = np.stack([x1, y1, x2, y2], axis=1)
+    src = rng.integers(0, base, n - base)
+    b = a[src].copy()
+    shift = rng.choice([-260.0, -256.0, -40.0, -1.0, 1.0, 40.0, 256.0, 260.0], (n - base, 2))
+    b[:, [0, 2]] += shift[:, :1]
+    b[:, [1, 3]] += shift[:, 1:]
+    touch = rng.integers(0, n - base, (n - base) // 10)
+    b[touch, 0] = a[src[touch], 2]                      # x1 on the source's x2
+    b[touch, 2] = b[touch, 0] + 256.0
+    boxes = np.concatenate([a, b])
+    boxes = np.clip(boxes, 0.0, 32766.0)
+    boxes[:, 2] = np.maximum(boxes[:, 2], boxes[:, 0] + 1.0)
+    boxes[:, 3] = np.maximum(boxes[:, 3], boxes[:, 1] + 1.0)
+    boxes[0] = [0.0, 0.0, 10.0, 10.0]                   # the extent: 0 .. 32766
+    boxes[1] = [32756.0, 32756.0, 32766.0, 32766.0]
+    boxes = boxes.astype(np.float32)
+    scores = rng.random(n).astype(np.float32)
+    w = workloads.Workload("coarse_cells_%d" % seed, boxes, scores, 0.3)
+    assert g.debug_plan(n)["rank_sort"] == 0            # radix-sorted: the pre-test words exist
+    note("coarse pre-test cell boundaries seed=%d" % seed)
+    m, order = g.debug_mask(to_dev(w.boxes, dev), to_dev(w.scores, dev), w.iou_threshold)
+    m = m.cpu().numpy().view(np.uint64)
+    order = order.cpu().numpy()
+    want = oracle.mask_rows(w.boxes, w.iou_threshold, order)
+    assert int(np.count_nonzero(want)) > n // 10        # overlaps to find
+    bad = np.argwhere(m != want)
+    assert bad.size == 0, "first differing (row, word): %s" % (bad[:5].tolist(),)
+    np.testing.assert_array_equal(gpu_nms(w.boxes, w.scores, w.iou_threshold),
+                                  oracle.c_nms(w.boxes, w.scores, w.iou_threshold))
