@@ -215,8 +215,10 @@ def _check_inputs(boxes, scores, class_ids, batch_offsets):
 PROFILE_NO_FUSION = 1  # nms_f32_profiled flag: mask and sweep as separate launches
 PROFILE_ONE_LAUNCH = 2  # nms_f32_profiled flag: the one-launch path for small inputs
 PROFILE_PASS_SORT = 4  # nms_f32_profiled flag: the radix sort as one launch per pass
+PROFILE_RADIX_SORT = 8  # nms_f32_profiled flag: one image: radix passes, not sample sort
 FLAG_ONE_LAUNCH = 1  # nms_f32_ex flag: the one-launch path for small inputs
 FLAG_PASS_SORT = 2   # nms_f32_ex flag: the radix sort as one launch per pass
+FLAG_RADIX_SORT = 4  # nms_f32_ex flag: one image: the team's radix passes, not sample sort
 
 
 def _check_out(out: Optional[torch.Tensor], n: int, device: torch.device) -> torch.Tensor:
@@ -240,7 +242,7 @@ def _check_out(out: Optional[torch.Tensor], n: int, device: torch.device) -> tor
 
 
 def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, profiled,
-         fuse=True, one_launch=False, pass_sort=False):
+         fuse=True, one_launch=False, pass_sort=False, radix_sort=False):
     boxes, scores, class_ids, batch_offsets, num_images = _check_inputs(
         boxes, scores, class_ids, batch_offsets)
     device = boxes.device
@@ -258,8 +260,10 @@ def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out,
         count = ctypes.c_int64(0)
         stage = (ctypes.c_float * len(STAGES))() if profiled else None
         flags = ((0 if fuse else PROFILE_NO_FUSION) | (PROFILE_ONE_LAUNCH if one_launch else 0) |
-                 (PROFILE_PASS_SORT if pass_sort else 0))
-        ex_flags = (FLAG_ONE_LAUNCH if one_launch else 0) | (FLAG_PASS_SORT if pass_sort else 0)
+                 (PROFILE_PASS_SORT if pass_sort else 0) |
+                 (PROFILE_RADIX_SORT if radix_sort else 0))
+        ex_flags = ((FLAG_ONE_LAUNCH if one_launch else 0) | (FLAG_PASS_SORT if pass_sort else 0) |
+                    (FLAG_RADIX_SORT if radix_sort else 0))
 
         def call(buf):
             args = [_ptr(boxes), _ptr(scores), n, ctypes.c_float(float(iou_threshold)),
@@ -285,17 +289,20 @@ def _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out,
 def nms(boxes: torch.Tensor, scores: torch.Tensor, iou_threshold: float,
         class_ids: Optional[torch.Tensor] = None, batch_offsets: Optional[torch.Tensor] = None,
         workspace: Optional[Workspace] = None, out: Optional[torch.Tensor] = None,
-        one_launch: bool = False, pass_sort: bool = False) -> torch.Tensor:
+        one_launch: bool = False, pass_sort: bool = False,
+        radix_sort: bool = False) -> torch.Tensor:
     """Greedy IoU NMS.  Returns the kept input indices (int64, on the boxes'
     device) in descending score order, ties by ascending index.  With
     ``class_ids`` and/or ``batch_offsets`` boxes suppress only boxes of the
     same (image, class); the result is one list in global score order.
     ``one_launch=True`` runs one image of at most 4096 boxes as a single
     launch (``nms_f32_ex`` with NMS_FLAG_ONE_LAUNCH); ``pass_sort=True``
-    sorts with one launch per radix pass (NMS_FLAG_PASS_SORT).  The result
-    is the same either way."""
+    sorts with one launch per radix pass (NMS_FLAG_PASS_SORT);
+    ``radix_sort=True`` sorts one image with the team's radix passes rather
+    than by sample sort (NMS_FLAG_RADIX_SORT).  The result is the same
+    either way."""
     return _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, False,
-                True, one_launch, pass_sort)
+                True, one_launch, pass_sort, radix_sort)
 
 
 STATIC_MAX_BOXES = 16384  # NMS_STATIC_MAX_BOXES
@@ -326,17 +333,19 @@ def nms_static(boxes: torch.Tensor, scores: torch.Tensor, iou_threshold: float,
 
 def nms_profiled(boxes, scores, iou_threshold, class_ids=None, batch_offsets=None,
                  workspace=None, out=None, fuse=True,
-                 one_launch=False, pass_sort=False) -> Tuple[torch.Tensor, Dict[str, float]]:
+                 one_launch=False, pass_sort=False,
+                 radix_sort=False) -> Tuple[torch.Tensor, Dict[str, float]]:
     """``nms`` plus per-stage GPU times in milliseconds (HIP events on the
     launch stream).  ``fuse=False`` runs the mask and the sweep as separate
     launches even where ``nms`` fuses them, so the mask kernel is timed
     alone; ``one_launch=True`` takes the one-launch path for small inputs
     (timed as the mask stage); ``pass_sort=True`` sorts with one launch per
-    radix pass."""
+    radix pass; ``radix_sort=True`` sorts one image with the team's radix
+    passes rather than by sample sort."""
     if one_launch and not fuse:
         raise ValueError("one_launch and fuse=False exclude each other")
     return _run(boxes, scores, iou_threshold, class_ids, batch_offsets, workspace, out, True,
-                fuse, one_launch, pass_sort)
+                fuse, one_launch, pass_sort, radix_sort)
 
 
 def debug_order(scores: torch.Tensor, class_ids=None, batch_offsets=None):
@@ -380,7 +389,8 @@ def debug_mask(boxes, scores, iou_threshold, class_ids=None, batch_offsets=None)
     return mask[:n, :words], order[:n]
 
 
-PLAN_FIELDS = ("mask_qshift", "fused", "fused_qshift", "rank_sort", "small", "team_sort")
+PLAN_FIELDS = ("mask_qshift", "fused", "fused_qshift", "rank_sort", "small", "team_sort",
+               "sample_sort")
 
 
 def debug_plan(n: int, num_images: int = 0, has_classes: bool = False) -> Dict[str, int]:

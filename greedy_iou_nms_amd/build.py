@@ -42,7 +42,7 @@ FLAGS = [
 # The team sort's workgroups wait on one another, so all of them must be
 # resident at once; scratch memory could limit that.
 GUARDED_KERNELS = ("12sweep_kernel", "17mask_sweep_kernel", "18group_sweep_kernel",
-                   "16small_nms_kernel", "16team_sort_kernel")
+                   "16small_nms_kernel", "16team_sort_kernel", "18team_sample_kernel")
 MAX_VGPRS = 255
 
 

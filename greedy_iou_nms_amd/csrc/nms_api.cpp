@@ -176,6 +176,7 @@ Problem make_problem(const float *boxes, const float *scores, int64_t n, float t
     P.strip = P.grouped ? STRIP_GROUPED : STRIP_SINGLE;
     P.dense = P.grouped;
     P.team_sort = true;
+    P.sample_sort = false;
     return P;
 }
 
@@ -311,7 +312,7 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
                    const int32_t *class_ids, const int64_t *offsets, int64_t num_images,
                    int64_t *keep_out, int64_t *num_kept, void *workspace, size_t ws_bytes,
                    void *stream_ptr, float *stage_ms, bool allow_fusion, bool one_launch,
-                   bool pinned_pool = true, bool team_sort = true) {
+                   bool pinned_pool = true, bool team_sort = true, bool sample_sort = true) {
     if (num_kept == nullptr) return NMS_INVALID_ARG;
     *num_kept = 0;
     if (stage_ms)
@@ -329,6 +330,7 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     // one image runs without dense mask rows first (see Problem::dense)
     Problem P = make_problem(boxes, scores, n, thresh, class_ids, offsets, num_images);
     P.team_sort = team_sort;
+    P.sample_sort = team_sort && sample_sort;
     if (ws_bytes < (P.dense ? L.total : L.off_mask)) return NMS_WORKSPACE_TOO_SMALL;
     const Work w = carve(workspace, L);
 
@@ -404,6 +406,11 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     Readback rb;
     st = collect(w, stream, slot.p, tag, &rb);
     if (st != NMS_OK) return st;
+    // the sample sort's buckets overflowed: again, with the radix passes
+    if ((rb.flags & FLAG_SORT_RETRY) != 0u && rb.error == 0u && P.sample_sort) {
+        P.sample_sort = false;
+        continue;
+    }
     if (P.dense || (rb.flags & FLAG_NEEDS_DENSE) == 0u || rb.error != 0u) return finish(rb, false);
     // a row tile's list overflowed: again, with dense rows, if they fit
     if (ws_bytes < L.total) return NMS_WORKSPACE_TOO_SMALL;
@@ -541,10 +548,12 @@ nms_status nms_f32_ex(const float *boxes, const float *scores, int64_t n, float 
                       int64_t *keep_out, int64_t *num_kept, void *workspace,
                       size_t workspace_bytes, void *stream, int flags) {
     if (num_kept != nullptr) *num_kept = 0;
-    if ((flags & ~(NMS_FLAG_ONE_LAUNCH | NMS_FLAG_PASS_SORT)) != 0) return NMS_INVALID_ARG;
+    if ((flags & ~(NMS_FLAG_ONE_LAUNCH | NMS_FLAG_PASS_SORT | NMS_FLAG_RADIX_SORT)) != 0)
+        return NMS_INVALID_ARG;
     return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
                    num_kept, workspace, workspace_bytes, stream, nullptr, true,
-                   (flags & NMS_FLAG_ONE_LAUNCH) != 0, true, (flags & NMS_FLAG_PASS_SORT) == 0);
+                   (flags & NMS_FLAG_ONE_LAUNCH) != 0, true, (flags & NMS_FLAG_PASS_SORT) == 0,
+                   (flags & NMS_FLAG_RADIX_SORT) == 0);
 }
 
 nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, float iou_thresh,
@@ -575,14 +584,16 @@ nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
                             int64_t *keep_out, int64_t *num_kept, void *workspace,
                             size_t workspace_bytes, void *stream, float *stage_ms,
                             int flags) {
-    const int known = NMS_PROFILE_NO_FUSION | NMS_PROFILE_ONE_LAUNCH | NMS_PROFILE_PASS_SORT;
+    const int known = NMS_PROFILE_NO_FUSION | NMS_PROFILE_ONE_LAUNCH | NMS_PROFILE_PASS_SORT |
+                      NMS_PROFILE_RADIX_SORT;
     const int both = NMS_PROFILE_NO_FUSION | NMS_PROFILE_ONE_LAUNCH;
     if (stage_ms == nullptr || (flags & ~known) != 0 || (flags & both) == both)
         return NMS_INVALID_ARG;
     return run_nms(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images, keep_out,
                    num_kept, workspace, workspace_bytes, stream, stage_ms,
                    (flags & NMS_PROFILE_NO_FUSION) == 0, (flags & NMS_PROFILE_ONE_LAUNCH) != 0,
-                   true, (flags & NMS_PROFILE_PASS_SORT) == 0);
+                   true, (flags & NMS_PROFILE_PASS_SORT) == 0,
+                   (flags & NMS_PROFILE_RADIX_SORT) == 0);
 }
 
 nms_status nms_matrix_workspace_size(int64_t n, size_t *bytes) {
@@ -637,9 +648,20 @@ nms_status nms_debug_order(const float *scores, int64_t n, const int32_t *class_
     make_layout(n, &L);
     if (workspace_bytes < L.total) return NMS_WORKSPACE_TOO_SMALL;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-    const Problem P = make_problem(nullptr, scores, n, 0.5f, class_ids, batch_offsets, num_images);
+    Problem P = make_problem(nullptr, scores, n, 0.5f, class_ids, batch_offsets, num_images);
+    P.sample_sort = true;
     const Work w = carve(workspace, L);
+    for (;;) {
     hipError_t e = launch_radix_sort(P, L, w, next_epoch(), stream);
+    Readback rb;
+    if (e == hipSuccess) {
+        st = read_back(w, stream, &rb);
+        if (st != NMS_OK) return st;
+        if ((rb.flags & FLAG_SORT_RETRY) != 0u && rb.error == 0u && P.sample_sort) {
+            P.sample_sort = false;  // the sample sort's buckets overflowed
+            continue;
+        }
+    }
     if (e == hipSuccess)
         e = hipMemcpyAsync(order_out, w.order, (size_t)n * 4, hipMemcpyDeviceToDevice, stream);
     if (e == hipSuccess && score_order_out) {
@@ -651,10 +673,9 @@ nms_status nms_debug_order(const float *scores, int64_t n, const int32_t *class_
                                hipMemcpyDeviceToDevice, stream);
     }
     if (e != hipSuccess) return NMS_HIP_ERROR;
-    Readback rb;
-    st = read_back(w, stream, &rb);
-    if (st != NMS_OK) return st;
+    if (hipStreamSynchronize(stream) != hipSuccess) return NMS_HIP_ERROR;
     return device_error(rb.error);
+    }
 }
 
 nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
@@ -675,8 +696,19 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     Problem P = make_problem(boxes, scores, n, iou_thresh, class_ids, batch_offsets, num_images);
     P.dense = true;  // the export reads the dense rows
+    P.sample_sort = true;
     const Work w = carve(workspace, L);
+    for (;;) {
     hipError_t e = launch_radix_sort(P, L, w, next_epoch(), stream);
+    if (e == hipSuccess) {
+        Readback rs;
+        st = read_back(w, stream, &rs);
+        if (st != NMS_OK) return st;
+        if ((rs.flags & FLAG_SORT_RETRY) != 0u && rs.error == 0u && P.sample_sort) {
+            P.sample_sort = false;  // the sample sort's buckets overflowed
+            continue;
+        }
+    }
     if (e == hipSuccess) e = launch_mask(P, L, w, stream);
     if (e == hipSuccess) e = launch_expand_mask(P, L, w, mask_out, stream);
     if (e == hipSuccess && order_out)
@@ -686,6 +718,7 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
     st = read_back(w, stream, &rb);
     if (st != NMS_OK) return st;
     return device_error(rb.error);
+    }
 }
 
 nms_status nms_debug_plan(int64_t n, int64_t num_images, int has_classes, int32_t *plan) {
@@ -705,6 +738,7 @@ nms_status nms_debug_plan(int64_t n, int64_t num_images, int has_classes, int32_
     plan[NMS_PLAN_RANK_SORT] = (!P.grouped && n <= RANK_SORT_MAX) ? 1 : 0;
     plan[NMS_PLAN_SMALL] = small_launch_applies(P) ? 1 : 0;
     plan[NMS_PLAN_TEAM_SORT] = L.off_team != 0 && team_sort_applies(P) ? 1 : 0;
+    plan[NMS_PLAN_SAMPLE_SORT] = L.off_team != 0 && team_sample_applies(P) ? 1 : 0;
     return NMS_OK;
 }
 

@@ -24,6 +24,10 @@ constexpr uint32_t FLAG_MATRIX_ZERO_PAIRS_MATTER = 2u;
 // than its list holds, so the sweep stopped without a result; the call has
 // to run again with dense rows.
 constexpr uint32_t FLAG_NEEDS_DENSE = 4u;
+// One image sorted by sample sort: a bucket held more boxes than one
+// workgroup sorts in LDS, so the sorted arrays are incomplete; the call runs
+// again with the radix passes.
+constexpr uint32_t FLAG_SORT_RETRY = 8u;
 
 // Per-call control block at the start of the workspace.  The sort kernel
 // initialises it; later kernels read plan fields and raise error bits.  The
@@ -317,6 +321,10 @@ struct Problem {
     // The sort may run in one launch (team_sort_applies); false: one launch
     // per radix pass, as for inputs too large for the team.
     bool team_sort;
+    // One image of RANK_SORT_MAX + 1 to TEAM_MAX_N boxes is sorted by sample
+    // sort in one launch (team_sample_applies) when set; a call whose buckets
+    // overflow runs again without it (FLAG_SORT_RETRY).
+    bool sample_sort;
 };
 
 // Stage launchers; all enqueue on `stream` and return the launch status.
@@ -328,6 +336,9 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w, u
 // TEAM_MAX_N boxes, or one image of RANK_SORT_MAX + 1 to TEAM_MAX_N boxes,
 // on a device with room for the team on one XCD.  epoch: new for every call.
 bool team_sort_applies(const Problem &P);
+bool team_sample_applies(const Problem &P);
+hipError_t launch_team_sample(const Problem &P, const Layout &L, const Work &w, uint64_t epoch,
+                              hipStream_t stream);
 hipError_t launch_team_sort(const Problem &P, const Layout &L, const Work &w, uint64_t epoch,
                             hipStream_t stream);
 // Matrix NMS after the sort (matrix.hip): scores, bounds and checks; the

@@ -787,6 +787,8 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w, u
                            stream, ka, bx);
         return hipGetLastError();
     }
+    if (P.sample_sort && P.team_sort && w.team != nullptr && team_sample_applies(P))
+        return launch_team_sample(P, L, w, epoch, stream);
     hipError_t e = hipSuccess;
     const bool team = P.team_sort && w.team != nullptr && team_sort_applies(P);
     if (team) {

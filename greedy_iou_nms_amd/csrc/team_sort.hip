@@ -972,6 +972,445 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
     }
 }
 
+// ------------------------------------------------------------ sample sort
+//
+// One image, in one launch, by sample sort: the same stable order as the
+// radix passes (score key ascending, i.e. score descending, equal scores in
+// input order: "LeetCUDA 14-nms", algorithm and data flow, step 1), with
+// three hand-overs between workgroups instead of one per radix pass plus
+// the counting round.
+//
+//   samples   member t keys its tile, checks its boxes and publishes their
+//             extent and the keys of SAMPLE_PER_MEMBER evenly spaced boxes
+//             (sample q is box q * stride, so its index needs no word).
+//   buckets   every member reads all samples (at most 1024, one per
+//             thread), sorts them in LDS (stable by key, so equal keys stay
+//             in index order) and takes 255 of them as splitters, (key,
+//             index) pairs in that order.  A box's bucket
+//             is the number of splitters at or below its (key, index); the
+//             buckets are ranges of the final order.  The member ranks its
+//             tile by bucket (stable), publishes the tile's bucket counts,
+//             reads every tile's counts (its prefix among the tiles before
+//             it, and the totals) and writes each box's (index, key) at its
+//             bucket's start + prefix + rank, the tile staged in bucket order
+//             in LDS so that each bucket's share goes out as one run.  Member
+//             0 publishes the totals.
+//   sort      every workgroup (members after their tile, the rest after their
+//             share of the per-call initialisation) takes buckets b, b +
+//             blocks, ...: it reads the bucket's boxes, sorts them in LDS by
+//             key (stable: they arrive in index order) and writes the sorted
+//             order, boxes, areas and pre-test words at the bucket's place.
+//
+// A bucket larger than the LDS holds (an input whose sampled boxes misjudge
+// the distribution badly) is not sorted: the call raises FLAG_SORT_RETRY and
+// the host runs it again with the radix passes.  Words carry the call's tags
+// as in the radix passes; every wait is bounded.
+
+constexpr int SAMPLE_PER_MEMBER = 32;   // samples per member tile
+constexpr int BUCKETS = 256;
+constexpr int SORT_CAP = 4096;           // boxes one workgroup sorts in LDS
+// member's report word: a bucket was too large
+constexpr uint32_t RETRY_BIT = 0x40000000u;
+
+struct SampleSmem {
+    struct Lds {
+        uint32_t key[SORT_CAP];
+        uint32_t val[SORT_CAP];
+        uint32_t perm[2][SORT_CAP];
+    } s;
+    uint32_t gtot[4 * 256];  // digit counts of an LDS sort
+    uint32_t wcnt[NW][256];
+    uint32_t wpre[NW][256];
+    uint32_t tcnt[256];
+    uint32_t tbase[256];
+    uint32_t gb[BUCKETS];     // bucket starts
+    uint32_t tot[BUCKETS];    // bucket sizes
+    int32_t gsh[BUCKETS];     // output position minus staged slot, per bucket
+    uint32_t part[8][256];    // look-back partial sums
+    uint64_t spl[BUCKETS];    // splitters (key << 32 | index); [0] unused
+    float4 ext[NW];
+    PackScale ps;
+    uint32_t varying;  // bits in which some key differs from the first
+    uint32_t err, unordered;
+};
+
+// OR over the lanes of the wave (DPP steps; lane 63 holds the result).
+__device__ __forceinline__ uint32_t wave_or_to_63(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return v;
+}
+
+// Stable sort of positions 0 .. cnt - 1 (cnt <= EI * NT) of sm.s.key by
+// key: 8-bit LSD passes, skipping a digit every key shares (found as the
+// bits in which no key differs from the first).  Returns the perm buffer
+// holding the sorted positions.
+template <int EI>
+__device__ int lds_sort(SampleSmem &sm, int cnt) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto &s = sm.s;
+    // the digits every key shares (those of the first key) need no pass
+    if (tid == 0) sm.varying = 0u;
+    __syncthreads();
+    const uint32_t k0 = s.key[0];
+    uint32_t dif = 0u;
+#pragma unroll
+    for (int e = 0; e < EI; ++e) {
+        const int v = e * NT + tid;
+        if (v < cnt) {
+            s.perm[0][v] = (uint32_t)v;
+            dif |= s.key[v] ^ k0;
+        }
+    }
+    dif = wave_or_to_63(dif);
+    if (lane == 63 && dif) atomicOr(&sm.varying, dif);
+    __syncthreads();
+    const uint32_t varying = sm.varying;
+    int cur = 0;
+    for (int q = 0; q < 4; ++q) {
+        if (((varying >> (8 * q)) & 255u) == 0u) continue;
+        const int shift = 8 * q;
+        uint32_t v[EI], d[EI], rk[EI];
+#pragma unroll
+        for (int e = 0; e < EI; ++e) {
+            const int i = wave * 64 * EI + e * 64 + lane;
+            v[e] = i < cnt ? s.perm[cur][i] : 0u;
+            d[e] = i < cnt ? (s.key[v[e]] >> shift) & 255u : 0u;
+        }
+        rank_digits<EI>(sm, d, cnt, rk);
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t run = 0;
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) {
+                const uint32_t c = sm.wcnt[wv][tid];
+                sm.wpre[wv][tid] = run;
+                run += c;
+            }
+            sm.tcnt[tid] = run;
+        }
+        __syncthreads();
+        if (wave == 0) scan256(sm.tcnt, sm.tbase);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < EI; ++e)
+            if (wave * 64 * EI + e * 64 + lane < cnt)
+                s.perm[cur ^ 1][sm.tbase[d[e]] + sm.wpre[wave][d[e]] + rk[e]] = v[e];
+        __syncthreads();
+        cur ^= 1;
+    }
+    return cur;
+}
+
+template <int E>
+__global__ __launch_bounds__(NT) void team_sample_kernel(TeamArgs a) {
+    constexpr int S = E * NT;
+    constexpr int STRIDE = S / SAMPLE_PER_MEMBER;
+    static_assert(STRIDE * SAMPLE_PER_MEMBER == S && TEAM_MAX * SAMPLE_PER_MEMBER <= NT,
+                  "every sample is one thread's in the LDS sort");
+    __shared__ SampleSmem sm;
+    const KeysArgs &ka = a.ka;
+    const Work &w = ka.w;
+    const TeamWork tw = team_work(a.team_ws, a.tl);
+    const uint32_t tag = (uint32_t)a.epoch;
+    const uint32_t tag_s = ring_tag(a.epoch, 0), tag_b = ring_tag(a.epoch, 1);
+    const int b = blockIdx.x, nb = (int)gridDim.x;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int T = a.team, n = ka.n;
+    const size_t ring_words = 2 * (size_t)ka.npad;
+    uint64_t *samples = a.ring;               // [ns]: tagged keys
+    uint64_t *bkt = a.ring + ring_words;      // [2 n]: (index, key) at each position
+    const int ns = (n + STRIDE - 1) / STRIDE;  // sample q is box q * STRIDE
+    if (tid == 0) {
+        sm.err = 0u;
+        sm.unordered = 0u;
+    }
+    __syncthreads();
+    bool ok = true;
+    // a checker's share of the per-call initialisation (members, which do
+    // none when there are checkers, go straight to their tile)
+    if (b >= T || a.checkers == 0) {
+        const uint32_t e = team_check<false>(a, b >= T ? b - T : b, a.checkers ? a.checkers : T);
+        if (e) atomicOr(&sm.err, e);
+    }
+    if (b < T) {
+        const int t = b;
+        // ------------------------------------------------------ samples
+        const int wbase = t * S + wave * 64 * E + lane;  // element e: wbase + 64 e
+        float s[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = wbase + e * 64;
+            s[e] = i < n ? ka.scores[i] : 0.0f;
+        }
+        bool finite = true, ordered = true;
+        float4 ex = make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
+        constexpr int CH = E < 4 ? E : 4;
+        if (ka.boxes != nullptr) {
+#pragma unroll
+            for (int e0 = 0; e0 < E; e0 += CH) {
+                float4 bx[CH];
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int i = wbase + (e0 + c) * 64;
+                    bx[c] = i < n ? ka.boxes[i] : make_float4(0.f, 0.f, 1.f, 1.f);
+                }
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    if (wbase + (e0 + c) * 64 >= n) continue;
+                    const float4 q = bx[c];
+                    finite = finite && isfinite(q.x) && isfinite(q.y) && isfinite(q.z) &&
+                             isfinite(q.w);
+                    const float ar = (q.z - q.x) * (q.w - q.y);
+                    ordered = ordered && q.x < q.z && q.y < q.w && ar > 0.0f && ar < INFINITY;
+                    ex = ext_min_max(ex, make_float4(fminf(q.x, q.z), fminf(q.y, q.w),
+                                                     fmaxf(q.x, q.z), fmaxf(q.y, q.w)));
+                }
+            }
+        }
+        uint32_t sk[E];
+        uint32_t err = finite ? 0u : ERR_NONFINITE;
+        if (!ordered) atomicOr(&sm.unordered, 1u);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = wbase + e * 64;
+            if (s[e] != s[e] && i < n) err |= ERR_NONFINITE;
+            sk[e] = score_key(s[e]);
+            if (i < n && i % STRIDE == 0) st_c(&samples[i / STRIDE], tagged(tag_s, sk[e]));
+        }
+        if (err) atomicOr(&sm.err, err);
+        const bool packs = ka.boxes != nullptr;
+        if (packs) {
+            ex = wave_ext(ex);
+            if (lane == 0) sm.ext[wave] = ex;
+        }
+        __syncthreads();
+        if (packs && tid == 0) {
+            float4 te = sm.ext[0];
+            for (int v = 1; v < NW; ++v) te = ext_min_max(te, sm.ext[v]);
+            uint64_t *x = tw.ext + (size_t)t * SLOT;
+            st_c(&x[0], tagged(tag, __float_as_uint(te.x)));
+            st_c(&x[1], tagged(tag, __float_as_uint(te.y)));
+            st_c(&x[2], tagged(tag, __float_as_uint(te.z)));
+            st_c(&x[3], tagged(tag, __float_as_uint(te.w)));
+        }
+        // ------------------------------------------------------ buckets
+        // every sample (in index order), sorted by key
+        {
+            uint32_t v[1] = {0u};
+            if (tid < ns && !poll_words<1>(&samples[tid], 0, 1u, tag_s, v)) ok = false;
+            if (tid < ns) sm.s.key[tid] = v[0];
+        }
+        __syncthreads();
+        const int sc = lds_sort<1>(sm, ns);
+        // splitter j (1 .. 255): the sample of sorted rank j * ns / 256
+        if (tid > 0 && tid < BUCKETS) {
+            const uint32_t q = sm.s.perm[sc][(int)(((int64_t)tid * ns) / BUCKETS)];
+            sm.spl[tid] = ((uint64_t)sm.s.key[q] << 32) | (uint64_t)(q * (uint32_t)STRIDE);
+        }
+        __syncthreads();
+        // each box's bucket: the splitters at or below its (key, index)
+        uint32_t bk[E], rk[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = wbase + e * 64;
+            const uint64_t x = ((uint64_t)sk[e] << 32) | (uint64_t)(uint32_t)i;
+            uint32_t lo = 0;
+#pragma unroll
+            for (int step = BUCKETS / 2; step > 0; step >>= 1)
+                if (sm.spl[lo + step] <= x) lo += step;
+            bk[e] = i < n ? lo : 0u;
+        }
+        const int count = n - t * S < S ? n - t * S : S;
+        rank_digits<E>(sm, bk, count, rk);
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t run = 0;
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) {
+                const uint32_t c = sm.wcnt[wv][tid];
+                sm.wpre[wv][tid] = run;
+                run += c;
+            }
+            sm.gtot[tid] = run;  // this tile's count of each bucket
+            st_c(&tw.cnt[(size_t)t * 256 + tid], tagged(tag, run));
+        }
+        // every tile's counts: thread (q, d) sums tiles q, q + 4, ...,
+        // those before t apart
+        {
+            const int d = tid & 255, q = tid >> 8;
+            constexpr int KT = TEAM_MAX / 4;
+            uint32_t want = 0;
+#pragma unroll
+            for (int m = 0; m < KT; ++m)
+                if (q + 4 * m < T) want |= 1u << m;
+            uint32_t c[KT];
+#pragma unroll
+            for (int m = 0; m < KT; ++m) c[m] = 0;
+            if (want && !poll_words<KT>(&tw.cnt[(size_t)q * 256 + d], 4 * 256, want, tag, c))
+                ok = false;
+            uint32_t before = 0, all = 0;
+#pragma unroll
+            for (int m = 0; m < KT; ++m) {
+                all += c[m];
+                if (q + 4 * m < t) before += c[m];
+            }
+            sm.part[q][d] = before;
+            sm.part[4 + q][d] = all;
+        }
+        __syncthreads();
+        if (tid < 256) {
+            const uint32_t all = sm.part[4][tid] + sm.part[5][tid] + sm.part[6][tid] +
+                                 sm.part[7][tid];
+            sm.tot[tid] = all;
+            sm.tcnt[tid] = sm.part[0][tid] + sm.part[1][tid] + sm.part[2][tid] + sm.part[3][tid];
+            if (t == 0) st_c(&tw.tot[tid], tagged(tag, all));
+        }
+        __syncthreads();
+        if (wave == 0) scan256(sm.tot, sm.gb);
+        if (wave == 1) scan256(sm.gtot, sm.tbase);
+        __syncthreads();
+        // The tile in bucket order through LDS, so that each bucket's boxes
+        // go out as one run: a box lands at its bucket's start + the boxes of
+        // its bucket in the tiles before + its rank in this tile.
+        if (tid < 256)
+            sm.gsh[tid] = (int32_t)(sm.gb[tid] + sm.tcnt[tid]) - (int32_t)sm.tbase[tid];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (wbase + e * 64 >= n) continue;
+            const uint32_t d = bk[e];
+            const uint32_t slot = sm.tbase[d] + sm.wpre[wave][d] + rk[e];
+            sm.s.key[slot] = sk[e];
+            sm.s.val[slot] = (uint32_t)(wbase + e * 64);
+            sm.s.perm[0][slot] = d;
+        }
+        __syncthreads();
+        for (int s0 = tid; s0 < count; s0 += NT) {
+            const int pos = s0 + sm.gsh[sm.s.perm[0][s0]];
+            if ((uint32_t)pos >= (uint32_t)n) {
+                ok = false;  // only after a wait gave up
+                continue;
+            }
+            st_c(&bkt[2 * (size_t)pos], tagged(tag_b, sm.s.val[s0]));
+            st_c(&bkt[2 * (size_t)pos + 1], tagged(tag_b, sm.s.key[s0]));
+        }
+        __syncthreads();  // the LDS sort below reuses the arrays
+    }
+
+    // ---------------------------------------------------------- sort
+    // the bucket sizes, and (boxes given) the extent of all boxes
+    {
+        uint32_t v[1] = {0};
+        if (tid < BUCKETS && !poll_words<1>(&tw.tot[tid], 0, 1u, tag, v)) ok = false;
+        if (tid < BUCKETS) sm.tot[tid] = v[0];
+    }
+    if (ka.boxes != nullptr && wave == 0) {
+        float4 e4 = make_float4(INFINITY, INFINITY, -INFINITY, -INFINITY);
+        if (lane < T) {
+            uint32_t v[4] = {0, 0, 0, 0};
+            if (!poll_words<4>(tw.ext + (size_t)lane * SLOT, 1, 0xFu, tag, v)) ok = false;
+            e4 = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                             __uint_as_float(v[3]));
+        }
+        e4 = wave_ext(e4);
+        if (lane == 0) {
+            sm.ps.x0 = e4.x;
+            sm.ps.y0 = e4.y;
+            sm.ps.sx = pack_step(e4.x, e4.z);
+            sm.ps.sy = pack_step(e4.y, e4.w);
+        }
+    }
+    __syncthreads();
+    if (wave == 0) scan256(sm.tot, sm.gb);
+    __syncthreads();
+    bool retry = false;
+    for (int bu = b; bu < BUCKETS; bu += nb) {
+        const int cnt = (int)sm.tot[bu];
+        const uint32_t start = sm.gb[bu];
+        if (cnt == 0) continue;
+        if (cnt > SORT_CAP || start + (uint32_t)cnt > (uint32_t)n) {
+            retry = true;
+            continue;
+        }
+        {
+            constexpr int K = SORT_CAP / NT;
+            uint32_t want = 0;
+#pragma unroll
+            for (int m = 0; m < K; ++m)
+                if (tid + m * NT < cnt) want |= 1u << m;
+            uint32_t vi[K], vk[K];
+#pragma unroll
+            for (int m = 0; m < K; ++m) vi[m] = vk[m] = 0u;
+            const uint64_t *p = bkt + 2 * ((size_t)start + tid);
+            if (!poll_words<K>(p, p + 1, 2 * (size_t)NT, want, tag_b, vi, vk)) ok = false;
+#pragma unroll
+            for (int m = 0; m < K; ++m) {
+                const int r = tid + m * NT;
+                if (r < cnt) {
+                    // an index out of range only after a wait gave up
+                    sm.s.val[r] = vi[m] < (uint32_t)n ? vi[m] : 0u;
+                    sm.s.key[r] = vk[m];
+                }
+            }
+        }
+        __syncthreads();
+        const int cur = lds_sort<SORT_CAP / NT>(sm, cnt);
+        const PackScale ps = sm.ps;
+        for (int r = tid; r < cnt; r += NT) {
+            const int pos = (int)start + r;
+            const int i = (int)sm.s.val[sm.s.perm[cur][r]];
+            w.order[pos] = i;
+            if (ka.boxes != nullptr) {
+                const float4 bj = ka.boxes[i];
+                w.sb[pos] = bj;
+                w.area[pos] = (bj.z - bj.x) * (bj.w - bj.y);
+                uint2 crs;
+                w.spk[pos] = pack_box(bj, ps, crs);
+                w.scol[pos] = crs.x;
+                w.srow[pos] = crs.y;
+            }
+        }
+        __syncthreads();  // the next bucket reuses the LDS
+    }
+    if (!ok) atomicOr(&sm.err, ERR_INTERNAL);
+    __syncthreads();
+    // ---------------------------------------------------------- report
+    const uint32_t mine = sm.err | (sm.unordered ? UNORDERED_BIT : 0u) | (retry ? RETRY_BIT : 0u);
+    if (b >= T) {
+        if (tid == 0) st_c(&tw.chk[(size_t)(b - T) * SLOT], tagged(tag, mine));
+        return;
+    }
+    // (retry is the same in every thread of a block: a block-wide property)
+    if (tid == 0) st_c(&tw.done[(size_t)b * SLOT], tagged(tag, mine));
+    if (b != 0) return;
+    if (tid == 0) sm.part[0][0] = 0u;
+    __syncthreads();
+    for (int j = tid; j < T + a.checkers; j += NT) {
+        uint32_t out[1] = {0};
+        if (!poll_words<1>(j < T ? &tw.done[(size_t)j * SLOT] : &tw.chk[(size_t)(j - T) * SLOT],
+                           0, 1u, tag, out))
+            out[0] = ERR_INTERNAL;
+        if (out[0]) atomicOr(&sm.part[0][0], out[0]);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t all = sm.part[0][0];
+        Ctrl *c = w.ctrl;
+        c->error = all & ~(UNORDERED_BIT | RETRY_BIT);
+        c->flags = ((all & UNORDERED_BIT) ? 0u : FLAG_ORDERED_BOXES) |
+                   ((all & RETRY_BIT) ? FLAG_SORT_RETRY : 0u);
+        c->count = 0;
+        c->num_items = item_base_full(ka.words, ka.words, ka.strip);
+        c->band_stride = ka.mstride;
+        c->num_segments = 1;
+        c->sweep_done = 0u;
+    }
+}
+
 // Elements per thread of a team of at most tmax members (tiles of e * NT
 // boxes) for n boxes; 0 when n is too large.
 int team_elems(int64_t n, int tmax) {
@@ -1019,22 +1458,27 @@ TeamShape team_shape(int64_t n) {
 
 }  // namespace
 
+bool team_sample_applies(const Problem &P) {
+    if (P.grouped || P.n <= RANK_SORT_MAX || P.n > TEAM_MAX_N) return false;
+    return team_shape(P.n).team > 0;
+}
+
 bool team_sort_applies(const Problem &P) {
     if (P.n < 1 || P.n > TEAM_MAX_N) return false;
     if (!P.grouped && P.n <= RANK_SORT_MAX) return false;
     return team_shape(P.n).team > 0;
 }
 
-hipError_t launch_team_sort(const Problem &P, const Layout &L, const Work &w, uint64_t epoch,
-                            hipStream_t stream) {
-    const TeamShape s = team_shape(P.n);
+namespace {
+
+// The launch's arguments; false when the workspace lacks the team's words.
+bool team_args(const Problem &P, const Layout &L, const Work &w, uint64_t epoch,
+               const TeamShape &s, TeamArgs &a) {
     const int tl = (int)team_layout_members(P.n);
-    if (s.team <= 0 || s.team > tl || L.off_team == 0 || w.team == nullptr)
-        return hipErrorInvalidValue;
+    if (s.team <= 0 || s.team > tl || L.off_team == 0 || w.team == nullptr) return false;
     // the carve must end where the layout's region ends
     const TeamWork tw = team_work(w.team, tl);
-    if ((size_t)(tw.end - w.team) * 8 != team_ws_bytes(tl)) return hipErrorInvalidValue;
-    TeamArgs a;
+    if ((size_t)(tw.end - w.team) * 8 != team_ws_bytes(tl)) return false;
     KeysArgs &ka = a.ka;
     ka.boxes = reinterpret_cast<const float4 *>(P.boxes);
     ka.scores = P.scores;
@@ -1058,7 +1502,16 @@ hipError_t launch_team_sort(const Problem &P, const Layout &L, const Work &w, ui
     a.team_ws = w.team;
     a.tl = tl;
     a.ring = w.team_ring;
-    if (a.ring == nullptr) return hipErrorInvalidValue;
+    return a.ring != nullptr;
+}
+
+}  // namespace
+
+hipError_t launch_team_sort(const Problem &P, const Layout &L, const Work &w, uint64_t epoch,
+                            hipStream_t stream) {
+    const TeamShape s = team_shape(P.n);
+    TeamArgs a;
+    if (!team_args(P, L, w, epoch, s, a)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)s.blocks), block(NT);
 #define GNMS_TEAM_LAUNCH(EV)                                                         \
     if (s.e == EV) {                                                                 \
@@ -1071,6 +1524,18 @@ hipError_t launch_team_sort(const Problem &P, const Layout &L, const Work &w, ui
     GNMS_TEAM_LAUNCH(2)
     GNMS_TEAM_LAUNCH(4)
 #undef GNMS_TEAM_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_team_sample(const Problem &P, const Layout &L, const Work &w, uint64_t epoch,
+                              hipStream_t stream) {
+    const TeamShape s = team_shape(P.n);
+    TeamArgs a;
+    if (P.grouped || !team_args(P, L, w, epoch, s, a)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)s.blocks), block(NT);
+    if (s.e == 1) hipLaunchKernelGGL(team_sample_kernel<1>, grid, block, 0, stream, a);
+    if (s.e == 2) hipLaunchKernelGGL(team_sample_kernel<2>, grid, block, 0, stream, a);
+    if (s.e == 4) hipLaunchKernelGGL(team_sample_kernel<4>, grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

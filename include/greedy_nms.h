@@ -209,11 +209,13 @@ nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, fl
                                  /* call in a single launch                  */
 #define NMS_FLAG_PASS_SORT 2     /* the radix sort as one launch per pass,   */
                                  /* as for inputs above 131072 boxes         */
+#define NMS_FLAG_RADIX_SORT 4    /* one image: the radix sort in one launch  */
+                                 /* instead of the sample sort               */
 
 /*
  * nms_f32_ex -- nms_f32 with launch-plan flags; flags 0 is nms_f32.
- *   flags   0, or NMS_FLAG_ONE_LAUNCH and/or NMS_FLAG_PASS_SORT (other bits:
- *           NMS_INVALID_ARG).
+ *   flags   0, or any of NMS_FLAG_ONE_LAUNCH, NMS_FLAG_PASS_SORT and
+ *           NMS_FLAG_RADIX_SORT (other bits: NMS_INVALID_ARG).
  * NMS_FLAG_ONE_LAUNCH: one image of 1 to 4096 boxes runs sort, mask, sweep
  * and output in one launch, against the fixed per-launch cost that the
  * "LeetCUDA 14-nms" page (measured results) blames for its losses at 1024
@@ -231,6 +233,11 @@ nms_status nms_f32_static(const float *boxes, const float *scores, int64_t n, fl
  * resident through every pass (one launch).  The result is identical; the
  * flag exists to compare the two (our reading: the pages fix the sort's
  * result, a stable descending order, not its form).
+ * NMS_FLAG_RADIX_SORT: one image of 16385 to 131072 boxes, which nms_f32
+ * sorts by sample sort in one launch (256 buckets between sampled
+ * splitters, each sorted in LDS by one workgroup; a call whose buckets
+ * outgrow the LDS runs again with the radix passes), is sorted by the team's
+ * radix passes instead.  Same result; the flag exists to compare the two.
  * Other arguments and returns as for nms_f32.
  */
 nms_status nms_f32_ex(const float *boxes, const float *scores, int64_t n, float iou_thresh,
@@ -244,14 +251,15 @@ nms_status nms_f32_ex(const float *boxes, const float *scores, int64_t n, float 
 #define NMS_PROFILE_ONE_LAUNCH 2 /* as NMS_FLAG_ONE_LAUNCH (timed as the    */
                                  /* mask stage)                              */
 #define NMS_PROFILE_PASS_SORT 4  /* as NMS_FLAG_PASS_SORT                    */
+#define NMS_PROFILE_RADIX_SORT 8 /* as NMS_FLAG_RADIX_SORT                   */
 
 /*
  * nms_f32_profiled -- nms_f32 with HIP events recorded on `stream` around
  * each stage.  stage_ms (host, NMS_NUM_STAGES floats) receives each stage's
  * elapsed GPU time in milliseconds (0 for a stage that did not run).  flags:
- * 0, NMS_PROFILE_NO_FUSION or NMS_PROFILE_ONE_LAUNCH, either with
- * NMS_PROFILE_PASS_SORT or not (other bits, or the first two together:
- * NMS_INVALID_ARG).  The result is identical to nms_f32's either way.
+ * 0, NMS_PROFILE_NO_FUSION or NMS_PROFILE_ONE_LAUNCH, with any of
+ * NMS_PROFILE_PASS_SORT and NMS_PROFILE_RADIX_SORT (other bits, or the
+ * first two together: NMS_INVALID_ARG).  The result is identical to nms_f32's either way.
  */
 nms_status nms_f32_profiled(const float *boxes, const float *scores, int64_t n,
                             float iou_thresh, const int32_t *class_ids,
@@ -318,6 +326,8 @@ nms_status nms_debug_mask(const float *boxes, const float *scores, int64_t n,
 #define NMS_PLAN_TEAM_SORT 5     /* 1: the radix sort runs in one launch (a team */
                                  /* of resident workgroups), 0: one launch per  */
                                  /* pass (or the ranking sort)                  */
+#define NMS_PLAN_SAMPLE_SORT 6   /* 1: one image sorted by sample sort in one   */
+                                 /* launch (before any fallback to the radix)   */
 #define NMS_PLAN_FIELDS 8
 
 /*

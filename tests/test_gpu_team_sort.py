@@ -249,3 +249,66 @@ def test_workspace_contents_do_not_matter(fill):
     note("team sort workspace filled with %#x" % fill)
     np.testing.assert_array_equal(_nms(w, False, ws),
                                   oracle.c_nms(w.boxes, w.scores, w.iou_threshold))
+
+
+# ---------------------------------------------------------------- sample sort
+# One image of 16,385 to 131,072 boxes is sorted by sample sort (samples,
+# splitters, buckets sorted in LDS); the team's radix passes remain for
+# grouped input, for the comparison flag and as the fallback of a call whose
+# buckets outgrow the LDS.
+
+def test_plan_names_the_sample_sort():
+    g = _g()
+    for n in (16385, 65536, 131072):
+        assert g.debug_plan(n)["sample_sort"] == 1, n
+    for n in (1, 16384, 131073):
+        assert g.debug_plan(n)["sample_sort"] == 0, n
+    assert g.debug_plan(64000, 16, True)["sample_sort"] == 0
+
+
+@pytest.mark.parametrize("cfg,seed", [(5, 0), (5, 1), (5, 6)])
+def test_sample_sort_vs_radix_team_vs_oracle(cfg, seed):
+    w = workloads.config(cfg, seed)
+    dev = device()
+    note("sample vs radix team sort cfg=%d seed=%d" % (cfg, seed))
+    want = oracle.c_nms(w.boxes, w.scores, w.iou_threshold)
+    b, s = to_dev(w.boxes, dev), to_dev(w.scores, dev)
+    np.testing.assert_array_equal(_g().nms(b, s, w.iou_threshold).cpu().numpy(), want)
+    np.testing.assert_array_equal(
+        _g().nms(b, s, w.iou_threshold, radix_sort=True).cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("n", [16385, 40000, 65536, 131072])
+def test_sample_sort_sorted_and_reversed_inputs(n):
+    # already in order, in reverse order, and one score for all but a few
+    dev = device()
+    rng = np.random.default_rng(n)
+    base = np.sort(rng.random(n).astype(np.float32))
+    for name, scores in (("ascending", base), ("descending", base[::-1].copy()),
+                         ("few_distinct", np.where(rng.random(n) < 0.001, rng.random(n),
+                                                   0.5).astype(np.float32))):
+        note("sample sort %s n=%d" % (name, n))
+        order, _ = _g().debug_order(to_dev(scores, dev))
+        np.testing.assert_array_equal(order.cpu().numpy(), np.argsort(-scores, kind="stable"),
+                                      err_msg=name)
+
+
+def test_sample_sort_fallback_when_a_bucket_overflows():
+    # One box in 16 scores high (a set that holds every box the sort samples:
+    # every 64th at 65,536 boxes) and every other box shares one low score:
+    # all splitters fall among the high boxes and the last bucket takes the
+    # low ones, more than one workgroup sorts in LDS.  The call runs again
+    # with the radix passes; the result must not change.
+    g = _g()
+    dev = device()
+    n = 65536
+    rng = np.random.default_rng(17)
+    scores = np.full(n, 0.125, np.float32)
+    scores[::16] = (0.5 + 0.5 * rng.random(n // 16)).astype(np.float32)
+    note("sample sort fallback n=%d" % n)
+    order, _ = g.debug_order(to_dev(scores, dev))
+    np.testing.assert_array_equal(order.cpu().numpy(), np.argsort(-scores, kind="stable"))
+    w = workloads.config(5, 3)
+    w = workloads.Workload("fallback", w.boxes, scores, w.iou_threshold)
+    np.testing.assert_array_equal(_nms(w, False), oracle.c_nms(w.boxes, w.scores,
+                                                                 w.iou_threshold))
