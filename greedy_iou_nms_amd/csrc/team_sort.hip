@@ -325,6 +325,10 @@ __device__ __forceinline__ void rank_digits(Smem &sm, const uint32_t (&d)[E], in
         const bool valid = wave * 64 * E + e * 64 + lane < count;
         const uint32_t nd = ~d[e];
         const uint64_t vm = __ballot(valid);
+        if (vm == 0ull) {  // no element here: nothing to rank or count
+            rk[e] = 0u;
+            continue;
+        }
         uint32_t plo = (uint32_t)vm, phi = (uint32_t)(vm >> 32);
 #pragma unroll
         for (int bit = 0; bit < 8; ++bit) {
@@ -1045,6 +1049,32 @@ __device__ __forceinline__ uint32_t wave_or_to_63(uint32_t v) {
     return v;
 }
 
+// Slots of one LDS pass, by one wave: sm.wpre[wv][d] = the elements of
+// digits below d plus those of digit d in the waves before wv, for the
+// first nwa waves (those holding elements; the others counted nothing).
+__device__ __forceinline__ void digit_slots(SampleSmem &sm, int nwa) {
+    const int lane = threadIdx.x & 63;
+    uint4 tot = make_uint4(0u, 0u, 0u, 0u);
+    for (int wv = 0; wv < nwa; ++wv) {
+        const uint4 c = *reinterpret_cast<const uint4 *>(&sm.wcnt[wv][4 * lane]);
+        tot.x += c.x;
+        tot.y += c.y;
+        tot.z += c.z;
+        tot.w += c.w;
+    }
+    const uint32_t sum = tot.x + tot.y + tot.z + tot.w;
+    const uint32_t ex = wave_incl_sum(sum) - sum;
+    uint4 run = make_uint4(ex, ex + tot.x, ex + tot.x + tot.y, ex + tot.x + tot.y + tot.z);
+    for (int wv = 0; wv < nwa; ++wv) {
+        const uint4 c = *reinterpret_cast<const uint4 *>(&sm.wcnt[wv][4 * lane]);
+        *reinterpret_cast<uint4 *>(&sm.wpre[wv][4 * lane]) = run;
+        run.x += c.x;
+        run.y += c.y;
+        run.z += c.z;
+        run.w += c.w;
+    }
+}
+
 // Stable sort of positions 0 .. cnt - 1 (cnt <= EI * NT) of sm.s.key by
 // key: 8-bit LSD passes, skipping a digit every key shares (found as the
 // bits in which no key differs from the first).  Returns the perm buffer
@@ -1070,6 +1100,7 @@ __device__ int lds_sort(SampleSmem &sm, int cnt) {
     if (lane == 63 && dif) atomicOr(&sm.varying, dif);
     __syncthreads();
     const uint32_t varying = sm.varying;
+    const int nwa = min(NW, (cnt + 64 * EI - 1) / (64 * EI));
     int cur = 0;
     for (int q = 0; q < 4; ++q) {
         if (((varying >> (8 * q)) & 255u) == 0u) continue;
@@ -1083,23 +1114,12 @@ __device__ int lds_sort(SampleSmem &sm, int cnt) {
         }
         rank_digits<EI>(sm, d, cnt, rk);
         __syncthreads();
-        if (tid < 256) {
-            uint32_t run = 0;
-#pragma unroll
-            for (int wv = 0; wv < NW; ++wv) {
-                const uint32_t c = sm.wcnt[wv][tid];
-                sm.wpre[wv][tid] = run;
-                run += c;
-            }
-            sm.tcnt[tid] = run;
-        }
-        __syncthreads();
-        if (wave == 0) scan256(sm.tcnt, sm.tbase);
+        if (wave == 0) digit_slots(sm, nwa);
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < EI; ++e)
             if (wave * 64 * EI + e * 64 + lane < cnt)
-                s.perm[cur ^ 1][sm.tbase[d[e]] + sm.wpre[wave][d[e]] + rk[e]] = v[e];
+                s.perm[cur ^ 1][sm.wpre[wave][d[e]] + rk[e]] = v[e];
         __syncthreads();
         cur ^= 1;
     }
@@ -1358,7 +1378,9 @@ __global__ __launch_bounds__(NT) void team_sample_kernel(TeamArgs a) {
             }
         }
         __syncthreads();
-        const int cur = lds_sort<SORT_CAP / NT>(sm, cnt);
+        const int cur = cnt <= NT       ? lds_sort<1>(sm, cnt)
+                        : cnt <= 2 * NT ? lds_sort<2>(sm, cnt)
+                                        : lds_sort<SORT_CAP / NT>(sm, cnt);
         const PackScale ps = sm.ps;
         for (int r = tid; r < cnt; r += NT) {
             const int pos = (int)start + r;
