@@ -385,16 +385,16 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     if (e == hipSuccess) e = launch_radix_sort(P, L, w, next_epoch(), stream);
     if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess) e = mark(2);
-    // One image of moderate size: the sweep runs inside the mask launch.  The
-    // plain sweep launch still follows; it does nothing when the fused sweep
-    // finished.
+    // One image of moderate size: the sweep runs inside the mask launch and
+    // posts the result.
     const bool fused = allow_fusion && fused_launch_applies(P, L);
     if (e == hipSuccess)
-        e = fused ? launch_mask_sweep(P, L, w, keep_out, stream) : launch_mask(P, L, w, stream);
+        e = fused ? launch_mask_sweep(P, L, w, keep_out, stream, slot.post(tag))
+                  : launch_mask(P, L, w, stream);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess && P.grouped) e = launch_group_sweep(P, L, w, stream);
-    // one image: the sweep is the last kernel and posts the result
-    if (e == hipSuccess)
+    // one image: otherwise the sweep is the last kernel and posts the result
+    if (e == hipSuccess && !fused)
         e = launch_sweep(P, L, w, keep_out, stream,
                          P.grouped ? Post{nullptr, 0} : slot.post(tag));
     if (e == hipSuccess) e = mark(4);
@@ -406,6 +406,15 @@ nms_status run_nms(const float *boxes, const float *scores, int64_t n, float thr
     Readback rb;
     st = collect(w, stream, slot.p, tag, &rb);
     if (st != NMS_OK) return st;
+    // the fused sweep stopped without a result: the plain sweep on the
+    // finished mask (it posts under a new tag)
+    if (fused && rb.sweep_done != 1u && rb.error == 0u && (rb.flags & FLAG_SORT_RETRY) == 0u) {
+        const uint64_t tag2 = next_epoch();
+        if (launch_sweep(P, L, w, keep_out, stream, slot.post(tag2)) != hipSuccess)
+            return NMS_HIP_ERROR;
+        st = collect(w, stream, slot.p, tag2, &rb);
+        if (st != NMS_OK) return st;
+    }
     // the sample sort's buckets overflowed: again, with the radix passes
     if ((rb.flags & FLAG_SORT_RETRY) != 0u && rb.error == 0u && P.sample_sort) {
         P.sample_sort = false;

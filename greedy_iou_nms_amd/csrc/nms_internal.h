@@ -358,11 +358,12 @@ hipError_t launch_sweep(const Problem &P, const Layout &L, const Work &w, int64_
 // kernel, where that kernel has many workgroups).
 hipError_t launch_publish(const Work &w, const Post &post, hipStream_t stream);
 // One image with FUSE_MIN_WORDS <= L.words <= FUSE_MAX_WORDS: mask and
-// sweep in one launch.
-// launch_sweep must still follow; it returns at once when the fused sweep
-// finished and otherwise (a tile's list overflowed) runs the sweep.
+// sweep in one launch, whose sweep workgroup posts the result.  A result
+// with sweep_done clear and no error (a tile's list overflowed, or the mask
+// took too long) means the sweep stopped: launch_sweep on the finished mask
+// then does the work and posts again.
 hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
-                             hipStream_t stream);
+                             hipStream_t stream, const Post &post);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

@@ -229,8 +229,8 @@ __device__ __forceinline__ void flag_store(uint32_t *p, uint32_t v) {
 // ABORT_NEEDS_DENSE: a tile's list overflowed and there are no dense rows
 // (FLAG_NEEDS_DENSE raised: the call runs again with them).
 // ABORT_BAIL: the fused sweep stops without a result (a tile's list
-// overflowed, or the mask took too long) and the plain sweep kernel that
-// follows it does the work.
+// overflowed, or the mask took too long); its post says so, and the host
+// runs the plain sweep kernel on the finished mask.
 constexpr uint32_t ABORT_ERROR = 1u;
 constexpr uint32_t ABORT_BAIL = 2u;
 constexpr uint32_t ABORT_NEEDS_DENSE = 3u;
@@ -768,9 +768,9 @@ __device__ __forceinline__ void post_from_workgroup(const Post &p, const Ctrl *c
 __global__ __launch_bounds__(NT) void sweep_kernel(SweepArgs a) {
     extern __shared__ uint64_t removed[];
     __shared__ SweepSmem sm;
-    // the fused mask + sweep kernel, or the grouped sweep (which runs
-    // whenever every band fits its window), may already have produced the
-    // result
+    // the grouped sweep (which runs whenever every band fits its window)
+    // may already have produced the result; after a fused launch this
+    // kernel runs only when that sweep stopped, and finds sweep_done clear
     const bool done = a.ctrl->sweep_done ||
                       (a.grouped && a.ctrl->band_stride <= GROUP_SWEEP_WIN);
     if (!done) sweep_body<false>(a, removed, sm);
@@ -875,7 +875,10 @@ __global__ __launch_bounds__(NT, 6) void mask_sweep_kernel(
     extern __shared__ uint64_t removed[];
     __shared__ SweepSmem sm;
     if (blockIdx.x == 0) {
+        // the sweep's workgroup posts the call's result (sweep_done clear if
+        // it stopped without one); every row it read was finished by then
         sweep_body<true>(sa, removed, sm);
+        post_from_workgroup(sa.post, sa.ctrl, true);
         return;
     }
     const maskcore::MaskPtrs m_{sb,     area,   nullptr, tile_cend, item_base,
@@ -1204,7 +1207,7 @@ bool fused_launch_applies(const Problem &P, const Layout &L) {
 }
 
 hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, int64_t *keep_out,
-                             hipStream_t stream) {
+                             hipStream_t stream, const Post &post) {
     if (!fused_launch_applies(P, L)) return hipErrorInvalidValue;
     const SweepArgs sa = make_sweep_args(P, L, w, keep_out);
     const size_t lds = (size_t)(L.words + NEAR_TILES) * sizeof(uint64_t);
@@ -1219,6 +1222,7 @@ hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, i
     if (blocks < 1) blocks = 1;
     SweepArgs sa2 = sa;
     sa2.done_shift = ma.qshift;  // a finished pair counts 64 << qshift
+    sa2.post = post;
     hipLaunchKernelGGL(mask_sweep_kernel, dim3((unsigned)(blocks + 1)), dim3(NT), lds, stream, ma,
                        w.ctrl, w.sb, w.area, w.tile_cend, w.item_base, w.mask, w.tcount,
                        w.tent_wk, w.tent_val, w.tnear, w.done, w.spk, sa2);
