@@ -57,9 +57,9 @@ __global__ __launch_bounds__(MASK_THREADS, 4) void mask_kernel(
     const int32_t *__restrict__ tile_cend, const int32_t *__restrict__ item_base,
     uint64_t *__restrict__ mask, uint32_t *__restrict__ tcount, uint32_t *__restrict__ tent_wk,
     uint64_t *__restrict__ tent_val, uint64_t *__restrict__ tnear,
-    const uint2 *__restrict__ spk) {
+    const uint32_t *__restrict__ scol) {
     const MaskPtrs m_{sb,     area,    seg,      tile_cend, item_base,
-                      mask,   tcount,  tent_wk,  tent_val,  tnear,     spk};
+                      mask,   tcount,  tent_wk,  tent_val,  tnear,     scol};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves_per_block = MASK_THREADS / 64;
     mask_items<S, GROUPED, false>(a, m_, ctrl, blockIdx.x * waves_per_block + wave,
@@ -187,12 +187,12 @@ hipError_t launch_mask(const Problem &P, const Layout &L, const Work &w, hipStre
         hipLaunchKernelGGL((mask_kernel<STRIP_GROUPED, true>), dim3((unsigned)blocks),
                            dim3(MASK_THREADS), 0, stream, a, w.ctrl, w.sb, w.area, w.seg,
                            w.tile_cend, w.item_base, w.mask, w.tcount, w.tent_wk, w.tent_val,
-                           w.tnear, w.spk);
+                           w.tnear, w.scol);
     else
         hipLaunchKernelGGL((mask_kernel<STRIP_SINGLE, false>), dim3((unsigned)blocks),
                            dim3(MASK_THREADS), 0, stream, a, w.ctrl, w.sb, w.area, w.seg,
                            w.tile_cend, w.item_base, w.mask, w.tcount, w.tent_wk, w.tent_val,
-                           w.tnear, w.spk);
+                           w.tnear, w.scol);
     return hipGetLastError();
 }
 

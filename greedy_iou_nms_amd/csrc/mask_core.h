@@ -129,7 +129,7 @@ struct MaskPtrs {
     uint32_t *__restrict__ tent_wk;
     uint64_t *__restrict__ tent_val;
     uint64_t *__restrict__ tnear;
-    const uint2 *__restrict__ spk;
+    const uint32_t *__restrict__ scol;  // coarse column words, then row words
 };
 
 // v_writelane_b32: lane `lane` of the returned VGPR value becomes `val` (an
@@ -272,20 +272,20 @@ __device__ __forceinline__ void fast_rows(const MaskArgs &a, const MaskPtrs &m_,
 }
 
 // The rows k_lo .. k_hi - 1 of a work item with the quantised pre-test
-// (one image, t > 0, ordered boxes, radix-sorted so the words exist).  First
-// the coarse question (COARSE_* in nms_internal.h): one subtraction per pair
-// asks all four coordinate orders at once, a set bit 7 in a byte rules the
-// overlap out.  Two tiles are asked together: the AND of their differences
-// can only lose bits, so a group where no lane is left with all four bits
-// clear has no overlap in either tile (the AND may keep a group that has
-// none, when the tiles are ruled out on different bytes; the questions
-// after it then find nothing).  Only the coarse column words are held in
-// registers.  A group that passes loads its two tiles' fine words (PACK_*:
-// per pair two subtractions and an OR, a set bit 31 or 15 rules the overlap
-// out) and, where a lane passes those, the float boxes, and computes the
-// float32 intersection and threshold test as fast_rows() does, with the
-// column's area recomputed by the sort's expression.  The loads come from
-// the cache: every item of the column tile reads them.
+// (one image, t > 0, ordered boxes, sorted by a path that writes the coarse
+// words).  The coarse question (COARSE_* in nms_internal.h): one
+// subtraction per pair asks all four coordinate orders at once, and a set
+// bit 7 in any byte rules the overlap out.  Each tile is asked on its own
+// (an AND across tiles would not do: columns on opposite sides of the row
+// clear each other's bits); the smallest of a lane's masked differences is
+// 0 exactly where one of its tiles may overlap, so one ballot settles the
+// row when no lane passes, as most rows do.  Only the coarse column words
+// are held in registers.  For a row that passes, each tile with a passing
+// lane loads its float column boxes (from the cache: every item of the
+// column tile reads them) and computes the float32 intersection and
+// threshold test as fast_rows() does, with the column's area recomputed by
+// the sort's expression; lanes that failed the question stay out of the
+// word.
 template <int S, bool GROUPED, int MODE, bool DIAG>
 __device__ __forceinline__ void packed_rows(const MaskArgs &a, const MaskPtrs &m_, int p0, int c0,
                                             int k_lo, int k_hi, const uint32_t (&ccw)[S],
@@ -293,8 +293,7 @@ __device__ __forceinline__ void packed_rows(const MaskArgs &a, const MaskPtrs &m
                                             uint32_t (&out_lo)[S], uint32_t (&out_hi)[S]) {
     static_assert(!GROUPED, "grouped input has no pre-test words");
     const int lane = threadIdx.x & 63;
-    const uint32_t *__restrict__ srow =
-        reinterpret_cast<const uint32_t *>(m_.spk + a.npad) + a.npad;
+    const uint32_t *__restrict__ srow = m_.scol + a.npad;
     // One row: the coarse question for its 8 tiles, then, where some lane
     // passes, the float test of the tiles that have such a lane.
     auto row = [&](int k, uint32_t rw) {
@@ -433,10 +432,9 @@ __device__ __forceinline__ void mask_item(const MaskArgs &a, const MaskPtrs &m_,
         const bool active = c >= r && c < cend;
         const int q = active ? 64 * c + lane : lane;
         if constexpr (PACKED) {
-            // the coarse column words (the fine ones are loaded where a
-            // group passes)
-            clo[t] = active ? reinterpret_cast<const uint32_t *>(m_.spk + a.npad)[q]
-                            : COARSE_NONE;
+            // the coarse column words (the float boxes are loaded where a
+            // row passes)
+            clo[t] = active ? m_.scol[q] : COARSE_NONE;
         } else {
             const float4 b = active ? m_.sb[q] : make_float4(0.f, 0.f, 0.f, 0.f);
             cx1[t] = b.x;

@@ -70,7 +70,7 @@ bool make_layout(int64_t n, Layout *out) {
     L.off_mhi = take(np * 8);
     L.off_mdrop = take((size_t)L.words * 8 + 8);
     L.off_tile_ext = take((size_t)L.tiles * 16);
-    L.off_spk = take(np * 16);  // fine words, then the coarse words
+    L.off_coarse = take(np * 8);  // coarse column words, then row words
     L.off_arrive = take((size_t)(L.words + 1) * 8);
     L.off_team = n <= TEAM_MAX_N ? take(team_ws_bytes(team_layout_members(n))) : 0;
     L.off_team_ring = n <= TEAM_MAX_N ? take((size_t)3 * 2 * 8 * np) : 0;
@@ -119,8 +119,7 @@ Work carve(void *workspace, const Layout &L) {
     w.mhi = reinterpret_cast<double *>(b + L.off_mhi);
     w.mdrop = reinterpret_cast<uint64_t *>(b + L.off_mdrop);
     w.tile_ext = reinterpret_cast<float4 *>(b + L.off_tile_ext);
-    w.spk = reinterpret_cast<uint2 *>(b + L.off_spk);
-    w.scol = reinterpret_cast<uint32_t *>(w.spk + L.npad);
+    w.scol = reinterpret_cast<uint32_t *>(b + L.off_coarse);
     w.srow = w.scol + L.npad;
     w.arrive = reinterpret_cast<uint64_t *>(b + L.off_arrive);
     w.team = L.off_team ? reinterpret_cast<uint64_t *>(b + L.off_team) : nullptr;

@@ -164,24 +164,13 @@ constexpr int TILE_LIST_CAP = 2048;
 // into tnear so that the 64 rows of a tile read word j with one coalesced
 // load.  Words further right are applied by helper waves from the lists.
 constexpr int NEAR_TILES = 4;
-// Quantised overlap pre-test (one image sorted by radix passes).  Every
-// sorted box also gets two 32-bit words, each holding two 16-bit fields of
-// coordinates quantised to 0 .. QMAX on a grid over the extent of all boxes:
-//   lo = qx1 << 16 | (QMAX - qy1)          hi = qx2' << 16 | (0x8000 + QMAX - qy2')
-// where q rounds down and qx2' = q(x2) + 1, qy2' = q(y2) + 1.  For a row box
-// r and a column box c, the 32-bit differences hi_c - lo_r and hi_r - lo_c
-// compare both axes at once (the low field never borrows from the high one):
-// bit 31 is set iff the x fields are ordered, bit 15 iff the y fields are,
-// in the way that rules an overlap out.  Rounding never reverses an order,
-// so a pair whose boxes overlap (x2_c > x1_r, ...) never has one of these
-// bits set; a pair with a bit set cannot overlap.  Columns that take no part
-// hold PACK_NONE, which always has bit 15 set against any row.
+// Quantised overlap pre-test (one image sorted by the radix passes or the
+// sample sort).  The sort quantises every sorted box's coordinates to
+// 0 .. PACK_QMAX - 1 on a grid over the extent of all boxes (q rounds down,
+// so it never reverses an order of two coordinates) and keeps 7 bits of each.
 constexpr uint32_t PACK_QMAX = 32767u;
-constexpr uint32_t PACK_SIGNS = 0x80008000u;
-constexpr uint32_t PACK_NONE_LO = 0x00007FFFu;
-constexpr uint32_t PACK_NONE_HI = 0x0000FFFFu;
-// The coarse pre-test, asked first: the same grid cut to 7 bits (v = min(q >>
-// 8, 126), which never reverses an order either) and all four comparisons of
+// The coarse pre-test: the grid cut to 7 bits (v = min(q >> 8, 126), which
+// never reverses an order either) and all four comparisons of
 // a pair in one 32-bit subtraction, one byte each.  A box's column word and
 // row word are
 //   col = (0xFF - vx2) | (0x7F + vx1) << 8 | (0xFF - vy2) << 16 | (0x7F + vy1) << 24
@@ -228,7 +217,7 @@ struct Layout {
     size_t off_gcls = 0, off_gimg = 0, off_pass_plan = 0, off_gbase = 0;
     size_t off_done = 0, off_seg_start = 0, off_start_bits = 0, off_block_cnt = 0;
     size_t off_momax = 0, off_mscore = 0, off_mlo = 0, off_mhi = 0, off_mdrop = 0;
-    size_t off_tile_ext = 0, off_spk = 0, off_arrive = 0;
+    size_t off_tile_ext = 0, off_coarse = 0, off_arrive = 0;
     size_t off_team = 0;       // 0: no team sort for this n
     size_t off_team_ring = 0;  // the team's pass buffers: 3 x 2 x npad tagged words
     // the suppression bitmask comes last: Matrix NMS uses everything before it
@@ -285,11 +274,10 @@ struct Work {
     double *mlo, *mhi;
     uint64_t *mdrop;
     // one image sorted by radix passes: per radix tile the extent of its
-    // boxes (min x1, min y1, max x2, max y2), and per sorted position the
-    // quantised words (lo, hi) of the overlap pre-test (see PACK_*); scol
-    // and srow (npad words each, after spk): the coarse words (see COARSE_*)
+    // boxes (min x1, min y1, max x2, max y2); one image sorted by radix
+    // passes or sample sort: per sorted position the column and row words
+    // of the coarse pre-test (see COARSE_*; npad words each, srow after scol)
     float4 *tile_ext;
-    uint2 *spk;
     uint32_t *scol, *srow;
     // one launch for small inputs: W + 1 slots, each the epoch of the last
     // call whose preparing workgroup finished

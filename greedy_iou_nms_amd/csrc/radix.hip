@@ -566,8 +566,7 @@ __global__ __launch_bounds__(NT) void radix_pass_kernel(PassArgs a) {
                 w.sb[pos[j]] = bj;
                 w.area[pos[j]] = ar;
                 if (packs) {
-                    uint2 crs;
-                    w.spk[pos[j]] = pack_box(bj, ps, crs);
+                    const uint2 crs = coarse_words(bj, ps);
                     w.scol[pos[j]] = crs.x;
                     w.srow[pos[j]] = crs.y;
                 }

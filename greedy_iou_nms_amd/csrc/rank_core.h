@@ -90,7 +90,6 @@ __device__ __forceinline__ void per_call_init(const KeysArgs &a, int gid, int gs
             store_x<COHERENT>(&w.area[p], 0.0f);
             if (GROUPED) store_x<COHERENT>(&w.seg[p], 0xFFFFFFFFu);
             else {
-                store_x<COHERENT>(&w.spk[p], make_uint2(PACK_NONE_LO, PACK_NONE_HI));
                 store_x<COHERENT>(&w.scol[p], COARSE_NONE);
                 store_x<COHERENT>(&w.srow[p], COARSE_NO_ROW);
             }

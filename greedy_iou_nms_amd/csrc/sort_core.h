@@ -67,9 +67,8 @@ __device__ __forceinline__ void scan256(const uint32_t *v, uint32_t *out) {
     out[4 * lane + 3] = ex + h0 + h1 + h2;
 }
 
-// The quantised pre-test words of one box (see PACK_* in nms_internal.h):
-// q(v) = min(floor((v - lo) * s), QMAX - 1), which never reverses an order;
-// the right and bottom edges take q + 1.
+// The grid of the quantised pre-test (see PACK_QMAX in nms_internal.h):
+// q(v) = min(floor((v - lo) * s), QMAX - 1), which never reverses an order.
 struct PackScale {
     float x0, y0, sx, sy;
 };
@@ -81,16 +80,15 @@ __device__ __forceinline__ uint32_t quantise(float v, float lo, float s) {
 
 __device__ __forceinline__ uint32_t coarse(uint32_t q) { return min(q >> 8, 126u); }
 
-// The fine words (returned) and the coarse words (col, row) of one box (see
-// PACK_* and COARSE_* in nms_internal.h).
-__device__ __forceinline__ uint2 pack_box(float4 b, const PackScale &ps, uint2 &crs) {
-    const uint32_t x1 = quantise(b.x, ps.x0, ps.sx), y1 = quantise(b.y, ps.y0, ps.sy);
-    const uint32_t x2 = quantise(b.z, ps.x0, ps.sx), y2 = quantise(b.w, ps.y0, ps.sy);
-    const uint32_t vx1 = coarse(x1), vy1 = coarse(y1), vx2 = coarse(x2), vy2 = coarse(y2);
-    crs.x = (0xFFu - vx2) | (0x7Fu + vx1) << 8 | (0xFFu - vy2) << 16 | (0x7Fu + vy1) << 24;
-    crs.y = (0x80u - vx1) | vx2 << 8 | (0x80u - vy1) << 16 | vy2 << 24;
-    return make_uint2((x1 << 16) | (PACK_QMAX - y1),
-                      ((x2 + 1u) << 16) | (0x8000u + PACK_QMAX - (y2 + 1u)));
+// The coarse words (col, row) of one box (see PACK_QMAX and COARSE_* in
+// nms_internal.h).
+__device__ __forceinline__ uint2 coarse_words(float4 b, const PackScale &ps) {
+    const uint32_t vx1 = coarse(quantise(b.x, ps.x0, ps.sx));
+    const uint32_t vy1 = coarse(quantise(b.y, ps.y0, ps.sy));
+    const uint32_t vx2 = coarse(quantise(b.z, ps.x0, ps.sx));
+    const uint32_t vy2 = coarse(quantise(b.w, ps.y0, ps.sy));
+    return make_uint2((0xFFu - vx2) | (0x7Fu + vx1) << 8 | (0xFFu - vy2) << 16 | (0x7Fu + vy1) << 24,
+                      (0x80u - vx1) | vx2 << 8 | (0x80u - vy1) << 16 | vy2 << 24);
 }
 
 // Grid step for an axis of extent lo .. hi: QMAX - 1 steps, or 0 (every

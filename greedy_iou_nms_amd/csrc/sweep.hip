@@ -871,7 +871,7 @@ __global__ __launch_bounds__(NT, 6) void mask_sweep_kernel(
     const int32_t *__restrict__ item_base, uint64_t *__restrict__ mask,
     uint32_t *__restrict__ tcount, uint32_t *__restrict__ tent_wk,
     uint64_t *__restrict__ tent_val, uint64_t *__restrict__ tnear, uint32_t *__restrict__ done,
-    const uint2 *__restrict__ spk, SweepArgs sa) {
+    const uint32_t *__restrict__ scol, SweepArgs sa) {
     extern __shared__ uint64_t removed[];
     __shared__ SweepSmem sm;
     if (blockIdx.x == 0) {
@@ -882,7 +882,7 @@ __global__ __launch_bounds__(NT, 6) void mask_sweep_kernel(
         return;
     }
     const maskcore::MaskPtrs m_{sb,     area,   nullptr, tile_cend, item_base,
-                                mask,   tcount, tent_wk, tent_val,  tnear,     spk};
+                                mask,   tcount, tent_wk, tent_val,  tnear,     scol};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __shared__ uint32_t item_queue;
     if (threadIdx.x == 0) item_queue = 0u;
@@ -1014,7 +1014,7 @@ __global__ __launch_bounds__(NT, 4) void small_nms_kernel(SmallArgs s, maskcore:
     if (!ready) return;
     const Work &w = s.ka.w;
     const maskcore::MaskPtrs m_{w.sb,     w.area,   nullptr,    w.tile_cend, w.item_base, w.mask,
-                                w.tcount, w.tent_wk, w.tent_val, w.tnear,     w.spk};
+                                w.tcount, w.tent_wk, w.tent_val, w.tnear,     w.scol};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     maskcore::mask_items<STRIP_SINGLE, false, true, false, true>(
         ma, m_, w.ctrl, (b - s.prep - 1) * NWAVES + wave, s.mask_waves, w.done);
@@ -1225,7 +1225,7 @@ hipError_t launch_mask_sweep(const Problem &P, const Layout &L, const Work &w, i
     sa2.post = post;
     hipLaunchKernelGGL(mask_sweep_kernel, dim3((unsigned)(blocks + 1)), dim3(NT), lds, stream, ma,
                        w.ctrl, w.sb, w.area, w.tile_cend, w.item_base, w.mask, w.tcount,
-                       w.tent_wk, w.tent_val, w.tnear, w.done, w.spk, sa2);
+                       w.tent_wk, w.tent_val, w.tnear, w.done, w.scol, sa2);
     return hipGetLastError();
 }
 

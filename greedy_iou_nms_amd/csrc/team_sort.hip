@@ -933,8 +933,7 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
                 w.sb[pos[q]] = bj;
                 w.area[pos[q]] = (bj.z - bj.x) * (bj.w - bj.y);
                 if (packs) {
-                    uint2 crs;
-                    w.spk[pos[q]] = pack_box(bj, ps, crs);
+                    const uint2 crs = coarse_words(bj, ps);
                     w.scol[pos[q]] = crs.x;
                     w.srow[pos[q]] = crs.y;
                 }
@@ -1390,8 +1389,7 @@ __global__ __launch_bounds__(NT) void team_sample_kernel(TeamArgs a) {
                 const float4 bj = ka.boxes[i];
                 w.sb[pos] = bj;
                 w.area[pos] = (bj.z - bj.x) * (bj.w - bj.y);
-                uint2 crs;
-                w.spk[pos] = pack_box(bj, ps, crs);
+                const uint2 crs = coarse_words(bj, ps);
                 w.scol[pos] = crs.x;
                 w.srow[pos] = crs.y;
             }
