@@ -605,7 +605,11 @@ __global__ __launch_bounds__(256) void group_starts_kernel(GroupPlanArgs a) {
         if (p == 0) {
             st = true;
         } else {
-            const uint32_t i = (uint32_t)w.order[p], j = (uint32_t)w.order[p - 1];
+            // clamped: a sort that gave up may leave stale entries (the
+            // call's result is then discarded)
+            const uint32_t last = (uint32_t)(a.n - 1);
+            const uint32_t i = min((uint32_t)w.order[p], last);
+            const uint32_t j = min((uint32_t)w.order[p - 1], last);
             st = w.gimg[i] != w.gimg[j] || w.gcls[i] != w.gcls[j];
         }
     }
@@ -763,6 +767,24 @@ __global__ __launch_bounds__(GP_THREADS) void group_plan_kernel(GroupPlanArgs a)
 
 }  // namespace
 
+// Grouped input, once sorted: the segment starts, then the plan.
+static hipError_t launch_group_plan(const Problem &P, const Layout &L, const Work &w,
+                                    hipStream_t stream) {
+    GroupPlanArgs ga;
+    ga.n = P.n;
+    ga.words = (int)L.words;
+    ga.npad = (int)L.npad;
+    ga.strip = P.strip;
+    ga.w = w;
+    hipLaunchKernelGGL(group_starts_kernel, dim3((unsigned)((P.n + 255) / 256)), dim3(256), 0,
+                       stream, ga);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(group_plan_kernel, dim3((unsigned)((L.words + GP_TILES - 1) / GP_TILES)),
+                       dim3(GP_THREADS), 0, stream, ga);
+    return hipGetLastError();
+}
+
 hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w, uint64_t epoch,
                              hipStream_t stream) {
     const int tiles = (int)L.tiles;
@@ -828,23 +850,7 @@ hipError_t launch_radix_sort(const Problem &P, const Layout &L, const Work &w, u
         hipLaunchKernelGGL(radix_pass_kernel, dim3(tiles), dim3(NT), 0, stream, pa);
         e = hipGetLastError();
     }
-    if (e == hipSuccess && P.grouped) {
-        GroupPlanArgs ga;
-        ga.n = P.n;
-        ga.words = (int)L.words;
-        ga.npad = (int)L.npad;
-        ga.strip = P.strip;
-        ga.w = w;
-        hipLaunchKernelGGL(group_starts_kernel, dim3((unsigned)((P.n + 255) / 256)), dim3(256), 0,
-                           stream, ga);
-        e = hipGetLastError();
-        if (e == hipSuccess) {
-            hipLaunchKernelGGL(group_plan_kernel,
-                               dim3((unsigned)((L.words + GP_TILES - 1) / GP_TILES)),
-                               dim3(GP_THREADS), 0, stream, ga);
-            e = hipGetLastError();
-        }
-    }
+    if (e == hipSuccess && P.grouped) e = launch_group_plan(P, L, w, stream);
     return e;
 }
 

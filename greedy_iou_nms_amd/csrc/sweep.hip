@@ -1043,9 +1043,12 @@ constexpr int CT_ROWS = COMPACT_CHUNK / CT;
 
 // Score rank r's input index and whether it was kept (its sorted position's
 // bit in the kept bitmap).
+// Both lookups are clamped into [0, n): a call whose sort gave up (an
+// error, or a sort to be run again) may leave stale entries, and its result
+// is discarded, but no read may leave the arrays.
 __device__ __forceinline__ bool rank_kept(const CompactArgs &a, int r, int32_t &i) {
-    i = a.score_order[r];
-    const int p = a.inv[i];
+    i = min((uint32_t)a.score_order[r], (uint32_t)(a.n - 1));
+    const int p = (int)min((uint32_t)a.inv[i], (uint32_t)(a.n - 1));
     return (a.kept[p >> 6] >> (p & 63)) & 1ull;
 }
 

@@ -348,6 +348,33 @@ __device__ __forceinline__ void rank_digits(Smem &sm, const uint32_t (&d)[E], in
     }
 }
 
+// Slots of one LDS pass, by one wave: sm.wpre[wv][d] = the elements of
+// digits below d plus those of digit d in the waves before wv, for the
+// first nwa waves (those holding elements; the others counted nothing).
+template <class Smem>
+__device__ __forceinline__ void digit_slots(Smem &sm, int nwa) {
+    const int lane = threadIdx.x & 63;
+    uint4 tot = make_uint4(0u, 0u, 0u, 0u);
+    for (int wv = 0; wv < nwa; ++wv) {
+        const uint4 c = *reinterpret_cast<const uint4 *>(&sm.wcnt[wv][4 * lane]);
+        tot.x += c.x;
+        tot.y += c.y;
+        tot.z += c.z;
+        tot.w += c.w;
+    }
+    const uint32_t sum = tot.x + tot.y + tot.z + tot.w;
+    const uint32_t ex = wave_incl_sum(sum) - sum;
+    uint4 run = make_uint4(ex, ex + tot.x, ex + tot.x + tot.y, ex + tot.x + tot.y + tot.z);
+    for (int wv = 0; wv < nwa; ++wv) {
+        const uint4 c = *reinterpret_cast<const uint4 *>(&sm.wcnt[wv][4 * lane]);
+        *reinterpret_cast<uint4 *>(&sm.wpre[wv][4 * lane]) = run;
+        run.x += c.x;
+        run.y += c.y;
+        run.z += c.z;
+        run.w += c.w;
+    }
+}
+
 // One image m of at most IMAGE_CAP boxes, by one block: its boxes in group
 // order (class key, then score key, then input index: stable 8-bit passes
 // in LDS from input order, score digits first) at the image's own
@@ -401,6 +428,7 @@ __device__ void image_sort(const KeysArgs &ka, Smem &sm, int m) {
         if (lane == 0) sm.skip[wave] = any ? 1u : 0u;
     }
     __syncthreads();
+    const int nwa = min(NW, (cnt + 64 * EI - 1) / (64 * EI));  // waves holding positions
     int cur = 0;
     for (int q = 0; q < 8; ++q) {
         if (sm.skip[q]) continue;
@@ -414,23 +442,12 @@ __device__ void image_sort(const KeysArgs &ka, Smem &sm, int m) {
         }
         rank_digits<EI>(sm, d, cnt, rk);
         __syncthreads();
-        if (tid < 256) {
-            uint32_t run = 0;
-#pragma unroll
-            for (int wv = 0; wv < NW; ++wv) {
-                const uint32_t c = sm.wcnt[wv][tid];
-                sm.wpre[wv][tid] = run;
-                run += c;
-            }
-            sm.tcnt[tid] = run;
-        }
-        __syncthreads();
-        if (wave == 0) scan256(sm.tcnt, sm.tbase);
+        if (wave == 0) digit_slots(sm, nwa);
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < EI; ++e)
             if (wave * 64 * EI + e * 64 + lane < cnt)
-                img.perm[cur ^ 1][sm.tbase[d[e]] + sm.wpre[wave][d[e]] + rk[e]] = v[e];
+                img.perm[cur ^ 1][sm.wpre[wave][d[e]] + rk[e]] = v[e];
         __syncthreads();
         cur ^= 1;
     }
@@ -1046,32 +1063,6 @@ __device__ __forceinline__ uint32_t wave_or_to_63(uint32_t v) {
     v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
     v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
     return v;
-}
-
-// Slots of one LDS pass, by one wave: sm.wpre[wv][d] = the elements of
-// digits below d plus those of digit d in the waves before wv, for the
-// first nwa waves (those holding elements; the others counted nothing).
-__device__ __forceinline__ void digit_slots(SampleSmem &sm, int nwa) {
-    const int lane = threadIdx.x & 63;
-    uint4 tot = make_uint4(0u, 0u, 0u, 0u);
-    for (int wv = 0; wv < nwa; ++wv) {
-        const uint4 c = *reinterpret_cast<const uint4 *>(&sm.wcnt[wv][4 * lane]);
-        tot.x += c.x;
-        tot.y += c.y;
-        tot.z += c.z;
-        tot.w += c.w;
-    }
-    const uint32_t sum = tot.x + tot.y + tot.z + tot.w;
-    const uint32_t ex = wave_incl_sum(sum) - sum;
-    uint4 run = make_uint4(ex, ex + tot.x, ex + tot.x + tot.y, ex + tot.x + tot.y + tot.z);
-    for (int wv = 0; wv < nwa; ++wv) {
-        const uint4 c = *reinterpret_cast<const uint4 *>(&sm.wcnt[wv][4 * lane]);
-        *reinterpret_cast<uint4 *>(&sm.wpre[wv][4 * lane]) = run;
-        run.x += c.x;
-        run.y += c.y;
-        run.z += c.z;
-        run.w += c.w;
-    }
 }
 
 // Stable sort of positions 0 .. cnt - 1 (cnt <= EI * NT) of sm.s.key by

@@ -263,7 +263,9 @@ def test_plan_names_the_sample_sort():
         assert g.debug_plan(n)["sample_sort"] == 1, n
     for n in (1, 16384, 131073):
         assert g.debug_plan(n)["sample_sort"] == 0, n
-    assert g.debug_plan(64000, 16, True)["sample_sort"] == 0
+    # grouped input: the team's passes (its checkers sort the images)
+    for n in (1, 16385, 64000, 131072):
+        assert g.debug_plan(n, 16, True)["sample_sort"] == 0, n
 
 
 @pytest.mark.parametrize("cfg,seed", [(5, 0), (5, 1), (5, 6)])
@@ -312,3 +314,25 @@ def test_sample_sort_fallback_when_a_bucket_overflows():
     w = workloads.Workload("fallback", w.boxes, scores, w.iou_threshold)
     np.testing.assert_array_equal(_nms(w, False), oracle.c_nms(w.boxes, w.scores,
                                                                  w.iou_threshold))
+
+
+@pytest.mark.parametrize("sizes", [[4096] * 5, [4097, 4096, 9000], [0, 20000], [1] * 17000])
+def test_grouped_image_limits_end_to_end(sizes):
+    # every image within the checkers' LDS sort (5 x 4096), an image above
+    # it (the team runs the class and image passes too), an empty image
+    # beside a large one, and more images than the LDS holds offsets for
+    dev = device()
+    n = int(sum(sizes))
+    rng = np.random.default_rng(n + len(sizes))
+    scores = _tied_scores(n, n + 7)
+    cls = rng.integers(0, 50, n).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    note("grouped image limits, %d images, n=%d" % (len(sizes), n))
+    order, sorder = _g().debug_order(to_dev(scores, dev), to_dev(cls, dev), to_dev(offs, dev))
+    want, swant = _grouped_want(scores, cls, offs)
+    np.testing.assert_array_equal(order.cpu().numpy(), want)
+    np.testing.assert_array_equal(sorder.cpu().numpy(), swant)
+    base = workloads.random_small(900 + len(sizes), n, canvas=400.0, score_levels=9, classes=6)
+    w = workloads.Workload("grouped_limits", base.boxes, base.scores, 0.5, cls, offs)
+    want = oracle.c_nms(w.boxes, w.scores, w.iou_threshold, w.class_ids, w.batch_offsets)
+    np.testing.assert_array_equal(_nms(w, False), want)
