@@ -1003,7 +1003,7 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
 //   samples   member t keys its tile, checks its boxes and publishes their
 //             extent and the keys of SAMPLE_PER_MEMBER evenly spaced boxes
 //             (sample q is box q * stride, so its index needs no word).
-//   buckets   every member reads all samples (at most 1024, one per
+//   buckets   every member reads all samples (at most 512, one per
 //             thread), sorts them in LDS (stable by key, so equal keys stay
 //             in index order) and takes 255 of them as splitters, (key,
 //             index) pairs in that order.  A box's bucket
@@ -1026,7 +1026,7 @@ __global__ __launch_bounds__(NT) void team_sort_kernel(TeamArgs a) {
 // the host runs it again with the radix passes.  Words carry the call's tags
 // as in the radix passes; every wait is bounded.
 
-constexpr int SAMPLE_PER_MEMBER = 32;   // samples per member tile
+constexpr int SAMPLE_PER_MEMBER = 16;   // samples per member tile
 constexpr int BUCKETS = 256;
 constexpr int SORT_CAP = 4096;           // boxes one workgroup sorts in LDS
 // member's report word: a bucket was too large

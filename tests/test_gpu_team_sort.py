@@ -297,7 +297,7 @@ def test_sample_sort_sorted_and_reversed_inputs(n):
 
 def test_sample_sort_fallback_when_a_bucket_overflows():
     # One box in 16 scores high (a set that holds every box the sort samples:
-    # every 64th at 65,536 boxes) and every other box shares one low score:
+    # every 128th at 65,536 boxes) and every other box shares one low score:
     # all splitters fall among the high boxes and the last bucket takes the
     # low ones, more than one workgroup sorts in LDS.  The call runs again
     # with the radix passes; the result must not change.
